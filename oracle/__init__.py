@@ -1,0 +1,5 @@
+"""CPU oracle for the rank-ordered gather.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the library.  See ``oracle/oracle.py``.
+"""
