@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark of the rank-ordered gather on one MI355X.
+
+One step is one rog_gather of the bandwidth workload: W = 8 payloads of
+64 MiB (bf16 values uniform in [-1, 1]) gathered into a 512 MiB output, with
+inputs and output resident in HBM before the timed region.  The bytes one step
+moves are 2*W*S (every payload byte read once, every output byte written once).
+
+Timing follows the pages (RL-Align/RL-Kernel PR #491, "Results": events around
+each call, median of 100 calls): HIP events (torch.cuda.Event on the stream the
+kernels run on) bracket every call; the timed region is bracketed by device
+synchronisation.  Besides the headline line the run measures the latency of
+small gathers (the pages' 1 - 128 KiB per-rank sizes at 2 and 8 payloads), the
+batched gather (16 tensors, W = 4, one launch) and the device-to-device copy
+ceiling, and times the CPU oracle on a bounded sample of the same workload.
+
+Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "rank-ordered gather HBM GB/s (% of peak) + p50 µs at 1–128 KiB/payload"
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, AMD's published peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flat_kernel_w8x64MiB_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "deterministic_collective_movement_amd", "csrc", f)
+                  for f in ("rog_kernels.hip", "rog_internal.h", "rog_plan.cpp")]
+LATENCY_SIZES_KIB = (1, 8, 32, 128)
+
+
+# ---------------------------------------------------------------------------
+# Pure helpers (CPU-testable)
+# ---------------------------------------------------------------------------
+
+def percentile(xs, q):
+    """Linear-interpolated percentile (q in [0, 100]) of a non-empty sequence."""
+    s = sorted(xs)
+    if not s:
+        raise ValueError("empty sample")
+    k = (len(s) - 1) * q / 100.0
+    lo = int(k)
+    hi = min(lo + 1, len(s) - 1)
+    return s[lo] + (s[hi] - s[lo]) * (k - lo)
+
+
+def summarize_ms(samples_ms):
+    return {"p10_us": 1e3 * percentile(samples_ms, 10), "p50_us": 1e3 * percentile(samples_ms, 50),
+            "p90_us": 1e3 * percentile(samples_ms, 90), "mean_us": 1e3 * statistics.fmean(samples_ms),
+            "n": len(samples_ms)}
+
+
+def gbps(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def kernel_source_digest(paths=KERNEL_SOURCES):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic(path=TRAFFIC_FILE, digest=None):
+    """HBM bytes per launch of the headline kernel from the committed counter
+    summary, or None when there is none or the kernel sources changed since the
+    counters were taken."""
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_d = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_d or not m_t:
+        return None
+    if m_d.group(1) != (digest or kernel_source_digest()):
+        return None
+    return float(m_t.group(1))
+
+
+def roofline(alg_bytes, mean_launch_ms, traffic):
+    achieved = gbps(alg_bytes, mean_launch_ms)
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": None if traffic is None else int(traffic)}
+
+
+def build_line(*, value, steps, warmup, ms_per_step, config, roof, cpu, extras):
+    line = {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": config, "roofline": roof, "cpu_baseline": cpu}
+    line.update(extras)
+    return line
+
+
+# ---------------------------------------------------------------------------
+# GPU measurement
+# ---------------------------------------------------------------------------
+
+class Call:
+    """A prepared rog_gather call: ctypes arguments built once."""
+
+    def __init__(self, rog, srcs, out, stream):
+        self.lib = rog.lib()
+        self.W = len(srcs)
+        self.S = srcs[0].numel() * srcs[0].element_size()
+        self.ptrs = (ctypes.c_void_p * self.W)(*[s.data_ptr() for s in srcs])
+        self.out = ctypes.c_void_p(out.data_ptr())
+        self.stream = ctypes.c_void_p(stream)
+
+    def __call__(self):
+        st = self.lib.rog_gather(self.ptrs, self.W, self.S, self.out, self.stream)
+        if st != 0:
+            raise RuntimeError("rog_gather failed with status %d" % st)
+
+
+def time_calls(torch, fn, steps, warmup):
+    """Per-call event intervals (ms) and the whole region's elapsed ms."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    region0.record()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    region1.record()
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)], region0.elapsed_time(region1)
+
+
+def to_device(torch, arrays, device):
+    return [torch.from_numpy(a).to(device) for a in arrays]
+
+
+def headline(torch, rog, wl, device, steps, warmup):
+    case = wl.config4()
+    payloads = [case.payload(r) for r in range(case.W)]
+    srcs = to_device(torch, payloads, device)
+    out = torch.empty(case.W * case.S, dtype=torch.uint8, device=device)
+    plan = rog.rog_plan(srcs, out)
+    call = Call(rog, srcs, out, torch.cuda.current_stream(device).cuda_stream)
+    per_call, region_ms = time_calls(torch, call, steps, warmup)
+    # Sampled parity of the timed launch configuration (first and last KiB of
+    # every segment) against the definition.
+    for r in range(case.W):
+        for lo in (0, case.S - 1024):
+            got = out[r * case.S + lo: r * case.S + lo + 1024].cpu().numpy()
+            if not (got == payloads[r][lo:lo + 1024]).all():
+                raise AssertionError("headline gather mismatch at rank %d offset %d" % (r, lo))
+    return case, payloads, plan, per_call, region_ms
+
+
+def latency_sweep(torch, rog, wl, device, steps, warmup):
+    rows = []
+    cases = wl.config1() + [c for c in wl.config2() if c.S <= 128 * wl.KiB]
+    stream = torch.cuda.current_stream(device).cuda_stream
+    for case in cases:
+        srcs = to_device(torch, [case.payload(r) for r in range(case.W)], device)
+        out = torch.empty(case.W * case.S, dtype=torch.uint8, device=device)
+        plan = rog.rog_plan(srcs, out)
+        per_call, _ = time_calls(torch, Call(rog, srcs, out, stream), steps, warmup)
+        s = summarize_ms(per_call)
+        rows.append({"W": case.W, "S_KiB": case.S // wl.KiB, "path": plan["path"], "kernel": plan["kernel"],
+                     "p10_us": round(s["p10_us"], 2), "p50_us": round(s["p50_us"], 2),
+                     "p90_us": round(s["p90_us"], 2),
+                     "eff_GBps": round(gbps(2 * case.W * case.S, s["p50_us"] * 1e-3), 1)})
+    return rows
+
+
+def batch_bench(torch, rog, wl, device, steps, warmup):
+    case = wl.config5(0)
+    srcs = [to_device(torch, [case.payload(t, r) for r in range(case.W)], device)
+            for t in range(len(case.tensors))]
+    batch, outs = [], []
+    for t, x in enumerate(case.tensors):
+        # place every payload at its byte offset inside a slightly larger buffer
+        views = []
+        for s in srcs[t]:
+            buf = torch.empty(x.in_off + x.S, dtype=torch.uint8, device=device)
+            buf[x.in_off:].copy_(s)
+            views.append(buf[x.in_off:])
+        batch.append(views)
+        ob = torch.empty(x.out_off + case.W * x.S, dtype=torch.uint8, device=device)
+        outs.append(ob[x.out_off:])
+    del srcs
+    fn = lambda: rog.rog_gather_many(batch, outs)  # noqa: E731
+    per_call, _ = time_calls(torch, fn, steps, warmup)
+    s = summarize_ms(per_call)
+    moved = case.total_bytes_moved()
+    odd = sum(1 for x in case.tensors if x.in_off or x.out_off)
+    return {"W": case.W, "n": len(case.tensors), "odd_offset_tensors": odd, "bytes_moved": moved,
+            "p50_us": round(s["p50_us"], 1), "GBps": round(gbps(moved, s["p50_us"] * 1e-3), 1)}
+
+
+def d2d_ceiling(torch, device, nbytes, steps, warmup):
+    a = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    b = torch.empty_like(a)
+    per_call, _ = time_calls(torch, lambda: b.copy_(a), steps, warmup)
+    return {"bytes": nbytes, "GBps": round(gbps(2 * nbytes, statistics.median(per_call)), 1),
+            "how": "torch copy_ of one contiguous buffer (hipMemcpyAsync device to device)"}
+
+
+def cpu_baseline(case, payloads, budget_s):
+    """The CPU oracle, single-threaded, on the full headline gather repeated for
+    about ``budget_s`` seconds of CPU work."""
+    import numpy as np
+    from oracle import oracle
+    out = np.empty(case.W * case.S, np.uint8)
+    oracle.gather_c(payloads, out)                  # untimed first touch of `out`
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gather_c(payloads, out)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    moved = 2 * case.W * case.S * reps
+    return {"value": round(moved / el / 1e9, 2), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d x the full W=8 x 64 MiB gather (%.1f s, single-threaded C per-byte loop)"
+                      % (reps, el)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline gather (for counter runs)")
+    ap.add_argument("--calibrate-bytes", type=int, default=0,
+                    help="also run a plain elementwise copy of this many bytes, for counter scaling")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: --gpus %d is not supported (use --gpus 1)" % args.gpus,
+              file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+    from deterministic_collective_movement_amd import rog
+    from deterministic_collective_movement_amd import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+
+    case, payloads, plan, per_call, region_ms = headline(torch, rog, wl, device, args.steps, args.warmup)
+    alg_bytes = 2 * case.W * case.S
+    mean_launch_ms = statistics.fmean(per_call)
+    value = gbps(alg_bytes * args.steps, region_ms)
+    extras = {"headline": {"p50_us": round(1e3 * statistics.median(per_call), 2),
+                           "mean_launch_us": round(1e3 * mean_launch_ms, 2),
+                           "kernel": plan["kernel"], "path": plan["path"], "grid": plan["grid"],
+                           "block": plan["block"],
+                           "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2)}}
+    if args.calibrate_bytes:
+        a = torch.zeros(args.calibrate_bytes // 4, dtype=torch.int32, device=device)
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            torch.bitwise_not(a, out=b)
+        torch.cuda.synchronize()
+        extras["calibration"] = {"kernel": "torch.bitwise_not int32", "bytes_read": args.calibrate_bytes,
+                                 "bytes_written": args.calibrate_bytes, "launches": args.steps}
+    if not args.headline_only:
+        extras["latency"] = latency_sweep(torch, rog, wl, device, args.steps, args.warmup)
+        extras["gather_many"] = batch_bench(torch, rog, wl, device, max(5, args.steps // 5),
+                                            max(1, args.warmup // 5))
+        extras["d2d_copy_ceiling"] = d2d_ceiling(torch, device, case.W * case.S, 20, 3)
+        cpu = cpu_baseline(case, payloads, args.cpu_budget)
+    else:
+        cpu = None
+    extras["device"] = torch.cuda.get_device_name(device)
+    config = {"workload": "rank-ordered gather of W=8 aligned bf16 payloads of 64 MiB into a 512 MiB "
+                          "output (1 GiB moved per step)",
+              "W": case.W, "bytes_per_rank": case.S, "bytes_moved_per_step": alg_bytes}
+    line = build_line(value=value, steps=args.steps, warmup=args.warmup, ms_per_step=region_ms / args.steps,
+                      config=config, roof=roofline(alg_bytes, mean_launch_ms, read_traffic()),
+                      cpu=cpu, extras=extras)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

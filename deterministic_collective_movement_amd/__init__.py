@@ -6,13 +6,16 @@ The library is the C-ABI shared object ``librog.so`` (declared in
 the same entry-point names.  Attributes of the binding are reachable from the
 package itself (``dcm.rog_gather``); the library is loaded on first use.
 """
+import importlib
 
-__all__ = ["rog", "workloads"]
+__all__ = ["rog", "workloads", "build"]
 
 
 def __getattr__(name):
-    if name.startswith("rog_") or name in ("RogError", "ROG_PATH_AUTO", "ROG_PATH_SINGLE_WG",
-                                           "ROG_PATH_MULTI_WG", "library_path"):
-        from . import rog as _rog
-        return getattr(_rog, name)
-    raise AttributeError(name)
+    if name.startswith("__") or name in ("rog", "workloads", "build"):
+        raise AttributeError(name)
+    mod = importlib.import_module(__name__ + ".rog")
+    try:
+        return getattr(mod, name)
+    except AttributeError:
+        raise AttributeError(name) from None

@@ -1,0 +1,136 @@
+// rog_internal.h -- launch plans and kernel-argument layouts shared by the host
+// planner (rog_plan.cpp) and the HIP kernels (rog_kernels.hip).  Internal to
+// librog.so; the public interface is include/rog.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "rog.h"
+
+namespace rog {
+
+// Kernel-argument capacities.  Everything a launch needs travels in the kernel
+// arguments, so the library never allocates device memory.  The largest
+// argument block (BatchArgs) stays below 4 KiB.
+constexpr int kMaxPeers = 64;
+constexpr int kMaxBatch = 32;
+constexpr int kMaxBatchPtrs = 192;
+
+// Tunables.  Each has a default measured on MI355X; a variant build may
+// override one with -D for a sweep.
+#ifndef ROG_SINGLE_WG_MAX_BYTES
+#define ROG_SINGLE_WG_MAX_BYTES (16 * 1024)
+#endif
+#ifndef ROG_VEC_UNROLL
+#define ROG_VEC_UNROLL 4
+#endif
+#ifndef ROG_BYTE_UNROLL
+#define ROG_BYTE_UNROLL 16
+#endif
+#ifndef ROG_NONTEMPORAL
+#define ROG_NONTEMPORAL 0
+#endif
+#ifndef ROG_GRID_CAP
+#define ROG_GRID_CAP (1u << 30)
+#endif
+
+// Output bytes up to which ROG_PATH_AUTO uses the single-workgroup path
+// (inclusive), measured by sweeping both forced paths.
+constexpr size_t kSingleWgMaxBytes = ROG_SINGLE_WG_MAX_BYTES;
+
+// Launch shapes.
+constexpr int kMultiBlock = 256;    // threads per workgroup, multi-WG path (4 waves)
+constexpr int kSingleBlock = 1024;  // threads of the single workgroup (16 waves)
+constexpr int kVecUnroll = ROG_VEC_UNROLL;    // 16-byte vectors per lane per chunk
+constexpr int kByteUnroll = ROG_BYTE_UNROLL;  // bytes per lane per tile, byte path
+constexpr bool kNonTemporal = ROG_NONTEMPORAL != 0;
+constexpr uint32_t kGridCap = ROG_GRID_CAP;   // workgroups of one launch, at most
+
+// A 64-lane wave copies 64 * kVecUnroll consecutive vectors per chunk; every
+// load/store instruction of the chunk covers 64 consecutive vectors (1 KiB).
+constexpr uint32_t kChunkVecs = 64 * kVecUnroll;
+
+// Exact floor(v / d) for every 32-bit v by one 32x32 high multiply:
+// t = mulhi(v, magic); q = (t + ((v - t) >> sh1)) >> sh2.
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994, unsigned case with the 33-bit multiplier.)
+struct Divider {
+    uint32_t magic;
+    uint32_t sh1;
+    uint32_t sh2;
+};
+
+Divider make_divider(uint32_t d);
+
+// ---------------------------------------------------------------------------
+// Kernel arguments
+// ---------------------------------------------------------------------------
+
+// FLAT: the whole output is one space of n_vec 16-byte vectors; vector v comes
+// from payload r = v / vpr at index v - r*vpr.
+struct FlatArgs {
+    const void *src[kMaxPeers];
+    void *out;
+    uint32_t n_vec;
+    uint32_t vpr;
+    Divider div;
+};
+
+// PEER: each payload is its own copy job.  Payload r with bit r of vec_ok set is
+// copied as floor(S/16) vectors plus S%16 tail bytes, otherwise byte by byte.
+// Multi-WG: workgroup b works on payload b / blocks_per_peer; single-WG
+// (blocks_per_peer == 0): the one workgroup takes the payloads in turn.
+struct PeerArgs {
+    const void *src[kMaxPeers];
+    void *out;
+    uint64_t S;
+    uint64_t vec_ok;
+    uint32_t blocks_per_peer;
+    uint32_t W;
+};
+
+// One tensor of a batch.  Workgroups [first_block, first_block + n_blocks) of the
+// launch belong to it.
+struct BatchTensor {
+    uint64_t out;
+    uint64_t S;
+    uint64_t vec_ok;            // PEER tensors
+    uint32_t first_block;
+    uint32_t n_blocks;
+    uint32_t flat;              // 1: FLAT tensor, 0: PEER tensor
+    uint32_t vpr;               // FLAT: vectors per rank
+    uint32_t n_vec;             // FLAT: W * vpr
+    uint32_t blocks_per_peer;   // PEER
+    Divider div;                // FLAT
+    uint32_t pad;
+};
+
+struct BatchArgs {
+    const void *src[kMaxBatchPtrs];   // tensor t's payloads at [t*W, t*W + W)
+    BatchTensor t[kMaxBatch];
+    uint32_t n;
+    uint32_t W;
+};
+
+static_assert(sizeof(BatchArgs) <= 4096, "kernel arguments must stay below 4 KiB");
+
+// ---------------------------------------------------------------------------
+// Plans
+// ---------------------------------------------------------------------------
+
+struct Plan {
+    rog_plan_info info;
+    FlatArgs flat;
+    PeerArgs peer;
+};
+
+// Validate and plan one gather (no HIP calls).
+rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out,
+                       rog_path path, Plan *plan);
+
+// Validate and plan a batch (no HIP calls).  grid == 0 means nothing to launch.
+rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *args,
+                      uint32_t *grid);
+
+}  // namespace rog

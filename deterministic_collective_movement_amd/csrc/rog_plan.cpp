@@ -1,0 +1,223 @@
+// rog_plan.cpp -- argument validation, alignment classification, path dispatch
+// and grid sizing for the rank-ordered gather.  Pure host code: no HIP calls,
+// so every decision here can be checked on a machine without a GPU.
+//
+// Decisions follow RL-Align/RL-Kernel PR #491 ("perf(cuda): vectorize the
+// deterministic all-gather copy and right-size its single-block path"):
+//  * "What", copy_rank_ordered bullet: one flat loop over all peers' 16-byte
+//    vectors when the output, the size and every payload are 16-byte aligned;
+//    otherwise peers one by one, vectors where aligned, bytes for the rest.
+//  * "What", kAllGatherSingleBlockMaxBytes bullet: the single-block path is
+//    chosen by output size, inclusive; the bound here is measured on MI355X.
+//  * review thread on grid sizing: size the multi-block grid from the vector
+//    count when the aligned path applies, from the per-peer work otherwise.
+#include <limits.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "rog_internal.h"
+
+namespace rog {
+
+Divider make_divider(uint32_t d) {
+    // d >= 1.  l = ceil(log2 d); magic = floor(2^32 * (2^l - d) / d) + 1.
+    uint32_t l = 0;
+    while (l < 32 && (uint64_t(1) << l) < d) ++l;
+    const uint64_t magic = ((((uint64_t(1) << l) - d) << 32) / d) + 1;
+    Divider r;
+    r.magic = uint32_t(magic);
+    r.sh1 = l < 1 ? l : 1;
+    r.sh2 = l > 0 ? l - 1 : 0;
+    return r;
+}
+
+namespace {
+
+constexpr uint64_t kMaxOutputBytes = uint64_t(1) << 36;   // 2^32 vectors of 16 bytes
+
+inline uintptr_t addr(const void *p) { return reinterpret_cast<uintptr_t>(p); }
+
+inline uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+// [a, a+na) and [b, b+nb) share a byte.
+inline bool ranges_overlap(uintptr_t a, uint64_t na, uintptr_t b, uint64_t nb) {
+    return na && nb && a < b + nb && b < a + na;
+}
+
+// Shared checks of one gather: pointers, limits, address wrap, overlap.
+rog_status validate(const void *const *srcs, int W, size_t S, const void *out,
+                    uint64_t *total_out) {
+    if (!srcs || W < 1 || W > kMaxPeers) return ROG_ERR_INVALID_ARGUMENT;
+    if (S == 0) { *total_out = 0; return ROG_OK; }
+    if (!out) return ROG_ERR_INVALID_ARGUMENT;
+    for (int r = 0; r < W; ++r)
+        if (!srcs[r]) return ROG_ERR_INVALID_ARGUMENT;
+    if (S > SIZE_MAX / size_t(W)) return ROG_ERR_TOO_LARGE;
+    const uint64_t total = uint64_t(S) * uint64_t(W);
+    if (total >= kMaxOutputBytes) return ROG_ERR_TOO_LARGE;
+    const uintptr_t o = addr(out);
+    if (o > UINTPTR_MAX - total) return ROG_ERR_INVALID_ARGUMENT;
+    for (int r = 0; r < W; ++r) {
+        const uintptr_t s = addr(srcs[r]);
+        if (s > UINTPTR_MAX - S) return ROG_ERR_INVALID_ARGUMENT;
+        // The one overlap allowed: payload r already sits in its own segment.
+        if (ranges_overlap(s, S, o, total) && s != o + uint64_t(r) * S)
+            return ROG_ERR_OVERLAP;
+    }
+    *total_out = total;
+    return ROG_OK;
+}
+
+bool is_flat(const void *const *srcs, int W, size_t S, const void *out) {
+    uintptr_t bits = addr(out) | uintptr_t(S);
+    for (int r = 0; r < W; ++r) bits |= addr(srcs[r]);
+    return (bits & 15) == 0;
+}
+
+uint64_t vec_ok_mask(const void *const *srcs, int W, size_t S, const void *out) {
+    uint64_t m = 0;
+    for (int r = 0; r < W; ++r) {
+        const uintptr_t d = addr(out) + uintptr_t(r) * S;
+        if (((addr(srcs[r]) | d) & 15) == 0) m |= uint64_t(1) << r;
+    }
+    return m;
+}
+
+// Multi-WG FLAT grid: one wave per chunk of kChunkVecs vectors.
+uint32_t flat_blocks(uint64_t n_vec, uint32_t cap) {
+    const uint64_t chunks = ceil_div(n_vec, kChunkVecs);
+    return uint32_t(std::max<uint64_t>(1, std::min<uint64_t>(ceil_div(chunks, kMultiBlock / 64), cap)));
+}
+
+// Multi-WG PEER grid: workgroups per payload, enough for the largest payload's
+// work at one tile per workgroup (vector tiles for aligned payloads, byte tiles
+// for the others).
+uint32_t peer_blocks_per_peer(int W, size_t S, uint64_t vec_ok, uint32_t cap) {
+    uint64_t tiles = 1;
+    for (int r = 0; r < W; ++r) {
+        const uint64_t t = ((vec_ok >> r) & 1)
+            ? ceil_div(S / 16, uint64_t(kMultiBlock) * kVecUnroll)
+            : ceil_div(S, uint64_t(kMultiBlock) * kByteUnroll);
+        tiles = std::max(tiles, t);
+    }
+    return uint32_t(std::max<uint64_t>(1, std::min<uint64_t>(tiles, cap / uint32_t(W))));
+}
+
+}  // namespace
+
+rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out,
+                       rog_path path, Plan *plan) {
+    if (path != ROG_PATH_AUTO && path != ROG_PATH_SINGLE_WG && path != ROG_PATH_MULTI_WG)
+        return ROG_ERR_INVALID_ARGUMENT;
+    uint64_t total = 0;
+    const rog_status st = validate(srcs, W, S, out, &total);
+    if (st != ROG_OK) return st;
+
+    rog_plan_info &info = plan->info;
+    memset(&info, 0, sizeof(info));
+    if (path == ROG_PATH_AUTO)
+        path = total <= kSingleWgMaxBytes ? ROG_PATH_SINGLE_WG : ROG_PATH_MULTI_WG;
+    info.path = path;
+    if (total == 0) {
+        info.kernel = ROG_KERNEL_NONE;
+        return ROG_OK;
+    }
+    const bool single = path == ROG_PATH_SINGLE_WG;
+    info.block = single ? kSingleBlock : kMultiBlock;
+
+    if (is_flat(srcs, W, S, out)) {
+        FlatArgs &a = plan->flat;
+        memset(&a, 0, sizeof(a));
+        for (int r = 0; r < W; ++r) a.src[r] = srcs[r];
+        a.out = const_cast<void *>(out);
+        a.n_vec = uint32_t(total / 16);
+        a.vpr = uint32_t(S / 16);
+        a.div = make_divider(a.vpr);
+        info.kernel = ROG_KERNEL_FLAT;
+        info.units = a.n_vec;
+        info.grid = single ? 1 : flat_blocks(a.n_vec, kGridCap);
+        info.peer_magic = a.div.magic;
+        info.peer_sh1 = a.div.sh1;
+        info.peer_sh2 = a.div.sh2;
+    } else {
+        PeerArgs &a = plan->peer;
+        memset(&a, 0, sizeof(a));
+        for (int r = 0; r < W; ++r) a.src[r] = srcs[r];
+        a.out = const_cast<void *>(out);
+        a.S = S;
+        a.W = uint32_t(W);
+        a.vec_ok = vec_ok_mask(srcs, W, S, out);
+        a.blocks_per_peer = single ? 0 : peer_blocks_per_peer(W, S, a.vec_ok, kGridCap);
+        info.kernel = ROG_KERNEL_PEER;
+        info.vec_ok_mask = a.vec_ok;
+        for (int r = 0; r < W; ++r)
+            info.units += ((a.vec_ok >> r) & 1) ? S / 16 + S % 16 : S;
+        info.grid = single ? 1 : a.blocks_per_peer * uint32_t(W);
+    }
+    return ROG_OK;
+}
+
+rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *args,
+                      uint32_t *grid) {
+    *grid = 0;
+    if (n < 0 || W < 1 || W > kMaxPeers) return ROG_ERR_INVALID_ARGUMENT;
+    if (n > 0 && !descs) return ROG_ERR_INVALID_ARGUMENT;
+    if (n > kMaxBatch || n * W > kMaxBatchPtrs) return ROG_ERR_TOO_LARGE;
+
+    uint64_t totals[kMaxBatch];
+    for (int t = 0; t < n; ++t) {
+        const rog_status st = validate(descs[t].srcs, W, descs[t].bytes_per_rank,
+                                       descs[t].out, &totals[t]);
+        if (st != ROG_OK) return st;
+    }
+    // Work of different tensors runs concurrently: no output may overlap another
+    // tensor's output or another tensor's sources.
+    for (int t = 0; t < n; ++t) {
+        if (!totals[t]) continue;
+        const uintptr_t o = addr(descs[t].out);
+        for (int u = 0; u < n; ++u) {
+            if (u == t || !totals[u]) continue;
+            if (ranges_overlap(o, totals[t], addr(descs[u].out), totals[u])) return ROG_ERR_OVERLAP;
+            for (int r = 0; r < W; ++r)
+                if (ranges_overlap(o, totals[t], addr(descs[u].srcs[r]), descs[u].bytes_per_rank))
+                    return ROG_ERR_OVERLAP;
+        }
+    }
+
+    memset(args, 0, sizeof(*args));
+    args->W = uint32_t(W);
+    // Per-tensor workgroup cap keeps the launch's total below 2^31.
+    const uint32_t cap = std::min<uint32_t>(kGridCap, (1u << 31) / uint32_t(kMaxBatch) - 1);
+    uint64_t next = 0;
+    uint32_t k = 0;
+    for (int t = 0; t < n; ++t) {
+        if (!totals[t]) continue;           // empty tensors get no workgroups
+        const rog_gather_desc &d = descs[t];
+        const size_t S = d.bytes_per_rank;
+        BatchTensor &bt = args->t[k];
+        for (int r = 0; r < W; ++r) args->src[k * uint32_t(W) + uint32_t(r)] = d.srcs[r];
+        bt.out = addr(d.out);
+        bt.S = S;
+        bt.first_block = uint32_t(next);
+        if (is_flat(d.srcs, W, S, d.out)) {
+            bt.flat = 1;
+            bt.n_vec = uint32_t(totals[t] / 16);
+            bt.vpr = uint32_t(S / 16);
+            bt.div = make_divider(bt.vpr);
+            bt.n_blocks = flat_blocks(bt.n_vec, cap);
+        } else {
+            bt.flat = 0;
+            bt.vec_ok = vec_ok_mask(d.srcs, W, S, d.out);
+            bt.blocks_per_peer = peer_blocks_per_peer(W, S, bt.vec_ok, cap);
+            bt.n_blocks = bt.blocks_per_peer * uint32_t(W);
+        }
+        next += bt.n_blocks;
+        ++k;
+    }
+    args->n = k;
+    *grid = uint32_t(next);
+    return ROG_OK;
+}
+
+}  // namespace rog

@@ -1,0 +1,305 @@
+"""ctypes binding of librog.so (include/rog.h): argument marshalling only.
+
+Every byte is moved by the library's HIP kernels; this module turns torch
+tensors into device pointers, byte counts and the current HIP stream, and
+status codes into exceptions.  PyTorch provides device memory and streams.
+
+Entry points keep the C names.  Tensor forms:
+
+* ``rog_gather(srcs, out=None, stream=None)`` -> ``out`` (the same object);
+* ``rog_gather_ex(srcs, out, path, stream=None)`` -> ``out``;
+* ``rog_gather_many(batch, outs=None, stream=None)`` -> list of outputs;
+* ``rog_plan(srcs, out, path=ROG_PATH_AUTO)`` -> dict (no GPU work).
+
+Raw-pointer forms (``*_ptrs``) take integer device addresses, for callers that
+manage their own memory.
+
+Semantics follow RL-Align/RL-Kernel PR #491 ("perf(cuda): vectorize the
+deterministic all-gather copy and right-size its single-block path"):
+``all_gather(input, out=)`` returns ``out`` itself and hands offset views to
+the kernel without copying them (author's replies to the size-test review).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import torch  # loads the process's HIP runtime before librog.so binds to it
+
+from .build import LIB_PATH
+
+ROG_OK = 0
+ROG_ERR_INVALID_ARGUMENT = 1
+ROG_ERR_OVERLAP = 2
+ROG_ERR_TOO_LARGE = 3
+ROG_ERR_LAUNCH = 4
+
+ROG_PATH_AUTO = 0
+ROG_PATH_SINGLE_WG = 1
+ROG_PATH_MULTI_WG = 2
+
+ROG_KERNEL_NONE = 0
+ROG_KERNEL_FLAT = 1
+ROG_KERNEL_PEER = 2
+
+PATH_NAMES = {ROG_PATH_AUTO: "auto", ROG_PATH_SINGLE_WG: "single_wg", ROG_PATH_MULTI_WG: "multi_wg"}
+KERNEL_NAMES = {ROG_KERNEL_NONE: "none", ROG_KERNEL_FLAT: "flat", ROG_KERNEL_PEER: "peer"}
+
+
+class RogError(RuntimeError):
+    """A non-zero rog_status."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class RogArgumentError(RogError, ValueError):
+    pass
+
+
+class rog_gather_desc(ctypes.Structure):
+    _fields_ = [("srcs", ctypes.POINTER(ctypes.c_void_p)),
+                ("out", ctypes.c_void_p),
+                ("bytes_per_rank", ctypes.c_size_t)]
+
+
+class rog_plan_info(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("kernel", ctypes.c_int32),
+                ("grid", ctypes.c_uint32), ("block", ctypes.c_uint32),
+                ("vec_ok_mask", ctypes.c_uint64), ("units", ctypes.c_uint64),
+                ("peer_magic", ctypes.c_uint32), ("peer_sh1", ctypes.c_uint32),
+                ("peer_sh2", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+def _hip_runtimes_mapped() -> set:
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) >= 6 and os.path.basename(parts[-1]).startswith("libamdhip64.so"):
+                paths.add(os.path.realpath(parts[-1]))
+    return paths
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "librog.so is not built (%s); run __graft_entry__.build() or "
+            "python -m deterministic_collective_movement_amd.build" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError("two HIP runtimes are mapped (%s); librog.so must share torch's"
+                          % ", ".join(sorted(runtimes)))
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    ptrs = ctypes.POINTER(ctypes.c_void_p)
+    lib.rog_gather.argtypes = [ptrs, i32, sz, vp, vp]
+    lib.rog_gather_ex.argtypes = [ptrs, i32, sz, vp, vp, i32]
+    lib.rog_gather_many.argtypes = [ctypes.POINTER(rog_gather_desc), i32, i32, vp]
+    lib.rog_plan.argtypes = [ptrs, i32, sz, vp, i32, ctypes.POINTER(rog_plan_info)]
+    for name in ("rog_gather", "rog_gather_ex", "rog_gather_many", "rog_plan"):
+        getattr(lib, name).restype = i32
+    lib.rog_single_wg_max_bytes.argtypes = []
+    lib.rog_single_wg_max_bytes.restype = sz
+    for name in ("rog_max_peers", "rog_max_batch", "rog_max_batch_pointers", "rog_last_hip_error"):
+        getattr(lib, name).argtypes = []
+        getattr(lib, name).restype = i32
+    lib.rog_status_string.argtypes = [i32]
+    lib.rog_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status == ROG_OK:
+        return
+    name = _lib.rog_status_string(status).decode()
+    if status == ROG_ERR_LAUNCH:
+        raise RogError(status, "%s: %s (hipError_t %d)" % (what, name, _lib.rog_last_hip_error()))
+    if status in (ROG_ERR_INVALID_ARGUMENT, ROG_ERR_OVERLAP, ROG_ERR_TOO_LARGE):
+        raise RogArgumentError(status, "%s: %s" % (what, name))
+    raise RogError(status, "%s: %s" % (what, name))
+
+
+# ---------------------------------------------------------------------------
+# Constants
+# ---------------------------------------------------------------------------
+
+def rog_single_wg_max_bytes() -> int:
+    return int(_lib.rog_single_wg_max_bytes())
+
+
+def rog_max_peers() -> int:
+    return int(_lib.rog_max_peers())
+
+
+def rog_max_batch() -> int:
+    return int(_lib.rog_max_batch())
+
+
+def rog_max_batch_pointers() -> int:
+    return int(_lib.rog_max_batch_pointers())
+
+
+def rog_last_hip_error() -> int:
+    return int(_lib.rog_last_hip_error())
+
+
+def rog_status_string(status: int) -> str:
+    return _lib.rog_status_string(status).decode()
+
+
+# ---------------------------------------------------------------------------
+# Raw-pointer forms
+# ---------------------------------------------------------------------------
+
+def _ptr_array(addrs: Sequence[int]):
+    return (ctypes.c_void_p * max(1, len(addrs)))(*[ctypes.c_void_p(a) for a in addrs])
+
+
+def rog_gather_ptrs(src_ptrs: Sequence[int], bytes_per_rank: int, out_ptr: int,
+                    stream: int = 0, path: int = ROG_PATH_AUTO) -> None:
+    """rog_gather_ex on raw device addresses; raises on a non-zero status."""
+    st = _lib.rog_gather_ex(_ptr_array(src_ptrs), len(src_ptrs), bytes_per_rank,
+                            ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream), path)
+    _check(st, "rog_gather")
+
+
+def rog_plan_ptrs(src_ptrs: Sequence[int], bytes_per_rank: int, out_ptr: int,
+                  path: int = ROG_PATH_AUTO) -> dict:
+    """rog_plan on raw addresses (no HIP call); raises on a non-zero status."""
+    info = rog_plan_info()
+    st = _lib.rog_plan(_ptr_array(src_ptrs), len(src_ptrs), bytes_per_rank,
+                       ctypes.c_void_p(out_ptr), path, ctypes.byref(info))
+    _check(st, "rog_plan")
+    return {"path": PATH_NAMES[info.path], "kernel": KERNEL_NAMES[info.kernel],
+            "grid": info.grid, "block": info.block, "vec_ok_mask": info.vec_ok_mask,
+            "units": info.units, "peer_magic": info.peer_magic, "peer_sh1": info.peer_sh1,
+            "peer_sh2": info.peer_sh2}
+
+
+def rog_status_of_ptrs(src_ptrs: Optional[Sequence[int]], W: int, bytes_per_rank: int,
+                       out_ptr: int, path: int = ROG_PATH_AUTO) -> int:
+    """Status rog_plan returns for these arguments (``src_ptrs=None`` passes NULL)."""
+    info = rog_plan_info()
+    arr = None if src_ptrs is None else _ptr_array(src_ptrs)
+    return int(_lib.rog_plan(arr, W, bytes_per_rank, ctypes.c_void_p(out_ptr), path,
+                             ctypes.byref(info)))
+
+
+def rog_gather_many_ptrs(batch_ptrs: Sequence[Sequence[int]], sizes: Sequence[int],
+                         out_ptrs: Sequence[int], W: int, stream: int = 0) -> None:
+    """rog_gather_many on raw addresses: tensor t has W sources batch_ptrs[t]."""
+    n = len(out_ptrs)
+    keep = [_ptr_array(p) for p in batch_ptrs]
+    descs = (rog_gather_desc * max(1, n))()
+    for t in range(n):
+        descs[t].srcs = ctypes.cast(keep[t], ctypes.POINTER(ctypes.c_void_p))
+        descs[t].out = ctypes.c_void_p(out_ptrs[t])
+        descs[t].bytes_per_rank = sizes[t]
+    st = _lib.rog_gather_many(descs, n, W, ctypes.c_void_p(stream))
+    _check(st, "rog_gather_many")
+
+
+# ---------------------------------------------------------------------------
+# Tensor forms
+# ---------------------------------------------------------------------------
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check_tensor(t: torch.Tensor, what: str, device: torch.device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % what)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU (got %s)" % (what, t.device))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (what, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % what)
+
+
+def _stream_handle(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return int(stream.cuda_stream)
+    return int(stream)
+
+
+def _prepare(srcs: Sequence[torch.Tensor], out: Optional[torch.Tensor]):
+    if len(srcs) == 0:
+        raise ValueError("need at least one source tensor")
+    device = srcs[0].device
+    for i, s in enumerate(srcs):
+        _check_tensor(s, "srcs[%d]" % i, device)
+    S = _nbytes(srcs[0])
+    if any(_nbytes(s) != S for s in srcs):
+        raise ValueError("every source must hold the same number of bytes")
+    if out is None:
+        out = torch.empty(len(srcs) * S, dtype=torch.uint8, device=device)
+    _check_tensor(out, "out", device)
+    if _nbytes(out) != len(srcs) * S:
+        raise ValueError("out must hold exactly W*S = %d bytes (has %d)" % (len(srcs) * S, _nbytes(out)))
+    return device, S, out
+
+
+def rog_gather_ex(srcs: Sequence[torch.Tensor], out: Optional[torch.Tensor] = None,
+                  path: int = ROG_PATH_AUTO, stream=None) -> torch.Tensor:
+    """Rank-ordered gather of equal-size tensors into ``out`` with the path forced."""
+    device, S, out = _prepare(srcs, out)
+    rog_gather_ptrs([s.data_ptr() for s in srcs], S, out.data_ptr(),
+                    _stream_handle(stream, device), path)
+    return out
+
+
+def rog_gather(srcs: Sequence[torch.Tensor], out: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """Rank-ordered gather: out[r*S:(r+1)*S] = bytes of srcs[r].  Returns ``out``."""
+    return rog_gather_ex(srcs, out, ROG_PATH_AUTO, stream)
+
+
+def rog_plan(srcs: Sequence[torch.Tensor], out: torch.Tensor, path: int = ROG_PATH_AUTO) -> dict:
+    """The launch rog_gather_ex would make for these tensors (no GPU work)."""
+    device, S, out = _prepare(srcs, out)
+    return rog_plan_ptrs([s.data_ptr() for s in srcs], S, out.data_ptr(), path)
+
+
+def rog_gather_many(batch: Sequence[Sequence[torch.Tensor]],
+                    outs: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                    stream=None) -> List[torch.Tensor]:
+    """Gather every tensor list ``batch[t]`` (W tensors each) into ``outs[t]``, one launch."""
+    n = len(batch)
+    if outs is None:
+        outs = [None] * n
+    if len(outs) != n:
+        raise ValueError("one output per tensor")
+    if n == 0:
+        return []
+    W = len(batch[0])
+    if any(len(b) != W for b in batch):
+        raise ValueError("every tensor of a batch has the same number of sources")
+    device = batch[0][0].device
+    ready, sizes = [], []
+    for t in range(n):
+        _, S, o = _prepare(batch[t], outs[t])
+        if batch[t][0].device != device:
+            raise ValueError("all tensors of a batch must be on one device")
+        ready.append(o)
+        sizes.append(S)
+    rog_gather_many_ptrs([[s.data_ptr() for s in b] for b in batch], sizes,
+                         [o.data_ptr() for o in ready], W, _stream_handle(stream, device))
+    return ready

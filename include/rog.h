@@ -1,0 +1,174 @@
+/*
+ * rog.h -- rank-ordered gather (rog) for MI355X (gfx950, CDNA4).
+ *
+ * C ABI of librog.so.  Plain C types, device pointers and sizes; no PyTorch
+ * types.  Every entry point below is implemented by hand-written HIP kernels in
+ * deterministic_collective_movement_amd/csrc/.
+ *
+ * The operation is the copy at the heart of a deterministic all-gather
+ * (RL-Align/RL-Kernel PR #491, "perf(cuda): vectorize the deterministic
+ * all-gather copy and right-size its single-block path", section "What", the
+ * copy_rank_ordered bullet): W payloads of S bytes are concatenated in rank
+ * order, so that
+ *
+ *     out[r*S + i] = srcs[r][i]     for 0 <= r < W, 0 <= i < S,
+ *
+ * byte-identical to a plain concatenation for every alignment and size.  On one
+ * GPU the W "peer payloads" are W caller-owned device buffers.
+ *
+ * Common rules for every entry point:
+ *  - Pointers to data (srcs[r], out, the descriptors' buffers) are device
+ *    pointers readable/writable by kernels on the current HIP device.  They are
+ *    not checked for residency; the Python binding checks tensor devices.
+ *  - Host arrays (the srcs array, the descriptor array) are read only during
+ *    the call; their contents are copied into the kernel arguments.
+ *  - The caller owns every buffer; buffers must stay valid until the work
+ *    enqueued on `stream` has completed.
+ *  - All argument errors are returned before anything is enqueued: on error no
+ *    byte of any output is written and no HIP call has been made.
+ *  - Success means the copy has been enqueued on `stream` (asynchronous).
+ *  - The library allocates no device or host memory, keeps no state except a
+ *    thread-local copy of the last HIP error, and may be called from any thread.
+ *  - Bytes outside [out, out + W*S) are never written.  Source bytes are never
+ *    written.  Reads are confined to the source ranges.
+ */
+#ifndef ROG_H
+#define ROG_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ROG_API __attribute__((visibility("default")))
+
+typedef enum {
+    ROG_OK = 0,
+    ROG_ERR_INVALID_ARGUMENT = 1, /* null pointer, W out of range, n < 0, bad path  */
+    ROG_ERR_OVERLAP = 2,          /* a source range partially overlaps the output   */
+    ROG_ERR_TOO_LARGE = 3,        /* size overflow or a limit below exceeded        */
+    ROG_ERR_LAUNCH = 4            /* the kernel launch failed; see rog_last_hip_error */
+} rog_status;
+
+typedef enum {
+    ROG_PATH_AUTO = 0,       /* single-WG iff W*S <= rog_single_wg_max_bytes()  */
+    ROG_PATH_SINGLE_WG = 1,  /* one 1024-thread workgroup copies the whole output */
+    ROG_PATH_MULTI_WG = 2    /* a grid of 256-thread workgroups sized from the work */
+} rog_path;
+
+typedef enum {
+    ROG_KERNEL_NONE = 0,     /* nothing to copy (S == 0): nothing is launched       */
+    ROG_KERNEL_FLAT = 1,     /* one flat loop over all peers' 16-byte vectors        */
+    ROG_KERNEL_PEER = 2      /* peers in turn: vectors where aligned, bytes otherwise */
+} rog_kernel;
+
+/* One tensor of a batch: W source pointers, its output, its per-rank bytes. */
+typedef struct {
+    const void *const *srcs;   /* W device pointers (host array)                 */
+    void *out;                 /* device pointer to W * bytes_per_rank bytes     */
+    size_t bytes_per_rank;     /* S of this tensor; 0 is allowed (nothing copied) */
+} rog_gather_desc;
+
+/* The launch a call would make (rog_plan), for tests and inspection. */
+typedef struct {
+    int32_t path;              /* resolved rog_path: SINGLE_WG or MULTI_WG (AUTO never) */
+    int32_t kernel;            /* rog_kernel                                            */
+    uint32_t grid;             /* workgroups launched (0 when kernel == NONE)           */
+    uint32_t block;            /* threads per workgroup                                 */
+    uint64_t vec_ok_mask;      /* PEER kernel: bit r set iff srcs[r] and out + r*S are
+                                  both 16-byte aligned (vector body + byte tail)        */
+    uint64_t units;            /* FLAT: 16-byte vectors W*S/16; PEER: total copy units   */
+    uint32_t peer_magic;       /* FLAT: floor(v / (S/16)) = (t + ((v - t) >> peer_sh1))  */
+    uint32_t peer_sh1;         /*       >> peer_sh2 with t = mulhi32(v, peer_magic),     */
+    uint32_t peer_sh2;         /*       exact for every 32-bit v                         */
+    uint32_t reserved;
+} rog_plan_info;
+
+/*
+ * rog_gather -- out[r*S + i] = srcs[r][i] for r < W, i < S, enqueued on `stream`.
+ *
+ * srcs            host array of W device pointers (payload r = rank r).
+ * W               number of payloads, 1 <= W <= rog_max_peers().
+ * bytes_per_rank  S, the byte size of every payload (one S for all, as in an
+ *                 all-gather; PR #491 "What": "the per-rank byte count").
+ * out             device pointer to W*S writable bytes.
+ * stream          HIP stream (0 = null stream) of the current device.
+ *
+ * Path: single-workgroup when W*S <= rog_single_wg_max_bytes(), multi-workgroup
+ * otherwise (PR #491 "What", kAllGatherSingleBlockMaxBytes bullet: a one-block
+ * gather copies the whole output alone and wins only for small outputs; the
+ * crossover here is measured on gfx950).  Kernel: FLAT when out, S and every
+ * srcs[r] are 16-byte aligned, else PEER (PR #491 "What", copy_rank_ordered).
+ *
+ * Errors (nothing enqueued):
+ *   ROG_ERR_INVALID_ARGUMENT  srcs NULL; W < 1 or W > rog_max_peers(); S > 0 and
+ *                             out or some srcs[r] NULL.
+ *   ROG_ERR_OVERLAP           some [srcs[r], srcs[r]+S) overlaps [out, out+W*S)
+ *                             other than exactly (srcs[r] == out + r*S, in place).
+ *   ROG_ERR_TOO_LARGE         W*S overflows, or W*S >= 2^36 (64 GiB).
+ *   ROG_ERR_LAUNCH            hipLaunchKernel failed (rog_last_hip_error()).
+ * S == 0: ROG_OK, nothing enqueued.  Sources may alias one another.
+ */
+ROG_API rog_status rog_gather(const void *const *srcs, int W, size_t bytes_per_rank,
+                              void *out, hipStream_t stream);
+
+/*
+ * rog_gather_ex -- rog_gather with the path forced.  ROG_PATH_AUTO behaves
+ * exactly like rog_gather.  Forcing SINGLE_WG or MULTI_WG changes only the launch
+ * shape, never the bytes written; it lets tests reach each path on every case
+ * (the pages' review of the size test asks that the otherwise unreachable
+ * single-block branch be covered).  path outside rog_path: INVALID_ARGUMENT.
+ */
+ROG_API rog_status rog_gather_ex(const void *const *srcs, int W, size_t bytes_per_rank,
+                                 void *out, hipStream_t stream, rog_path path);
+
+/*
+ * rog_gather_many -- n independent gathers sharing W, in one kernel launch.
+ * Tensor t: out_t[r*S_t + i] = srcs_t[r][i].  The pages' all_gather_many
+ * (PR #491 review threads on the benchmark) gathers a list of tensors with one
+ * handshake and no packing; here every tensor keeps its own caller-provided
+ * output and its own alignment class (flat or per-peer).
+ *
+ * descs  host array of n descriptors (each with a host array of W pointers).
+ * n      0 <= n <= rog_max_batch(); n == 0 or all S_t == 0: ROG_OK, nothing
+ *        enqueued.  n*W must not exceed rog_max_batch_pointers().
+ * Errors: as rog_gather for each tensor; outputs of different tensors must not
+ * overlap each other (ROG_ERR_OVERLAP), and a tensor's sources must not overlap
+ * another tensor's output; limits exceeded: ROG_ERR_TOO_LARGE.
+ */
+ROG_API rog_status rog_gather_many(const rog_gather_desc *descs, int n, int W,
+                                   hipStream_t stream);
+
+/*
+ * rog_plan -- validate exactly as rog_gather_ex and describe the launch it would
+ * make, without any HIP call.  info must be non-NULL (else INVALID_ARGUMENT).
+ * Pointers are only inspected as addresses.
+ */
+ROG_API rog_status rog_plan(const void *const *srcs, int W, size_t bytes_per_rank,
+                            const void *out, rog_path path, rog_plan_info *info);
+
+/* Output bytes up to which ROG_PATH_AUTO takes the single-workgroup path
+ * (inclusive), measured on MI355X. */
+ROG_API size_t rog_single_wg_max_bytes(void);
+
+/* Largest W accepted (kernel-argument capacity). */
+ROG_API int rog_max_peers(void);
+
+/* Largest n accepted by rog_gather_many, and the largest n*W. */
+ROG_API int rog_max_batch(void);
+ROG_API int rog_max_batch_pointers(void);
+
+/* hipError_t of the last failed launch on this thread (0 if none). */
+ROG_API int rog_last_hip_error(void);
+
+/* Static, human-readable name of a status code ("ROG_OK", ...). */
+ROG_API const char *rog_status_string(rog_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROG_H */

@@ -1,0 +1,115 @@
+"""bench.py's arithmetic and JSON contract on the CPU, with made-up timings
+(the idea of the pages' benchmark unit tests, which run the harness against a
+mocked event class: RL-Align/RL-Kernel PR #491, author's replies on the
+benchmark tests)."""
+from __future__ import annotations
+
+import json
+import os
+
+import pytest
+
+import bench
+
+
+def test_percentile_and_summary():
+    xs = [5.0, 1.0, 3.0, 2.0, 4.0]
+    assert bench.percentile(xs, 50) == 3.0
+    assert bench.percentile(xs, 0) == 1.0
+    assert bench.percentile(xs, 100) == 5.0
+    assert bench.percentile(xs, 25) == 2.0
+    assert bench.percentile([7.0], 90) == 7.0
+    s = bench.summarize_ms([0.010, 0.020, 0.030])
+    assert s["p50_us"] == pytest.approx(20.0)
+    assert s["n"] == 3
+    with pytest.raises(ValueError):
+        bench.percentile([], 50)
+
+
+def test_gbps_and_roofline():
+    # 1 GiB moved in 0.2 ms
+    one_gib = 1 << 30
+    assert bench.gbps(one_gib, 0.2) == pytest.approx(one_gib / 2e-4 / 1e9)
+    r = bench.roofline(one_gib, 0.2, traffic=1.07e9)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert r["frac"] == pytest.approx(r["achieved"] / 8000.0, rel=1e-3)
+    assert r["traffic"] == 1070000000
+    assert bench.roofline(one_gib, 0.2, traffic=None)["traffic"] is None
+
+
+def test_json_line_contract():
+    line = bench.build_line(value=5000.0, steps=100, warmup=10, ms_per_step=0.2,
+                            config={"workload": "x"}, roof=bench.roofline(1 << 30, 0.2, None),
+                            cpu={"value": 1.0, "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": "s"},
+                            extras={"latency": []})
+    s = json.dumps(line)
+    back = json.loads(s)
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+              "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert k in back, k
+    assert back["metric"] == json.load(open(os.path.join(bench.ROOT, "BASELINE.json")))["metric"]
+    assert back["n_gpus"] == 1 and back["higher_is_better"] is True and back["vs_baseline"] is None
+    assert back["config"]["workload"] == "x"
+    assert "model" not in back["config"]
+
+
+def test_traffic_file_is_ignored_when_kernel_sources_change(tmp_path):
+    digest = bench.kernel_source_digest()
+    p = tmp_path / "t.md"
+    p.write_text("kernel_source_sha256: %s\ntraffic_bytes_per_launch: 1.1e9\n" % digest)
+    assert bench.read_traffic(str(p), digest) == pytest.approx(1.1e9)
+    assert bench.read_traffic(str(p), "0" * 64) is None
+    assert bench.read_traffic(str(tmp_path / "missing.md"), digest) is None
+    p.write_text("nothing here\n")
+    assert bench.read_traffic(str(p), digest) is None
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
+
+
+def test_bad_step_counts_are_refused():
+    assert bench.main(["--steps", "0"]) == 2
+    assert bench.main(["--warmup", "-1"]) == 2
+
+
+class FakeEvent:
+    """Stands in for torch.cuda.Event: times come from a scripted clock."""
+    clock = [0.0]
+
+    def __init__(self, enable_timing=True):
+        self.t = None
+
+    def record(self):
+        self.t = FakeEvent.clock[0]
+
+    def elapsed_time(self, other):
+        return other.t - self.t
+
+
+class FakeCuda:
+    Event = FakeEvent
+
+    @staticmethod
+    def synchronize():
+        pass
+
+
+class FakeTorch:
+    cuda = FakeCuda
+
+
+def test_time_calls_attributes_each_interval_to_its_call():
+    durations = [0.5, 0.25, 1.0, 0.125]
+    calls = []
+
+    def fn():
+        i = len(calls)
+        calls.append(i)
+        FakeEvent.clock[0] += durations[i - 2] if i >= 2 else 7.0   # 2 warmups
+    FakeEvent.clock[0] = 0.0
+    per_call, region = bench.time_calls(FakeTorch, fn, steps=4, warmup=2)
+    assert per_call == durations
+    assert region == pytest.approx(sum(durations))
+    assert len(calls) == 6

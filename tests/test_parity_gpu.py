@@ -1,0 +1,241 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, every byte
+of every guarded buffer, on every forced path (auto, single-WG, multi-WG).
+
+Cases are the workloads of the pages (RL-Align/RL-Kernel PR #491 "Results" and
+"Tests"): the 2-payload 1 KiB gather, the size sweep at 2 and 8 payloads, the
+alignment/tail sweep with odd offsets, the 8 x 64 MiB bandwidth case, the
+batched gather, the pages' own size-test sizes, and edge cases (empty,
+single payload, the maximum W, in place, aliased sources, payload boundaries
+inside a wave's chunk).
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from deterministic_collective_movement_amd import rog
+from deterministic_collective_movement_amd import workloads as wl
+from tests import gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def test_config1_two_1k_payloads(gpu):
+    (case,) = wl.config1()
+    gc.run_all_paths(gc.place_case(case, gpu), case.label())
+
+
+@pytest.mark.parametrize("case", wl.config2(), ids=lambda c: c.label())
+def test_config2_size_sweep(gpu, case):
+    gc.run_all_paths(gc.place_case(case, gpu), case.label())
+
+
+@pytest.mark.parametrize("case", wl.config3(), ids=lambda c: c.label())
+def test_config3_alignment_and_tails(gpu, case):
+    placed = gc.place_case(case, gpu)
+    gc.run_all_paths(placed, case.label())
+
+
+def test_config4_bandwidth_case_full_output(gpu):
+    case = wl.config4()
+    placed = gc.place_case(case, gpu)
+    plan = rog.rog_plan(placed.srcs, placed.out)
+    assert plan["kernel"] == "flat" and plan["path"] == "multi_wg"
+    gc.run_all_paths(placed, case.label())
+
+
+def test_config5_batched_one_launch(gpu):
+    case = wl.config5(0)
+    gc.place_batch(case, gpu).run("c5#0 W=4 n=16")
+
+
+@pytest.mark.parametrize("index", range(1, 9))
+def test_batched_small_mixes(gpu, index):
+    """Batches of small tensors: flat and per-peer tensors side by side, empty
+    tensors, W in {1, 3, 4, 8}."""
+    W = (1, 3, 4, 8)[index % 4]
+    case = wl.config5(index, n=12, W=W, max_rows=40)
+    pb = gc.place_batch(case, gpu)
+    pb.run("c5#%d small W=%d" % (index, W))
+
+
+def test_batched_with_empty_tensors_and_mixed_sizes(gpu):
+    rng = np.random.default_rng(17)
+    W = 3
+    sizes = [0, 16, 1, 4096, 0, 17, 65536, 255, 0]
+    payloads = [[np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(W)] for S in sizes]
+    in_offs = [0, 0, 3, 0, 1, 8, 0, 1, 0]
+    out_offs = [0, 0, 1, 8, 0, 8, 0, 3, 5]
+    gc.PlacedBatch(W, payloads, in_offs, out_offs, gpu).run("batch mixed")
+
+
+def test_batched_maximum_batch(gpu):
+    n = rog.rog_max_batch()
+    W = rog.rog_max_batch_pointers() // n
+    rng = np.random.default_rng(23)
+    sizes = [int(rng.integers(1, 3000)) * 16 + (t % 3) for t in range(n)]
+    payloads = [[np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(W)] for S in sizes]
+    gc.PlacedBatch(W, payloads, [t % 2 for t in range(n)], [0] * n, gpu).run("batch max n=%d W=%d" % (n, W))
+
+
+def _page_sizes():
+    out = []
+    with open(os.path.join(GOLDEN, "page_sizes.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                out.append(int(line))
+    return out
+
+
+@pytest.mark.parametrize("W", (2, 8))
+@pytest.mark.parametrize("S", _page_sizes())
+@pytest.mark.parametrize("offs", [(0, 0), (1, 3), (8, 8)])
+def test_page_test_sizes(gpu, W, S, offs):
+    case = wl.GatherCase(6, S * 10 + W, W, S, (offs[0],) * W, offs[1])
+    gc.run_all_paths(gc.place_case(case, gpu), case.label())
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+
+def test_zero_bytes_writes_nothing(gpu):
+    placed = gc.Placed([np.zeros(0, np.uint8)] * 3, [0, 1, 2], 3, gpu)
+    gc.run_all_paths(placed, "S=0")
+
+
+@pytest.mark.parametrize("S", [1, 16, 1000, 4096, 1 << 20])
+def test_single_payload_is_a_copy(gpu, S):
+    case = wl.GatherCase(7, S, 1, S, (0,), 0)
+    gc.run_all_paths(gc.place_case(case, gpu), case.label())
+
+
+@pytest.mark.parametrize("S", [1, 15, 16, 48, 4096 + 3])
+def test_maximum_W(gpu, S):
+    W = rog.rog_max_peers()
+    case = wl.GatherCase(8, S, W, S, tuple(r % 4 for r in range(W)) if S % 16 else (0,) * W, 0)
+    gc.run_all_paths(gc.place_case(case, gpu), case.label())
+
+
+@pytest.mark.parametrize("W,vpr", [(8, 1), (64, 1), (5, 3), (3, 255), (3, 257), (7, 1000), (2, 64 * 4 * 4 + 1)])
+def test_payload_boundaries_inside_wave_chunks(gpu, W, vpr):
+    """FLAT: payloads of vpr vectors, so chunks of 64*U vectors straddle one or
+    many payload boundaries."""
+    S = 16 * vpr
+    payloads = [wl.tagged_payload(r, S) for r in range(W)]
+    placed = gc.Placed(payloads, [0] * W, 0, gpu)
+    assert rog.rog_plan(placed.srcs, placed.out)["kernel"] == "flat"
+    gc.run_all_paths(placed, "tagged W=%d vpr=%d" % (W, vpr))
+
+
+@pytest.mark.parametrize("S,W", [(16 * 1000, 4), (4095, 3), (1 << 20, 8)])
+def test_exact_in_place_segments(gpu, S, W):
+    """Payloads 1 and 3 already sit in their own output segments."""
+    rng = np.random.default_rng(S + W)
+    payloads = [np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(W)]
+    placed = gc.Placed(payloads, [0] * W, 0, gpu)
+    for path in gc.PATHS:
+        placed.reset_output()
+        srcs = list(placed.srcs)
+        for r in (1, 3):
+            if r < W:
+                placed.out[r * S:(r + 1) * S].copy_(placed.srcs[r])
+                srcs[r] = placed.out[r * S:(r + 1) * S]
+        rog.rog_gather_ex(srcs, placed.out, path)
+        placed.check("in place S=%d W=%d path=%d" % (S, W, path))
+
+
+def test_aliased_sources(gpu):
+    rng = np.random.default_rng(31)
+    S = 12345
+    p = np.frombuffer(rng.bytes(S), np.uint8).copy()
+    placed = gc.Placed([p], [1], 0, gpu)
+    out = torch.full((4 * S,), 0, dtype=torch.uint8, device=gpu)
+    for path in gc.PATHS:
+        out.zero_()
+        rog.rog_gather_ex([placed.srcs[0]] * 4, out, path)
+        torch.cuda.synchronize()
+        assert out.cpu().numpy().tobytes() == p.tobytes() * 4
+
+
+def test_returns_out_and_allocates_when_absent(gpu):
+    a = torch.arange(64, dtype=torch.int16, device=gpu)
+    b = -a
+    out = rog.rog_gather([a, b])
+    torch.cuda.synchronize()
+    assert out.dtype == torch.uint8 and out.numel() == 256
+    assert torch.equal(out.view(torch.int16), torch.cat([a, b]))
+    o2 = torch.empty(128, dtype=torch.int16, device=gpu)
+    assert rog.rog_gather([a, b], out=o2) is o2
+
+
+def test_runs_on_the_given_stream(gpu):
+    s = torch.cuda.Stream(device=gpu)
+    a = torch.randint(0, 255, (1 << 20,), dtype=torch.uint8, device=gpu)
+    b = torch.randint(0, 255, (1 << 20,), dtype=torch.uint8, device=gpu)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        out = rog.rog_gather([a, b])
+    s.synchronize()
+    assert torch.equal(out, torch.cat([a, b]))
+
+
+def test_binding_rejects_bad_tensors(gpu):
+    a = torch.zeros(16, dtype=torch.uint8, device=gpu)
+    with pytest.raises(ValueError):
+        rog.rog_gather([a, torch.zeros(17, dtype=torch.uint8, device=gpu)])
+    with pytest.raises(ValueError):
+        rog.rog_gather([a, a], out=torch.zeros(31, dtype=torch.uint8, device=gpu))
+    with pytest.raises(ValueError):
+        rog.rog_gather([a, torch.zeros(16, dtype=torch.uint8)])
+    with pytest.raises(ValueError):
+        rog.rog_gather([a, a], out=torch.zeros(64, dtype=torch.uint8, device=gpu)[::2])
+    with pytest.raises(rog.RogArgumentError):
+        buf = torch.zeros(64, dtype=torch.uint8, device=gpu)
+        rog.rog_gather([buf[8:24], a], out=buf[0:32])
+
+
+def test_largest_vector_index(gpu):
+    """FLAT at the top of the 32-bit vector index: W*S just below 2^36 bytes.
+    Checked at full size through properties that hold at any size: sampled
+    windows at both ends of every segment, across payload boundaries and at the
+    very end of the output equal the corresponding source bytes."""
+    W = 8
+    S = (1 << 33) - 16                     # 8 GiB - 16 per payload
+    total = W * S                          # 2^36 - 128 bytes: n_vec = 2^32 - 8
+    free, _ = torch.cuda.mem_get_info(gpu)
+    if free < 2 * total + (8 << 30):
+        pytest.skip("needs %d GiB of free device memory" % ((2 * total >> 30) + 8))
+    srcs = []
+    for r in range(W):
+        t = torch.empty(S, dtype=torch.uint8, device=gpu)
+        t.fill_(r * 29 + 7)
+        srcs.append(t)
+    rng = np.random.default_rng(99)
+    win = 4096
+    windows = [0, S - win, S // 2]
+    for r in range(W):
+        for lo in windows:
+            srcs[r][lo:lo + win].copy_(torch.from_numpy(np.frombuffer(rng.bytes(win), np.uint8).copy()))
+    out = torch.empty(total, dtype=torch.uint8, device=gpu)
+    assert rog.rog_plan(srcs, out)["kernel"] == "flat"
+    print("largest vector index W=8 S=%d" % S, flush=True)
+    rog.rog_gather(srcs, out)
+    torch.cuda.synchronize()
+    for r in range(W):
+        for lo in windows:
+            got = out[r * S + lo: r * S + lo + win].cpu()
+            want = srcs[r][lo:lo + win].cpu()
+            assert torch.equal(got, want), (r, lo)
+    # the filled stretches between windows carry the per-rank fill value
+    for r in range(W):
+        mid = out[r * S + win: r * S + win + (1 << 20)].cpu()
+        assert torch.all(mid == r * 29 + 7)
+    del out, srcs
+    torch.cuda.empty_cache()
