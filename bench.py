@@ -6,10 +6,12 @@ One step is one rog_gather of the bandwidth workload: W = 8 payloads of
 inputs and output resident in HBM before the timed region.  The bytes one step
 moves are 2*W*S (every payload byte read once, every output byte written once).
 
-Timing follows the pages (RL-Align/RL-Kernel PR #491, "Results": events around
-each call, median of 100 calls): HIP events (torch.cuda.Event on the stream the
-kernels run on) bracket every call; the timed region is bracketed by device
-synchronisation.  Besides the headline line the run measures the latency of
+The timed region is K back-to-back calls bracketed by device synchronisation and
+two HIP events on the calls' stream (torch.cuda.Event on torch's current stream,
+which the calls use); ``value`` and the kernel's average launch duration come
+from it.  A second, untimed pass brackets every call with its own events, as
+the pages time each call (RL-Align/RL-Kernel PR #491, "Results": median of 100
+calls), for the per-call p50.  Besides the headline line the run measures the latency of
 small gathers (the pages' 1 - 128 KiB per-rank sizes at 2 and 8 payloads), the
 batched gather (16 tensors, W = 4, one launch) and the device-to-device copy
 ceiling, and times the CPU oracle on a bounded sample of the same workload.
@@ -126,8 +128,25 @@ class Call:
             raise RuntimeError("rog_gather failed with status %d" % st)
 
 
+def time_region(torch, fn, steps, warmup):
+    """Elapsed ms of ``steps`` back-to-back calls, bracketed by synchronisation
+    and two events on the calls' stream (the timed region)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1)
+
+
 def time_calls(torch, fn, steps, warmup):
-    """Per-call event intervals (ms) and the whole region's elapsed ms."""
+    """Per-call event intervals (ms), as the pages time each call, and the
+    elapsed ms of the whole sequence."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -157,7 +176,8 @@ def headline(torch, rog, wl, device, steps, warmup):
     out = torch.empty(case.W * case.S, dtype=torch.uint8, device=device)
     plan = rog.rog_plan(srcs, out)
     call = Call(rog, srcs, out, torch.cuda.current_stream(device).cuda_stream)
-    per_call, region_ms = time_calls(torch, call, steps, warmup)
+    region_ms = time_region(torch, call, steps, warmup)
+    per_call, _ = time_calls(torch, call, steps, 0)
     # Sampled parity of the timed launch configuration (first and last KiB of
     # every segment) against the definition.
     for r in range(case.W):
@@ -218,6 +238,45 @@ def d2d_ceiling(torch, device, nbytes, steps, warmup):
             "how": "torch copy_ of one contiguous buffer (hipMemcpyAsync device to device)"}
 
 
+CROSSOVER_TOTALS = (256, 1024, 4096, 8192, 16384, 32768, 40960, 49152, 65536, 81920, 98304,
+                    114688, 131072, 262144, 1 << 20, 4 << 20)
+
+
+def crossover(torch, rog, device, steps, warmup, totals=CROSSOVER_TOTALS):
+    """Both forced paths on aligned outputs of the given sizes at W = 2 and 8,
+    each call event-timed (the single-WG bound is chosen from these and from the
+    kernel-only durations of the same command under rocprofv3 --kernel-trace).
+    Call order per case: one checked call, ``warmup`` calls, ``steps`` timed
+    calls; single-WG first, then multi-WG."""
+    lib = rog.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    g = torch.Generator(device=device)
+    g.manual_seed(7)
+    rows = []
+    for W in (2, 8):
+        for total in totals:
+            S = total // W
+            srcs = [torch.randint(0, 256, (S,), dtype=torch.uint8, device=device, generator=g)
+                    for _ in range(W)]
+            out = torch.empty(total, dtype=torch.uint8, device=device)
+            ptrs = (ctypes.c_void_p * W)(*[x.data_ptr() for x in srcs])
+            o = ctypes.c_void_p(out.data_ptr())
+            row = {"W": W, "output_bytes": total}
+            for path, name in ((rog.ROG_PATH_SINGLE_WG, "single_wg"), (rog.ROG_PATH_MULTI_WG, "multi_wg")):
+                call = lambda: lib.rog_gather_ex(ptrs, W, S, o, stream, path)  # noqa: E731
+                out.zero_()
+                if call() != 0:
+                    raise RuntimeError("rog_gather_ex failed")
+                torch.cuda.synchronize()
+                if not torch.equal(out, torch.cat(srcs)):
+                    raise AssertionError("crossover case W=%d total=%d path=%s is wrong" % (W, total, name))
+                per_call, _ = time_calls(torch, call, steps, warmup)
+                row[name + "_p50_us"] = round(1e3 * statistics.median(per_call), 2)
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+    return rows
+
+
 def cpu_baseline(case, payloads, budget_s):
     """The CPU oracle, single-threaded, on the full headline gather repeated for
     about ``budget_s`` seconds of CPU work."""
@@ -248,6 +307,8 @@ def main(argv=None):
                     help="time only the headline gather (for counter runs)")
     ap.add_argument("--calibrate-bytes", type=int, default=0,
                     help="also run a plain elementwise copy of this many bytes, for counter scaling")
+    ap.add_argument("--crossover", action="store_true",
+                    help="time both forced paths over small outputs instead (one JSON line per case)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: --gpus %d is not supported (use --gpus 1)" % args.gpus,
@@ -265,10 +326,15 @@ def main(argv=None):
         return 2
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
+    if args.crossover:
+        crossover(torch, rog, device, args.steps, args.warmup)
+        return 0
 
     case, payloads, plan, per_call, region_ms = headline(torch, rog, wl, device, args.steps, args.warmup)
     alg_bytes = 2 * case.W * case.S
-    mean_launch_ms = statistics.fmean(per_call)
+    # Average launch duration of the headline kernel: the timed region's
+    # back-to-back launches on one stream, divided by their number.
+    mean_launch_ms = region_ms / args.steps
     value = gbps(alg_bytes * args.steps, region_ms)
     extras = {"headline": {"p50_us": round(1e3 * statistics.median(per_call), 2),
                            "mean_launch_us": round(1e3 * mean_launch_ms, 2),

@@ -17,19 +17,38 @@ constexpr int kMaxPeers = 64;
 constexpr int kMaxBatch = 32;
 constexpr int kMaxBatchPtrs = 192;
 
-// Tunables.  Each has a default measured on MI355X; a variant build may
-// override one with -D for a sweep.
+// Tunables.  Each default was measured on MI355X (bench sweeps over forced
+// paths, workgroup sizes, unroll depths and cache policies); a variant build
+// may override one with -D for a sweep.
 #ifndef ROG_SINGLE_WG_MAX_BYTES
-#define ROG_SINGLE_WG_MAX_BYTES (16 * 1024)
+#define ROG_SINGLE_WG_MAX_BYTES (32 * 1024)
 #endif
-#ifndef ROG_VEC_UNROLL
-#define ROG_VEC_UNROLL 4
+#ifndef ROG_FLAT_BLOCK
+#define ROG_FLAT_BLOCK 64
+#endif
+#ifndef ROG_FLAT_UNROLL
+#define ROG_FLAT_UNROLL 1
+#endif
+#ifndef ROG_SINGLE_UNROLL
+#define ROG_SINGLE_UNROLL 4
+#endif
+#ifndef ROG_PEER_BLOCK
+#define ROG_PEER_BLOCK 256
+#endif
+#ifndef ROG_PEER_UNROLL
+#define ROG_PEER_UNROLL 8
 #endif
 #ifndef ROG_BYTE_UNROLL
-#define ROG_BYTE_UNROLL 16
+#define ROG_BYTE_UNROLL 32
 #endif
-#ifndef ROG_NONTEMPORAL
-#define ROG_NONTEMPORAL 0
+#ifndef ROG_BATCH_BLOCK
+#define ROG_BATCH_BLOCK 256
+#endif
+#ifndef ROG_NT_STORE
+#define ROG_NT_STORE 1
+#endif
+#ifndef ROG_NT_LOAD_MIN_BYTES
+#define ROG_NT_LOAD_MIN_BYTES (384ull << 20)
 #endif
 #ifndef ROG_GRID_CAP
 #define ROG_GRID_CAP (1u << 30)
@@ -39,17 +58,25 @@ constexpr int kMaxBatchPtrs = 192;
 // (inclusive), measured by sweeping both forced paths.
 constexpr size_t kSingleWgMaxBytes = ROG_SINGLE_WG_MAX_BYTES;
 
-// Launch shapes.
-constexpr int kMultiBlock = 256;    // threads per workgroup, multi-WG path (4 waves)
-constexpr int kSingleBlock = 1024;  // threads of the single workgroup (16 waves)
-constexpr int kVecUnroll = ROG_VEC_UNROLL;    // 16-byte vectors per lane per chunk
-constexpr int kByteUnroll = ROG_BYTE_UNROLL;  // bytes per lane per tile, byte path
-constexpr bool kNonTemporal = ROG_NONTEMPORAL != 0;
-constexpr uint32_t kGridCap = ROG_GRID_CAP;   // workgroups of one launch, at most
-
-// A 64-lane wave copies 64 * kVecUnroll consecutive vectors per chunk; every
-// load/store instruction of the chunk covers 64 consecutive vectors (1 KiB).
-constexpr uint32_t kChunkVecs = 64 * kVecUnroll;
+// Launch shapes.  A FLAT wave copies a chunk of 64 * unroll consecutive 16-byte
+// vectors; each of its loads and stores is one dwordx4 instruction over 64
+// consecutive vectors (1 KiB).  Small workgroups of one wave, one 1 KiB chunk
+// each, measured fastest for HBM-bound gathers.
+constexpr int kFlatBlock = ROG_FLAT_BLOCK;        // multi-WG FLAT workgroup (threads)
+constexpr int kFlatUnroll = ROG_FLAT_UNROLL;      // vectors per lane per chunk
+constexpr int kSingleBlock = 1024;                // the single workgroup (16 waves)
+constexpr int kSingleUnroll = ROG_SINGLE_UNROLL;  // single-WG FLAT vectors per lane
+constexpr int kPeerBlock = ROG_PEER_BLOCK;        // multi-WG PEER workgroup
+constexpr int kPeerUnroll = ROG_PEER_UNROLL;      // PEER vectors per thread per tile
+constexpr int kByteUnroll = ROG_BYTE_UNROLL;      // PEER bytes per thread per tile
+constexpr int kSinglePeerUnroll = 4;              // single-WG PEER vectors per thread
+constexpr int kSingleByteUnroll = 8;              // single-WG PEER bytes per thread
+constexpr int kBatchBlock = ROG_BATCH_BLOCK;      // rog_gather_many workgroup
+constexpr bool kNtStore = ROG_NT_STORE != 0;      // non-temporal 16-byte stores
+// Source bytes from which 16-byte loads are non-temporal: below it the payloads
+// may still sit in the 256 MB Infinity Cache, and cached loads then win.
+constexpr uint64_t kNtLoadMinBytes = ROG_NT_LOAD_MIN_BYTES;
+constexpr uint32_t kGridCap = ROG_GRID_CAP;       // workgroups of one launch, at most
 
 // Exact floor(v / d) for every 32-bit v by one 32x32 high multiply:
 // t = mulhi(v, magic); q = (t + ((v - t) >> sh1)) >> sh2.
@@ -80,7 +107,7 @@ struct FlatArgs {
 // PEER: each payload is its own copy job.  Payload r with bit r of vec_ok set is
 // copied as floor(S/16) vectors plus S%16 tail bytes, otherwise byte by byte.
 // Multi-WG: workgroup b works on payload b / blocks_per_peer; single-WG
-// (blocks_per_peer == 0): the one workgroup takes the payloads in turn.
+// (blocks_per_peer unused): the one workgroup takes the payloads in turn.
 struct PeerArgs {
     const void *src[kMaxPeers];
     void *out;
@@ -130,7 +157,8 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
                        rog_path path, Plan *plan);
 
 // Validate and plan a batch (no HIP calls).  grid == 0 means nothing to launch.
+// *nt_loads: the launch streams its loads past the caches.
 rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *args,
-                      uint32_t *grid);
+                      uint32_t *grid, bool *nt_loads);
 
 }  // namespace rog

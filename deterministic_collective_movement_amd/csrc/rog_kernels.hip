@@ -35,13 +35,15 @@ namespace rog {
 
 typedef uint32_t vec16 __attribute__((ext_vector_type(4)));
 
+// 16-byte loads: non-temporal (streamed past the caches) when NT, else cached.
+template <bool NT>
 __device__ __forceinline__ vec16 ld16(const vec16 *p) {
-    if constexpr (kNonTemporal) return __builtin_nontemporal_load(p);
+    if constexpr (NT) return __builtin_nontemporal_load(p);
     else return *p;
 }
 
 __device__ __forceinline__ void st16(vec16 *p, vec16 v) {
-    if constexpr (kNonTemporal) __builtin_nontemporal_store(v, p);
+    if constexpr (kNtStore) __builtin_nontemporal_store(v, p);
     else *p = v;
 }
 
@@ -56,25 +58,26 @@ __device__ __forceinline__ uint32_t divide(uint32_t v, const Divider &d) {
 }
 
 // ---------------------------------------------------------------------------
-// FLAT: vectors [0, n_vec) of one gather, by workgroups `block` of `nblocks`.
-// Vector v comes from payload r = v / vpr at index v - r*vpr.
+// FLAT: vectors [0, n_vec) of one gather, by workgroups `block` of `nblocks`,
+// each of `waves` waves.  Vector v comes from payload r = v / vpr at index
+// v - r*vpr.  A wave owns chunks of 64*U consecutive vectors, grid-strided.
 // ---------------------------------------------------------------------------
-template <int BLOCK>
+template <int U, bool NTL>
 __device__ __forceinline__ void flat_copy(const void *const *src, void *out, uint32_t n_vec,
                                           uint32_t vpr, const Divider &div, uint32_t block,
-                                          uint32_t nblocks) {
-    constexpr uint32_t kWaves = BLOCK / 64;
+                                          uint32_t nblocks, uint32_t waves) {
+    constexpr uint32_t kChunk = 64 * U;
     const uint32_t lane = __lane_id();
     const uint32_t wave = uniform(threadIdx.x / 64);
-    // n_vec < 2^32; no expression below wraps: b + kChunkVecs - 1 <= 2^32 - 1
-    // because b is a multiple of kChunkVecs below n_vec.
-    const uint32_t n_chunks = n_vec / kChunkVecs + (n_vec % kChunkVecs != 0);
-    const uint32_t stride = nblocks * kWaves;
+    // n_vec < 2^32 and b is a multiple of kChunk below n_vec, so no expression
+    // below wraps (b + kChunk - 1 <= 2^32 - 1; seg_lo + vpr <= n_vec).
+    const uint32_t n_chunks = n_vec / kChunk + (n_vec % kChunk != 0);
+    const uint32_t stride = nblocks * waves;
     vec16 *o = static_cast<vec16 *>(out);
 
-    for (uint32_t c = block * kWaves + wave; c < n_chunks; c += stride) {
-        const uint32_t b = c * kChunkVecs;              // first vector of the chunk
-        const uint32_t n = min(n_vec - b, kChunkVecs);  // vectors in the chunk
+    for (uint32_t c = block * waves + wave; c < n_chunks; c += stride) {
+        const uint32_t b = c * kChunk;                  // first vector of the chunk
+        const uint32_t n = min(n_vec - b, kChunk);      // vectors in the chunk
         const uint32_t e = b + n;                       // chunk end
         const uint32_t r = divide(b, div);              // payload of b (scalar)
         const uint32_t seg_lo = r * vpr;
@@ -82,30 +85,31 @@ __device__ __forceinline__ void flat_copy(const void *const *src, void *out, uin
             // The whole chunk lies in payload r: scalar bases, lane offsets.
             const vec16 *s = static_cast<const vec16 *>(src[r]) + (b - seg_lo);
             vec16 *d = o + b;
-            if (n == kChunkVecs) {
-                vec16 v[kVecUnroll];
+            if (n == kChunk) {
+                vec16 v[U];
 #pragma unroll
-                for (int u = 0; u < kVecUnroll; ++u) v[u] = ld16(s + u * 64 + lane);
+                for (int u = 0; u < U; ++u) v[u] = ld16<NTL>(s + u * 64 + lane);
 #pragma unroll
-                for (int u = 0; u < kVecUnroll; ++u) st16(d + u * 64 + lane, v[u]);
+                for (int u = 0; u < U; ++u) st16(d + u * 64 + lane, v[u]);
             } else {
 #pragma unroll
-                for (int u = 0; u < kVecUnroll; ++u) {
+                for (int u = 0; u < U; ++u) {
                     const uint32_t k = u * 64 + lane;
-                    if (k < n) st16(d + k, ld16(s + k));
+                    if (k < n) st16(d + k, ld16<NTL>(s + k));
                 }
             }
         } else {
-            // The chunk crosses payload boundaries: visit each payload it
-            // touches (uniform loop, at most W turns); lanes copy the vectors
-            // that fall in the current payload's range.
-            for (uint32_t rr = r, lo = seg_lo; lo < e; ++rr, lo += vpr) {
-                const vec16 *s = static_cast<const vec16 *>(src[rr]);
-                const uint32_t hi = lo + vpr;
+            // The chunk crosses payload boundaries (rare unless payloads are
+            // small): each lane finds its own payload with the same multiply-
+            // high and reads that payload's base pointer itself, so all lanes
+            // proceed at once whatever the number of payloads in the chunk.
 #pragma unroll
-                for (int u = 0; u < kVecUnroll; ++u) {
-                    const uint32_t k = b + u * 64 + lane;
-                    if (k >= lo && k < hi && k < e) st16(o + k, ld16(s + (k - lo)));
+            for (int u = 0; u < U; ++u) {
+                const uint32_t k = b + u * 64 + lane;
+                if (k < e) {
+                    const uint32_t rk = divide(k, div);
+                    const vec16 *s = static_cast<const vec16 *>(src[rk]);
+                    st16(o + k, ld16<NTL>(s + (k - rk * vpr)));
                 }
             }
         }
@@ -113,53 +117,62 @@ __device__ __forceinline__ void flat_copy(const void *const *src, void *out, uin
 }
 
 // ---------------------------------------------------------------------------
-// PEER: one payload of S bytes from s to d, tiles part, part+parts, ...
+// PEER: one payload of S bytes from sp to dp by a workgroup of BLOCK threads
+// (BLOCK >= 16); this workgroup takes tiles part, part + parts, ...  Vector
+// tiles are BLOCK*U vectors, byte tiles BLOCK*UB bytes; within a tile thread t
+// handles elements t, t + BLOCK, ... (coalesced).
 // ---------------------------------------------------------------------------
-template <int BLOCK>
+template <int U, int UB, bool NTL>
 __device__ __forceinline__ void peer_copy(const void *sp, void *dp, uint64_t S, bool vec,
-                                          uint32_t part, uint32_t parts) {
+                                          uint32_t part, uint32_t parts, uint32_t BLOCK) {
     const uint32_t tid = threadIdx.x;
+    // Tile bases are wave-uniform (scalar registers); each lane adds a 32-bit
+    // offset below BLOCK * max(U, UB), so no lane carries 64-bit addresses.
     if (vec) {
         // 16-byte vectors, then the S % 16 tail bytes (by tile 0's workgroup).
-        const vec16 *s = static_cast<const vec16 *>(sp);
-        vec16 *d = static_cast<vec16 *>(dp);
         const uint64_t nv = S >> 4;
-        constexpr uint32_t kTile = BLOCK * kVecUnroll;
+        const uint32_t kTile = BLOCK * U;
         for (uint64_t base = uint64_t(part) * kTile; base < nv; base += uint64_t(parts) * kTile) {
+            const vec16 *s = static_cast<const vec16 *>(sp) + base;
+            vec16 *d = static_cast<vec16 *>(dp) + base;
             if (base + kTile <= nv) {
-                vec16 v[kVecUnroll];
+                vec16 v[U];
 #pragma unroll
-                for (int u = 0; u < kVecUnroll; ++u) v[u] = ld16(s + base + u * BLOCK + tid);
+                for (int u = 0; u < U; ++u) v[u] = ld16<NTL>(s + (u * BLOCK + tid));
 #pragma unroll
-                for (int u = 0; u < kVecUnroll; ++u) st16(d + base + u * BLOCK + tid, v[u]);
+                for (int u = 0; u < U; ++u) st16(d + (u * BLOCK + tid), v[u]);
             } else {
+                const uint32_t n = uint32_t(nv - base);
 #pragma unroll
-                for (int u = 0; u < kVecUnroll; ++u) {
-                    const uint64_t k = base + u * BLOCK + tid;
-                    if (k < nv) st16(d + k, ld16(s + k));
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t k = u * BLOCK + tid;
+                    if (k < n) st16(d + k, ld16<NTL>(s + k));
                 }
             }
         }
         if (part == 0) {
-            const uint64_t k = (nv << 4) + tid;
-            if (k < S) static_cast<uint8_t *>(dp)[k] = static_cast<const uint8_t *>(sp)[k];
+            const uint32_t k = tid;                   // BLOCK >= 16 covers the tail
+            const uint8_t *s = static_cast<const uint8_t *>(sp) + (nv << 4);
+            uint8_t *d = static_cast<uint8_t *>(dp) + (nv << 4);
+            if (k < (S & 15)) d[k] = s[k];
         }
     } else {
-        const uint8_t *s = static_cast<const uint8_t *>(sp);
-        uint8_t *d = static_cast<uint8_t *>(dp);
-        constexpr uint32_t kTile = BLOCK * kByteUnroll;
+        const uint32_t kTile = BLOCK * UB;
         for (uint64_t base = uint64_t(part) * kTile; base < S; base += uint64_t(parts) * kTile) {
+            const uint8_t *s = static_cast<const uint8_t *>(sp) + base;
+            uint8_t *d = static_cast<uint8_t *>(dp) + base;
             if (base + kTile <= S) {
-                uint8_t v[kByteUnroll];
+                uint8_t v[UB];
 #pragma unroll
-                for (int u = 0; u < kByteUnroll; ++u) v[u] = s[base + u * BLOCK + tid];
+                for (int u = 0; u < UB; ++u) v[u] = s[u * BLOCK + tid];
 #pragma unroll
-                for (int u = 0; u < kByteUnroll; ++u) d[base + u * BLOCK + tid] = v[u];
+                for (int u = 0; u < UB; ++u) d[u * BLOCK + tid] = v[u];
             } else {
+                const uint32_t n = uint32_t(min(S - base, uint64_t(kTile)));
 #pragma unroll
-                for (int u = 0; u < kByteUnroll; ++u) {
-                    const uint64_t k = base + u * BLOCK + tid;
-                    if (k < S) d[k] = s[k];
+                for (int u = 0; u < UB; ++u) {
+                    const uint32_t k = u * BLOCK + tid;
+                    if (k < n) d[k] = s[k];
                 }
             }
         }
@@ -169,26 +182,40 @@ __device__ __forceinline__ void peer_copy(const void *sp, void *dp, uint64_t S, 
 // ---------------------------------------------------------------------------
 // Kernels
 // ---------------------------------------------------------------------------
-template <int BLOCK>
+// Multi-WG FLAT: workgroups of BLOCK threads over the whole output.
+template <int BLOCK, bool NTL>
 __global__ __launch_bounds__(BLOCK) void rog_flat_kernel(FlatArgs a) {
-    flat_copy<BLOCK>(a.src, a.out, a.n_vec, a.vpr, a.div, blockIdx.x, gridDim.x);
+    flat_copy<kFlatUnroll, NTL>(a.src, a.out, a.n_vec, a.vpr, a.div, blockIdx.x, gridDim.x, BLOCK / 64);
 }
 
-template <int BLOCK>
+// Single-WG FLAT: one workgroup of as many waves as there are chunks (<= 16).
+template <bool NTL>
+__global__ __launch_bounds__(kSingleBlock) void rog_flat_single_kernel(FlatArgs a) {
+    flat_copy<kSingleUnroll, NTL>(a.src, a.out, a.n_vec, a.vpr, a.div, 0, 1, blockDim.x / 64);
+}
+
+// Multi-WG PEER: W groups of blocks_per_peer workgroups, one group per payload.
+template <int BLOCK, bool NTL>
 __global__ __launch_bounds__(BLOCK) void rog_peer_kernel(PeerArgs a) {
-    uint8_t *out = static_cast<uint8_t *>(a.out);
-    if (a.blocks_per_peer == 0) {
-        for (uint32_t r = 0; r < a.W; ++r)
-            peer_copy<BLOCK>(a.src[r], out + uint64_t(r) * a.S, a.S, (a.vec_ok >> r) & 1, 0, 1);
-    } else {
-        const uint32_t r = blockIdx.x / a.blocks_per_peer;
-        const uint32_t part = blockIdx.x - r * a.blocks_per_peer;
-        peer_copy<BLOCK>(a.src[r], out + uint64_t(r) * a.S, a.S, (a.vec_ok >> r) & 1, part,
-                         a.blocks_per_peer);
-    }
+    const uint32_t r = blockIdx.x / a.blocks_per_peer;
+    const uint32_t part = blockIdx.x - r * a.blocks_per_peer;
+    peer_copy<kPeerUnroll, kByteUnroll, NTL>(a.src[r], static_cast<uint8_t *>(a.out) + uint64_t(r) * a.S,
+                                             a.S, (a.vec_ok >> r) & 1, part, a.blocks_per_peer, BLOCK);
 }
 
-__global__ __launch_bounds__(kMultiBlock) void rog_batch_kernel(BatchArgs a) {
+// Single-WG PEER: one workgroup takes the payloads in turn.  Its block size is
+// known only at run time, so its unroll is smaller (register budget of a
+// 1024-thread workgroup: 128 VGPRs per lane).
+template <bool NTL>
+__global__ __launch_bounds__(kSingleBlock) void rog_peer_single_kernel(PeerArgs a) {
+    for (uint32_t r = 0; r < a.W; ++r)
+        peer_copy<kSinglePeerUnroll, kSingleByteUnroll, NTL>(
+            a.src[r], static_cast<uint8_t *>(a.out) + uint64_t(r) * a.S, a.S, (a.vec_ok >> r) & 1, 0, 1,
+            blockDim.x);
+}
+
+template <bool NTL>
+__global__ __launch_bounds__(kBatchBlock) void rog_batch_kernel(BatchArgs a) {
     const uint32_t b = blockIdx.x;
     // Last tensor whose first workgroup is <= b (first_block strictly increases).
     uint32_t lo = 0, hi = a.n;
@@ -201,13 +228,14 @@ __global__ __launch_bounds__(kMultiBlock) void rog_batch_kernel(BatchArgs a) {
     const uint32_t lb = b - t.first_block;
     const void *const *src = a.src + lo * a.W;
     if (t.flat) {
-        flat_copy<kMultiBlock>(src, reinterpret_cast<void *>(t.out), t.n_vec, t.vpr, t.div, lb,
-                               t.n_blocks);
+        flat_copy<kFlatUnroll, NTL>(src, reinterpret_cast<void *>(t.out), t.n_vec, t.vpr, t.div, lb,
+                                    t.n_blocks, kBatchBlock / 64);
     } else {
         const uint32_t r = lb / t.blocks_per_peer;
         const uint32_t part = lb - r * t.blocks_per_peer;
-        peer_copy<kMultiBlock>(src[r], reinterpret_cast<uint8_t *>(t.out) + uint64_t(r) * t.S, t.S,
-                               (t.vec_ok >> r) & 1, part, t.blocks_per_peer);
+        peer_copy<kPeerUnroll, kByteUnroll, NTL>(
+            src[r], reinterpret_cast<uint8_t *>(t.out) + uint64_t(r) * t.S, t.S, (t.vec_ok >> r) & 1,
+            part, t.blocks_per_peer, kBatchBlock);
     }
 }
 
@@ -230,20 +258,25 @@ rog_status launch(const void *kernel, uint32_t grid, uint32_t block, Args &args,
     return ROG_OK;
 }
 
+template <typename K>
+const void *kfn(K *k) { return reinterpret_cast<const void *>(k); }
+
 rog_status launch_plan(Plan &p, hipStream_t stream) {
     const rog_plan_info &i = p.info;
     const bool single = i.path == ROG_PATH_SINGLE_WG;
+    const bool ntl = (i.flags & ROG_PLAN_NT_LOADS) != 0;
+    const void *k = nullptr;
     switch (i.kernel) {
     case ROG_KERNEL_NONE:
         return ROG_OK;
     case ROG_KERNEL_FLAT:
-        return single
-            ? launch(reinterpret_cast<const void *>(&rog_flat_kernel<kSingleBlock>), i.grid, i.block, p.flat, stream)
-            : launch(reinterpret_cast<const void *>(&rog_flat_kernel<kMultiBlock>), i.grid, i.block, p.flat, stream);
+        if (single) k = ntl ? kfn(&rog_flat_single_kernel<true>) : kfn(&rog_flat_single_kernel<false>);
+        else        k = ntl ? kfn(&rog_flat_kernel<kFlatBlock, true>) : kfn(&rog_flat_kernel<kFlatBlock, false>);
+        return launch(k, i.grid, i.block, p.flat, stream);
     case ROG_KERNEL_PEER:
-        return single
-            ? launch(reinterpret_cast<const void *>(&rog_peer_kernel<kSingleBlock>), i.grid, i.block, p.peer, stream)
-            : launch(reinterpret_cast<const void *>(&rog_peer_kernel<kMultiBlock>), i.grid, i.block, p.peer, stream);
+        if (single) k = ntl ? kfn(&rog_peer_single_kernel<true>) : kfn(&rog_peer_single_kernel<false>);
+        else        k = ntl ? kfn(&rog_peer_kernel<kPeerBlock, true>) : kfn(&rog_peer_kernel<kPeerBlock, false>);
+        return launch(k, i.grid, i.block, p.peer, stream);
     default:
         return ROG_ERR_INVALID_ARGUMENT;
     }
@@ -274,10 +307,11 @@ ROG_API rog_status rog_gather_many(const rog_gather_desc *descs, int n, int W,
                                    hipStream_t stream) {
     rog::BatchArgs args;
     uint32_t grid = 0;
-    const rog_status st = rog::plan_batch(descs, n, W, &args, &grid);
+    bool ntl = false;
+    const rog_status st = rog::plan_batch(descs, n, W, &args, &grid, &ntl);
     if (st != ROG_OK || grid == 0) return st;
-    return rog::launch(reinterpret_cast<const void *>(&rog::rog_batch_kernel), grid,
-                       rog::kMultiBlock, args, stream);
+    const void *k = ntl ? rog::kfn(&rog::rog_batch_kernel<true>) : rog::kfn(&rog::rog_batch_kernel<false>);
+    return rog::launch(k, grid, rog::kBatchBlock, args, stream);
 }
 
 ROG_API rog_status rog_plan(const void *const *srcs, int W, size_t bytes_per_rank,

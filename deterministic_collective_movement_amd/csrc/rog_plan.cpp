@@ -84,24 +84,53 @@ uint64_t vec_ok_mask(const void *const *srcs, int W, size_t S, const void *out) 
     return m;
 }
 
-// Multi-WG FLAT grid: one wave per chunk of kChunkVecs vectors.
-uint32_t flat_blocks(uint64_t n_vec, uint32_t cap) {
-    const uint64_t chunks = ceil_div(n_vec, kChunkVecs);
-    return uint32_t(std::max<uint64_t>(1, std::min<uint64_t>(ceil_div(chunks, kMultiBlock / 64), cap)));
+// Largest grid for a workgroup size: an AMD dispatch counts work-items in 32
+// bits, so grid * block must stay below 2^32.  Kernels grid-stride, so a capped
+// grid still covers all work.
+uint32_t max_grid(int block) {
+    return std::min<uint32_t>(kGridCap, 0xFFFFFFFFu / uint32_t(block));
+}
+
+// Multi-WG FLAT grid: one wave per chunk of 64*unroll vectors.
+uint32_t flat_blocks(uint64_t n_vec, int block, int unroll, uint32_t cap) {
+    const uint64_t chunks = ceil_div(n_vec, 64 * uint64_t(unroll));
+    const uint64_t blocks = ceil_div(chunks, uint64_t(block) / 64);
+    return uint32_t(std::max<uint64_t>(1, std::min<uint64_t>(blocks, cap)));
 }
 
 // Multi-WG PEER grid: workgroups per payload, enough for the largest payload's
 // work at one tile per workgroup (vector tiles for aligned payloads, byte tiles
 // for the others).
-uint32_t peer_blocks_per_peer(int W, size_t S, uint64_t vec_ok, uint32_t cap) {
+uint32_t peer_blocks_per_peer(int W, size_t S, uint64_t vec_ok, int block, uint32_t cap) {
     uint64_t tiles = 1;
     for (int r = 0; r < W; ++r) {
         const uint64_t t = ((vec_ok >> r) & 1)
-            ? ceil_div(S / 16, uint64_t(kMultiBlock) * kVecUnroll)
-            : ceil_div(S, uint64_t(kMultiBlock) * kByteUnroll);
+            ? ceil_div(S / 16, uint64_t(block) * kPeerUnroll)
+            : ceil_div(S, uint64_t(block) * kByteUnroll);
         tiles = std::max(tiles, t);
     }
     return uint32_t(std::max<uint64_t>(1, std::min<uint64_t>(tiles, cap / uint32_t(W))));
+}
+
+uint32_t round_up_64(uint64_t threads) {
+    return uint32_t(std::min<uint64_t>(kSingleBlock, std::max<uint64_t>(64, (threads + 63) / 64 * 64)));
+}
+
+// Single-WG FLAT workgroup: one wave per chunk of 64*kSingleUnroll vectors, at
+// most 16 waves (idle waves only cost launch time).
+uint32_t flat_single_block(uint64_t n_vec) {
+    return round_up_64(ceil_div(n_vec, 64 * uint64_t(kSingleUnroll)) * 64);
+}
+
+// Single-WG PEER workgroup: enough threads for one tile of the largest payload.
+uint32_t peer_single_block(int W, size_t S, uint64_t vec_ok) {
+    uint64_t threads = 16;
+    for (int r = 0; r < W; ++r) {
+        const uint64_t t = ((vec_ok >> r) & 1) ? ceil_div(S / 16, kSinglePeerUnroll)
+                                               : ceil_div(S, kSingleByteUnroll);
+        threads = std::max(threads, t);
+    }
+    return round_up_64(threads);
 }
 
 }  // namespace
@@ -124,7 +153,7 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
         return ROG_OK;
     }
     const bool single = path == ROG_PATH_SINGLE_WG;
-    info.block = single ? kSingleBlock : kMultiBlock;
+    if (total >= kNtLoadMinBytes) info.flags |= ROG_PLAN_NT_LOADS;
 
     if (is_flat(srcs, W, S, out)) {
         FlatArgs &a = plan->flat;
@@ -136,7 +165,8 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
         a.div = make_divider(a.vpr);
         info.kernel = ROG_KERNEL_FLAT;
         info.units = a.n_vec;
-        info.grid = single ? 1 : flat_blocks(a.n_vec, kGridCap);
+        info.block = single ? flat_single_block(a.n_vec) : kFlatBlock;
+        info.grid = single ? 1 : flat_blocks(a.n_vec, kFlatBlock, kFlatUnroll, max_grid(kFlatBlock));
         info.peer_magic = a.div.magic;
         info.peer_sh1 = a.div.sh1;
         info.peer_sh2 = a.div.sh2;
@@ -148,7 +178,8 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
         a.S = S;
         a.W = uint32_t(W);
         a.vec_ok = vec_ok_mask(srcs, W, S, out);
-        a.blocks_per_peer = single ? 0 : peer_blocks_per_peer(W, S, a.vec_ok, kGridCap);
+        a.blocks_per_peer = single ? 0 : peer_blocks_per_peer(W, S, a.vec_ok, kPeerBlock, max_grid(kPeerBlock));
+        info.block = single ? peer_single_block(W, S, a.vec_ok) : kPeerBlock;
         info.kernel = ROG_KERNEL_PEER;
         info.vec_ok_mask = a.vec_ok;
         for (int r = 0; r < W; ++r)
@@ -159,8 +190,9 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
 }
 
 rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *args,
-                      uint32_t *grid) {
+                      uint32_t *grid, bool *nt_loads) {
     *grid = 0;
+    *nt_loads = false;
     if (n < 0 || W < 1 || W > kMaxPeers) return ROG_ERR_INVALID_ARGUMENT;
     if (n > 0 && !descs) return ROG_ERR_INVALID_ARGUMENT;
     if (n > kMaxBatch || n * W > kMaxBatchPtrs) return ROG_ERR_TOO_LARGE;
@@ -187,8 +219,8 @@ rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *arg
 
     memset(args, 0, sizeof(*args));
     args->W = uint32_t(W);
-    // Per-tensor workgroup cap keeps the launch's total below 2^31.
-    const uint32_t cap = std::min<uint32_t>(kGridCap, (1u << 31) / uint32_t(kMaxBatch) - 1);
+    // Per-tensor workgroup cap keeps the launch's total within max_grid.
+    const uint32_t cap = max_grid(kBatchBlock) / uint32_t(kMaxBatch);
     uint64_t next = 0;
     uint32_t k = 0;
     for (int t = 0; t < n; ++t) {
@@ -205,11 +237,11 @@ rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *arg
             bt.n_vec = uint32_t(totals[t] / 16);
             bt.vpr = uint32_t(S / 16);
             bt.div = make_divider(bt.vpr);
-            bt.n_blocks = flat_blocks(bt.n_vec, cap);
+            bt.n_blocks = flat_blocks(bt.n_vec, kBatchBlock, kFlatUnroll, cap);
         } else {
             bt.flat = 0;
             bt.vec_ok = vec_ok_mask(d.srcs, W, S, d.out);
-            bt.blocks_per_peer = peer_blocks_per_peer(W, S, bt.vec_ok, cap);
+            bt.blocks_per_peer = peer_blocks_per_peer(W, S, bt.vec_ok, kBatchBlock, cap);
             bt.n_blocks = bt.blocks_per_peer * uint32_t(W);
         }
         next += bt.n_blocks;
@@ -217,6 +249,9 @@ rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *arg
     }
     args->n = k;
     *grid = uint32_t(next);
+    uint64_t source_bytes = 0;
+    for (int t = 0; t < n; ++t) source_bytes += totals[t];
+    *nt_loads = source_bytes >= kNtLoadMinBytes;
     return ROG_OK;
 }
 

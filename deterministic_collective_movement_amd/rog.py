@@ -39,6 +39,8 @@ ROG_PATH_AUTO = 0
 ROG_PATH_SINGLE_WG = 1
 ROG_PATH_MULTI_WG = 2
 
+ROG_PLAN_NT_LOADS = 1
+
 ROG_KERNEL_NONE = 0
 ROG_KERNEL_FLAT = 1
 ROG_KERNEL_PEER = 2
@@ -70,7 +72,7 @@ class rog_plan_info(ctypes.Structure):
                 ("grid", ctypes.c_uint32), ("block", ctypes.c_uint32),
                 ("vec_ok_mask", ctypes.c_uint64), ("units", ctypes.c_uint64),
                 ("peer_magic", ctypes.c_uint32), ("peer_sh1", ctypes.c_uint32),
-                ("peer_sh2", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+                ("peer_sh2", ctypes.c_uint32), ("flags", ctypes.c_uint32)]
 
 
 def _hip_runtimes_mapped() -> set:
@@ -187,7 +189,7 @@ def rog_plan_ptrs(src_ptrs: Sequence[int], bytes_per_rank: int, out_ptr: int,
     return {"path": PATH_NAMES[info.path], "kernel": KERNEL_NAMES[info.kernel],
             "grid": info.grid, "block": info.block, "vec_ok_mask": info.vec_ok_mask,
             "units": info.units, "peer_magic": info.peer_magic, "peer_sh1": info.peer_sh1,
-            "peer_sh2": info.peer_sh2}
+            "peer_sh2": info.peer_sh2, "nt_loads": bool(info.flags & ROG_PLAN_NT_LOADS)}
 
 
 def rog_status_of_ptrs(src_ptrs: Optional[Sequence[int]], W: int, bytes_per_rank: int,

@@ -56,7 +56,7 @@ typedef enum {
 typedef enum {
     ROG_PATH_AUTO = 0,       /* single-WG iff W*S <= rog_single_wg_max_bytes()  */
     ROG_PATH_SINGLE_WG = 1,  /* one 1024-thread workgroup copies the whole output */
-    ROG_PATH_MULTI_WG = 2    /* a grid of 256-thread workgroups sized from the work */
+    ROG_PATH_MULTI_WG = 2    /* a grid of small workgroups sized from the work      */
 } rog_path;
 
 typedef enum {
@@ -84,8 +84,13 @@ typedef struct {
     uint32_t peer_magic;       /* FLAT: floor(v / (S/16)) = (t + ((v - t) >> peer_sh1))  */
     uint32_t peer_sh1;         /*       >> peer_sh2 with t = mulhi32(v, peer_magic),     */
     uint32_t peer_sh2;         /*       exact for every 32-bit v                         */
-    uint32_t reserved;
+    uint32_t flags;            /* ROG_PLAN_* bits                                       */
 } rog_plan_info;
+
+/* rog_plan_info.flags: the kernel's 16-byte loads are non-temporal (streamed
+ * past the caches); set when the W*S source bytes are too many to stay in the
+ * 256 MB Infinity Cache.  Stores are always non-temporal.  Affects speed only. */
+#define ROG_PLAN_NT_LOADS 1u
 
 /*
  * rog_gather -- out[r*S + i] = srcs[r][i] for r < W, i < S, enqueued on `stream`.

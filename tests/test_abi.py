@@ -19,8 +19,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rog.h")
 
 A = 1 << 20          # a 16-byte aligned fake device address
-VEC_UNROLL = 4       # 16-byte vectors per lane per wave chunk (kVecUnroll)
-BYTE_UNROLL = 16     # bytes per lane per tile on the byte path (kByteUnroll)
+FLAT_BLOCK, FLAT_UNROLL = 64, 1      # multi-WG FLAT: threads per WG, vectors per lane per chunk
+SINGLE_UNROLL = 4                    # single-WG FLAT: vectors per lane per chunk
+SINGLE_PEER_UNROLL, SINGLE_BYTE_UNROLL = 4, 8   # single-WG PEER: vectors and bytes per thread
+PEER_BLOCK, PEER_UNROLL, BYTE_UNROLL = 256, 8, 32   # multi-WG PEER: threads, vectors and bytes per thread
+NT_LOAD_MIN_BYTES = 384 << 20        # source bytes from which loads are non-temporal
 OK, INVALID, OVERLAP, TOO_LARGE = (rog.ROG_OK, rog.ROG_ERR_INVALID_ARGUMENT,
                                    rog.ROG_ERR_OVERLAP, rog.ROG_ERR_TOO_LARGE)
 
@@ -220,23 +223,55 @@ def test_auto_path_follows_the_exported_crossover_inclusively():
 
 def test_grid_sizes():
     out = 1 << 34
-    # FLAT multi-WG: one wave per chunk of 64*U vectors, 4 waves per workgroup.
+    # FLAT multi-WG: one wave per chunk of 64*U vectors.
     for W, S in [(2, 1024), (8, 1 << 20), (8, 64 << 20), (3, 16 * 257), (1, 16)]:
         srcs = [A + (S + 4096) * r for r in range(W)]
         p = rog.rog_plan_ptrs(srcs, S, out, rog.ROG_PATH_MULTI_WG)
         n_vec = W * S // 16
-        chunk = 64 * VEC_UNROLL
-        chunks = -(-n_vec // chunk)
-        assert p["kernel"] == "flat" and p["block"] == 256
-        assert p["grid"] == max(1, -(-chunks // 4))
+        chunks = -(-n_vec // (64 * FLAT_UNROLL))
+        assert p["kernel"] == "flat" and p["block"] == FLAT_BLOCK
+        assert p["grid"] == max(1, -(-chunks // (FLAT_BLOCK // 64)))
         s = rog.rog_plan_ptrs(srcs, S, out, rog.ROG_PATH_SINGLE_WG)
-        assert s["grid"] == 1 and s["block"] == 1024
+        single_chunks = -(-n_vec // (64 * SINGLE_UNROLL))
+        assert s["grid"] == 1 and s["block"] == min(1024, max(64, 64 * single_chunks))
     # PEER multi-WG: W groups, each sized for the largest payload's tiles.
     S = 100_001
     srcs = [A + 1 + (S + 4096) * r for r in range(4)]
     p = rog.rog_plan_ptrs(srcs, S, out, rog.ROG_PATH_MULTI_WG)
-    assert p["kernel"] == "peer" and p["vec_ok_mask"] == 0
-    assert p["grid"] == 4 * -(-S // (256 * BYTE_UNROLL))
+    assert p["kernel"] == "peer" and p["vec_ok_mask"] == 0 and p["block"] == PEER_BLOCK
+    assert p["grid"] == 4 * -(-S // (PEER_BLOCK * BYTE_UNROLL))
+
+
+def test_single_wg_peer_block_fits_the_largest_payload():
+    out = 1 << 34
+    # (W, S, source offset, output offset, threads one tile of the largest payload needs)
+    for W, S, io, oo, want_threads in [(2, 1, 1, 1, 16), (2, 4095, 1, 1, -(-4095 // SINGLE_BYTE_UNROLL)),
+                                       (1, 16 * 5000 + 3, 0, 0, -(-5000 // SINGLE_PEER_UNROLL)),
+                                       (2, 1 << 20, 3, 1, 1 << 20)]:
+        p = rog.rog_plan_ptrs([A + io + (S + 4096) * r for r in range(W)], S, out + oo,
+                              rog.ROG_PATH_SINGLE_WG)
+        assert p["kernel"] == "peer" and p["grid"] == 1
+        assert p["block"] == min(1024, max(64, -(-want_threads // 64) * 64)), S
+
+
+def test_grid_times_block_fits_a_dispatch():
+    """An AMD dispatch counts work-items in 32 bits: grid * block < 2^32 even at
+    the largest output (the kernels grid-stride over what a capped grid leaves)."""
+    S = ((1 << 36) - 16) // 8 // 16 * 16
+    p = rog.rog_plan_ptrs([A + (S + 4096) * r for r in range(8)], S, 1 << 45, rog.ROG_PATH_MULTI_WG)
+    assert p["kernel"] == "flat"
+    assert p["grid"] * p["block"] < (1 << 32)
+    p = rog.rog_plan_ptrs([A + 1 + (S + 4096) * r for r in range(8)], S, 1 << 45, rog.ROG_PATH_MULTI_WG)
+    assert p["kernel"] == "peer"
+    assert p["grid"] * p["block"] < (1 << 32)
+
+
+def test_nt_load_policy_follows_source_bytes():
+    out = 1 << 40
+    for W, S, want in [(8, 64 << 20, True), (8, 32 << 20, False), (1, NT_LOAD_MIN_BYTES, True),
+                       (1, NT_LOAD_MIN_BYTES - 16, False), (2, 1024, False)]:
+        srcs = [A + (S + 4096) * r for r in range(W)]
+        assert rog.rog_plan_ptrs(srcs, S, out)["nt_loads"] is want, (W, S)
 
 
 def _divide(v, magic, sh1, sh2):

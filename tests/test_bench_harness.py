@@ -100,6 +100,17 @@ class FakeTorch:
     cuda = FakeCuda
 
 
+def test_time_region_spans_only_the_timed_calls():
+    calls = []
+
+    def fn():
+        calls.append(1)
+        FakeEvent.clock[0] += 3.0 if len(calls) <= 2 else 0.5
+    FakeEvent.clock[0] = 0.0
+    assert bench.time_region(FakeTorch, fn, steps=4, warmup=2) == pytest.approx(2.0)
+    assert len(calls) == 6
+
+
 def test_time_calls_attributes_each_interval_to_its_call():
     durations = [0.5, 0.25, 1.0, 0.125]
     calls = []
