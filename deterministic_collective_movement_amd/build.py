@@ -1,7 +1,7 @@
 """Build librog.so (the C-ABI library) in-tree for gfx950.
 
-``build_library()`` compiles the host planner with g++ and the HIP kernels
-with hipcc for gfx950, then links ``deterministic_collective_movement_amd/librog.so``.
+``build_library()`` compiles the host planner and the HIP kernels with hipcc
+for gfx950, then links ``deterministic_collective_movement_amd/librog.so``.
 Intermediate objects go to ``_build/`` at the repository root.
 ``python -m deterministic_collective_movement_amd.build`` does the same.
 """
@@ -26,8 +26,11 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror",
              "--offload-arch=" + ARCH,
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]
-HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror",
-              "-D__HIP_PLATFORM_AMD__"]
+# Host planner: compiled as HIP source too (it shares the payload-cut helper
+# with the kernels), but it holds host code only.
+HOST_FLAGS = ["-x", "hip", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Werror",
+              "--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              "-Wno-unused-command-line-argument"]
 
 
 def _run(cmd):
@@ -42,7 +45,7 @@ def build_library(out: str = LIB_PATH, defines=(), build_dir: str = BUILD_DIR) -
     dflags = ["-D" + d for d in defines]
     plan_o = os.path.join(build_dir, "rog_plan.o")
     kern_o = os.path.join(build_dir, "rog_kernels.o")
-    _run(["g++"] + HOST_FLAGS + dflags + inc + ["-c", os.path.join(CSRC, "rog_plan.cpp"), "-o", plan_o])
+    _run([hipcc] + HOST_FLAGS + dflags + inc + ["-c", os.path.join(CSRC, "rog_plan.cpp"), "-o", plan_o])
     _run([hipcc] + HIP_FLAGS + dflags + inc + ["-c", os.path.join(CSRC, "rog_kernels.hip"), "-o", kern_o])
     tmp = out + ".tmp%d" % os.getpid()
     _run([hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, plan_o, kern_o,

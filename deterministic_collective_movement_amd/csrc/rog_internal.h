@@ -3,6 +3,7 @@
 // librog.so; the public interface is include/rog.h.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -38,9 +39,6 @@ constexpr int kMaxBatchPtrs = 192;
 #ifndef ROG_PEER_UNROLL
 #define ROG_PEER_UNROLL 8
 #endif
-#ifndef ROG_BYTE_UNROLL
-#define ROG_BYTE_UNROLL 32
-#endif
 #ifndef ROG_BATCH_BLOCK
 #define ROG_BATCH_BLOCK 256
 #endif
@@ -68,9 +66,7 @@ constexpr int kSingleBlock = 1024;                // the single workgroup (16 wa
 constexpr int kSingleUnroll = ROG_SINGLE_UNROLL;  // single-WG FLAT vectors per lane
 constexpr int kPeerBlock = ROG_PEER_BLOCK;        // multi-WG PEER workgroup
 constexpr int kPeerUnroll = ROG_PEER_UNROLL;      // PEER vectors per thread per tile
-constexpr int kByteUnroll = ROG_BYTE_UNROLL;      // PEER bytes per thread per tile
 constexpr int kSinglePeerUnroll = 4;              // single-WG PEER vectors per thread
-constexpr int kSingleByteUnroll = 8;              // single-WG PEER bytes per thread
 constexpr int kBatchBlock = ROG_BATCH_BLOCK;      // rog_gather_many workgroup
 constexpr bool kNtStore = ROG_NT_STORE != 0;      // non-temporal 16-byte stores
 // Source bytes from which 16-byte loads are non-temporal: below it the payloads
@@ -90,6 +86,37 @@ struct Divider {
 
 Divider make_divider(uint32_t d);
 
+// How the PEER kernel cuts a payload that is not 16-byte aligned on both sides
+// (source address sa, destination address da, S bytes): bytes [0, lo) and
+// [hi, S) move one by one; bytes [lo, hi) as aligned 16-byte stores whose data
+// comes from the aligned source vectors that start at sa + lo - delta -- one per
+// output vector when delta == 0, else two neighbours funnel-shifted by delta
+// bytes.  The cut keeps every one of those aligned source vectors inside
+// [sa, sa + S): vectors whose source blocks would reach outside move as bytes.
+struct PeerSplit {
+    uint64_t lo;      // first byte of the aligned body (da + lo is 16-byte aligned)
+    uint64_t hi;      // end of the body; (hi - lo) % 16 == 0; lo == hi: no body
+    uint32_t delta;   // (sa + lo) % 16
+};
+
+__host__ __device__ inline PeerSplit split_payload(uint64_t sa, uint64_t da, uint64_t S) {
+    const uint64_t h = ((16 - (da & 15)) & 15) < S ? ((16 - (da & 15)) & 15) : S;
+    const uint64_t nb = (S - h) >> 4;                   // aligned output vectors after h
+    const uint32_t delta = uint32_t((sa + h) & 15);
+    uint64_t jlo = 0, jhi = nb;
+    if (delta != 0) {
+        // Output vector j reads source blocks at P0 + 16j and P0 + 16(j+1),
+        // P0 = sa + h - delta; both must lie inside [sa, sa + S).
+        const uint64_t p0 = sa + h - delta;
+        jlo = p0 < sa ? 1 : 0;
+        const uint64_t lim = (sa + S - p0) >> 4;
+        jhi = lim > 1 ? lim - 1 : 0;
+        if (jhi > nb) jhi = nb;
+    }
+    if (jhi <= jlo) return PeerSplit{S, S, 0};           // too small for a body
+    return PeerSplit{h + 16 * jlo, h + 16 * jhi, delta};
+}
+
 // ---------------------------------------------------------------------------
 // Kernel arguments
 // ---------------------------------------------------------------------------
@@ -105,7 +132,9 @@ struct FlatArgs {
 };
 
 // PEER: each payload is its own copy job.  Payload r with bit r of vec_ok set is
-// copied as floor(S/16) vectors plus S%16 tail bytes, otherwise byte by byte.
+// copied as floor(S/16) vectors plus S%16 tail bytes; any other payload as a
+// byte head, a body of aligned 16-byte stores (from aligned or funnel-shifted
+// aligned source vectors) and a byte tail.
 // Multi-WG: workgroup b works on payload b / blocks_per_peer; single-WG
 // (blocks_per_peer unused): the one workgroup takes the payloads in turn.
 struct PeerArgs {

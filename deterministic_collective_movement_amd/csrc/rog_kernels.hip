@@ -118,64 +118,129 @@ __device__ __forceinline__ void flat_copy(const void *const *src, void *out, uin
 
 // ---------------------------------------------------------------------------
 // PEER: one payload of S bytes from sp to dp by a workgroup of BLOCK threads
-// (BLOCK >= 16); this workgroup takes tiles part, part + parts, ...  Vector
-// tiles are BLOCK*U vectors, byte tiles BLOCK*UB bytes; within a tile thread t
-// handles elements t, t + BLOCK, ... (coalesced).
+// (BLOCK >= 64); this workgroup takes tiles part, part + parts, ...  Tiles are
+// BLOCK*U 16-byte output vectors; within a tile thread t handles vectors t,
+// t + BLOCK, ... (coalesced).  Tile bases are wave-uniform (scalar registers);
+// lanes add 32-bit offsets.
 // ---------------------------------------------------------------------------
-template <int U, int UB, bool NTL>
+
+// Bytes [lo, hi) of a payload, one byte per thread per step (heads and tails).
+__device__ __forceinline__ void copy_bytes(const uint8_t *s, uint8_t *d, uint64_t lo, uint64_t hi,
+                                           uint32_t BLOCK) {
+    for (uint64_t i = lo + threadIdx.x; i < hi; i += BLOCK) d[i] = s[i];
+}
+
+// count aligned 16-byte vectors from s to d.
+template <int U, bool NTL>
+__device__ __forceinline__ void vec_body(const vec16 *s0, vec16 *d0, uint64_t count, uint32_t part,
+                                         uint32_t parts, uint32_t BLOCK) {
+    const uint32_t tid = threadIdx.x;
+    const uint32_t kTile = BLOCK * U;
+    for (uint64_t base = uint64_t(part) * kTile; base < count; base += uint64_t(parts) * kTile) {
+        const vec16 *s = s0 + base;
+        vec16 *d = d0 + base;
+        if (base + kTile <= count) {
+            vec16 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = ld16<NTL>(s + (u * BLOCK + tid));
+#pragma unroll
+            for (int u = 0; u < U; ++u) st16(d + (u * BLOCK + tid), v[u]);
+        } else {
+            const uint32_t n = uint32_t(count - base);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t k = u * BLOCK + tid;
+                if (k < n) st16(d + k, ld16<NTL>(s + k));
+            }
+        }
+    }
+}
+
+// The 16 bytes that start 4*Q + sh bytes into the 32 bytes a:b (little-endian
+// byte order, a first): each output dword joins two neighbouring input dwords
+// with one v_alignbyte_b32.
+template <int Q>
+__device__ __forceinline__ vec16 funnel(const vec16 &a, const vec16 &b, uint32_t sh) {
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    vec16 r;
+    r.x = __builtin_amdgcn_alignbyte(w[Q + 1], w[Q + 0], sh);
+    r.y = __builtin_amdgcn_alignbyte(w[Q + 2], w[Q + 1], sh);
+    r.z = __builtin_amdgcn_alignbyte(w[Q + 3], w[Q + 2], sh);
+    r.w = __builtin_amdgcn_alignbyte(w[Q + 4], w[Q + 3], sh);
+    return r;
+}
+
+// count aligned 16-byte output vectors d[k], each the 16 bytes that start
+// delta = 4*Q + sh bytes into the aligned source vectors p[k], p[k+1].
+template <int U, int Q>
+__device__ __forceinline__ void shift_body(const vec16 *p0, vec16 *d0, uint64_t count, uint32_t sh,
+                                           uint32_t part, uint32_t parts, uint32_t BLOCK) {
+    const uint32_t tid = threadIdx.x;
+    const uint32_t kTile = BLOCK * U;
+    for (uint64_t base = uint64_t(part) * kTile; base < count; base += uint64_t(parts) * kTile) {
+        const vec16 *p = p0 + base;
+        vec16 *d = d0 + base;
+        if (base + kTile <= count) {
+            vec16 a[U], b[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                a[u] = ld16<false>(p + (u * BLOCK + tid));
+                b[u] = ld16<false>(p + (u * BLOCK + tid + 1));
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) st16(d + (u * BLOCK + tid), funnel<Q>(a[u], b[u], sh));
+        } else {
+            const uint32_t n = uint32_t(count - base);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t k = u * BLOCK + tid;
+                if (k < n) st16(d + k, funnel<Q>(ld16<false>(p + k), ld16<false>(p + k + 1), sh));
+            }
+        }
+    }
+}
+
+// One payload.  vec (source and destination both 16-byte aligned): vectors,
+// then the S % 16 tail bytes.  Otherwise the destination is split at its first
+// and last 16-byte boundaries: a byte head, a body of aligned 16-byte stores,
+// a byte tail.  The body's data comes from aligned source vectors -- directly
+// when source and destination are equally misaligned, else funnel-shifted from
+// two neighbouring aligned vectors.  Body vectors whose aligned source vectors
+// would reach outside the payload go to the head or tail, so every read stays
+// inside [sp, sp + S).  Every output byte is written exactly once.
+template <int U, bool NTL>
 __device__ __forceinline__ void peer_copy(const void *sp, void *dp, uint64_t S, bool vec,
                                           uint32_t part, uint32_t parts, uint32_t BLOCK) {
-    const uint32_t tid = threadIdx.x;
-    // Tile bases are wave-uniform (scalar registers); each lane adds a 32-bit
-    // offset below BLOCK * max(U, UB), so no lane carries 64-bit addresses.
+    const uint8_t *s = static_cast<const uint8_t *>(sp);
+    uint8_t *d = static_cast<uint8_t *>(dp);
     if (vec) {
-        // 16-byte vectors, then the S % 16 tail bytes (by tile 0's workgroup).
         const uint64_t nv = S >> 4;
-        const uint32_t kTile = BLOCK * U;
-        for (uint64_t base = uint64_t(part) * kTile; base < nv; base += uint64_t(parts) * kTile) {
-            const vec16 *s = static_cast<const vec16 *>(sp) + base;
-            vec16 *d = static_cast<vec16 *>(dp) + base;
-            if (base + kTile <= nv) {
-                vec16 v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) v[u] = ld16<NTL>(s + (u * BLOCK + tid));
-#pragma unroll
-                for (int u = 0; u < U; ++u) st16(d + (u * BLOCK + tid), v[u]);
-            } else {
-                const uint32_t n = uint32_t(nv - base);
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const uint32_t k = u * BLOCK + tid;
-                    if (k < n) st16(d + k, ld16<NTL>(s + k));
-                }
-            }
-        }
-        if (part == 0) {
-            const uint32_t k = tid;                   // BLOCK >= 16 covers the tail
-            const uint8_t *s = static_cast<const uint8_t *>(sp) + (nv << 4);
-            uint8_t *d = static_cast<uint8_t *>(dp) + (nv << 4);
-            if (k < (S & 15)) d[k] = s[k];
-        }
-    } else {
-        const uint32_t kTile = BLOCK * UB;
-        for (uint64_t base = uint64_t(part) * kTile; base < S; base += uint64_t(parts) * kTile) {
-            const uint8_t *s = static_cast<const uint8_t *>(sp) + base;
-            uint8_t *d = static_cast<uint8_t *>(dp) + base;
-            if (base + kTile <= S) {
-                uint8_t v[UB];
-#pragma unroll
-                for (int u = 0; u < UB; ++u) v[u] = s[u * BLOCK + tid];
-#pragma unroll
-                for (int u = 0; u < UB; ++u) d[u * BLOCK + tid] = v[u];
-            } else {
-                const uint32_t n = uint32_t(min(S - base, uint64_t(kTile)));
-#pragma unroll
-                for (int u = 0; u < UB; ++u) {
-                    const uint32_t k = u * BLOCK + tid;
-                    if (k < n) d[k] = s[k];
-                }
-            }
-        }
+        vec_body<U, NTL>(reinterpret_cast<const vec16 *>(s), reinterpret_cast<vec16 *>(d), nv, part, parts,
+                         BLOCK);
+        if (part == 0) copy_bytes(s, d, nv << 4, S, BLOCK);
+        return;
+    }
+    const PeerSplit cut = split_payload(reinterpret_cast<uintptr_t>(s), reinterpret_cast<uintptr_t>(d), S);
+    const uint64_t lo = cut.lo, hi = cut.hi;
+    const uint32_t delta = cut.delta;
+    if (part == 0) {
+        copy_bytes(s, d, 0, lo, BLOCK);
+        copy_bytes(s, d, hi, S, BLOCK);
+    }
+    if (hi == lo) return;
+    vec16 *D = reinterpret_cast<vec16 *>(d + lo);
+    const uint64_t count = (hi - lo) >> 4;
+    if (delta == 0) {
+        vec_body<U, NTL>(reinterpret_cast<const vec16 *>(s + lo), D, count, part, parts, BLOCK);
+        return;
+    }
+    const vec16 *P = reinterpret_cast<const vec16 *>(s + lo - delta);
+    const uint32_t sh = delta & 3;
+    switch (delta >> 2) {
+    case 0: shift_body<U, 0>(P, D, count, sh, part, parts, BLOCK); break;
+    case 1: shift_body<U, 1>(P, D, count, sh, part, parts, BLOCK); break;
+    case 2: shift_body<U, 2>(P, D, count, sh, part, parts, BLOCK); break;
+    default: shift_body<U, 3>(P, D, count, sh, part, parts, BLOCK); break;
     }
 }
 
@@ -199,7 +264,7 @@ template <int BLOCK, bool NTL>
 __global__ __launch_bounds__(BLOCK) void rog_peer_kernel(PeerArgs a) {
     const uint32_t r = blockIdx.x / a.blocks_per_peer;
     const uint32_t part = blockIdx.x - r * a.blocks_per_peer;
-    peer_copy<kPeerUnroll, kByteUnroll, NTL>(a.src[r], static_cast<uint8_t *>(a.out) + uint64_t(r) * a.S,
+    peer_copy<kPeerUnroll, NTL>(a.src[r], static_cast<uint8_t *>(a.out) + uint64_t(r) * a.S,
                                              a.S, (a.vec_ok >> r) & 1, part, a.blocks_per_peer, BLOCK);
 }
 
@@ -209,7 +274,7 @@ __global__ __launch_bounds__(BLOCK) void rog_peer_kernel(PeerArgs a) {
 template <bool NTL>
 __global__ __launch_bounds__(kSingleBlock) void rog_peer_single_kernel(PeerArgs a) {
     for (uint32_t r = 0; r < a.W; ++r)
-        peer_copy<kSinglePeerUnroll, kSingleByteUnroll, NTL>(
+        peer_copy<kSinglePeerUnroll, NTL>(
             a.src[r], static_cast<uint8_t *>(a.out) + uint64_t(r) * a.S, a.S, (a.vec_ok >> r) & 1, 0, 1,
             blockDim.x);
 }
@@ -233,7 +298,7 @@ __global__ __launch_bounds__(kBatchBlock) void rog_batch_kernel(BatchArgs a) {
     } else {
         const uint32_t r = lb / t.blocks_per_peer;
         const uint32_t part = lb - r * t.blocks_per_peer;
-        peer_copy<kPeerUnroll, kByteUnroll, NTL>(
+        peer_copy<kPeerUnroll, NTL>(
             src[r], reinterpret_cast<uint8_t *>(t.out) + uint64_t(r) * t.S, t.S, (t.vec_ok >> r) & 1,
             part, t.blocks_per_peer, kBatchBlock);
     }

@@ -98,18 +98,12 @@ uint32_t flat_blocks(uint64_t n_vec, int block, int unroll, uint32_t cap) {
     return uint32_t(std::max<uint64_t>(1, std::min<uint64_t>(blocks, cap)));
 }
 
-// Multi-WG PEER grid: workgroups per payload, enough for the largest payload's
-// work at one tile per workgroup (vector tiles for aligned payloads, byte tiles
-// for the others).
-uint32_t peer_blocks_per_peer(int W, size_t S, uint64_t vec_ok, int block, uint32_t cap) {
-    uint64_t tiles = 1;
-    for (int r = 0; r < W; ++r) {
-        const uint64_t t = ((vec_ok >> r) & 1)
-            ? ceil_div(S / 16, uint64_t(block) * kPeerUnroll)
-            : ceil_div(S, uint64_t(block) * kByteUnroll);
-        tiles = std::max(tiles, t);
-    }
-    return uint32_t(std::max<uint64_t>(1, std::min<uint64_t>(tiles, cap / uint32_t(W))));
+// Multi-WG PEER grid: workgroups per payload, enough for one tile of BLOCK*U
+// 16-byte output vectors per workgroup over the largest payload (every payload
+// has at most S/16 body vectors, aligned or not).
+uint32_t peer_blocks_per_peer(int W, size_t S, int block, uint32_t cap) {
+    const uint64_t tiles = std::max<uint64_t>(1, ceil_div(S / 16, uint64_t(block) * kPeerUnroll));
+    return uint32_t(std::min<uint64_t>(tiles, cap / uint32_t(W)));
 }
 
 uint32_t round_up_64(uint64_t threads) {
@@ -123,14 +117,8 @@ uint32_t flat_single_block(uint64_t n_vec) {
 }
 
 // Single-WG PEER workgroup: enough threads for one tile of the largest payload.
-uint32_t peer_single_block(int W, size_t S, uint64_t vec_ok) {
-    uint64_t threads = 16;
-    for (int r = 0; r < W; ++r) {
-        const uint64_t t = ((vec_ok >> r) & 1) ? ceil_div(S / 16, kSinglePeerUnroll)
-                                               : ceil_div(S, kSingleByteUnroll);
-        threads = std::max(threads, t);
-    }
-    return round_up_64(threads);
+uint32_t peer_single_block(size_t S) {
+    return round_up_64(ceil_div(S / 16, kSinglePeerUnroll));
 }
 
 }  // namespace
@@ -178,12 +166,11 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
         a.S = S;
         a.W = uint32_t(W);
         a.vec_ok = vec_ok_mask(srcs, W, S, out);
-        a.blocks_per_peer = single ? 0 : peer_blocks_per_peer(W, S, a.vec_ok, kPeerBlock, max_grid(kPeerBlock));
-        info.block = single ? peer_single_block(W, S, a.vec_ok) : kPeerBlock;
+        a.blocks_per_peer = single ? 0 : peer_blocks_per_peer(W, S, kPeerBlock, max_grid(kPeerBlock));
+        info.block = single ? peer_single_block(S) : kPeerBlock;
         info.kernel = ROG_KERNEL_PEER;
         info.vec_ok_mask = a.vec_ok;
-        for (int r = 0; r < W; ++r)
-            info.units += ((a.vec_ok >> r) & 1) ? S / 16 + S % 16 : S;
+        info.units = total;
         info.grid = single ? 1 : a.blocks_per_peer * uint32_t(W);
     }
     return ROG_OK;
@@ -241,7 +228,7 @@ rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *arg
         } else {
             bt.flat = 0;
             bt.vec_ok = vec_ok_mask(d.srcs, W, S, d.out);
-            bt.blocks_per_peer = peer_blocks_per_peer(W, S, bt.vec_ok, kBatchBlock, cap);
+            bt.blocks_per_peer = peer_blocks_per_peer(W, S, kBatchBlock, cap);
             bt.n_blocks = bt.blocks_per_peer * uint32_t(W);
         }
         next += bt.n_blocks;

@@ -30,7 +30,7 @@
  *  - The library allocates no device or host memory, keeps no state except a
  *    thread-local copy of the last HIP error, and may be called from any thread.
  *  - Bytes outside [out, out + W*S) are never written.  Source bytes are never
- *    written.  Reads are confined to the source ranges.
+ *    written.  Every read lies inside a source range [srcs[r], srcs[r] + S).
  */
 #ifndef ROG_H
 #define ROG_H
@@ -62,7 +62,8 @@ typedef enum {
 typedef enum {
     ROG_KERNEL_NONE = 0,     /* nothing to copy (S == 0): nothing is launched       */
     ROG_KERNEL_FLAT = 1,     /* one flat loop over all peers' 16-byte vectors        */
-    ROG_KERNEL_PEER = 2      /* peers in turn: vectors where aligned, bytes otherwise */
+    ROG_KERNEL_PEER = 2      /* per payload: vectors where aligned, else byte head,
+                                aligned (funnel-shifted) body, byte tail           */
 } rog_kernel;
 
 /* One tensor of a batch: W source pointers, its output, its per-rank bytes. */
@@ -80,7 +81,7 @@ typedef struct {
     uint32_t block;            /* threads per workgroup                                 */
     uint64_t vec_ok_mask;      /* PEER kernel: bit r set iff srcs[r] and out + r*S are
                                   both 16-byte aligned (vector body + byte tail)        */
-    uint64_t units;            /* FLAT: 16-byte vectors W*S/16; PEER: total copy units   */
+    uint64_t units;            /* FLAT: 16-byte vectors W*S/16; PEER: bytes W*S          */
     uint32_t peer_magic;       /* FLAT: floor(v / (S/16)) = (t + ((v - t) >> peer_sh1))  */
     uint32_t peer_sh1;         /*       >> peer_sh2 with t = mulhi32(v, peer_magic),     */
     uint32_t peer_sh2;         /*       exact for every 32-bit v                         */
@@ -107,6 +108,11 @@ typedef struct {
  * gather copies the whole output alone and wins only for small outputs; the
  * crossover here is measured on gfx950).  Kernel: FLAT when out, S and every
  * srcs[r] are 16-byte aligned, else PEER (PR #491 "What", copy_rank_ordered).
+ * PEER copies a payload whose source and destination are both 16-byte aligned
+ * as vectors plus a byte tail, as the pages' fallback does; any other payload
+ * as a byte head, a body of aligned 16-byte stores fed by aligned 16-byte loads
+ * (funnel-shifted when source and destination are misaligned differently) and
+ * a byte tail.  Same bytes as a byte-by-byte copy, at vector speed.
  *
  * Errors (nothing enqueued):
  *   ROG_ERR_INVALID_ARGUMENT  srcs NULL; W < 1 or W > rog_max_peers(); S > 0 and

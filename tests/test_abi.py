@@ -21,8 +21,8 @@ HEADER = os.path.join(ROOT, "include", "rog.h")
 A = 1 << 20          # a 16-byte aligned fake device address
 FLAT_BLOCK, FLAT_UNROLL = 64, 1      # multi-WG FLAT: threads per WG, vectors per lane per chunk
 SINGLE_UNROLL = 4                    # single-WG FLAT: vectors per lane per chunk
-SINGLE_PEER_UNROLL, SINGLE_BYTE_UNROLL = 4, 8   # single-WG PEER: vectors and bytes per thread
-PEER_BLOCK, PEER_UNROLL, BYTE_UNROLL = 256, 8, 32   # multi-WG PEER: threads, vectors and bytes per thread
+SINGLE_PEER_UNROLL = 4               # single-WG PEER: 16-byte vectors per thread
+PEER_BLOCK, PEER_UNROLL = 256, 8     # multi-WG PEER: threads per WG, 16-byte vectors per thread
 NT_LOAD_MIN_BYTES = 384 << 20        # source bytes from which loads are non-temporal
 OK, INVALID, OVERLAP, TOO_LARGE = (rog.ROG_OK, rog.ROG_ERR_INVALID_ARGUMENT,
                                    rog.ROG_ERR_OVERLAP, rog.ROG_ERR_TOO_LARGE)
@@ -202,7 +202,7 @@ def test_vec_ok_mask_per_peer():
             want |= 1 << r
     assert p["kernel"] == "peer"
     assert p["vec_ok_mask"] == want == 0b00010001  # ranks 0 and 4
-    assert p["units"] == 2 * (S // 16 + S % 16) + 6 * S
+    assert p["units"] == 8 * S
 
 
 def test_auto_path_follows_the_exported_crossover_inclusively():
@@ -239,18 +239,17 @@ def test_grid_sizes():
     srcs = [A + 1 + (S + 4096) * r for r in range(4)]
     p = rog.rog_plan_ptrs(srcs, S, out, rog.ROG_PATH_MULTI_WG)
     assert p["kernel"] == "peer" and p["vec_ok_mask"] == 0 and p["block"] == PEER_BLOCK
-    assert p["grid"] == 4 * -(-S // (PEER_BLOCK * BYTE_UNROLL))
+    assert p["grid"] == 4 * -(-(S // 16) // (PEER_BLOCK * PEER_UNROLL))
 
 
 def test_single_wg_peer_block_fits_the_largest_payload():
     out = 1 << 34
-    # (W, S, source offset, output offset, threads one tile of the largest payload needs)
-    for W, S, io, oo, want_threads in [(2, 1, 1, 1, 16), (2, 4095, 1, 1, -(-4095 // SINGLE_BYTE_UNROLL)),
-                                       (1, 16 * 5000 + 3, 0, 0, -(-5000 // SINGLE_PEER_UNROLL)),
-                                       (2, 1 << 20, 3, 1, 1 << 20)]:
+    # (W, S, source offset, output offset)
+    for W, S, io, oo in [(2, 1, 1, 1), (2, 4095, 1, 1), (1, 16 * 5000 + 3, 0, 0), (2, 1 << 20, 3, 1)]:
         p = rog.rog_plan_ptrs([A + io + (S + 4096) * r for r in range(W)], S, out + oo,
                               rog.ROG_PATH_SINGLE_WG)
-        assert p["kernel"] == "peer" and p["grid"] == 1
+        assert p["kernel"] == "peer" and p["grid"] == 1 and p["units"] == W * S
+        want_threads = -(-(S // 16) // SINGLE_PEER_UNROLL)
         assert p["block"] == min(1024, max(64, -(-want_threads // 64) * 64)), S
 
 

@@ -239,3 +239,29 @@ def test_largest_vector_index(gpu):
         assert torch.all(mid == r * 29 + 7)
     del out, srcs
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("W", [1, 3])
+def test_every_source_and_destination_misalignment(gpu, W):
+    """The per-peer path's head / aligned body / tail cut for every pair of
+    source and destination misalignments (mod 16), at sizes around the
+    smallest payload with a body and at sizes with a long body, on every path.
+    Payloads are peer-tagged, so a misplaced or shifted byte cannot hide."""
+    sizes = (17, 47, 48, 49, 63, 64, 100, 1000, 70001)
+    for so in range(16):
+        for do in range(16):
+            for S in sizes:
+                payloads = [wl.tagged_payload(r + 3 * so, S) for r in range(W)]
+                placed = gc.Placed(payloads, [so] * W, do, gpu)
+                gc.run_all_paths(placed, "misaligned W=%d S=%d src%%16=%d dst%%16=%d" % (W, S, so, do))
+
+
+def test_misaligned_large_payloads(gpu):
+    """Multi-workgroup tiling of the shifted body over payloads of 8 MiB + 5."""
+    S = (8 << 20) + 5
+    rng = np.random.default_rng(41)
+    payloads = [np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(4)]
+    for io, oo in [(1, 3), (3, 3), (0, 9), (15, 0)]:
+        placed = gc.Placed(payloads, [io, io + 4, io, 8], oo, gpu)
+        gc.run_all_paths(placed, "misaligned large in=%d out=%d" % (io, oo),
+                         paths=(rog.ROG_PATH_AUTO, rog.ROG_PATH_MULTI_WG))
