@@ -37,10 +37,13 @@ constexpr int kMaxBatchPtrs = 192;
 #define ROG_PEER_BLOCK 256
 #endif
 #ifndef ROG_PEER_UNROLL
-#define ROG_PEER_UNROLL 8
+#define ROG_PEER_UNROLL 2
 #endif
 #ifndef ROG_BATCH_BLOCK
 #define ROG_BATCH_BLOCK 256
+#endif
+#ifndef ROG_BATCH_PEER_UNROLL
+#define ROG_BATCH_PEER_UNROLL 1
 #endif
 #ifndef ROG_NT_STORE
 #define ROG_NT_STORE 1
@@ -68,6 +71,7 @@ constexpr int kPeerBlock = ROG_PEER_BLOCK;        // multi-WG PEER workgroup
 constexpr int kPeerUnroll = ROG_PEER_UNROLL;      // PEER vectors per thread per tile
 constexpr int kSinglePeerUnroll = 4;              // single-WG PEER vectors per thread
 constexpr int kBatchBlock = ROG_BATCH_BLOCK;      // rog_gather_many workgroup
+constexpr int kBatchPeerUnroll = ROG_BATCH_PEER_UNROLL;  // its PEER vectors per thread
 constexpr bool kNtStore = ROG_NT_STORE != 0;      // non-temporal 16-byte stores
 // Source bytes from which 16-byte loads are non-temporal: below it the payloads
 // may still sit in the 256 MB Infinity Cache, and cached loads then win.

@@ -101,8 +101,8 @@ uint32_t flat_blocks(uint64_t n_vec, int block, int unroll, uint32_t cap) {
 // Multi-WG PEER grid: workgroups per payload, enough for one tile of BLOCK*U
 // 16-byte output vectors per workgroup over the largest payload (every payload
 // has at most S/16 body vectors, aligned or not).
-uint32_t peer_blocks_per_peer(int W, size_t S, int block, uint32_t cap) {
-    const uint64_t tiles = std::max<uint64_t>(1, ceil_div(S / 16, uint64_t(block) * kPeerUnroll));
+uint32_t peer_blocks_per_peer(int W, size_t S, int block, int unroll, uint32_t cap) {
+    const uint64_t tiles = std::max<uint64_t>(1, ceil_div(S / 16, uint64_t(block) * unroll));
     return uint32_t(std::min<uint64_t>(tiles, cap / uint32_t(W)));
 }
 
@@ -166,7 +166,7 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
         a.S = S;
         a.W = uint32_t(W);
         a.vec_ok = vec_ok_mask(srcs, W, S, out);
-        a.blocks_per_peer = single ? 0 : peer_blocks_per_peer(W, S, kPeerBlock, max_grid(kPeerBlock));
+        a.blocks_per_peer = single ? 0 : peer_blocks_per_peer(W, S, kPeerBlock, kPeerUnroll, max_grid(kPeerBlock));
         info.block = single ? peer_single_block(S) : kPeerBlock;
         info.kernel = ROG_KERNEL_PEER;
         info.vec_ok_mask = a.vec_ok;
@@ -228,7 +228,7 @@ rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *arg
         } else {
             bt.flat = 0;
             bt.vec_ok = vec_ok_mask(d.srcs, W, S, d.out);
-            bt.blocks_per_peer = peer_blocks_per_peer(W, S, kBatchBlock, cap);
+            bt.blocks_per_peer = peer_blocks_per_peer(W, S, kBatchBlock, kBatchPeerUnroll, cap);
             bt.n_blocks = bt.blocks_per_peer * uint32_t(W);
         }
         next += bt.n_blocks;

@@ -22,7 +22,7 @@ A = 1 << 20          # a 16-byte aligned fake device address
 FLAT_BLOCK, FLAT_UNROLL = 64, 1      # multi-WG FLAT: threads per WG, vectors per lane per chunk
 SINGLE_UNROLL = 4                    # single-WG FLAT: vectors per lane per chunk
 SINGLE_PEER_UNROLL = 4               # single-WG PEER: 16-byte vectors per thread
-PEER_BLOCK, PEER_UNROLL = 256, 8     # multi-WG PEER: threads per WG, 16-byte vectors per thread
+PEER_BLOCK, PEER_UNROLL = 256, 2     # multi-WG PEER: threads per WG, 16-byte vectors per thread
 NT_LOAD_MIN_BYTES = 384 << 20        # source bytes from which loads are non-temporal
 OK, INVALID, OVERLAP, TOO_LARGE = (rog.ROG_OK, rog.ROG_ERR_INVALID_ARGUMENT,
                                    rog.ROG_ERR_OVERLAP, rog.ROG_ERR_TOO_LARGE)
