@@ -12,8 +12,8 @@ which the calls use); ``value`` and the kernel's average launch duration come
 from it.  A second, untimed pass brackets every call with its own events, as
 the pages time each call (RL-Align/RL-Kernel PR #491, "Results": median of 100
 calls), for the per-call p50.  Besides the headline line the run measures the latency of
-small gathers (the pages' 1 - 128 KiB per-rank sizes at 2 and 8 payloads), the
-batched gather (16 tensors, W = 4, one launch) and the device-to-device copy
+small gathers (the pages' 1 - 128 KiB per-rank sizes at 2 and 8 payloads), per
+call and replayed from a HIP graph of 100 calls, the batched gather (16 tensors, W = 4, one launch) and the device-to-device copy
 ceiling, and times the CPU oracle on a bounded sample of the same workload.
 
 Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
@@ -226,6 +226,31 @@ def latency_sweep(torch, rog, wl, device, steps, warmup):
     return rows
 
 
+def graph_latency(torch, rog, wl, device, per_graph=100):
+    """Small gathers captured in a HIP graph: ``per_graph`` back-to-back calls per
+    graph, replayed; the GPU time per gather with the host launch path removed."""
+    rows = []
+    cases = wl.config1() + [c for c in wl.config2() if c.S <= 128 * wl.KiB]
+    for case in cases:
+        srcs = to_device(torch, [case.payload(r) for r in range(case.W)], device)
+        out = torch.empty(case.W * case.S, dtype=torch.uint8, device=device)
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(device=device)
+        side.wait_stream(torch.cuda.current_stream(device))
+        with torch.cuda.stream(side):
+            Call(rog, srcs, out, side.cuda_stream)()
+        torch.cuda.current_stream(device).wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            call = Call(rog, srcs, out, torch.cuda.current_stream(device).cuda_stream)
+            for _ in range(per_graph):
+                call()
+        per_replay, _ = time_calls(torch, g.replay, 10, 2)
+        rows.append({"W": case.W, "S_KiB": case.S // wl.KiB,
+                     "us_per_gather": round(1e3 * statistics.median(per_replay) / per_graph, 2)})
+    return rows
+
+
 def batch_bench(torch, rog, wl, device, steps, warmup):
     case = wl.config5(0)
     srcs = [to_device(torch, [case.payload(t, r) for r in range(case.W)], device)
@@ -373,6 +398,7 @@ def main(argv=None):
                                  "bytes_written": args.calibrate_bytes, "launches": args.steps}
     if not args.headline_only:
         extras["latency"] = latency_sweep(torch, rog, wl, device, args.steps, args.warmup)
+        extras["latency_in_graph"] = graph_latency(torch, rog, wl, device)
         extras["gather_many"] = batch_bench(torch, rog, wl, device, max(5, args.steps // 5),
                                             max(1, args.warmup // 5))
         extras["d2d_copy_ceiling"] = d2d_ceiling(torch, device, case.W * case.S, 20, 3)

@@ -1,0 +1,93 @@
+"""rog_gather and rog_gather_many inside a captured HIP graph.
+
+Each call is one kernel launch on the caller's stream with every argument in
+the kernel arguments -- no allocation, no memset, no synchronisation -- so a
+graph captures it as one kernel node.  The graph is replayed several times
+with eager work and synchronisation between replays; the sources change
+between replays, and every replay is checked against the CPU oracle for the
+sources of that moment.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from deterministic_collective_movement_amd import rog
+from deterministic_collective_movement_amd import workloads as wl
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _expected(srcs_dev):
+    payloads = [s.cpu().numpy() for s in srcs_dev]
+    out = np.empty(sum(p.shape[0] for p in payloads), np.uint8)
+    oracle.gather_c(payloads, out)
+    return out
+
+
+def test_graph_replays_follow_the_current_sources(gpu):
+    torch.cuda.synchronize()
+    # three gathers of different classes: flat single-WG, per-peer, flat multi-WG
+    specs = [(2, 1024, 0, 0), (3, 4095, 1, 3), (8, 128 * 1024, 0, 0)]
+    cases = []
+    for W, S, io, oo in specs:
+        bufs = [torch.zeros(S + io + 16, dtype=torch.uint8, device=gpu) for _ in range(W)]
+        srcs = [b[io:io + S] for b in bufs]
+        ob = torch.full((W * S + oo + 16,), 0xA5, dtype=torch.uint8, device=gpu)
+        cases.append((srcs, ob, ob[oo:oo + W * S], oo))
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(device=gpu)
+    side.wait_stream(torch.cuda.current_stream(gpu))
+    with torch.cuda.stream(side):
+        for srcs, _, out, _ in cases:          # warm-up outside the capture
+            rog.rog_gather(srcs, out)
+    torch.cuda.current_stream(gpu).wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for srcs, _, out, _ in cases:
+            rog.rog_gather(srcs, out)
+    rng = np.random.default_rng(5)
+    for replay in range(4):
+        # eager work between replays: new source bytes, and the outputs reset
+        for srcs, ob, _, _ in cases:
+            for s in srcs:
+                s.copy_(torch.from_numpy(np.frombuffer(rng.bytes(s.numel()), np.uint8).copy()).to(gpu))
+            ob.fill_(0xA5)
+        torch.cuda.synchronize()
+        print("graph replay %d" % replay, flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        for srcs, ob, out, oo in cases:
+            got = ob.cpu().numpy()
+            assert np.array_equal(got[oo:oo + out.numel()], _expected(srcs)), (replay, len(srcs))
+            assert np.all(got[:oo] == 0xA5) and np.all(got[oo + out.numel():] == 0xA5)
+
+
+def test_graph_captures_a_batched_gather(gpu):
+    case = wl.config5(3, n=6, W=4, max_rows=64)
+    batch, outs, bufs = [], [], []
+    for t, x in enumerate(case.tensors):
+        srcs = []
+        for r in range(case.W):
+            b = torch.from_numpy(case.payload(t, r)).to(gpu)
+            buf = torch.empty(x.in_off + x.S, dtype=torch.uint8, device=gpu)
+            buf[x.in_off:].copy_(b)
+            srcs.append(buf[x.in_off:])
+        batch.append(srcs)
+        ob = torch.empty(x.out_off + case.W * x.S, dtype=torch.uint8, device=gpu)
+        outs.append(ob[x.out_off:])
+    rog.rog_gather_many(batch, outs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rog.rog_gather_many(batch, outs)
+    for replay in range(3):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for srcs, o in zip(batch, outs):
+            assert np.array_equal(o.cpu().numpy(), _expected(srcs)), replay
