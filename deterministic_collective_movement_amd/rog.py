@@ -259,12 +259,32 @@ def _prepare(srcs: Sequence[torch.Tensor], out: Optional[torch.Tensor]):
     return device, S, out
 
 
+class _on_device:
+    """Make ``device`` the calling thread's current HIP device for the call (the
+    library launches on the current device), restoring the previous one."""
+
+    def __init__(self, device: torch.device):
+        self.index = device.index if device.index is not None else torch.cuda.current_device()
+        self.prev = None
+
+    def __enter__(self):
+        cur = torch.cuda.current_device()
+        if cur != self.index:
+            self.prev = cur
+            torch.cuda.set_device(self.index)
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            torch.cuda.set_device(self.prev)
+
+
 def rog_gather_ex(srcs: Sequence[torch.Tensor], out: Optional[torch.Tensor] = None,
                   path: int = ROG_PATH_AUTO, stream=None) -> torch.Tensor:
     """Rank-ordered gather of equal-size tensors into ``out`` with the path forced."""
     device, S, out = _prepare(srcs, out)
-    rog_gather_ptrs([s.data_ptr() for s in srcs], S, out.data_ptr(),
-                    _stream_handle(stream, device), path)
+    with _on_device(device):
+        rog_gather_ptrs([s.data_ptr() for s in srcs], S, out.data_ptr(),
+                        _stream_handle(stream, device), path)
     return out
 
 
@@ -302,6 +322,7 @@ def rog_gather_many(batch: Sequence[Sequence[torch.Tensor]],
             raise ValueError("all tensors of a batch must be on one device")
         ready.append(o)
         sizes.append(S)
-    rog_gather_many_ptrs([[s.data_ptr() for s in b] for b in batch], sizes,
-                         [o.data_ptr() for o in ready], W, _stream_handle(stream, device))
+    with _on_device(device):
+        rog_gather_many_ptrs([[s.data_ptr() for s in b] for b in batch], sizes,
+                             [o.data_ptr() for o in ready], W, _stream_handle(stream, device))
     return ready
