@@ -11,10 +11,14 @@ two HIP events on the calls' stream (torch.cuda.Event on torch's current stream,
 which the calls use); ``value`` and the kernel's average launch duration come
 from it.  A second, untimed pass brackets every call with its own events, as
 the pages time each call (RL-Align/RL-Kernel PR #491, "Results": median of 100
-calls), for the per-call p50.  Besides the headline line the run measures the latency of
-small gathers (the pages' 1 - 128 KiB per-rank sizes at 2 and 8 payloads), per
-call and replayed from a HIP graph of 100 calls, the batched gather (16 tensors, W = 4, one launch) and the device-to-device copy
-ceiling, and times the CPU oracle on a bounded sample of the same workload.
+calls), for the per-call p50.
+
+Besides the headline line the run measures: the same gather with every payload
+and the output at odd byte offsets (the per-payload path); small gathers (the
+pages' 1 - 128 KiB per-rank sizes at 2 and 8 payloads), per call and replayed
+from a HIP graph of 100 calls; the batched gather (16 tensors, W = 4, one
+launch); the device-to-device copy ceiling; and the CPU oracle on a bounded
+sample of the headline workload.
 
 Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
 """
@@ -206,7 +210,31 @@ def headline(torch, rog, wl, device, steps, warmup):
             got = out[r * case.S + lo: r * case.S + lo + 1024].cpu().numpy()
             if not (got == payloads[r][lo:lo + 1024]).all():
                 raise AssertionError("headline gather mismatch at rank %d offset %d" % (r, lo))
-    return case, payloads, plan, per_call, region_ms
+    return case, payloads, plan, per_call, region_ms, srcs
+
+
+def misaligned(torch, rog, case, payloads, srcs, device, steps, warmup, in_off=1, out_off=3):
+    """The headline payloads again, each at byte offset ``in_off`` of its own
+    buffer, gathered to byte offset ``out_off``: the per-payload path with a
+    funnel-shifted aligned body.  Returns GB/s of the timed region and the plan."""
+    views = []
+    for s in srcs:
+        buf = torch.empty(in_off + case.S, dtype=torch.uint8, device=device)
+        buf[in_off:].copy_(s)
+        views.append(buf[in_off:])
+    obuf = torch.empty(out_off + case.W * case.S, dtype=torch.uint8, device=device)
+    out = obuf[out_off:]
+    plan = rog.rog_plan(views, out)
+    region_ms = time_region(torch, Call(rog, views, out, torch.cuda.current_stream(device).cuda_stream),
+                            steps, warmup)
+    for r in range(case.W):
+        for lo in (0, case.S - 1024):
+            got = out[r * case.S + lo: r * case.S + lo + 1024].cpu().numpy()
+            if not (got == payloads[r][lo:lo + 1024]).all():
+                raise AssertionError("misaligned gather mismatch at rank %d offset %d" % (r, lo))
+    return {"W": case.W, "bytes_per_rank": case.S, "src_offset": in_off, "out_offset": out_off,
+            "kernel": plan["kernel"], "GBps": round(gbps(2 * case.W * case.S * steps, region_ms), 1),
+            "ms_per_gather": round(region_ms / steps, 4)}
 
 
 def latency_sweep(torch, rog, wl, device, steps, warmup):
@@ -351,7 +379,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
     ap.add_argument("--headline-only", action="store_true",
-                    help="time only the headline gather (for counter runs)")
+                    help="time only the headline gather and its misaligned variant (for counter runs)")
     ap.add_argument("--calibrate-bytes", type=int, default=0,
                     help="also run a plain elementwise copy of this many bytes, for counter scaling")
     ap.add_argument("--crossover", action="store_true",
@@ -377,7 +405,7 @@ def main(argv=None):
         crossover(torch, rog, device, args.steps, args.warmup)
         return 0
 
-    case, payloads, plan, per_call, region_ms = headline(torch, rog, wl, device, args.steps, args.warmup)
+    case, payloads, plan, per_call, region_ms, srcs = headline(torch, rog, wl, device, args.steps, args.warmup)
     alg_bytes = 2 * case.W * case.S
     # Average launch duration of the headline kernel: the timed region's
     # back-to-back launches on one stream, divided by their number.
@@ -396,6 +424,8 @@ def main(argv=None):
         torch.cuda.synchronize()
         extras["calibration"] = {"kernel": "torch.bitwise_not int32", "bytes_read": args.calibrate_bytes,
                                  "bytes_written": args.calibrate_bytes, "launches": args.steps}
+    extras["misaligned"] = misaligned(torch, rog, case, payloads, srcs, device,
+                                      max(10, args.steps // 5), max(2, args.warmup // 5))
     if not args.headline_only:
         extras["latency"] = latency_sweep(torch, rog, wl, device, args.steps, args.warmup)
         extras["latency_in_graph"] = graph_latency(torch, rog, wl, device)

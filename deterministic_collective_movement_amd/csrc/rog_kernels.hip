@@ -15,9 +15,11 @@
 //    is found once per chunk, in scalar registers, by one 32-bit multiply-high
 //    (no division on the device at all); a chunk that crosses a payload
 //    boundary walks the few payloads it touches with per-lane range masks.
-//  * PEER kernel (anything else): each payload on its own, 16-byte vectors plus
-//    a byte tail where its source and destination are both 16-byte aligned,
-//    byte by byte otherwise.  Multi-WG, the grid is split into W groups of
+//  * PEER kernel (anything else): each payload on its own -- a byte head, a
+//    body of aligned 16-byte stores and a byte tail; the body loads aligned
+//    source vectors, funnel-shifted when source and destination are misaligned
+//    differently (the pages' fallback copies such payloads byte by byte; the
+//    bytes written are the same).  Multi-WG, the grid is split into W groups of
 //    workgroups, one group per payload, so all payloads are copied at once;
 //    single-WG, the one workgroup takes the payloads in turn.
 //  * BATCH kernel (rog_gather_many): one launch; each workgroup finds its
@@ -204,26 +206,18 @@ __device__ __forceinline__ void shift_body(const vec16 *p0, vec16 *d0, uint64_t 
     }
 }
 
-// One payload.  vec (source and destination both 16-byte aligned): vectors,
-// then the S % 16 tail bytes.  Otherwise the destination is split at its first
-// and last 16-byte boundaries: a byte head, a body of aligned 16-byte stores,
-// a byte tail.  The body's data comes from aligned source vectors -- directly
-// when source and destination are equally misaligned, else funnel-shifted from
-// two neighbouring aligned vectors.  Body vectors whose aligned source vectors
-// would reach outside the payload go to the head or tail, so every read stays
-// inside [sp, sp + S).  Every output byte is written exactly once.
+// One payload.  The destination is cut at 256-byte boundaries (split_payload):
+// a byte head, a body of aligned 16-byte stores, a byte tail.  The body's data
+// comes from aligned source vectors -- one per output vector when source and
+// destination are equally misaligned (in particular both 16-byte aligned),
+// else two neighbours funnel-shifted.  Body vectors whose aligned source
+// vectors would reach outside the payload go to the head or tail, so every
+// read stays inside [sp, sp + S).  Every output byte is written exactly once.
 template <int U, bool NTL>
-__device__ __forceinline__ void peer_copy(const void *sp, void *dp, uint64_t S, bool vec,
-                                          uint32_t part, uint32_t parts, uint32_t BLOCK) {
+__device__ __forceinline__ void peer_copy(const void *sp, void *dp, uint64_t S, uint32_t part,
+                                          uint32_t parts, uint32_t BLOCK) {
     const uint8_t *s = static_cast<const uint8_t *>(sp);
     uint8_t *d = static_cast<uint8_t *>(dp);
-    if (vec) {
-        const uint64_t nv = S >> 4;
-        vec_body<U, NTL>(reinterpret_cast<const vec16 *>(s), reinterpret_cast<vec16 *>(d), nv, part, parts,
-                         BLOCK);
-        if (part == 0) copy_bytes(s, d, nv << 4, S, BLOCK);
-        return;
-    }
     const PeerSplit cut = split_payload(reinterpret_cast<uintptr_t>(s), reinterpret_cast<uintptr_t>(d), S);
     const uint64_t lo = cut.lo, hi = cut.hi;
     const uint32_t delta = cut.delta;
@@ -268,8 +262,8 @@ template <int BLOCK, bool NTL>
 __global__ __launch_bounds__(BLOCK) void rog_peer_kernel(PeerArgs a) {
     const uint32_t r = blockIdx.x / a.blocks_per_peer;
     const uint32_t part = blockIdx.x - r * a.blocks_per_peer;
-    peer_copy<kPeerUnroll, NTL>(a.src[r], static_cast<uint8_t *>(a.out) + uint64_t(r) * a.S,
-                                             a.S, (a.vec_ok >> r) & 1, part, a.blocks_per_peer, BLOCK);
+    peer_copy<kPeerUnroll, NTL>(a.src[r], static_cast<uint8_t *>(a.out) + uint64_t(r) * a.S, a.S, part,
+                                a.blocks_per_peer, BLOCK);
 }
 
 // Single-WG PEER: one workgroup takes the payloads in turn.  Its block size is
@@ -278,9 +272,8 @@ __global__ __launch_bounds__(BLOCK) void rog_peer_kernel(PeerArgs a) {
 template <bool NTL>
 __global__ __launch_bounds__(kSingleBlock) void rog_peer_single_kernel(PeerArgs a) {
     for (uint32_t r = 0; r < a.W; ++r)
-        peer_copy<kSinglePeerUnroll, NTL>(
-            a.src[r], static_cast<uint8_t *>(a.out) + uint64_t(r) * a.S, a.S, (a.vec_ok >> r) & 1, 0, 1,
-            blockDim.x);
+        peer_copy<kSinglePeerUnroll, NTL>(a.src[r], static_cast<uint8_t *>(a.out) + uint64_t(r) * a.S, a.S,
+                                          0, 1, blockDim.x);
 }
 
 template <bool NTL>
@@ -302,9 +295,8 @@ __global__ __launch_bounds__(kBatchBlock) void rog_batch_kernel(BatchArgs a) {
     } else {
         const uint32_t r = lb / t.blocks_per_peer;
         const uint32_t part = lb - r * t.blocks_per_peer;
-        peer_copy<kBatchPeerUnroll, NTL>(
-            src[r], reinterpret_cast<uint8_t *>(t.out) + uint64_t(r) * t.S, t.S, (t.vec_ok >> r) & 1,
-            part, t.blocks_per_peer, kBatchBlock);
+        peer_copy<kBatchPeerUnroll, NTL>(src[r], reinterpret_cast<uint8_t *>(t.out) + uint64_t(r) * t.S, t.S,
+                                         part, t.blocks_per_peer, kBatchBlock);
     }
 }
 

@@ -165,11 +165,10 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
         a.out = const_cast<void *>(out);
         a.S = S;
         a.W = uint32_t(W);
-        a.vec_ok = vec_ok_mask(srcs, W, S, out);
         a.blocks_per_peer = single ? 0 : peer_blocks_per_peer(W, S, kPeerBlock, kPeerUnroll, max_grid(kPeerBlock));
         info.block = single ? peer_single_block(S) : kPeerBlock;
         info.kernel = ROG_KERNEL_PEER;
-        info.vec_ok_mask = a.vec_ok;
+        info.vec_ok_mask = vec_ok_mask(srcs, W, S, out);
         info.units = total;
         info.grid = single ? 1 : a.blocks_per_peer * uint32_t(W);
     }
@@ -227,7 +226,6 @@ rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *arg
             bt.n_blocks = flat_blocks(bt.n_vec, kBatchBlock, kFlatUnroll, cap);
         } else {
             bt.flat = 0;
-            bt.vec_ok = vec_ok_mask(d.srcs, W, S, d.out);
             bt.blocks_per_peer = peer_blocks_per_peer(W, S, kBatchBlock, kBatchPeerUnroll, cap);
             bt.n_blocks = bt.blocks_per_peer * uint32_t(W);
         }

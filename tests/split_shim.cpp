@@ -8,3 +8,5 @@ extern "C" void rog_test_split(uint64_t sa, uint64_t da, uint64_t S, uint64_t *o
     out3[1] = p.hi;
     out3[2] = p.delta;
 }
+
+extern "C" uint64_t rog_test_body_align(void) { return rog::kBodyAlign; }
