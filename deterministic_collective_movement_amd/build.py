@@ -49,7 +49,7 @@ def build_library(out: str = LIB_PATH, defines=(), build_dir: str = BUILD_DIR) -
     _run([hipcc] + HIP_FLAGS + dflags + inc + ["-c", os.path.join(CSRC, "rog_kernels.hip"), "-o", kern_o])
     tmp = out + ".tmp%d" % os.getpid()
     _run([hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, plan_o, kern_o,
-          "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-Wl,--no-undefined", "-o", tmp])
+          "-Wl,-soname,librog.so", "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-Wl,--no-undefined", "-o", tmp])
     os.replace(tmp, out)
     return out
 

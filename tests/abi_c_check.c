@@ -1,0 +1,194 @@
+/*
+ * abi_c_check.c -- a plain C consumer of librog.so (include/rog.h): no Python,
+ * no PyTorch.  It allocates device memory with the HIP runtime, gathers on a
+ * stream it created, copies back, and compares every byte -- guards around
+ * each output included -- with the CPU oracle (oracle/rog_oracle.c, linked in).
+ * Built by the package build step; run by tests/test_abi_c_gpu.py.
+ *
+ * Cases: aligned (flat) and misaligned (per-payload) gathers on every path,
+ * a batch of three tensors in one launch, S = 0, and the argument errors that
+ * must be reported before anything is enqueued.
+ * Exit status 0 = every check passed; the first failure is printed.
+ */
+#include <hip/hip_runtime_api.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "rog.h"
+
+void rog_oracle_gather(const unsigned char *const *srcs, int W, size_t S, unsigned char *out);
+
+#define GUARD 64
+#define FILL 0xA5
+
+static int failures = 0;
+
+#define CHECK_HIP(x)                                                              \
+    do {                                                                          \
+        hipError_t e_ = (x);                                                      \
+        if (e_ != hipSuccess) {                                                   \
+            fprintf(stderr, "HIP error %d at %s:%d: %s\n", (int)e_, __FILE__,     \
+                    __LINE__, #x);                                                \
+            exit(2);                                                              \
+        }                                                                         \
+    } while (0)
+
+static unsigned char byte_at(unsigned seed, size_t i) {
+    unsigned x = seed * 2654435761u + (unsigned)i * 40503u;
+    x ^= x >> 13;
+    x *= 0x5bd1e995u;
+    return (unsigned char)(x >> 24);
+}
+
+/* One gather of W payloads of S bytes at the given offsets, on `path`. */
+static void gather_case(int W, size_t S, size_t in_off, size_t out_off, rog_path path,
+                        hipStream_t st) {
+    unsigned char *host_src[64];
+    unsigned char *dev_buf[64];
+    const void *dev_src[64];
+    size_t sbytes = GUARD + in_off + S + GUARD;
+    for (int r = 0; r < W; ++r) {
+        host_src[r] = (unsigned char *)malloc(sbytes);
+        memset(host_src[r], FILL, sbytes);
+        for (size_t i = 0; i < S; ++i) host_src[r][GUARD + in_off + i] = byte_at(17u * r + 3u, i);
+        CHECK_HIP(hipMalloc((void **)&dev_buf[r], sbytes));
+        CHECK_HIP(hipMemcpy(dev_buf[r], host_src[r], sbytes, hipMemcpyHostToDevice));
+        dev_src[r] = dev_buf[r] + GUARD + in_off;
+    }
+    size_t obytes = GUARD + out_off + (size_t)W * S + GUARD;
+    unsigned char *want = (unsigned char *)malloc(obytes);
+    unsigned char *got = (unsigned char *)malloc(obytes);
+    memset(want, FILL, obytes);
+    const unsigned char *hs[64];
+    for (int r = 0; r < W; ++r) hs[r] = host_src[r] + GUARD + in_off;
+    rog_oracle_gather(hs, W, S, want + GUARD + out_off);
+
+    unsigned char *dev_out;
+    CHECK_HIP(hipMalloc((void **)&dev_out, obytes));
+    CHECK_HIP(hipMemset(dev_out, FILL, obytes));
+    rog_status s = rog_gather_ex(dev_src, W, S, dev_out + GUARD + out_off, st, path);
+    if (s != ROG_OK) {
+        fprintf(stderr, "FAIL W=%d S=%zu in=%zu out=%zu path=%d: %s\n", W, S, in_off, out_off,
+                (int)path, rog_status_string(s));
+        ++failures;
+    } else {
+        CHECK_HIP(hipStreamSynchronize(st));
+        CHECK_HIP(hipMemcpy(got, dev_out, obytes, hipMemcpyDeviceToHost));
+        if (memcmp(got, want, obytes) != 0) {
+            size_t k = 0;
+            while (got[k] == want[k]) ++k;
+            fprintf(stderr, "FAIL W=%d S=%zu in=%zu out=%zu path=%d: byte %zu got %d want %d\n", W, S,
+                    in_off, out_off, (int)path, k, got[k], want[k]);
+            ++failures;
+        }
+    }
+    CHECK_HIP(hipFree(dev_out));
+    for (int r = 0; r < W; ++r) {
+        CHECK_HIP(hipFree(dev_buf[r]));
+        free(host_src[r]);
+    }
+    free(want);
+    free(got);
+}
+
+static void batch_case(hipStream_t st) {
+    enum { N = 3, W = 4 };
+    const size_t sizes[N] = {4096, 1001, 65536 + 7};
+    const size_t offs[N] = {0, 3, 1};
+    unsigned char *hsrc[N][W], *dsrc[N][W], *dout[N], *want[N], *got[N];
+    const void *ptrs[N][W];
+    rog_gather_desc desc[N];
+    for (int t = 0; t < N; ++t) {
+        const size_t S = sizes[t];
+        for (int r = 0; r < W; ++r) {
+            hsrc[t][r] = (unsigned char *)malloc(S);
+            for (size_t i = 0; i < S; ++i) hsrc[t][r][i] = byte_at(101u * t + r, i);
+            CHECK_HIP(hipMalloc((void **)&dsrc[t][r], S + offs[t]));
+            CHECK_HIP(hipMemcpy(dsrc[t][r] + offs[t], hsrc[t][r], S, hipMemcpyHostToDevice));
+            ptrs[t][r] = dsrc[t][r] + offs[t];
+        }
+        want[t] = (unsigned char *)malloc(W * S);
+        got[t] = (unsigned char *)malloc(W * S);
+        rog_oracle_gather((const unsigned char *const *)hsrc[t], W, S, want[t]);
+        CHECK_HIP(hipMalloc((void **)&dout[t], W * S + 5));
+        desc[t].srcs = ptrs[t];
+        desc[t].out = dout[t] + 5 * (t % 2);
+        desc[t].bytes_per_rank = S;
+    }
+    rog_status s = rog_gather_many(desc, N, W, st);
+    if (s != ROG_OK) {
+        fprintf(stderr, "FAIL batch: %s\n", rog_status_string(s));
+        ++failures;
+    } else {
+        CHECK_HIP(hipStreamSynchronize(st));
+        for (int t = 0; t < N; ++t) {
+            CHECK_HIP(hipMemcpy(got[t], desc[t].out, W * sizes[t], hipMemcpyDeviceToHost));
+            if (memcmp(got[t], want[t], W * sizes[t]) != 0) {
+                fprintf(stderr, "FAIL batch tensor %d\n", t);
+                ++failures;
+            }
+        }
+    }
+    for (int t = 0; t < N; ++t) {
+        for (int r = 0; r < W; ++r) {
+            CHECK_HIP(hipFree(dsrc[t][r]));
+            free(hsrc[t][r]);
+        }
+        CHECK_HIP(hipFree(dout[t]));
+        free(want[t]);
+        free(got[t]);
+    }
+}
+
+static void expect_status(rog_status got, rog_status want, const char *what) {
+    if (got != want) {
+        fprintf(stderr, "FAIL %s: got %s want %s\n", what, rog_status_string(got), rog_status_string(want));
+        ++failures;
+    }
+}
+
+static void error_cases(hipStream_t st) {
+    unsigned char *buf;
+    CHECK_HIP(hipMalloc((void **)&buf, 4096));
+    CHECK_HIP(hipMemset(buf, FILL, 4096));
+    const void *two[2] = {buf + 1024, buf + 2048};
+    expect_status(rog_gather(NULL, 2, 16, buf, st), ROG_ERR_INVALID_ARGUMENT, "NULL srcs");
+    expect_status(rog_gather(two, 0, 16, buf, st), ROG_ERR_INVALID_ARGUMENT, "W = 0");
+    expect_status(rog_gather(two, 2, 16, NULL, st), ROG_ERR_INVALID_ARGUMENT, "NULL out");
+    expect_status(rog_gather(two, 2, 1024, buf + 512, st), ROG_ERR_OVERLAP, "partial overlap");
+    expect_status(rog_gather(two, 2, (size_t)1 << 40, buf, st), ROG_ERR_TOO_LARGE, "too large");
+    expect_status(rog_gather_ex(two, 2, 16, buf, st, (rog_path)9), ROG_ERR_INVALID_ARGUMENT, "bad path");
+    expect_status(rog_gather(two, 2, 0, buf, st), ROG_OK, "S = 0");
+    /* nothing above may have written a byte */
+    unsigned char host[4096];
+    CHECK_HIP(hipStreamSynchronize(st));
+    CHECK_HIP(hipMemcpy(host, buf, 4096, hipMemcpyDeviceToHost));
+    for (int i = 0; i < 4096; ++i)
+        if (host[i] != FILL) {
+            fprintf(stderr, "FAIL an error path wrote byte %d\n", i);
+            ++failures;
+            break;
+        }
+    CHECK_HIP(hipFree(buf));
+}
+
+int main(void) {
+    hipStream_t st;
+    CHECK_HIP(hipStreamCreate(&st));
+    const rog_path paths[3] = {ROG_PATH_AUTO, ROG_PATH_SINGLE_WG, ROG_PATH_MULTI_WG};
+    const size_t sizes[] = {1, 16, 1024, 4095, 65536, 262151, 1 << 20};
+    const size_t offs[][2] = {{0, 0}, {1, 3}, {8, 8}, {0, 5}};
+    const int Ws[] = {1, 2, 8};
+    for (int p = 0; p < 3; ++p)
+        for (unsigned w = 0; w < sizeof Ws / sizeof Ws[0]; ++w)
+            for (unsigned s = 0; s < sizeof sizes / sizeof sizes[0]; ++s)
+                for (unsigned o = 0; o < sizeof offs / sizeof offs[0]; ++o)
+                    gather_case(Ws[w], sizes[s], offs[o][0], offs[o][1], paths[p], st);
+    batch_case(st);
+    error_cases(st);
+    CHECK_HIP(hipStreamDestroy(st));
+    printf("abi_c_check: %d failures; single-WG bound %zu bytes, max W %d\n", failures,
+           rog_single_wg_max_bytes(), rog_max_peers());
+    return failures ? 1 : 0;
+}
