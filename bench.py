@@ -216,7 +216,7 @@ def headline(torch, rog, wl, device, steps, warmup):
 def misaligned(torch, rog, case, payloads, srcs, device, steps, warmup, in_off=1, out_off=3):
     """The headline payloads again, each at byte offset ``in_off`` of its own
     buffer, gathered to byte offset ``out_off``: the per-payload path with a
-    funnel-shifted aligned body.  Returns GB/s of the timed region and the plan."""
+    16-byte body of aligned stores fed by unaligned loads.  Returns GB/s of the timed region and the plan."""
     views = []
     for s in srcs:
         buf = torch.empty(in_off + case.S, dtype=torch.uint8, device=device)

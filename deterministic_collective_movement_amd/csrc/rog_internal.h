@@ -19,8 +19,8 @@ constexpr int kMaxBatch = 32;
 constexpr int kMaxBatchPtrs = 192;
 
 // Tunables.  Each default was measured on MI355X (bench sweeps over forced
-// paths, workgroup sizes, unroll depths and cache policies); a variant build
-// may override one with -D for a sweep.
+// paths, workgroup sizes, unroll depths, cache policies and workgroup-to-XCD
+// placement); a variant build may override one with -D for a sweep.
 #ifndef ROG_SINGLE_WG_MAX_BYTES
 #define ROG_SINGLE_WG_MAX_BYTES (32 * 1024)
 #endif
@@ -33,18 +33,6 @@ constexpr int kMaxBatchPtrs = 192;
 #ifndef ROG_SINGLE_UNROLL
 #define ROG_SINGLE_UNROLL 4
 #endif
-#ifndef ROG_PEER_BLOCK
-#define ROG_PEER_BLOCK 256
-#endif
-#ifndef ROG_PEER_UNROLL
-#define ROG_PEER_UNROLL 2
-#endif
-#ifndef ROG_BATCH_BLOCK
-#define ROG_BATCH_BLOCK 256
-#endif
-#ifndef ROG_BATCH_PEER_UNROLL
-#define ROG_BATCH_PEER_UNROLL 1
-#endif
 #ifndef ROG_NT_STORE
 #define ROG_NT_STORE 1
 #endif
@@ -54,6 +42,9 @@ constexpr int kMaxBatchPtrs = 192;
 #ifndef ROG_BODY_ALIGN
 #define ROG_BODY_ALIGN 256
 #endif
+#ifndef ROG_XCD_RUN
+#define ROG_XCD_RUN 128
+#endif
 #ifndef ROG_GRID_CAP
 #define ROG_GRID_CAP (1u << 30)
 #endif
@@ -62,19 +53,16 @@ constexpr int kMaxBatchPtrs = 192;
 // (inclusive), measured by sweeping both forced paths.
 constexpr size_t kSingleWgMaxBytes = ROG_SINGLE_WG_MAX_BYTES;
 
-// Launch shapes.  A FLAT wave copies a chunk of 64 * unroll consecutive 16-byte
-// vectors; each of its loads and stores is one dwordx4 instruction over 64
-// consecutive vectors (1 KiB).  Small workgroups of one wave, one 1 KiB chunk
-// each, measured fastest for HBM-bound gathers.
+// Launch shapes.  A multi-WG wave copies a chunk of 64 * unroll consecutive
+// 16-byte vectors; each of its loads and stores is one dwordx4 instruction over
+// 64 consecutive vectors (1 KiB).  Small workgroups of one wave, one 1 KiB chunk
+// each, measured fastest for HBM-bound gathers (FLAT, PEER and BATCH alike).
 constexpr int kFlatBlock = ROG_FLAT_BLOCK;        // multi-WG FLAT workgroup (threads)
 constexpr int kFlatUnroll = ROG_FLAT_UNROLL;      // vectors per lane per chunk
+constexpr int kWaveBlock = 64;                    // multi-WG PEER and BATCH workgroup
 constexpr int kSingleBlock = 1024;                // the single workgroup (16 waves)
 constexpr int kSingleUnroll = ROG_SINGLE_UNROLL;  // single-WG FLAT vectors per lane
-constexpr int kPeerBlock = ROG_PEER_BLOCK;        // multi-WG PEER workgroup
-constexpr int kPeerUnroll = ROG_PEER_UNROLL;      // PEER vectors per thread per tile
 constexpr int kSinglePeerUnroll = 4;              // single-WG PEER vectors per thread
-constexpr int kBatchBlock = ROG_BATCH_BLOCK;      // rog_gather_many workgroup
-constexpr int kBatchPeerUnroll = ROG_BATCH_PEER_UNROLL;  // its PEER vectors per thread
 constexpr bool kNtStore = ROG_NT_STORE != 0;      // non-temporal 16-byte stores
 // Source bytes from which 16-byte loads are non-temporal: below it the payloads
 // may still sit in the 256 MB Infinity Cache, and cached loads then win.
@@ -85,6 +73,12 @@ constexpr uint32_t kGridCap = ROG_GRID_CAP;       // workgroups of one launch, a
 // 256 measured best (vs 16: +4.7 % on 8 x 64 MiB at offsets 1/3).
 constexpr uint64_t kBodyAlign = ROG_BODY_ALIGN;
 static_assert(kBodyAlign >= 16 && (kBodyAlign & (kBodyAlign - 1)) == 0, "body alignment");
+// Workgroups are dispatched to the 8 XCDs round-robin.  PEER and BATCH
+// launches hand each XCD runs of kXcdRun consecutive 1 KiB chunks (128 measured
+// best of 1..1024: a misaligned chunk straddles one cache line with its
+// neighbour, which then sits in the same L2).
+constexpr uint32_t kXcds = 8;
+constexpr uint32_t kXcdRun = ROG_XCD_RUN;
 
 // Exact floor(v / d) for every 32-bit v by one 32x32 high multiply:
 // t = mulhi(v, magic); q = (t + ((v - t) >> sh1)) >> sh2.
@@ -98,38 +92,21 @@ struct Divider {
 
 Divider make_divider(uint32_t d);
 
-// How the PEER kernel cuts a payload that is not 16-byte aligned on both sides
-// (source address sa, destination address da, S bytes): bytes [0, lo) and
-// [hi, S) move one by one; bytes [lo, hi) as aligned 16-byte stores whose data
-// comes from the aligned source vectors that start at sa + lo - delta -- one per
-// output vector when delta == 0, else two neighbours funnel-shifted by delta
-// bytes.  The cut keeps every one of those aligned source vectors inside
-// [sa, sa + S): vectors whose source blocks would reach outside move as bytes.
+// How the PEER path cuts a payload that is not 16-byte aligned on both sides
+// (destination address da, S bytes): bytes [0, lo) and [hi, S) move one by one,
+// bytes [lo, hi) as aligned 16-byte stores, each fed by one 16-byte load from
+// the source at the same payload offset (aligned or not).  The body starts at
+// the first kBodyAlign-aligned destination byte, so every read lies inside
+// [sa, sa + S) and every store is aligned.
 struct PeerSplit {
-    uint64_t lo;      // first byte of the aligned body (da + lo is 16-byte aligned)
+    uint64_t lo;      // first byte of the body (da + lo is kBodyAlign-aligned)
     uint64_t hi;      // end of the body; (hi - lo) % 16 == 0; lo == hi: no body
-    uint32_t delta;   // (sa + lo) % 16
 };
 
-__host__ __device__ inline PeerSplit split_payload(uint64_t sa, uint64_t da, uint64_t S) {
-    // The body starts at a kBodyAlign-aligned destination byte, so that the
-    // 1 KiB a wave stores covers whole cache lines.
+__host__ __device__ inline PeerSplit split_payload(uint64_t da, uint64_t S) {
     const uint64_t to_line = (kBodyAlign - (da & (kBodyAlign - 1))) & (kBodyAlign - 1);
-    const uint64_t h = to_line < S ? to_line : S;
-    const uint64_t nb = (S - h) >> 4;                   // aligned output vectors after h
-    const uint32_t delta = uint32_t((sa + h) & 15);
-    uint64_t jlo = 0, jhi = nb;
-    if (delta != 0) {
-        // Output vector j reads source blocks at P0 + 16j and P0 + 16(j+1),
-        // P0 = sa + h - delta; both must lie inside [sa, sa + S).
-        const uint64_t p0 = sa + h - delta;
-        jlo = p0 < sa ? 1 : 0;
-        const uint64_t lim = (sa + S - p0) >> 4;
-        jhi = lim > 1 ? lim - 1 : 0;
-        if (jhi > nb) jhi = nb;
-    }
-    if (jhi <= jlo) return PeerSplit{S, S, 0};           // too small for a body
-    return PeerSplit{h + 16 * jlo, h + 16 * jhi, delta};
+    if (S < to_line + 16) return PeerSplit{S, S};          // too small for a body
+    return PeerSplit{to_line, to_line + ((S - to_line) & ~uint64_t(15))};
 }
 
 // ---------------------------------------------------------------------------
@@ -147,30 +124,36 @@ struct FlatArgs {
 };
 
 // PEER: each payload is its own copy job, cut by split_payload into a byte
-// head, a body of aligned 16-byte stores (from aligned or funnel-shifted
-// aligned source vectors) and a byte tail.
-// Multi-WG: workgroup b works on payload b / blocks_per_peer; single-WG
-// (blocks_per_peer unused): the one workgroup takes the payloads in turn.
+// head, a body of aligned 16-byte stores and a byte tail.
+// Multi-WG: chunk b of n_chunks = W * chunks_per_peer is chunk b % chunks_per_peer
+// of payload b / chunks_per_peer (cdiv divides by chunks_per_peer); a chunk is
+// 64 body vectors, and chunk 0 also moves the head and tail bytes.
+// Single-WG (chunk fields unused): the one workgroup takes the payloads in turn.
 struct PeerArgs {
     const void *src[kMaxPeers];
     void *out;
     uint64_t S;
-    uint32_t blocks_per_peer;
     uint32_t W;
+    uint32_t chunks_per_peer;
+    uint32_t n_chunks;
+    Divider cdiv;
 };
 
-// One tensor of a batch.  Workgroups [first_block, first_block + n_blocks) of the
-// launch belong to it.
+// One tensor of a batch.  Chunks [first_chunk, first_chunk + n_chunks) of the
+// launch belong to it.  FLAT tensors: chunk c covers output vectors
+// [64c, 64c + 64), the payload found by div (divides by vpr).  PEER tensors:
+// chunk c is chunk c % chunks_per_peer of payload c / chunks_per_peer (div
+// divides by chunks_per_peer).
 struct BatchTensor {
     uint64_t out;
     uint64_t S;
-    uint32_t first_block;
-    uint32_t n_blocks;
+    uint32_t first_chunk;
+    uint32_t n_chunks;
     uint32_t flat;              // 1: FLAT tensor, 0: PEER tensor
     uint32_t vpr;               // FLAT: vectors per rank
     uint32_t n_vec;             // FLAT: W * vpr
-    uint32_t blocks_per_peer;   // PEER
-    Divider div;                // FLAT
+    uint32_t chunks_per_peer;   // PEER
+    Divider div;
 };
 
 struct BatchArgs {
@@ -178,6 +161,7 @@ struct BatchArgs {
     BatchTensor t[kMaxBatch];
     uint32_t n;
     uint32_t W;
+    uint32_t n_chunks;                // all tensors' chunks
 };
 
 static_assert(sizeof(BatchArgs) <= 4096, "kernel arguments must stay below 4 KiB");

@@ -15,16 +15,19 @@
 //    is found once per chunk, in scalar registers, by one 32-bit multiply-high
 //    (no division on the device at all); a chunk that crosses a payload
 //    boundary walks the few payloads it touches with per-lane range masks.
-//  * PEER kernel (anything else): each payload on its own -- a byte head, a
-//    body of aligned 16-byte stores and a byte tail; the body loads aligned
-//    source vectors, funnel-shifted when source and destination are misaligned
-//    differently (the pages' fallback copies such payloads byte by byte; the
-//    bytes written are the same).  Multi-WG, the grid is split into W groups of
-//    workgroups, one group per payload, so all payloads are copied at once;
-//    single-WG, the one workgroup takes the payloads in turn.
-//  * BATCH kernel (rog_gather_many): one launch; each workgroup finds its
-//    tensor by a scalar binary search over the tensors' first workgroups and
-//    runs the FLAT or PEER work of that tensor.
+//  * PEER kernel (anything else): each payload on its own -- a byte head up to
+//    a 256-byte boundary of its destination, a body of aligned 16-byte stores,
+//    a byte tail.  Every body store is fed by one 16-byte load from the source
+//    at the same payload offset, at whatever byte alignment the source has
+//    (gfx950 global loads run in unaligned-access mode under the HSA runtime:
+//    still one global_load_dwordx4).  The pages' fallback copies such payloads
+//    byte by byte ("vectors where aligned, byte-wise tail"); the bytes written
+//    are the same.  Multi-WG, the body is cut into 1 KiB chunks, one wave per
+//    chunk, all payloads at once; single-WG, the one workgroup takes the
+//    payloads in turn.
+//  * BATCH kernel (rog_gather_many): one launch; every wave finds its tensor by
+//    a scalar binary search over the tensors' first chunks and does one FLAT
+//    or PEER chunk of that tensor.
 //
 // Everything a launch needs is in its kernel arguments; there are no scratch
 // buffers, atomics or inter-workgroup synchronisation, and every output byte
@@ -36,12 +39,22 @@
 namespace rog {
 
 typedef uint32_t vec16 __attribute__((ext_vector_type(4)));
+// The same 16 bytes at any byte address.
+typedef uint32_t vec16u __attribute__((ext_vector_type(4), aligned(1)));
 
 // 16-byte loads: non-temporal (streamed past the caches) when NT, else cached.
 template <bool NT>
 __device__ __forceinline__ vec16 ld16(const vec16 *p) {
     if constexpr (NT) return __builtin_nontemporal_load(p);
     else return *p;
+}
+
+// The 16 bytes at p, any byte alignment.
+template <bool NT>
+__device__ __forceinline__ vec16 ldu16(const uint8_t *p) {
+    const vec16u *q = reinterpret_cast<const vec16u *>(p);
+    if constexpr (NT) return __builtin_nontemporal_load(q);
+    else return *q;
 }
 
 __device__ __forceinline__ void st16(vec16 *p, vec16 v) {
@@ -59,186 +72,129 @@ __device__ __forceinline__ uint32_t divide(uint32_t v, const Divider &d) {
     return (t + ((v - t) >> d.sh1)) >> d.sh2;
 }
 
+// Workgroups go to the 8 XCDs round-robin (b mod 8).  Hand each XCD runs of
+// kXcdRun consecutive chunks, so that neighbouring chunks -- which share the
+// cache line a misaligned chunk straddles -- meet in the same L2.  A bijection
+// on [0, n): whole spans of 8 * kXcdRun are permuted, the rest is left as is.
+__device__ __forceinline__ uint32_t xcd_grouped(uint32_t b, uint32_t n) {
+    constexpr uint32_t kSpan = kXcds * kXcdRun;
+    if (kXcdRun <= 1 || b >= n - n % kSpan) return b;
+    const uint32_t x = b % kXcds, k = b / kXcds;
+    return (k / kXcdRun) * kSpan + x * kXcdRun + k % kXcdRun;
+}
+
 // ---------------------------------------------------------------------------
-// FLAT: vectors [0, n_vec) of one gather, by workgroups `block` of `nblocks`,
-// each of `waves` waves.  Vector v comes from payload r = v / vpr at index
-// v - r*vpr.  A wave owns chunks of 64*U consecutive vectors, grid-strided.
+// FLAT: vectors [0, n_vec) of one gather.  Vector v comes from payload
+// r = v / vpr at index v - r*vpr.  Chunk c is vectors [64*U*c, 64*U*(c + 1)).
 // ---------------------------------------------------------------------------
+template <int U, bool NTL>
+__device__ __forceinline__ void flat_chunk(const void *const *src, vec16 *o, uint32_t n_vec,
+                                           uint32_t vpr, const Divider &div, uint32_t c) {
+    constexpr uint32_t kChunk = 64 * U;
+    const uint32_t lane = __lane_id();
+    // n_vec < 2^32 and b is a multiple of kChunk below n_vec, so no expression
+    // below wraps (b + kChunk - 1 <= 2^32 - 1; seg_lo + vpr <= n_vec).
+    const uint32_t b = c * kChunk;                  // first vector of the chunk
+    const uint32_t n = min(n_vec - b, kChunk);      // vectors in the chunk
+    const uint32_t e = b + n;                       // chunk end
+    const uint32_t r = divide(b, div);              // payload of b (scalar)
+    const uint32_t seg_lo = r * vpr;
+    if (e <= seg_lo + vpr) {
+        // The whole chunk lies in payload r: scalar bases, lane offsets.
+        const vec16 *s = static_cast<const vec16 *>(src[r]) + (b - seg_lo);
+        vec16 *d = o + b;
+        if (n == kChunk) {
+            vec16 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = ld16<NTL>(s + u * 64 + lane);
+#pragma unroll
+            for (int u = 0; u < U; ++u) st16(d + u * 64 + lane, v[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t k = u * 64 + lane;
+                if (k < n) st16(d + k, ld16<NTL>(s + k));
+            }
+        }
+    } else {
+        // The chunk crosses payload boundaries (rare unless payloads are
+        // small): each lane finds its own payload with the same multiply-high
+        // and reads that payload's base pointer itself, so all lanes proceed at
+        // once whatever the number of payloads in the chunk.
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t k = b + u * 64 + lane;
+            if (k < e) {
+                const uint32_t rk = divide(k, div);
+                const vec16 *s = static_cast<const vec16 *>(src[rk]);
+                st16(o + k, ld16<NTL>(s + (k - rk * vpr)));
+            }
+        }
+    }
+}
+
+// FLAT by workgroups `block` of `nblocks`, each of `waves` waves: a wave owns
+// chunks wave_id, wave_id + stride, ... (grid-stride over a capped grid).
 template <int U, bool NTL>
 __device__ __forceinline__ void flat_copy(const void *const *src, void *out, uint32_t n_vec,
                                           uint32_t vpr, const Divider &div, uint32_t block,
                                           uint32_t nblocks, uint32_t waves) {
     constexpr uint32_t kChunk = 64 * U;
-    const uint32_t lane = __lane_id();
     const uint32_t wave = uniform(threadIdx.x / 64);
-    // n_vec < 2^32 and b is a multiple of kChunk below n_vec, so no expression
-    // below wraps (b + kChunk - 1 <= 2^32 - 1; seg_lo + vpr <= n_vec).
     const uint32_t n_chunks = n_vec / kChunk + (n_vec % kChunk != 0);
     const uint32_t stride = nblocks * waves;
     vec16 *o = static_cast<vec16 *>(out);
+    for (uint32_t c = block * waves + wave; c < n_chunks; c += stride)
+        flat_chunk<U, NTL>(src, o, n_vec, vpr, div, c);
+}
 
-    for (uint32_t c = block * waves + wave; c < n_chunks; c += stride) {
-        const uint32_t b = c * kChunk;                  // first vector of the chunk
-        const uint32_t n = min(n_vec - b, kChunk);      // vectors in the chunk
-        const uint32_t e = b + n;                       // chunk end
-        const uint32_t r = divide(b, div);              // payload of b (scalar)
-        const uint32_t seg_lo = r * vpr;
-        if (e <= seg_lo + vpr) {
-            // The whole chunk lies in payload r: scalar bases, lane offsets.
-            const vec16 *s = static_cast<const vec16 *>(src[r]) + (b - seg_lo);
-            vec16 *d = o + b;
-            if (n == kChunk) {
-                vec16 v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) v[u] = ld16<NTL>(s + u * 64 + lane);
-#pragma unroll
-                for (int u = 0; u < U; ++u) st16(d + u * 64 + lane, v[u]);
-            } else {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const uint32_t k = u * 64 + lane;
-                    if (k < n) st16(d + k, ld16<NTL>(s + k));
-                }
-            }
-        } else {
-            // The chunk crosses payload boundaries (rare unless payloads are
-            // small): each lane finds its own payload with the same multiply-
-            // high and reads that payload's base pointer itself, so all lanes
-            // proceed at once whatever the number of payloads in the chunk.
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t k = b + u * 64 + lane;
-                if (k < e) {
-                    const uint32_t rk = divide(k, div);
-                    const vec16 *s = static_cast<const vec16 *>(src[rk]);
-                    st16(o + k, ld16<NTL>(s + (k - rk * vpr)));
-                }
-            }
-        }
+// ---------------------------------------------------------------------------
+// PEER: one payload of S bytes from s to d, cut by split_payload into a byte
+// head [0, lo), a body [lo, hi) of aligned 16-byte stores -- each fed by the
+// 16 source bytes at the same payload offset, read inside [s, s + S) -- and a
+// byte tail [hi, S).  Every output byte is written exactly once.
+// ---------------------------------------------------------------------------
+
+// One wave: body chunk j (body vectors [64j, 64j + 64)); chunk 0 also moves the
+// head and tail bytes (at most kBodyAlign - 1 and 15 of them).
+template <bool NTL>
+__device__ __forceinline__ void peer_chunk(const uint8_t *s, uint8_t *d, uint64_t S, uint32_t j) {
+    const uint32_t lane = __lane_id();
+    const PeerSplit cut = split_payload(reinterpret_cast<uintptr_t>(d), S);
+    if (j == 0) {
+        for (uint64_t i = lane; i < cut.lo; i += 64) d[i] = s[i];
+        for (uint64_t i = cut.hi + lane; i < S; i += 64) d[i] = s[i];
     }
+    const uint64_t off = cut.lo + 16 * (uint64_t(j) * 64 + lane);
+    if (off < cut.hi) st16(reinterpret_cast<vec16 *>(d + off), ldu16<NTL>(s + off));
 }
 
-// ---------------------------------------------------------------------------
-// PEER: one payload of S bytes from sp to dp by a workgroup of BLOCK threads
-// (BLOCK >= 64); this workgroup takes tiles part, part + parts, ...  Tiles are
-// BLOCK*U 16-byte output vectors; within a tile thread t handles vectors t,
-// t + BLOCK, ... (coalesced).  Tile bases are wave-uniform (scalar registers);
-// lanes add 32-bit offsets.
-// ---------------------------------------------------------------------------
-
-// Bytes [lo, hi) of a payload, one byte per thread per step (heads and tails).
-__device__ __forceinline__ void copy_bytes(const uint8_t *s, uint8_t *d, uint64_t lo, uint64_t hi,
-                                           uint32_t BLOCK) {
-    for (uint64_t i = lo + threadIdx.x; i < hi; i += BLOCK) d[i] = s[i];
-}
-
-// count aligned 16-byte vectors from s to d.
+// One workgroup of nt threads, the whole payload: head and tail bytes, then the
+// body in tiles of nt * U vectors (U loads in flight per thread).
 template <int U, bool NTL>
-__device__ __forceinline__ void vec_body(const vec16 *s0, vec16 *d0, uint64_t count, uint32_t part,
-                                         uint32_t parts, uint32_t BLOCK) {
+__device__ __forceinline__ void peer_whole(const uint8_t *s, uint8_t *d, uint64_t S, uint32_t nt) {
     const uint32_t tid = threadIdx.x;
-    const uint32_t kTile = BLOCK * U;
-    for (uint64_t base = uint64_t(part) * kTile; base < count; base += uint64_t(parts) * kTile) {
-        const vec16 *s = s0 + base;
-        vec16 *d = d0 + base;
-        if (base + kTile <= count) {
+    const PeerSplit cut = split_payload(reinterpret_cast<uintptr_t>(d), S);
+    for (uint64_t i = tid; i < cut.lo; i += nt) d[i] = s[i];
+    for (uint64_t i = cut.hi + tid; i < S; i += nt) d[i] = s[i];
+    const uint8_t *sb = s + cut.lo;
+    vec16 *db = reinterpret_cast<vec16 *>(d + cut.lo);
+    const uint64_t count = (cut.hi - cut.lo) >> 4;
+    const uint64_t tile = uint64_t(nt) * U;
+    for (uint64_t base = 0; base < count; base += tile) {
+        if (base + tile <= count) {
             vec16 v[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = ld16<NTL>(s + (u * BLOCK + tid));
+            for (int u = 0; u < U; ++u) v[u] = ldu16<NTL>(sb + 16 * (base + u * nt + tid));
 #pragma unroll
-            for (int u = 0; u < U; ++u) st16(d + (u * BLOCK + tid), v[u]);
+            for (int u = 0; u < U; ++u) st16(db + base + u * nt + tid, v[u]);
         } else {
-            const uint32_t n = uint32_t(count - base);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const uint32_t k = u * BLOCK + tid;
-                if (k < n) st16(d + k, ld16<NTL>(s + k));
+                const uint64_t k = base + u * nt + tid;
+                if (k < count) st16(db + k, ldu16<NTL>(sb + 16 * k));
             }
         }
-    }
-}
-
-// The 16 bytes that start 4*Q + sh bytes into the 32 bytes a:b (little-endian
-// byte order, a first): each output dword joins two neighbouring input dwords
-// with one v_alignbyte_b32.
-template <int Q>
-__device__ __forceinline__ vec16 funnel(const vec16 &a, const vec16 &b, uint32_t sh) {
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    vec16 r;
-    r.x = __builtin_amdgcn_alignbyte(w[Q + 1], w[Q + 0], sh);
-    r.y = __builtin_amdgcn_alignbyte(w[Q + 2], w[Q + 1], sh);
-    r.z = __builtin_amdgcn_alignbyte(w[Q + 3], w[Q + 2], sh);
-    r.w = __builtin_amdgcn_alignbyte(w[Q + 4], w[Q + 3], sh);
-    return r;
-}
-
-// count aligned 16-byte output vectors d[k], each the 16 bytes that start
-// delta = 4*Q + sh bytes into the aligned source vectors p[k], p[k+1].  Both
-// loads are cached: lane t's p[k+1] is lane t+1's p[k], fetched by the same
-// wave an instruction earlier, so the second load is served by the cache.
-// (Measured faster than streaming loads, and than passing the neighbour's
-// block across lanes with a DPP wavefront shift.)
-template <int U, int Q>
-__device__ __forceinline__ void shift_body(const vec16 *p0, vec16 *d0, uint64_t count, uint32_t sh,
-                                           uint32_t part, uint32_t parts, uint32_t BLOCK) {
-    const uint32_t tid = threadIdx.x;
-    const uint32_t kTile = BLOCK * U;
-    for (uint64_t base = uint64_t(part) * kTile; base < count; base += uint64_t(parts) * kTile) {
-        const vec16 *p = p0 + base;
-        vec16 *d = d0 + base;
-        if (base + kTile <= count) {
-            vec16 a[U], b[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                a[u] = ld16<false>(p + (u * BLOCK + tid));
-                b[u] = ld16<false>(p + (u * BLOCK + tid + 1));
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) st16(d + (u * BLOCK + tid), funnel<Q>(a[u], b[u], sh));
-        } else {
-            const uint32_t n = uint32_t(count - base);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const uint32_t k = u * BLOCK + tid;
-                if (k < n) st16(d + k, funnel<Q>(ld16<false>(p + k), ld16<false>(p + k + 1), sh));
-            }
-        }
-    }
-}
-
-// One payload.  The destination is cut at 256-byte boundaries (split_payload):
-// a byte head, a body of aligned 16-byte stores, a byte tail.  The body's data
-// comes from aligned source vectors -- one per output vector when source and
-// destination are equally misaligned (in particular both 16-byte aligned),
-// else two neighbours funnel-shifted.  Body vectors whose aligned source
-// vectors would reach outside the payload go to the head or tail, so every
-// read stays inside [sp, sp + S).  Every output byte is written exactly once.
-template <int U, bool NTL>
-__device__ __forceinline__ void peer_copy(const void *sp, void *dp, uint64_t S, uint32_t part,
-                                          uint32_t parts, uint32_t BLOCK) {
-    const uint8_t *s = static_cast<const uint8_t *>(sp);
-    uint8_t *d = static_cast<uint8_t *>(dp);
-    const PeerSplit cut = split_payload(reinterpret_cast<uintptr_t>(s), reinterpret_cast<uintptr_t>(d), S);
-    const uint64_t lo = cut.lo, hi = cut.hi;
-    const uint32_t delta = cut.delta;
-    if (part == 0) {
-        copy_bytes(s, d, 0, lo, BLOCK);
-        copy_bytes(s, d, hi, S, BLOCK);
-    }
-    if (hi == lo) return;
-    vec16 *D = reinterpret_cast<vec16 *>(d + lo);
-    const uint64_t count = (hi - lo) >> 4;
-    if (delta == 0) {
-        vec_body<U, NTL>(reinterpret_cast<const vec16 *>(s + lo), D, count, part, parts, BLOCK);
-        return;
-    }
-    const vec16 *P = reinterpret_cast<const vec16 *>(s + lo - delta);
-    const uint32_t sh = delta & 3;
-    switch (delta >> 2) {
-    case 0: shift_body<U, 0>(P, D, count, sh, part, parts, BLOCK); break;
-    case 1: shift_body<U, 1>(P, D, count, sh, part, parts, BLOCK); break;
-    case 2: shift_body<U, 2>(P, D, count, sh, part, parts, BLOCK); break;
-    default: shift_body<U, 3>(P, D, count, sh, part, parts, BLOCK); break;
     }
 }
 
@@ -257,13 +213,16 @@ __global__ __launch_bounds__(kSingleBlock) void rog_flat_single_kernel(FlatArgs 
     flat_copy<kSingleUnroll, NTL>(a.src, a.out, a.n_vec, a.vpr, a.div, 0, 1, blockDim.x / 64);
 }
 
-// Multi-WG PEER: W groups of blocks_per_peer workgroups, one group per payload.
-template <int BLOCK, bool NTL>
-__global__ __launch_bounds__(BLOCK) void rog_peer_kernel(PeerArgs a) {
-    const uint32_t r = blockIdx.x / a.blocks_per_peer;
-    const uint32_t part = blockIdx.x - r * a.blocks_per_peer;
-    peer_copy<kPeerUnroll, NTL>(a.src[r], static_cast<uint8_t *>(a.out) + uint64_t(r) * a.S, a.S, part,
-                                a.blocks_per_peer, BLOCK);
+// Multi-WG PEER: one wave per workgroup and per body chunk, chunks grouped by
+// XCD, grid-strided over the n_chunks = W * chunks_per_peer chunks.
+template <bool NTL>
+__global__ __launch_bounds__(kWaveBlock) void rog_peer_kernel(PeerArgs a) {
+    for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x) {
+        const uint32_t b = xcd_grouped(vb, a.n_chunks);
+        const uint32_t r = divide(b, a.cdiv);
+        peer_chunk<NTL>(static_cast<const uint8_t *>(a.src[r]), static_cast<uint8_t *>(a.out) + uint64_t(r) * a.S,
+                        a.S, b - r * a.chunks_per_peer);
+    }
 }
 
 // Single-WG PEER: one workgroup takes the payloads in turn.  Its block size is
@@ -272,31 +231,33 @@ __global__ __launch_bounds__(BLOCK) void rog_peer_kernel(PeerArgs a) {
 template <bool NTL>
 __global__ __launch_bounds__(kSingleBlock) void rog_peer_single_kernel(PeerArgs a) {
     for (uint32_t r = 0; r < a.W; ++r)
-        peer_copy<kSinglePeerUnroll, NTL>(a.src[r], static_cast<uint8_t *>(a.out) + uint64_t(r) * a.S, a.S,
-                                          0, 1, blockDim.x);
+        peer_whole<kSinglePeerUnroll, NTL>(static_cast<const uint8_t *>(a.src[r]),
+                                           static_cast<uint8_t *>(a.out) + uint64_t(r) * a.S, a.S, blockDim.x);
 }
 
+// BATCH: one wave per workgroup and per chunk of some tensor, chunks grouped by
+// XCD over the whole launch.
 template <bool NTL>
-__global__ __launch_bounds__(kBatchBlock) void rog_batch_kernel(BatchArgs a) {
-    const uint32_t b = blockIdx.x;
-    // Last tensor whose first workgroup is <= b (first_block strictly increases).
-    uint32_t lo = 0, hi = a.n;
-    while (hi - lo > 1) {
-        const uint32_t mid = (lo + hi) / 2;
-        if (a.t[mid].first_block <= b) lo = mid;
-        else hi = mid;
-    }
-    const BatchTensor &t = a.t[lo];
-    const uint32_t lb = b - t.first_block;
-    const void *const *src = a.src + lo * a.W;
-    if (t.flat) {
-        flat_copy<kFlatUnroll, NTL>(src, reinterpret_cast<void *>(t.out), t.n_vec, t.vpr, t.div, lb,
-                                    t.n_blocks, kBatchBlock / 64);
-    } else {
-        const uint32_t r = lb / t.blocks_per_peer;
-        const uint32_t part = lb - r * t.blocks_per_peer;
-        peer_copy<kBatchPeerUnroll, NTL>(src[r], reinterpret_cast<uint8_t *>(t.out) + uint64_t(r) * t.S, t.S,
-                                         part, t.blocks_per_peer, kBatchBlock);
+__global__ __launch_bounds__(kWaveBlock) void rog_batch_kernel(BatchArgs a) {
+    for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x) {
+        const uint32_t c = xcd_grouped(vb, a.n_chunks);
+        // Last tensor whose first chunk is <= c (first_chunk strictly increases).
+        uint32_t lo = 0, hi = a.n;
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) / 2;
+            if (a.t[mid].first_chunk <= c) lo = mid;
+            else hi = mid;
+        }
+        const BatchTensor &t = a.t[lo];
+        const uint32_t lc = c - t.first_chunk;
+        const void *const *src = a.src + lo * a.W;
+        if (t.flat) {
+            flat_chunk<kFlatUnroll, NTL>(src, reinterpret_cast<vec16 *>(t.out), t.n_vec, t.vpr, t.div, lc);
+        } else {
+            const uint32_t r = divide(lc, t.div);
+            peer_chunk<NTL>(static_cast<const uint8_t *>(src[r]), reinterpret_cast<uint8_t *>(t.out) + uint64_t(r) * t.S,
+                            t.S, lc - r * t.chunks_per_peer);
+        }
     }
 }
 
@@ -336,7 +297,7 @@ rog_status launch_plan(Plan &p, hipStream_t stream) {
         return launch(k, i.grid, i.block, p.flat, stream);
     case ROG_KERNEL_PEER:
         if (single) k = ntl ? kfn(&rog_peer_single_kernel<true>) : kfn(&rog_peer_single_kernel<false>);
-        else        k = ntl ? kfn(&rog_peer_kernel<kPeerBlock, true>) : kfn(&rog_peer_kernel<kPeerBlock, false>);
+        else        k = ntl ? kfn(&rog_peer_kernel<true>) : kfn(&rog_peer_kernel<false>);
         return launch(k, i.grid, i.block, p.peer, stream);
     default:
         return ROG_ERR_INVALID_ARGUMENT;
@@ -372,7 +333,7 @@ ROG_API rog_status rog_gather_many(const rog_gather_desc *descs, int n, int W,
     const rog_status st = rog::plan_batch(descs, n, W, &args, &grid, &ntl);
     if (st != ROG_OK || grid == 0) return st;
     const void *k = ntl ? rog::kfn(&rog::rog_batch_kernel<true>) : rog::kfn(&rog::rog_batch_kernel<false>);
-    return rog::launch(k, grid, rog::kBatchBlock, args, stream);
+    return rog::launch(k, grid, rog::kWaveBlock, args, stream);
 }
 
 ROG_API rog_status rog_plan(const void *const *srcs, int W, size_t bytes_per_rank,

@@ -98,12 +98,11 @@ uint32_t flat_blocks(uint64_t n_vec, int block, int unroll, uint32_t cap) {
     return uint32_t(std::max<uint64_t>(1, std::min<uint64_t>(blocks, cap)));
 }
 
-// Multi-WG PEER grid: workgroups per payload, enough for one tile of BLOCK*U
-// 16-byte output vectors per workgroup over the largest payload (every payload
-// has at most S/16 body vectors, aligned or not).
-uint32_t peer_blocks_per_peer(int W, size_t S, int block, int unroll, uint32_t cap) {
-    const uint64_t tiles = std::max<uint64_t>(1, ceil_div(S / 16, uint64_t(block) * unroll));
-    return uint32_t(std::min<uint64_t>(tiles, cap / uint32_t(W)));
+// Multi-WG PEER: 1 KiB body chunks per payload, enough for the largest body
+// (every payload has at most S/16 body vectors, whatever its alignment).
+// S/16 < 2^32 / W, so W * chunks_per_peer stays below 2^26 + W.
+uint32_t peer_chunks_per_peer(size_t S) {
+    return uint32_t(std::max<uint64_t>(1, ceil_div(S / 16, 64)));
 }
 
 uint32_t round_up_64(uint64_t threads) {
@@ -165,12 +164,19 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
         a.out = const_cast<void *>(out);
         a.S = S;
         a.W = uint32_t(W);
-        a.blocks_per_peer = single ? 0 : peer_blocks_per_peer(W, S, kPeerBlock, kPeerUnroll, max_grid(kPeerBlock));
-        info.block = single ? peer_single_block(S) : kPeerBlock;
         info.kernel = ROG_KERNEL_PEER;
         info.vec_ok_mask = vec_ok_mask(srcs, W, S, out);
         info.units = total;
-        info.grid = single ? 1 : a.blocks_per_peer * uint32_t(W);
+        if (single) {
+            info.block = peer_single_block(S);
+            info.grid = 1;
+        } else {
+            a.chunks_per_peer = peer_chunks_per_peer(S);
+            a.n_chunks = a.chunks_per_peer * uint32_t(W);
+            a.cdiv = make_divider(a.chunks_per_peer);
+            info.block = kWaveBlock;
+            info.grid = std::min(a.n_chunks, max_grid(kWaveBlock));
+        }
     }
     return ROG_OK;
 }
@@ -205,35 +211,39 @@ rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *arg
 
     memset(args, 0, sizeof(*args));
     args->W = uint32_t(W);
-    // Per-tensor workgroup cap keeps the launch's total within max_grid.
-    const uint32_t cap = max_grid(kBatchBlock) / uint32_t(kMaxBatch);
+    // One chunk per wave: 64 * kFlatUnroll output vectors of a FLAT tensor, 64
+    // body vectors of one payload of a PEER tensor.  Each tensor has fewer than
+    // 2^26 + W chunks, so the batch's chunk count fits 32 bits.
     uint64_t next = 0;
     uint32_t k = 0;
     for (int t = 0; t < n; ++t) {
-        if (!totals[t]) continue;           // empty tensors get no workgroups
+        if (!totals[t]) continue;           // empty tensors get no chunks
         const rog_gather_desc &d = descs[t];
         const size_t S = d.bytes_per_rank;
         BatchTensor &bt = args->t[k];
         for (int r = 0; r < W; ++r) args->src[k * uint32_t(W) + uint32_t(r)] = d.srcs[r];
         bt.out = addr(d.out);
         bt.S = S;
-        bt.first_block = uint32_t(next);
+        bt.first_chunk = uint32_t(next);
         if (is_flat(d.srcs, W, S, d.out)) {
             bt.flat = 1;
             bt.n_vec = uint32_t(totals[t] / 16);
             bt.vpr = uint32_t(S / 16);
             bt.div = make_divider(bt.vpr);
-            bt.n_blocks = flat_blocks(bt.n_vec, kBatchBlock, kFlatUnroll, cap);
+            bt.n_chunks = uint32_t(ceil_div(bt.n_vec, 64 * uint64_t(kFlatUnroll)));
         } else {
             bt.flat = 0;
-            bt.blocks_per_peer = peer_blocks_per_peer(W, S, kBatchBlock, kBatchPeerUnroll, cap);
-            bt.n_blocks = bt.blocks_per_peer * uint32_t(W);
+            bt.chunks_per_peer = peer_chunks_per_peer(S);
+            bt.div = make_divider(bt.chunks_per_peer);
+            bt.n_chunks = bt.chunks_per_peer * uint32_t(W);
         }
-        next += bt.n_blocks;
+        next += bt.n_chunks;
         ++k;
     }
+    if (next > UINT32_MAX) return ROG_ERR_TOO_LARGE;
     args->n = k;
-    *grid = uint32_t(next);
+    args->n_chunks = uint32_t(next);
+    *grid = uint32_t(std::min<uint64_t>(next, max_grid(kWaveBlock)));
     uint64_t source_bytes = 0;
     for (int t = 0; t < n; ++t) source_bytes += totals[t];
     *nt_loads = source_bytes >= kNtLoadMinBytes;

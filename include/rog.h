@@ -62,8 +62,8 @@ typedef enum {
 typedef enum {
     ROG_KERNEL_NONE = 0,     /* nothing to copy (S == 0): nothing is launched       */
     ROG_KERNEL_FLAT = 1,     /* one flat loop over all peers' 16-byte vectors        */
-    ROG_KERNEL_PEER = 2      /* per payload: byte head, aligned 16-byte body
-                                (funnel-shifted if needed), byte tail               */
+    ROG_KERNEL_PEER = 2      /* per payload: byte head, 16-byte body (aligned
+                                stores, loads at any alignment), byte tail          */
 } rog_kernel;
 
 /* One tensor of a batch: W source pointers, its output, its per-rank bytes. */
@@ -81,7 +81,8 @@ typedef struct {
     uint32_t block;            /* threads per workgroup                                 */
     uint64_t vec_ok_mask;      /* PEER kernel: bit r set iff srcs[r] and out + r*S are
                                   both 16-byte aligned (the pages' "vectors where
-                                  aligned"; such payloads need no funnel shift)      */
+                                  aligned"); informational, every payload gets a
+                                  16-byte body whatever its alignment              */
     uint64_t units;            /* FLAT: 16-byte vectors W*S/16; PEER: bytes W*S          */
     uint32_t peer_magic;       /* FLAT: floor(v / (S/16)) = (t + ((v - t) >> peer_sh1))  */
     uint32_t peer_sh1;         /*       >> peer_sh2 with t = mulhi32(v, peer_magic),     */
@@ -110,10 +111,10 @@ typedef struct {
  * crossover here is measured on gfx950).  Kernel: FLAT when out, S and every
  * srcs[r] are 16-byte aligned, else PEER (PR #491 "What", copy_rank_ordered).
  * PEER copies each payload as a byte head up to a 256-byte boundary of its
- * destination, a body of aligned 16-byte stores fed by aligned 16-byte loads
- * (funnel-shifted when source and destination are misaligned differently) and
- * a byte tail: the pages' fallback ("vectors where aligned, byte-wise tail")
- * extended to misaligned payloads, same bytes as a byte-by-byte copy.
+ * destination, a body of aligned 16-byte stores, each fed by one 16-byte load
+ * of the source bytes at the same payload offset (at any source alignment),
+ * and a byte tail: the pages' fallback ("vectors where aligned, byte-wise
+ * tail") extended to misaligned payloads, same bytes as a byte-by-byte copy.
  *
  * Errors (nothing enqueued):
  *   ROG_ERR_INVALID_ARGUMENT  srcs NULL; W < 1 or W > rog_max_peers(); S > 0 and

@@ -22,7 +22,7 @@ A = 1 << 20          # a 16-byte aligned fake device address
 FLAT_BLOCK, FLAT_UNROLL = 64, 1      # multi-WG FLAT: threads per WG, vectors per lane per chunk
 SINGLE_UNROLL = 4                    # single-WG FLAT: vectors per lane per chunk
 SINGLE_PEER_UNROLL = 4               # single-WG PEER: 16-byte vectors per thread
-PEER_BLOCK, PEER_UNROLL = 256, 2     # multi-WG PEER: threads per WG, 16-byte vectors per thread
+PEER_BLOCK = 64                      # multi-WG PEER: one wave per workgroup, 64 body vectors each
 NT_LOAD_MIN_BYTES = 384 << 20        # source bytes from which loads are non-temporal
 OK, INVALID, OVERLAP, TOO_LARGE = (rog.ROG_OK, rog.ROG_ERR_INVALID_ARGUMENT,
                                    rog.ROG_ERR_OVERLAP, rog.ROG_ERR_TOO_LARGE)
@@ -234,12 +234,13 @@ def test_grid_sizes():
         s = rog.rog_plan_ptrs(srcs, S, out, rog.ROG_PATH_SINGLE_WG)
         single_chunks = -(-n_vec // (64 * SINGLE_UNROLL))
         assert s["grid"] == 1 and s["block"] == min(1024, max(64, 64 * single_chunks))
-    # PEER multi-WG: W groups, each sized for the largest payload's tiles.
-    S = 100_001
-    srcs = [A + 1 + (S + 4096) * r for r in range(4)]
-    p = rog.rog_plan_ptrs(srcs, S, out, rog.ROG_PATH_MULTI_WG)
-    assert p["kernel"] == "peer" and p["vec_ok_mask"] == 0 and p["block"] == PEER_BLOCK
-    assert p["grid"] == 4 * -(-(S // 16) // (PEER_BLOCK * PEER_UNROLL))
+    # PEER multi-WG: W payloads, each cut into 1 KiB body chunks (enough for
+    # the longest possible body, S // 16 vectors), one wave per chunk.
+    for W, S in [(4, 100_001), (2, 1), (8, 1023), (3, 64 * 16 * 7 + 15)]:
+        srcs = [A + 1 + (S + 4096) * r for r in range(W)]
+        p = rog.rog_plan_ptrs(srcs, S, out, rog.ROG_PATH_MULTI_WG)
+        assert p["kernel"] == "peer" and p["vec_ok_mask"] == 0 and p["block"] == PEER_BLOCK
+        assert p["grid"] == W * max(1, -(-(S // 16) // 64)), (W, S)
 
 
 def test_single_wg_peer_block_fits_the_largest_payload():

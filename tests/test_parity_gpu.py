@@ -257,7 +257,8 @@ def test_every_source_and_destination_misalignment(gpu, W):
 
 
 def test_misaligned_large_payloads(gpu):
-    """Multi-workgroup tiling of the shifted body over payloads of 8 MiB + 5."""
+    """Multi-workgroup 1 KiB chunks of the body over payloads of 8 MiB + 5
+    (32768 chunks: whole spans of XCD-grouped chunks)."""
     S = (8 << 20) + 5
     rng = np.random.default_rng(41)
     payloads = [np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(4)]
@@ -265,3 +266,16 @@ def test_misaligned_large_payloads(gpu):
         placed = gc.Placed(payloads, [io, io + 4, io, 8], oo, gpu)
         gc.run_all_paths(placed, "misaligned large in=%d out=%d" % (io, oo),
                          paths=(rog.ROG_PATH_AUTO, rog.ROG_PATH_MULTI_WG))
+
+
+@pytest.mark.parametrize("W,S", [(5, (256 << 10) + 3), (3, (1 << 20) + 7), (7, 64 * 16 * 150 + 9)])
+def test_chunk_counts_beyond_whole_xcd_spans(gpu, W, S):
+    """Chunk counts that leave a remainder after the whole spans of XCD-grouped
+    chunks (5 x 256 KiB+3: 1280 chunks = one span of 1024 + 256), or fill them
+    exactly (3 x 1 MiB+7: 3072), or have no whole span (7 x 150 chunks); every
+    payload peer-tagged and misaligned differently."""
+    payloads = [wl.tagged_payload(r + 11, S) for r in range(W)]
+    offs = [(3 * r + 1) % 16 for r in range(W)]
+    placed = gc.Placed(payloads, offs, 5, gpu)
+    gc.run_all_paths(placed, "chunk spans W=%d S=%d" % (W, S),
+                     paths=(rog.ROG_PATH_AUTO, rog.ROG_PATH_MULTI_WG))

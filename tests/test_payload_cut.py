@@ -1,8 +1,10 @@
-"""The PEER kernel's cut of a misaligned payload into a byte head, an aligned
-16-byte body and a byte tail (split_payload, shared by host and device code),
-checked exhaustively on the CPU for every source/destination misalignment:
-each output byte is covered exactly once, every aligned source block the body
-reads lies inside the payload, and payloads of 48 bytes or more do get a body."""
+"""The PEER kernel's cut of a payload into a byte head, a 16-byte body and a
+byte tail (split_payload, shared by host and device code), checked exhaustively
+on the CPU for every destination misalignment: each output byte is covered
+exactly once, the body starts on a body-alignment boundary of the destination,
+heads and tails stay short, and every payload long enough gets a body.  The
+body's loads read the source bytes at the body's own payload offsets, so they
+lie inside the payload whenever the body lies inside [0, S)."""
 from __future__ import annotations
 
 import ctypes
@@ -19,7 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 @pytest.fixture(scope="module", params=[None, 16, 64, 128, 256], ids=["built", "A16", "A64", "A128", "A256"])
 def split(request, tmp_path_factory):
-    """The cut as built, and with the body alignment overridden to 16, 128, 256."""
+    """The cut as built, and with the body alignment overridden to 16 .. 256."""
     hipcc = shutil.which("hipcc") or os.path.join(b.ROCM, "bin", "hipcc")
     so = str(tmp_path_factory.mktemp("shim") / "libsplit.so")
     define = [] if request.param is None else ["-DROG_BODY_ALIGN=%d" % request.param]
@@ -29,63 +31,54 @@ def split(request, tmp_path_factory):
                           stderr=subprocess.DEVNULL)
     lib = ctypes.CDLL(so)
     lib.rog_test_body_align.restype = ctypes.c_uint64
-    lib.rog_test_split.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
-                                   ctypes.POINTER(ctypes.c_uint64)]
-    out = (ctypes.c_uint64 * 3)()
+    lib.rog_test_split.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]
+    out = (ctypes.c_uint64 * 2)()
 
-    def f(sa, da, S):
-        lib.rog_test_split(sa, da, S, out)
-        return out[0], out[1], out[2]
+    def f(da, S):
+        lib.rog_test_split(da, S, out)
+        return out[0], out[1]
     f.align = int(lib.rog_test_body_align())
     return f
 
 
-SIZES = list(range(0, 400)) + [255, 256, 257, 4095, 4096, 4097, 65535, 65536, 65537, 262151,
-                                (1 << 30) + 7, (1 << 35) + 3]
+SIZES = list(range(0, 400)) + [255, 256, 257, 271, 272, 273, 4095, 4096, 4097, 65535, 65536, 65537,
+                                262151, (1 << 30) + 7, (1 << 35) + 3]
 
 
-def check(split, sa, da, S):
+def check(split, da, S):
     A = split.align                       # destination alignment of the body
-    lo, hi, delta = split(sa, da, S)
-    assert 0 <= lo <= hi <= S, (sa, da, S, lo, hi)
+    lo, hi = split(da, S)
+    assert 0 <= lo <= hi <= S, (da, S, lo, hi)
     assert (hi - lo) % 16 == 0
+    to_line = (-da) % A                   # bytes up to the first A-aligned destination byte
     if lo == hi:
         assert (lo, hi) == (S, S)        # everything moves as bytes
-        assert S < A + 48, (sa % 16, da % 16, S)
+        assert S < to_line + 16, (da % A, S)
         return
-    assert (da + lo) % 16 == 0            # aligned stores
-    assert (da + lo) % A == 0 or (da + lo) % A == 16   # the body starts on (or one vector past) a line
-    assert delta == (sa + lo) % 16
-    count = (hi - lo) // 16
-    if delta == 0:
-        first, end = sa + lo, sa + hi     # aligned source vectors, one per output
-    else:
-        first = sa + lo - delta           # two neighbouring blocks per output
-        end = first + 16 * (count + 1)
-    assert first % 16 == 0 and end % 16 == 0
-    assert sa <= first and end <= sa + S, (sa % 16, da % 16, S, lo, hi, delta)
-    assert lo <= A + 15 and S - hi <= 31  # heads and tails stay short
+    assert (da + lo) % A == 0             # the body starts on a line
+    assert lo == to_line                  # ... the first one
+    assert S - hi < 16                    # the longest body that fits
+    assert lo <= A - 1
 
 
 def test_every_misalignment_and_small_size(split):
-    base_s, base_d = 1 << 20, 1 << 32
-    for so in range(16):
-        for do in range(0, 2 * split.align, 1 if split.align <= 16 else 3):
-            for S in SIZES:
-                check(split, base_s + so, base_d + do, S)
+    base_d = 1 << 32
+    for do in range(0, 2 * split.align, 1 if split.align <= 16 else 3):
+        for S in SIZES:
+            check(split, base_d + do, S)
 
 
 def test_a_concrete_cut(split):
-    # source at 3 mod 16, destination at 9 mod A: A - 9 bytes reach the first
-    # A-aligned destination byte, where the source sits (3 + A - 9) mod 16 bytes
-    # into its block.
+    # destination at 9 mod A: A - 9 bytes reach the first A-aligned byte, and
+    # the body runs to the last whole vector of the payload.
     A = split.align
-    sa, da, S = (1 << 20) + 3, (1 << 24) + 9, 5000
-    lo, hi, delta = split(sa, da, S)
-    h = A - 9
-    d = (3 + h) % 16
-    want_lo = h + (16 if d > h else 0)    # the first block would start before the payload
-    assert (lo, delta) == (want_lo, (3 + want_lo) % 16)
-    # the last body vector's second source block ends inside the payload
-    assert sa + lo - delta + 16 * ((hi - lo) // 16 + 1) <= sa + S
-    assert S - hi <= 31
+    da, S = (1 << 24) + 9, 5000
+    lo, hi = split(da, S)
+    assert lo == A - 9
+    assert hi == lo + 16 * ((S - lo) // 16)
+    assert S - hi < 16
+
+
+def test_aligned_destination_has_no_head(split):
+    lo, hi = split(1 << 40, 4096 + 5)
+    assert lo == 0 and hi == 4096
