@@ -16,8 +16,10 @@ calls), for the per-call p50.
 Besides the headline line the run measures: the same gather with every payload
 and the output at odd byte offsets (the per-payload path); small gathers (the
 pages' 1 - 128 KiB per-rank sizes at 2 and 8 payloads), per call and replayed
-from a HIP graph of 100 calls; the batched gather (16 tensors, W = 4, one
-launch); the device-to-device copy ceiling; and the CPU oracle on a bounded
+from a HIP graph of 100 calls, next to the eager floor of one tiny torch
+kernel timed the same way; the batched gather (16 tensors, W = 4, one launch);
+the device-to-device copy ceiling; aligned gathers with 64 - 512 MiB outputs,
+warm and with rotating buffer sets (cold); and the CPU oracle on a bounded
 sample of the headline workload.
 
 Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
@@ -313,6 +315,76 @@ def d2d_ceiling(torch, device, nbytes, steps, warmup):
             "how": "torch copy_ of one contiguous buffer (hipMemcpyAsync device to device)"}
 
 
+SWEEP_OUT_MIB = (64, 128, 256, 512)
+SWEEP_FOOTPRINT = 2 << 30      # bytes of rotating buffer sets per cold case (8 x the 256 MB cache)
+
+
+def bandwidth_sweep(torch, rog, device, calls, out_mib=SWEEP_OUT_MIB, footprint=SWEEP_FOOTPRINT):
+    """Aligned gathers with outputs of 64 - 512 MiB at W = 2 and 8 (the north
+    star's "outputs >= 64 MiB"), timed two ways over ``calls`` back-to-back
+    launches: warm, the same buffers every call (as the pages time a call), and
+    cold, rotating through K buffer sets that together span ``footprint`` bytes,
+    so that no call finds its sources in the 256 MB Infinity Cache.  Sampled
+    bytes of every set are checked against its sources."""
+    lib = rog.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    g = torch.Generator(device=device)
+    g.manual_seed(20260)
+    rows = []
+    for W in (2, 8):
+        for mib in out_mib:
+            S = (mib << 20) // W
+            K = max(1, footprint // (2 * W * S))
+            sets = []
+            for _ in range(K):
+                srcs = [torch.randint(0, 256, (S,), dtype=torch.uint8, device=device, generator=g)
+                        for _ in range(W)]
+                out = torch.empty(W * S, dtype=torch.uint8, device=device)
+                sets.append((srcs, out, (ctypes.c_void_p * W)(*[x.data_ptr() for x in srcs]),
+                             ctypes.c_void_p(out.data_ptr())))
+
+            def run(seq):
+                for _, _, ptrs, o in seq[:K + 1]:
+                    if lib.rog_gather(ptrs, W, S, o, stream) != 0:
+                        raise RuntimeError("rog_gather failed")
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _, _, ptrs, o in seq:
+                    lib.rog_gather(ptrs, W, S, o, stream)
+                e1.record()
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) / len(seq)
+
+            warm_ms = run([sets[0]] * calls)
+            cold_ms = run([sets[i % K] for i in range(max(calls, 2 * K))])
+            for srcs, out, _, _ in sets:
+                for r in range(W):
+                    for lo in (0, S // 2, S - 1024):
+                        if not torch.equal(out[r * S + lo: r * S + lo + 1024], srcs[r][lo:lo + 1024]):
+                            raise AssertionError("sweep gather W=%d S=%d wrong at rank %d" % (W, S, r))
+            moved = 2 * W * S
+            rows.append({"W": W, "out_MiB": mib, "sets": K,
+                         "warm_GBps": round(gbps(moved, warm_ms), 1),
+                         "warm_pct_of_peak": round(100 * gbps(moved, warm_ms) / PEAK_HBM_GBPS, 1),
+                         "cold_GBps": round(gbps(moved, cold_ms), 1),
+                         "cold_pct_of_peak": round(100 * gbps(moved, cold_ms) / PEAK_HBM_GBPS, 1),
+                         "cold_us_per_gather": round(1e3 * cold_ms, 2)})
+            del sets
+            torch.cuda.empty_cache()
+    return rows
+
+
+def launch_floor(torch, device, steps, warmup):
+    """The eager floor of the per-call p50: one tiny torch kernel (a 1-element
+    fill) issued from Python between the same two event records as a gather."""
+    x = torch.empty(1, dtype=torch.int32, device=device)
+    per_call, _ = time_calls(torch, x.zero_, steps, warmup)
+    s = summarize_ms(per_call)
+    return {"p10_us": round(s["p10_us"], 2), "p50_us": round(s["p50_us"], 2), "p90_us": round(s["p90_us"], 2),
+            "how": "torch zero_ of a 1-element tensor, event-timed like the small gathers"}
+
+
 CROSSOVER_TOTALS = (256, 1024, 4096, 8192, 16384, 32768, 40960, 49152, 65536, 81920, 98304,
                     114688, 131072, 262144, 1 << 20, 4 << 20)
 
@@ -428,10 +500,12 @@ def main(argv=None):
                                       max(10, args.steps // 5), max(2, args.warmup // 5))
     if not args.headline_only:
         extras["latency"] = latency_sweep(torch, rog, wl, device, args.steps, args.warmup)
+        extras["latency_floor"] = launch_floor(torch, device, args.steps, args.warmup)
         extras["latency_in_graph"] = graph_latency(torch, rog, wl, device)
         extras["gather_many"] = batch_bench(torch, rog, wl, device, max(5, args.steps // 5),
                                             max(1, args.warmup // 5))
         extras["d2d_copy_ceiling"] = d2d_ceiling(torch, device, case.W * case.S, 20, 3)
+        extras["bandwidth_sweep"] = bandwidth_sweep(torch, rog, device, 20)
         cpu = cpu_baseline(case, payloads, args.cpu_budget)
     else:
         cpu = None
