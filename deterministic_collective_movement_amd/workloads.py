@@ -1,7 +1,8 @@
-"""Seeded synthetic inputs for the rank-ordered gather.
+"""Seeded synthetic inputs for the rank-ordered gather and the rank-ordered sum.
 
 This module generates input bytes and case lists only.  It holds none of the
-gather's arithmetic: no concatenation, no output layout, no alignment decision.
+methods' arithmetic: no concatenation, no output layout, no alignment decision,
+no addition and no rounding to bf16 of a sum.
 Both the GPU tests and the CPU oracle draw their inputs from here, so both see
 the same bytes.
 
@@ -207,6 +208,109 @@ def config5(index: int = 0, n: int = 16, W: int = 4, max_rows: int = CONFIG5_MAX
             io = oo = 0
         tensors.append(BatchTensor(rows, cols, io, oo))
     return BatchCase(5, index, W, tuple(tensors))
+
+
+# ---------------------------------------------------------------------------
+# Rank-ordered sum (the reduction of a deterministic all-reduce)
+# ---------------------------------------------------------------------------
+
+#: Bytes of one element of each element type of the sum.
+REDUCE_ESIZE = {"f32": 4, "bf16": 2}
+
+
+def reduce_payloads(seed: int, W: int, n: int, dtype: str, kind: str = "uniform") -> List[np.ndarray]:
+    """W payloads of n elements, reproducible from (seed, payload index).
+
+    dtype "f32": float32 arrays; "bf16": uint16 arrays of bf16 bit patterns.
+    kind "uniform": values uniform in [-1, 1) (bf16: the float32 draw cut to its
+    top 16 bits, i.e. rounded toward zero); "bits": uniformly random bit
+    patterns (NaNs, infinities and subnormals included).
+    """
+    out = []
+    for r in range(W):
+        rng = _rng(seed, r)
+        if kind == "bits":
+            b = rng.bytes(n * REDUCE_ESIZE[dtype])
+            out.append(np.frombuffer(b, np.float32 if dtype == "f32" else np.uint16).copy())
+            continue
+        f = rng.random(n, dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
+        out.append(f if dtype == "f32" else (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16))
+    return out
+
+
+@dataclass(frozen=True)
+class ReduceCase:
+    """One rank-ordered sum: W payloads of n elements; payload r starts in_offs[r]
+    elements into its own guarded buffer, the output out_off elements into its."""
+    config: int
+    index: int
+    W: int
+    n: int
+    dtype: str
+    in_offs: Tuple[int, ...]
+    out_off: int
+    kind: str = "uniform"
+
+    @property
+    def seed(self) -> int:
+        return case_seed(self.config, self.index)
+
+    @property
+    def esize(self) -> int:
+        return REDUCE_ESIZE[self.dtype]
+
+    def payloads(self) -> List[np.ndarray]:
+        return reduce_payloads(self.seed, self.W, self.n, self.dtype, self.kind)
+
+    def label(self) -> str:
+        offs = ",".join(str(o) for o in self.in_offs)
+        return f"r{self.config}#{self.index}:W={self.W},n={self.n},{self.dtype},in=[{offs}],out={self.out_off}"
+
+
+REDUCE_SWEEP_W = (2, 8)
+#: Per-rank bytes of the pages' deterministic collective sweep, across the
+#: 256 KiB single-block bound of their all_reduce / reduce_scatter.
+REDUCE_SWEEP_BYTES = (1 * KiB, 8 * KiB, 32 * KiB, 128 * KiB, 256 * KiB, 512 * KiB, 1 * MiB, 4 * MiB)
+
+
+def reduce_config1() -> List[ReduceCase]:
+    """W=2 bf16 payloads of 1 KiB (512 elements), aligned."""
+    return [ReduceCase(11, 0, 2, 512, "bf16", (0, 0), 0)]
+
+
+def reduce_config2() -> List[ReduceCase]:
+    """Size sweep: W in {2, 8} x per-rank 1 KiB .. 4 MiB of bf16, aligned."""
+    cases = []
+    for W in REDUCE_SWEEP_W:
+        for nb in REDUCE_SWEEP_BYTES:
+            cases.append(ReduceCase(12, len(cases), W, nb // 2, "bf16", (0,) * W, 0))
+    return cases
+
+
+REDUCE_TAIL_N = (1, 7, 9, 2047, 32767, 32768, 32769, 131075)
+REDUCE_ELEM_OFFSETS = (0, 1, 3, 8)
+
+
+def reduce_config3() -> List[ReduceCase]:
+    """Alignment / tail sweep: bf16 and f32 x W in {2, 3, 8} x n x element
+    offsets of the sources (all alike) and of the output, plus a mixed-offset
+    case per (dtype, W, n) and random-bit-pattern cases."""
+    cases = []
+    for dtype in ("bf16", "f32"):
+        for W in (2, 3, 8):
+            for n in REDUCE_TAIL_N:
+                for io in REDUCE_ELEM_OFFSETS:
+                    for oo in REDUCE_ELEM_OFFSETS:
+                        cases.append(ReduceCase(13, len(cases), W, n, dtype, (io,) * W, oo))
+                offs = tuple(REDUCE_ELEM_OFFSETS[r % 4] for r in range(W))
+                cases.append(ReduceCase(13, len(cases), W, n, dtype, offs, 1))
+                cases.append(ReduceCase(13, len(cases), W, n, dtype, offs, 0, "bits"))
+    return cases
+
+
+def reduce_config4() -> ReduceCase:
+    """Bandwidth regime: W=8 aligned bf16 payloads of 64 MiB (32 Mi elements)."""
+    return ReduceCase(14, 0, 8, 32 * MiB, "bf16", (0,) * 8, 0)
 
 
 def carve(total: int, offset: int) -> Tuple[int, int]:

@@ -1,4 +1,4 @@
-"""CPU oracle for the rank-ordered gather (Python side).
+"""CPU oracle for the rank-ordered gather and the rank-ordered sum (Python side).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this module.  It shares no code with
@@ -10,6 +10,14 @@ Two independent implementations of one definition:
   gcc by ``build_oracle``): a per-peer byte loop in rank order.
 * ``gather_py`` is a pure-Python per-byte loop for tiny inputs.
 
+The rank-ordered sum (the reduction of a deterministic all-reduce or
+reduce-scatter) likewise has a C form, ``reduce_c``, and a pure-Python form,
+``reduce_py``, which rounds every binary32 addition through ``struct`` (an
+addition of two binary32 numbers in binary64 followed by one rounding to
+binary32 is the correctly rounded binary32 sum: 53 >= 2*24 + 2) and rounds to
+bf16 with its own integer arithmetic.  The reading of the pages it follows is
+stated in ``rog_oracle.c``.
+
 Definition (RL-Align/RL-Kernel PR #491, "perf(cuda): vectorize the deterministic
 all-gather copy and right-size its single-block path", section "What", the
 copy_rank_ordered bullet): the copy is a pure rank-ordered copy with a
@@ -20,9 +28,11 @@ all_gather_many: every tensor of the list gets its own gathered output.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
+import struct
 import subprocess
-from typing import Sequence
+from typing import List, Sequence
 
 import numpy as np
 
@@ -37,7 +47,7 @@ def build_oracle(force: bool = True) -> str:
     """Compile rog_oracle.c into oracle/liboracle.so with gcc -O2."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared",
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
                                "-Wall", "-Wextra", "-Werror", _SRC, "-o", tmp])
         os.replace(tmp, _LIB)
     return _LIB
@@ -57,6 +67,12 @@ def _load():
                                                ctypes.POINTER(ctypes.c_void_p),
                                                ctypes.POINTER(ctypes.c_size_t),
                                                ctypes.c_int, ctypes.c_int]
+        for name, ct in (("rog_oracle_reduce_f32", ctypes.c_void_p), ("rog_oracle_reduce_bf16", ctypes.c_void_p)):
+            f = getattr(lib, name)
+            f.restype = None
+            f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_size_t, ct]
+        lib.rog_oracle_f32_to_bf16.restype = ctypes.c_uint16
+        lib.rog_oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         _lib = lib
     return _lib
 
@@ -120,4 +136,98 @@ def gather_py(srcs: Sequence[bytes], S: int) -> bytearray:
         src = srcs[r]
         for i in range(S):
             out[r * S + i] = src[i]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Rank-ordered sum
+# ---------------------------------------------------------------------------
+
+#: Element types of the sum: numpy storage dtype of one element.
+REDUCE_DTYPES = {"f32": np.dtype(np.float32), "bf16": np.dtype(np.uint16)}
+
+
+def reduce_c(srcs: Sequence[np.ndarray], out: np.ndarray, dtype: str) -> np.ndarray:
+    """out[i] = rank-ordered binary32 sum of srcs[r][i], rounded to ``dtype``.
+
+    ``dtype`` "f32": float32 arrays; "bf16": uint16 arrays holding bf16 bits.
+    All arrays 1-D, equal length, aligned to their element size.
+    """
+    want = REDUCE_DTYPES[dtype]
+    W = len(srcs)
+    if W < 1:
+        raise ValueError("need at least one payload")
+    n = out.shape[0]
+    for a in list(srcs) + [out]:
+        if a.dtype != want or a.ndim != 1 or a.shape[0] != n:
+            raise ValueError("reduce_c wants 1-D %s arrays of one length" % want)
+        if a.ctypes.data % want.itemsize:
+            raise ValueError("elements must be aligned to their size")
+    if not out.flags.writeable:
+        raise ValueError("out must be writeable")
+    ptrs = (ctypes.c_void_p * W)(*[a.ctypes.data for a in srcs])
+    fn = _load().rog_oracle_reduce_f32 if dtype == "f32" else _load().rog_oracle_reduce_bf16
+    fn(ptrs, W, n, out.ctypes.data)
+    return out
+
+
+def f32_to_bf16_c(x: np.ndarray) -> np.ndarray:
+    """The C oracle's binary32 -> bf16 rounding, element by element (uint16 bits)."""
+    lib = _load()
+    return np.array([lib.rog_oracle_f32_to_bf16(float(v)) for v in np.asarray(x, np.float32)], np.uint16)
+
+
+#: Magnitudes from which rounding to binary32 gives infinity: the midpoint
+#: between the largest binary32 number, (2 - 2^-23) 2^127, and 2^128; that
+#: largest number has an odd significand, so the tie itself rounds up.
+_F32_OVERFLOW = 2.0 ** 128 - 2.0 ** 103
+
+
+def _f32(x: float) -> float:
+    """Round a Python float (binary64) to the nearest binary32, ties to even."""
+    if not math.isnan(x) and abs(x) >= _F32_OVERFLOW:
+        return math.copysign(math.inf, x)
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def _f32_bits(x: float) -> int:
+    return struct.unpack("<I", struct.pack("<f", x))[0]
+
+
+def bf16_bits_to_float(h: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", (h & 0xFFFF) << 16))[0]
+
+
+def f32_to_bf16_py(x: float) -> int:
+    """binary32 value -> bf16 bits, nearest-even on the dropped 16 bits; a NaN
+    becomes a quiet NaN with the same sign (payload not specified)."""
+    u = _f32_bits(x)
+    if math.isnan(x):
+        return ((u >> 16) | 0x0040) & 0xFFFF
+    upper, dropped = u >> 16, u & 0xFFFF
+    if dropped > 0x8000 or (dropped == 0x8000 and upper & 1):
+        upper += 1
+    return upper & 0xFFFF
+
+
+def reduce_py(srcs: Sequence[Sequence], dtype: str) -> List:
+    """Pure-Python rank-ordered sum, element by element (tiny inputs only).
+
+    "f32": sequences of Python floats that are binary32 values; returns floats.
+    "bf16": sequences of bf16 bit patterns (ints); returns bf16 bit patterns.
+    """
+    W = len(srcs)
+    n = len(srcs[0])
+    out = []
+    for i in range(n):
+        if dtype == "f32":
+            acc = _f32(float(srcs[0][i]))
+            for r in range(1, W):
+                acc = _f32(acc + _f32(float(srcs[r][i])))
+            out.append(acc)
+        else:
+            acc = bf16_bits_to_float(int(srcs[0][i]))
+            for r in range(1, W):
+                acc = _f32(acc + bf16_bits_to_float(int(srcs[r][i])))
+            out.append(f32_to_bf16_py(acc))
     return out

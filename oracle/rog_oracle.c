@@ -23,6 +23,8 @@
  * mistakes that each pin must catch.
  */
 #include <stddef.h>
+#include <stdint.h>
+#include <string.h>
 
 /* out[r*S + i] = srcs[r][i] for r in [0, W), i in [0, S).  Host memory. */
 void rog_oracle_gather(const unsigned char *const *srcs, int W, size_t S,
@@ -49,4 +51,65 @@ void rog_oracle_gather_many(const unsigned char *const *srcs, unsigned char *con
 {
     for (int t = 0; t < n; ++t)
         rog_oracle_gather(srcs + (size_t)t * W, W, bytes_per_rank[t], outs[t]);
+}
+
+/*
+ * Deterministic sum of W payloads (the reduction at the heart of a
+ * deterministic all-reduce or reduce-scatter).  The pages name these
+ * collectives beside the gather and say only that their results must not
+ * depend on timing (RL-Align/RL-Kernel PR #491, section "Not in this PR", on
+ * the all_reduce / reduce_scatter single-block paths); they print no
+ * arithmetic.  The reading taken here is the plainest deterministic one:
+ *
+ *     out[i] = round( ((x_0[i] + x_1[i]) + x_2[i]) + ... + x_{W-1}[i] )
+ *
+ * with the sum taken in rank order, every addition in IEEE binary32 rounded
+ * to nearest-even, the first term taken as it is (not added to a zero, so a
+ * lone -0 stays -0), bf16 inputs widened to binary32 exactly, and the result
+ * rounded once to the element type (bf16: nearest-even on the 16 dropped
+ * bits; a NaN stays a NaN).  Host memory; elements aligned to their size.
+ * Built with -ffp-contract=off; x86-64 evaluates float in float (SSE).
+ */
+
+static float oracle_bf16_to_f32(uint16_t h)
+{
+    const uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* binary32 -> bf16, round to nearest, ties to even.  A NaN keeps its sign and
+ * top payload bits and is made quiet. */
+uint16_t rog_oracle_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t upper = u >> 16;
+    const uint32_t dropped = u & 0xFFFFu;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (upper & 1u)))
+        upper += 1u;    /* a carry into the exponent is the right result */
+    return (uint16_t)upper;
+}
+
+void rog_oracle_reduce_f32(const float *const *srcs, int W, size_t count, float *out)
+{
+    for (size_t i = 0; i < count; ++i) {
+        float acc = srcs[0][i];
+        for (int r = 1; r < W; ++r)
+            acc = acc + srcs[r][i];
+        out[i] = acc;
+    }
+}
+
+void rog_oracle_reduce_bf16(const uint16_t *const *srcs, int W, size_t count, uint16_t *out)
+{
+    for (size_t i = 0; i < count; ++i) {
+        float acc = oracle_bf16_to_f32(srcs[0][i]);
+        for (int r = 1; r < W; ++r)
+            acc = acc + oracle_bf16_to_f32(srcs[r][i]);
+        out[i] = rog_oracle_f32_to_bf16(acc);
+    }
 }
