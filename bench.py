@@ -44,7 +44,7 @@ METRIC = "rank-ordered gather HBM GB/s (% of peak) + p50 µs at 1–128 KiB/payl
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, AMD's published peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flat_kernel_w8x64MiB_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "deterministic_collective_movement_amd", "csrc", f)
-                  for f in ("rog_kernels.hip", "rog_internal.h", "rog_plan.cpp")]
+                  for f in ("rog_kernels.hip", "rog_internal.h", "rog_plan.cpp", "rog_device.h")]
 LATENCY_SIZES_KIB = (1, 8, 32, 128)
 
 

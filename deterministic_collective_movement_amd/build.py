@@ -1,6 +1,7 @@
 """Build librog.so (the C-ABI library) in-tree for gfx950.
 
-``build_library()`` compiles the host planner and the HIP kernels with hipcc
+``build_library()`` compiles the host planner and the HIP kernels (gathers and
+rank-ordered sums) with hipcc
 for gfx950, then links ``deterministic_collective_movement_amd/librog.so``.
 Intermediate objects go to ``_build/`` at the repository root.
 ``python -m deterministic_collective_movement_amd.build`` does the same.
@@ -45,10 +46,12 @@ def build_library(out: str = LIB_PATH, defines=(), build_dir: str = BUILD_DIR) -
     dflags = ["-D" + d for d in defines]
     plan_o = os.path.join(build_dir, "rog_plan.o")
     kern_o = os.path.join(build_dir, "rog_kernels.o")
+    red_o = os.path.join(build_dir, "rog_reduce.o")
     _run([hipcc] + HOST_FLAGS + dflags + inc + ["-c", os.path.join(CSRC, "rog_plan.cpp"), "-o", plan_o])
     _run([hipcc] + HIP_FLAGS + dflags + inc + ["-c", os.path.join(CSRC, "rog_kernels.hip"), "-o", kern_o])
+    _run([hipcc] + HIP_FLAGS + dflags + inc + ["-c", os.path.join(CSRC, "rog_reduce.hip"), "-o", red_o])
     tmp = out + ".tmp%d" % os.getpid()
-    _run([hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, plan_o, kern_o,
+    _run([hipcc, "-shared", "-fPIC", "--offload-arch=" + ARCH, plan_o, kern_o, red_o,
           "-Wl,-soname,librog.so", "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-Wl,--no-undefined", "-o", tmp])
     os.replace(tmp, out)
     return out

@@ -1,6 +1,6 @@
 // rog_internal.h -- launch plans and kernel-argument layouts shared by the host
-// planner (rog_plan.cpp) and the HIP kernels (rog_kernels.hip).  Internal to
-// librog.so; the public interface is include/rog.h.
+// planner (rog_plan.cpp) and the HIP kernels (rog_kernels.hip, rog_reduce.hip).
+// Internal to librog.so; the public interface is include/rog.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,6 +23,9 @@ constexpr int kMaxBatchPtrs = 192;
 // placement); a variant build may override one with -D for a sweep.
 #ifndef ROG_SINGLE_WG_MAX_BYTES
 #define ROG_SINGLE_WG_MAX_BYTES (32 * 1024)
+#endif
+#ifndef ROG_REDUCE_SINGLE_WG_MAX_BYTES
+#define ROG_REDUCE_SINGLE_WG_MAX_BYTES (32 * 1024)
 #endif
 #ifndef ROG_FLAT_BLOCK
 #define ROG_FLAT_BLOCK 64
@@ -52,6 +55,8 @@ constexpr int kMaxBatchPtrs = 192;
 // Output bytes up to which ROG_PATH_AUTO uses the single-workgroup path
 // (inclusive), measured by sweeping both forced paths.
 constexpr size_t kSingleWgMaxBytes = ROG_SINGLE_WG_MAX_BYTES;
+// The same bound for rog_reduce, on its output bytes.
+constexpr size_t kReduceSingleWgMaxBytes = ROG_REDUCE_SINGLE_WG_MAX_BYTES;
 
 // Launch shapes.  A multi-WG wave copies a chunk of 64 * unroll consecutive
 // 16-byte vectors; each of its loads and stores is one dwordx4 instruction over
@@ -166,6 +171,19 @@ struct BatchArgs {
 
 static_assert(sizeof(BatchArgs) <= 4096, "kernel arguments must stay below 4 KiB");
 
+// REDUCE: out[i] = rank-ordered binary32 sum of src[r][i], rounded to the
+// element type.  The output is cut by split_payload into an element head, a
+// body of 16-byte vectors (8 bf16 or 4 f32 elements each) and an element tail;
+// multi-WG chunk j is body vectors [64j, 64j + 64), and chunk 0 also sums the
+// head and tail elements.
+struct ReduceArgs {
+    const void *src[kMaxPeers];
+    void *out;
+    uint64_t count;             // elements
+    uint32_t W;
+    uint32_t n_chunks;          // multi-WG
+};
+
 // ---------------------------------------------------------------------------
 // Plans
 // ---------------------------------------------------------------------------
@@ -174,11 +192,20 @@ struct Plan {
     rog_plan_info info;
     FlatArgs flat;
     PeerArgs peer;
+    ReduceArgs reduce;
+    rog_dtype dtype;
 };
+
+// hipError_t of this thread's last failed launch (rog_last_hip_error).
+extern thread_local int g_last_hip_error;
 
 // Validate and plan one gather (no HIP calls).
 rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out,
                        rog_path path, Plan *plan);
+
+// Validate and plan one rank-ordered sum (no HIP calls).
+rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype dtype,
+                       const void *out, rog_path path, Plan *plan);
 
 // Validate and plan a batch (no HIP calls).  grid == 0 means nothing to launch.
 // *nt_loads: the launch streams its loads past the caches.

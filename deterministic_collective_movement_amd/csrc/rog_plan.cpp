@@ -181,6 +181,64 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
     return ROG_OK;
 }
 
+rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype dtype,
+                       const void *out, rog_path path, Plan *plan) {
+    if (path != ROG_PATH_AUTO && path != ROG_PATH_SINGLE_WG && path != ROG_PATH_MULTI_WG)
+        return ROG_ERR_INVALID_ARGUMENT;
+    if (dtype != ROG_DTYPE_F32 && dtype != ROG_DTYPE_BF16) return ROG_ERR_INVALID_ARGUMENT;
+    if (!srcs || W < 1 || W > kMaxPeers) return ROG_ERR_INVALID_ARGUMENT;
+    const size_t esize = dtype == ROG_DTYPE_F32 ? 4 : 2;
+    rog_plan_info &info = plan->info;
+    memset(&info, 0, sizeof(info));
+    plan->dtype = dtype;
+    if (count == 0) {
+        info.path = path == ROG_PATH_AUTO ? ROG_PATH_SINGLE_WG : path;
+        info.kernel = ROG_KERNEL_NONE;
+        return ROG_OK;
+    }
+    if (!out) return ROG_ERR_INVALID_ARGUMENT;
+    for (int r = 0; r < W; ++r)
+        if (!srcs[r]) return ROG_ERR_INVALID_ARGUMENT;
+    if (count > SIZE_MAX / esize) return ROG_ERR_TOO_LARGE;
+    const uint64_t bytes = uint64_t(count) * esize;
+    if (bytes >= kMaxOutputBytes) return ROG_ERR_TOO_LARGE;
+    const uintptr_t o = addr(out);
+    if (o % esize) return ROG_ERR_INVALID_ARGUMENT;
+    if (o > UINTPTR_MAX - bytes) return ROG_ERR_INVALID_ARGUMENT;
+    for (int r = 0; r < W; ++r) {
+        const uintptr_t s = addr(srcs[r]);
+        if (s % esize) return ROG_ERR_INVALID_ARGUMENT;
+        if (s > UINTPTR_MAX - bytes) return ROG_ERR_INVALID_ARGUMENT;
+        // In place (out is exactly this source) is allowed: every element is
+        // read from every source before the one thread that owns it writes it.
+        if (ranges_overlap(s, bytes, o, bytes) && s != o) return ROG_ERR_OVERLAP;
+    }
+    if (path == ROG_PATH_AUTO)
+        path = bytes <= kReduceSingleWgMaxBytes ? ROG_PATH_SINGLE_WG : ROG_PATH_MULTI_WG;
+    info.path = path;
+    info.kernel = ROG_KERNEL_REDUCE;
+    info.units = count;
+    if (uint64_t(W) * bytes >= kNtLoadMinBytes) info.flags |= ROG_PLAN_NT_LOADS;
+
+    ReduceArgs &a = plan->reduce;
+    memset(&a, 0, sizeof(a));
+    for (int r = 0; r < W; ++r) a.src[r] = srcs[r];
+    a.out = const_cast<void *>(out);
+    a.count = count;
+    a.W = uint32_t(W);
+    if (path == ROG_PATH_SINGLE_WG) {
+        // One thread per 16-byte output vector, at most 1024.
+        info.block = round_up_64(ceil_div(bytes, 16));
+        info.grid = 1;
+    } else {
+        // One wave per 1 KiB chunk of the body (at most bytes / 16 vectors).
+        a.n_chunks = uint32_t(std::max<uint64_t>(1, ceil_div(bytes / 16, 64)));
+        info.block = kWaveBlock;
+        info.grid = std::min(a.n_chunks, max_grid(kWaveBlock));
+    }
+    return ROG_OK;
+}
+
 rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *args,
                       uint32_t *grid, bool *nt_loads) {
     *grid = 0;

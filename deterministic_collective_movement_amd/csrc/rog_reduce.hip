@@ -1,0 +1,208 @@
+// rog_reduce.hip -- HIP kernels of the rank-ordered sum for gfx950 (CDNA4) and
+// the C entry points that launch them.
+//
+// out[i] = round(((x_0[i] + x_1[i]) + x_2[i]) + ... + x_{W-1}[i]): the
+// reduction of a deterministic all-reduce or reduce-scatter (RL-Align/RL-Kernel
+// PR #491 names these collectives in "Not in this PR"; their single-block
+// paths have the same size cliff as the gather had).  Every element is summed
+// by exactly one lane, in rank order, in binary32 (v_add_f32, round to
+// nearest-even, subnormals kept), and rounded once to the element type
+// (v_cvt_pk_bf16_f32 for bf16), so the bits never depend on the launch.
+//
+// The output is cut like a PEER payload (split_payload): an element head up to
+// the first 256-byte boundary of out, a body of 16-byte vectors, an element
+// tail.  A body lane loads the 16 bytes at the same offset of every source --
+// one global_load_dwordx4 each, at whatever element alignment the source has --
+// with up to 8 loads in flight, accumulates them in rank order and stores one
+// aligned 16-byte vector.  Multi-WG: one wave per 1 KiB chunk of the body,
+// chunks handed to the XCDs in runs (xcd_grouped); single-WG: one workgroup
+// strides over the whole output.  Bandwidth bound: (W + 1) * count * esize
+// bytes per call.
+#include <hip/hip_runtime.h>
+
+#include "rog_device.h"
+
+namespace rog {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <bool BF16>
+struct Elem {
+    static constexpr int kPerVec = BF16 ? 8 : 4;   // elements per 16-byte vector
+    static constexpr uint32_t kSize = BF16 ? 2 : 4;
+};
+
+__device__ __forceinline__ float from_bits(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// Two binary32 values -> two bf16 (element 0 in the low half), nearest-even.
+__device__ __forceinline__ uint32_t to_bf16x2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// The elements of one 16-byte vector, widened to binary32.
+template <bool BF16>
+__device__ __forceinline__ void widen(const vec16 &v, float (&x)[Elem<BF16>::kPerVec]) {
+    if constexpr (BF16) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[2 * k] = from_bits(v[k] << 16);
+            x[2 * k + 1] = from_bits(v[k] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = from_bits(v[k]);
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ vec16 narrow(const float (&a)[Elem<BF16>::kPerVec]) {
+    vec16 v;
+    if constexpr (BF16) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = to_bf16x2(a[2 * k], a[2 * k + 1]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = __builtin_bit_cast(uint32_t, a[k]);
+    }
+    return v;
+}
+
+constexpr uint32_t kGroup = 8;   // source loads in flight per lane
+
+// The rank-ordered sum of the 16-byte vectors at byte offset off of every source.
+template <bool BF16, bool NTL>
+__device__ __forceinline__ vec16 sum_vec(const void *const *src, uint32_t W, uint64_t off) {
+    constexpr int E = Elem<BF16>::kPerVec;
+    float acc[E];
+    for (uint32_t r0 = 0; r0 < W; r0 += kGroup) {
+        const uint32_t g = min(W - r0, kGroup);
+        vec16 v[kGroup];
+#pragma unroll
+        for (uint32_t q = 0; q < kGroup; ++q)
+            if (q < g) v[q] = ldu16<NTL>(static_cast<const uint8_t *>(src[r0 + q]) + off);
+#pragma unroll
+        for (uint32_t q = 0; q < kGroup; ++q) {
+            if (q < g) {
+                float x[E];
+                widen<BF16>(v[q], x);
+                if (r0 + q == 0) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[e] = x[e];       // the first term as it is
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[e] += x[e];
+                }
+            }
+        }
+    }
+    return narrow<BF16>(acc);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void *p, uint64_t i) {
+    if constexpr (BF16) return from_bits(uint32_t(static_cast<const uint16_t *>(p)[i]) << 16);
+    else return static_cast<const float *>(p)[i];
+}
+
+// One element: the rank-ordered sum of element i of every source, stored to out.
+template <bool BF16>
+__device__ __forceinline__ void sum_elem(const void *const *src, uint32_t W, uint64_t i, void *out) {
+    float acc = load_elem<BF16>(src[0], i);
+    for (uint32_t r = 1; r < W; ++r) acc += load_elem<BF16>(src[r], i);
+    if constexpr (BF16) static_cast<uint16_t *>(out)[i] = uint16_t(to_bf16x2(acc, 0.0f) & 0xFFFFu);
+    else static_cast<float *>(out)[i] = acc;
+}
+
+// Multi-WG: one wave per workgroup and per 1 KiB chunk of the body; chunk 0
+// also sums the head and tail elements.
+template <bool BF16, bool NTL>
+__global__ __launch_bounds__(kWaveBlock) void rog_reduce_kernel(ReduceArgs a) {
+    const uint32_t lane = __lane_id();
+    const uint64_t bytes = a.count * Elem<BF16>::kSize;
+    const PeerSplit cut = split_payload(reinterpret_cast<uintptr_t>(a.out), bytes);
+    uint8_t *o = static_cast<uint8_t *>(a.out);
+    for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x) {
+        const uint32_t j = xcd_grouped(vb, a.n_chunks);
+        if (j == 0) {
+            for (uint64_t i = lane; i < cut.lo / Elem<BF16>::kSize; i += 64) sum_elem<BF16>(a.src, a.W, i, a.out);
+            for (uint64_t i = cut.hi / Elem<BF16>::kSize + lane; i < a.count; i += 64)
+                sum_elem<BF16>(a.src, a.W, i, a.out);
+        }
+        const uint64_t off = cut.lo + 16 * (uint64_t(j) * 64 + lane);
+        if (off < cut.hi) st16(reinterpret_cast<vec16 *>(o + off), sum_vec<BF16, NTL>(a.src, a.W, off));
+    }
+}
+
+// Single-WG: one workgroup over the whole output.
+template <bool BF16, bool NTL>
+__global__ __launch_bounds__(kSingleBlock) void rog_reduce_single_kernel(ReduceArgs a) {
+    const uint32_t tid = threadIdx.x, nt = blockDim.x;
+    const uint64_t bytes = a.count * Elem<BF16>::kSize;
+    const PeerSplit cut = split_payload(reinterpret_cast<uintptr_t>(a.out), bytes);
+    uint8_t *o = static_cast<uint8_t *>(a.out);
+    for (uint64_t i = tid; i < cut.lo / Elem<BF16>::kSize; i += nt) sum_elem<BF16>(a.src, a.W, i, a.out);
+    for (uint64_t i = cut.hi / Elem<BF16>::kSize + tid; i < a.count; i += nt) sum_elem<BF16>(a.src, a.W, i, a.out);
+    for (uint64_t off = cut.lo + 16 * uint64_t(tid); off < cut.hi; off += 16 * uint64_t(nt))
+        st16(reinterpret_cast<vec16 *>(o + off), sum_vec<BF16, NTL>(a.src, a.W, off));
+}
+
+template <typename K>
+const void *kfn(K *k) { return reinterpret_cast<const void *>(k); }
+
+template <bool BF16>
+const void *reduce_kernel(bool single, bool ntl) {
+    if (single) return ntl ? kfn(&rog_reduce_single_kernel<BF16, true>) : kfn(&rog_reduce_single_kernel<BF16, false>);
+    return ntl ? kfn(&rog_reduce_kernel<BF16, true>) : kfn(&rog_reduce_kernel<BF16, false>);
+}
+
+rog_status launch_reduce(Plan &p, hipStream_t stream) {
+    const rog_plan_info &i = p.info;
+    if (i.kernel == ROG_KERNEL_NONE) return ROG_OK;
+    const bool single = i.path == ROG_PATH_SINGLE_WG;
+    const bool ntl = (i.flags & ROG_PLAN_NT_LOADS) != 0;
+    const void *k = p.dtype == ROG_DTYPE_BF16 ? reduce_kernel<true>(single, ntl) : reduce_kernel<false>(single, ntl);
+    void *params[] = {&p.reduce};
+    const hipError_t e = hipLaunchKernel(k, dim3(i.grid), dim3(i.block), params, 0, stream);
+    if (e != hipSuccess) {
+        g_last_hip_error = int(e);
+        return ROG_ERR_LAUNCH;
+    }
+    return ROG_OK;
+}
+
+}  // namespace
+}  // namespace rog
+
+// ---------------------------------------------------------------------------
+// C ABI (include/rog.h)
+// ---------------------------------------------------------------------------
+extern "C" {
+
+ROG_API rog_status rog_reduce_ex(const void *const *srcs, int W, size_t count, rog_dtype dtype, void *out,
+                                 hipStream_t stream, rog_path path) {
+    rog::Plan p;
+    const rog_status st = rog::plan_reduce(srcs, W, count, dtype, out, path, &p);
+    if (st != ROG_OK) return st;
+    return rog::launch_reduce(p, stream);
+}
+
+ROG_API rog_status rog_reduce(const void *const *srcs, int W, size_t count, rog_dtype dtype, void *out,
+                              hipStream_t stream) {
+    return rog_reduce_ex(srcs, W, count, dtype, out, stream, ROG_PATH_AUTO);
+}
+
+ROG_API rog_status rog_reduce_plan(const void *const *srcs, int W, size_t count, rog_dtype dtype,
+                                   const void *out, rog_path path, rog_plan_info *info) {
+    if (!info) return ROG_ERR_INVALID_ARGUMENT;
+    rog::Plan p;
+    const rog_status st = rog::plan_reduce(srcs, W, count, dtype, out, path, &p);
+    if (st == ROG_OK) *info = p.info;
+    return st;
+}
+
+ROG_API size_t rog_reduce_single_wg_max_bytes(void) { return rog::kReduceSingleWgMaxBytes; }
+
+}  // extern "C"

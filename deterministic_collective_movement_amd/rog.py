@@ -9,7 +9,13 @@ Entry points keep the C names.  Tensor forms:
 * ``rog_gather(srcs, out=None, stream=None)`` -> ``out`` (the same object);
 * ``rog_gather_ex(srcs, out, path, stream=None)`` -> ``out``;
 * ``rog_gather_many(batch, outs=None, stream=None)`` -> list of outputs;
-* ``rog_plan(srcs, out, path=ROG_PATH_AUTO)`` -> dict (no GPU work).
+* ``rog_plan(srcs, out, path=ROG_PATH_AUTO)`` -> dict (no GPU work);
+* ``rog_reduce(srcs, out=None, stream=None)`` -> ``out``: the rank-ordered sum
+  of W float32 or bfloat16 tensors;
+* ``rog_reduce_ex(srcs, out, path, stream=None)``, ``rog_reduce_plan(srcs, out, path)``;
+* ``rog_reduce_scatter(inputs, rank, out=None, stream=None)`` -> ``out``: rank
+  ``rank``'s share of a reduce-scatter, i.e. ``rog_reduce`` over shard
+  ``rank`` of each input (views; nothing is copied).
 
 Raw-pointer forms (``*_ptrs``) take integer device addresses, for callers that
 manage their own memory.
@@ -44,9 +50,15 @@ ROG_PLAN_NT_LOADS = 1
 ROG_KERNEL_NONE = 0
 ROG_KERNEL_FLAT = 1
 ROG_KERNEL_PEER = 2
+ROG_KERNEL_REDUCE = 3
+
+ROG_DTYPE_F32 = 0
+ROG_DTYPE_BF16 = 1
 
 PATH_NAMES = {ROG_PATH_AUTO: "auto", ROG_PATH_SINGLE_WG: "single_wg", ROG_PATH_MULTI_WG: "multi_wg"}
-KERNEL_NAMES = {ROG_KERNEL_NONE: "none", ROG_KERNEL_FLAT: "flat", ROG_KERNEL_PEER: "peer"}
+KERNEL_NAMES = {ROG_KERNEL_NONE: "none", ROG_KERNEL_FLAT: "flat", ROG_KERNEL_PEER: "peer",
+                ROG_KERNEL_REDUCE: "reduce"}
+DTYPES = {torch.float32: ROG_DTYPE_F32, torch.bfloat16: ROG_DTYPE_BF16}
 
 
 class RogError(RuntimeError):
@@ -101,10 +113,15 @@ def _load() -> ctypes.CDLL:
     lib.rog_gather_ex.argtypes = [ptrs, i32, sz, vp, vp, i32]
     lib.rog_gather_many.argtypes = [ctypes.POINTER(rog_gather_desc), i32, i32, vp]
     lib.rog_plan.argtypes = [ptrs, i32, sz, vp, i32, ctypes.POINTER(rog_plan_info)]
-    for name in ("rog_gather", "rog_gather_ex", "rog_gather_many", "rog_plan"):
+    lib.rog_reduce.argtypes = [ptrs, i32, sz, i32, vp, vp]
+    lib.rog_reduce_ex.argtypes = [ptrs, i32, sz, i32, vp, vp, i32]
+    lib.rog_reduce_plan.argtypes = [ptrs, i32, sz, i32, vp, i32, ctypes.POINTER(rog_plan_info)]
+    for name in ("rog_gather", "rog_gather_ex", "rog_gather_many", "rog_plan", "rog_reduce", "rog_reduce_ex",
+                 "rog_reduce_plan"):
         getattr(lib, name).restype = i32
-    lib.rog_single_wg_max_bytes.argtypes = []
-    lib.rog_single_wg_max_bytes.restype = sz
+    for name in ("rog_single_wg_max_bytes", "rog_reduce_single_wg_max_bytes"):
+        getattr(lib, name).argtypes = []
+        getattr(lib, name).restype = sz
     for name in ("rog_max_peers", "rog_max_batch", "rog_max_batch_pointers", "rog_last_hip_error"):
         getattr(lib, name).argtypes = []
         getattr(lib, name).restype = i32
@@ -141,6 +158,10 @@ def _check(status: int, what: str) -> None:
 
 def rog_single_wg_max_bytes() -> int:
     return int(_lib.rog_single_wg_max_bytes())
+
+
+def rog_reduce_single_wg_max_bytes() -> int:
+    return int(_lib.rog_reduce_single_wg_max_bytes())
 
 
 def rog_max_peers() -> int:
@@ -186,10 +207,7 @@ def rog_plan_ptrs(src_ptrs: Sequence[int], bytes_per_rank: int, out_ptr: int,
     st = _lib.rog_plan(_ptr_array(src_ptrs), len(src_ptrs), bytes_per_rank,
                        ctypes.c_void_p(out_ptr), path, ctypes.byref(info))
     _check(st, "rog_plan")
-    return {"path": PATH_NAMES[info.path], "kernel": KERNEL_NAMES[info.kernel],
-            "grid": info.grid, "block": info.block, "vec_ok_mask": info.vec_ok_mask,
-            "units": info.units, "peer_magic": info.peer_magic, "peer_sh1": info.peer_sh1,
-            "peer_sh2": info.peer_sh2, "nt_loads": bool(info.flags & ROG_PLAN_NT_LOADS)}
+    return _plan_dict(info)
 
 
 def rog_status_of_ptrs(src_ptrs: Optional[Sequence[int]], W: int, bytes_per_rank: int,
@@ -199,6 +217,33 @@ def rog_status_of_ptrs(src_ptrs: Optional[Sequence[int]], W: int, bytes_per_rank
     arr = None if src_ptrs is None else _ptr_array(src_ptrs)
     return int(_lib.rog_plan(arr, W, bytes_per_rank, ctypes.c_void_p(out_ptr), path,
                              ctypes.byref(info)))
+
+
+def _plan_dict(info) -> dict:
+    return {"path": PATH_NAMES[info.path], "kernel": KERNEL_NAMES[info.kernel],
+            "grid": info.grid, "block": info.block, "vec_ok_mask": info.vec_ok_mask,
+            "units": info.units, "peer_magic": info.peer_magic, "peer_sh1": info.peer_sh1,
+            "peer_sh2": info.peer_sh2, "nt_loads": bool(info.flags & ROG_PLAN_NT_LOADS)}
+
+
+def rog_reduce_ptrs(src_ptrs: Sequence[int], count: int, dtype: int, out_ptr: int,
+                    stream: int = 0, path: int = ROG_PATH_AUTO) -> None:
+    """rog_reduce_ex on raw device addresses; raises on a non-zero status."""
+    st = _lib.rog_reduce_ex(_ptr_array(src_ptrs), len(src_ptrs), count, dtype,
+                            ctypes.c_void_p(out_ptr), ctypes.c_void_p(stream), path)
+    _check(st, "rog_reduce")
+
+
+def rog_reduce_plan_ptrs(src_ptrs: Optional[Sequence[int]], count: int, dtype: int, out_ptr: int,
+                         path: int = ROG_PATH_AUTO, W: Optional[int] = None) -> dict:
+    """rog_reduce_plan on raw addresses (no HIP call); raises on a non-zero status.
+    ``src_ptrs=None`` passes NULL with the given W."""
+    info = rog_plan_info()
+    arr = None if src_ptrs is None else _ptr_array(src_ptrs)
+    st = _lib.rog_reduce_plan(arr, len(src_ptrs) if W is None else W, count, dtype,
+                              ctypes.c_void_p(out_ptr), path, ctypes.byref(info))
+    _check(st, "rog_reduce_plan")
+    return _plan_dict(info)
 
 
 def rog_gather_many_ptrs(batch_ptrs: Sequence[Sequence[int]], sizes: Sequence[int],
@@ -326,3 +371,65 @@ def rog_gather_many(batch: Sequence[Sequence[torch.Tensor]],
         rog_gather_many_ptrs([[s.data_ptr() for s in b] for b in batch], sizes,
                              [o.data_ptr() for o in ready], W, _stream_handle(stream, device))
     return ready
+
+
+def _prepare_reduce(srcs: Sequence[torch.Tensor], out: Optional[torch.Tensor]):
+    if len(srcs) == 0:
+        raise ValueError("need at least one source tensor")
+    device = srcs[0].device
+    dtype = srcs[0].dtype
+    if dtype not in DTYPES:
+        raise ValueError("rog_reduce sums float32 or bfloat16 tensors (got %s)" % dtype)
+    n = srcs[0].numel()
+    for i, s in enumerate(srcs):
+        _check_tensor(s, "srcs[%d]" % i, device)
+        if s.dtype != dtype or s.numel() != n:
+            raise ValueError("every source must have the dtype and element count of srcs[0]")
+    if out is None:
+        out = torch.empty(n, dtype=dtype, device=device)
+    _check_tensor(out, "out", device)
+    if out.dtype != dtype or out.numel() != n:
+        raise ValueError("out must hold %d elements of %s" % (n, dtype))
+    return device, n, DTYPES[dtype], out
+
+
+def rog_reduce_ex(srcs: Sequence[torch.Tensor], out: Optional[torch.Tensor] = None,
+                  path: int = ROG_PATH_AUTO, stream=None) -> torch.Tensor:
+    """Rank-ordered sum of equal-shape tensors into ``out`` with the path forced."""
+    device, n, dt, out = _prepare_reduce(srcs, out)
+    with _on_device(device):
+        rog_reduce_ptrs([s.data_ptr() for s in srcs], n, dt, out.data_ptr(),
+                        _stream_handle(stream, device), path)
+    return out
+
+
+def rog_reduce(srcs: Sequence[torch.Tensor], out: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """out[i] = rank-ordered binary32 sum of srcs[r][i], rounded to the tensors'
+    dtype (float32 or bfloat16).  ``out`` may be one of ``srcs`` (in place)."""
+    return rog_reduce_ex(srcs, out, ROG_PATH_AUTO, stream)
+
+
+def rog_reduce_plan(srcs: Sequence[torch.Tensor], out: torch.Tensor, path: int = ROG_PATH_AUTO) -> dict:
+    """The launch rog_reduce_ex would make for these tensors (no GPU work)."""
+    device, n, dt, out = _prepare_reduce(srcs, out)
+    return rog_reduce_plan_ptrs([s.data_ptr() for s in srcs], n, dt, out.data_ptr(), path)
+
+
+def rog_reduce_scatter(inputs: Sequence[torch.Tensor], rank: int, out: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Rank ``rank``'s share of a reduce-scatter over the W ``inputs``: each input
+    holds W shards of n elements; out = rog_reduce over shard ``rank`` of every
+    input (views into the inputs, no copy)."""
+    W = len(inputs)
+    if W == 0:
+        raise ValueError("need at least one input")
+    if not 0 <= rank < W:
+        raise ValueError("rank must be in [0, %d)" % W)
+    total = inputs[0].numel()
+    if total % W:
+        raise ValueError("each input must hold W equal shards (numel %% W == 0)")
+    n = total // W
+    for i, t in enumerate(inputs):
+        _check_tensor(t, "inputs[%d]" % i, inputs[0].device)
+    return rog_reduce([t.reshape(-1)[rank * n:(rank + 1) * n] for t in inputs], out, stream)

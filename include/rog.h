@@ -1,5 +1,6 @@
 /*
- * rog.h -- rank-ordered gather (rog) for MI355X (gfx950, CDNA4).
+ * rog.h -- rank-ordered gather (rog) and rank-ordered sum for MI355X (gfx950,
+ * CDNA4).
  *
  * C ABI of librog.so.  Plain C types, device pointers and sizes; no PyTorch
  * types.  Every entry point below is implemented by hand-written HIP kernels in
@@ -62,9 +63,18 @@ typedef enum {
 typedef enum {
     ROG_KERNEL_NONE = 0,     /* nothing to copy (S == 0): nothing is launched       */
     ROG_KERNEL_FLAT = 1,     /* one flat loop over all peers' 16-byte vectors        */
-    ROG_KERNEL_PEER = 2      /* per payload: byte head, 16-byte body (aligned
+    ROG_KERNEL_PEER = 2,     /* per payload: byte head, 16-byte body (aligned
                                 stores, loads at any alignment), byte tail          */
+    ROG_KERNEL_REDUCE = 3    /* rank-ordered sum: element head, 16-byte body of
+                                aligned stores (loads at any element alignment),
+                                element tail                                         */
 } rog_kernel;
+
+/* Element types of the rank-ordered sum. */
+typedef enum {
+    ROG_DTYPE_F32 = 0,       /* IEEE binary32, 4 bytes                               */
+    ROG_DTYPE_BF16 = 1       /* bfloat16 (top 16 bits of a binary32), 2 bytes       */
+} rog_dtype;
 
 /* One tensor of a batch: W source pointers, its output, its per-rank bytes. */
 typedef struct {
@@ -83,7 +93,8 @@ typedef struct {
                                   both 16-byte aligned (the pages' "vectors where
                                   aligned"); informational, every payload gets a
                                   16-byte body whatever its alignment              */
-    uint64_t units;            /* FLAT: 16-byte vectors W*S/16; PEER: bytes W*S          */
+    uint64_t units;            /* FLAT: 16-byte vectors W*S/16; PEER: bytes W*S;
+                                  REDUCE: elements per payload                        */
     uint32_t peer_magic;       /* FLAT: floor(v / (S/16)) = (t + ((v - t) >> peer_sh1))  */
     uint32_t peer_sh1;         /*       >> peer_sh2 with t = mulhi32(v, peer_magic),     */
     uint32_t peer_sh2;         /*       exact for every 32-bit v                         */
@@ -166,6 +177,63 @@ ROG_API rog_status rog_plan(const void *const *srcs, int W, size_t bytes_per_ran
 /* Output bytes up to which ROG_PATH_AUTO takes the single-workgroup path
  * (inclusive), measured on MI355X. */
 ROG_API size_t rog_single_wg_max_bytes(void);
+
+/*
+ * rog_reduce -- the rank-ordered sum of W payloads of `count` elements:
+ *
+ *     out[i] = round( ((x_0[i] + x_1[i]) + x_2[i]) + ... + x_{W-1}[i] ),
+ *
+ * x_r = srcs[r], the sum taken in rank order with every addition an IEEE
+ * binary32 addition rounded to nearest-even, bf16 elements widened to binary32
+ * exactly, the first term taken as it is (a lone -0 stays -0), and the result
+ * rounded once to `dtype` (bf16: nearest-even; a NaN stays a NaN, its payload
+ * unspecified).  Every element is summed by one thread in that fixed order, so
+ * the result is the same bits on every call, whatever the launch shape.
+ *
+ * This is the reduction at the heart of the pages' deterministic all_reduce
+ * and reduce_scatter (RL-Align/RL-Kernel PR #491, "Not in this PR": their
+ * single-block paths grow with size as the gather's did; 523 us at 256 KiB
+ * per rank on 8 GPUs).  The pages print no arithmetic; the order and precision
+ * above are this library's reading.  On one GPU the W "ranks" are W caller-owned
+ * device buffers: an all-reduce is rog_reduce over the W inputs, rank r's share
+ * of a reduce-scatter is rog_reduce over the W inputs' r-th shards.
+ *
+ * srcs    host array of W device pointers, each to `count` elements of dtype,
+ *         aligned to the element size (any alignment beyond that).
+ * W       1 <= W <= rog_max_peers().
+ * count   elements per payload (and in out).
+ * dtype   ROG_DTYPE_F32 or ROG_DTYPE_BF16.
+ * out     device pointer to `count` writable elements, element-aligned.  out
+ *         may be exactly one (or several) of the srcs (in place); any other
+ *         overlap with a source is an error.  Sources may alias each other.
+ * stream  HIP stream of the current device.
+ *
+ * Path: single-workgroup when count * element size <= rog_reduce_single_wg_max_bytes()
+ * (inclusive, measured on gfx950), multi-workgroup otherwise.
+ * Errors (nothing enqueued):
+ *   ROG_ERR_INVALID_ARGUMENT  srcs NULL; W out of range; dtype or path unknown;
+ *                             count > 0 and out or some srcs[r] NULL or not
+ *                             aligned to the element size.
+ *   ROG_ERR_OVERLAP           a source overlaps out other than exactly.
+ *   ROG_ERR_TOO_LARGE         count * element size overflows or is >= 2^36.
+ *   ROG_ERR_LAUNCH            hipLaunchKernel failed (rog_last_hip_error()).
+ * count == 0: ROG_OK, nothing enqueued.
+ */
+ROG_API rog_status rog_reduce(const void *const *srcs, int W, size_t count, rog_dtype dtype,
+                              void *out, hipStream_t stream);
+
+/* rog_reduce with the path forced (changes the launch shape, never the bits). */
+ROG_API rog_status rog_reduce_ex(const void *const *srcs, int W, size_t count, rog_dtype dtype,
+                                 void *out, hipStream_t stream, rog_path path);
+
+/* Validate exactly as rog_reduce_ex and describe the launch, without any HIP
+ * call (kernel ROG_KERNEL_REDUCE, units = count). */
+ROG_API rog_status rog_reduce_plan(const void *const *srcs, int W, size_t count, rog_dtype dtype,
+                                   const void *out, rog_path path, rog_plan_info *info);
+
+/* Output bytes up to which ROG_PATH_AUTO runs rog_reduce on one workgroup
+ * (inclusive), measured on MI355X. */
+ROG_API size_t rog_reduce_single_wg_max_bytes(void);
 
 /* Largest W accepted (kernel-argument capacity). */
 ROG_API int rog_max_peers(void);

@@ -1,6 +1,7 @@
 """Helpers of the GPU parity tests: place a case's payloads in guarded device
 buffers, run the library through its C ABI, and compare every byte of every
-guarded buffer with the CPU oracle's result."""
+guarded buffer with the CPU oracle's result (gathers), or every element of the
+output with the oracle's rank-ordered sum, bit for bit (sums)."""
 from __future__ import annotations
 
 from typing import List, Sequence
@@ -109,3 +110,107 @@ def place_batch(case: wl.BatchCase, device) -> PlacedBatch:
     payloads = [[case.payload(t, r) for r in range(case.W)] for t in range(len(case.tensors))]
     return PlacedBatch(case.W, payloads, [x.in_off for x in case.tensors],
                        [x.out_off for x in case.tensors], device)
+
+
+# ---------------------------------------------------------------------------
+# Rank-ordered sum
+# ---------------------------------------------------------------------------
+
+TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _same_elements(got: np.ndarray, want: np.ndarray, dtype: str) -> np.ndarray:
+    """Per element: equal bits, or both NaN (NaN payloads are not specified)."""
+    if dtype == "f32":
+        g, w = got.view(np.uint32), want.view(np.uint32)
+        gn = (g & 0x7FFFFFFF) > 0x7F800000
+        wn = (w & 0x7FFFFFFF) > 0x7F800000
+    else:
+        g, w = got.view(np.uint16), want.view(np.uint16)
+        gn = (g & 0x7FFF) > 0x7F80
+        wn = (w & 0x7FFF) > 0x7F80
+    return (g == w) | (gn & wn)
+
+
+class PlacedReduce:
+    """A rank-ordered sum's payloads and output in guarded byte buffers, each at
+    an element offset, on host and device."""
+
+    def __init__(self, payloads: Sequence[np.ndarray], in_offs: Sequence[int], out_off: int,
+                 dtype: str, device: torch.device, in_place: int = -1):
+        self.W = len(payloads)
+        self.n = int(payloads[0].shape[0])
+        self.dtype = dtype
+        self.es = wl.REDUCE_ESIZE[dtype]
+        self.payloads = [np.ascontiguousarray(p) for p in payloads]
+        self.out_off = out_off
+        self.in_place = in_place
+        nb = self.n * self.es
+        self.src_host, self.src_dev, self.srcs = [], [], []
+        for p, o in zip(self.payloads, in_offs):
+            h = guarded_host(nb, o * self.es)
+            start = wl.GUARD + o * self.es
+            h[start:start + nb] = p.view(np.uint8)
+            d = torch.from_numpy(h).to(device)
+            self.src_host.append(h)
+            self.src_dev.append(d)
+            self.srcs.append(d[start:start + nb].view(TORCH_DTYPES[dtype]))
+        self.out_start = wl.GUARD + out_off * self.es
+        self.out_dev = torch.full((self.out_start + nb + wl.GUARD,), wl.GUARD_BYTE, dtype=torch.uint8,
+                                  device=device)
+        self.out = self.out_dev[self.out_start:self.out_start + nb].view(TORCH_DTYPES[dtype])
+        if in_place >= 0:
+            # the output is source `in_place` itself
+            self.out_dev = self.src_dev[in_place]
+            self.out_start = wl.GUARD + in_offs[in_place] * self.es
+            self.out = self.srcs[in_place]
+        self._expected = None
+
+    def expected(self) -> np.ndarray:
+        if self._expected is None:
+            want = np.empty(self.n, dtype=oracle.REDUCE_DTYPES[self.dtype])
+            oracle.reduce_c(self.payloads, want, self.dtype)
+            self._expected = want
+        return self._expected
+
+    def reset(self) -> None:
+        if self.in_place >= 0:
+            h = self.src_host[self.in_place]
+            self.out_dev.copy_(torch.from_numpy(h))
+        else:
+            self.out_dev.fill_(wl.GUARD_BYTE)
+
+    def check(self, label: str) -> None:
+        torch.cuda.synchronize()
+        buf = self.out_dev.cpu().numpy()
+        nb = self.n * self.es
+        if self.in_place < 0:
+            pre, post = buf[:self.out_start], buf[self.out_start + nb:]
+            if not (np.all(pre == wl.GUARD_BYTE) and np.all(post == wl.GUARD_BYTE)):
+                raise AssertionError("%s: a guard byte changed" % label)
+        got = buf[self.out_start:self.out_start + nb].copy().view(oracle.REDUCE_DTYPES[self.dtype])
+        ok = _same_elements(got, self.expected(), self.dtype)
+        if not ok.all():
+            i = int(np.flatnonzero(~ok)[0])
+            bits = np.uint32 if self.es == 4 else np.uint16
+            raise AssertionError("%s: %d of %d elements differ; first %d: got %s want %s"
+                                 % (label, int((~ok).sum()), self.n, i, hex(int(got.view(bits)[i])),
+                                    hex(int(self.expected().view(bits)[i]))))
+        for r, (h, d) in enumerate(zip(self.src_host, self.src_dev)):
+            if r == self.in_place:
+                continue
+            if not np.array_equal(d.cpu().numpy(), h):
+                raise AssertionError("%s: source buffer %d changed" % (label, r))
+
+
+def place_reduce(case: wl.ReduceCase, device) -> PlacedReduce:
+    return PlacedReduce(case.payloads(), case.in_offs, case.out_off, case.dtype, device)
+
+
+def run_reduce_all_paths(placed: PlacedReduce, label: str, paths=PATHS) -> None:
+    for path in paths:
+        placed.reset()
+        print("%s path=%s" % (label, rog.PATH_NAMES[path]), flush=True)
+        ret = rog.rog_reduce_ex(placed.srcs, placed.out, path)
+        assert ret is placed.out
+        placed.check("%s path=%s" % (label, rog.PATH_NAMES[path]))

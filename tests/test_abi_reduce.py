@@ -1,0 +1,121 @@
+"""The rank-ordered sum's C ABI on the CPU: argument validation, in-place and
+overlap rules, path dispatch and grid sizing (include/rog.h, rog_reduce*).
+rog_reduce_plan never calls HIP, and every rog_reduce call below fails
+validation or has nothing to do, so none of them launches a kernel."""
+from __future__ import annotations
+
+import ctypes
+
+import pytest
+
+from deterministic_collective_movement_amd import rog
+
+A = 1 << 33
+F32, BF16 = rog.ROG_DTYPE_F32, rog.ROG_DTYPE_BF16
+OK, INVALID, OVERLAP, TOO_LARGE = (rog.ROG_OK, rog.ROG_ERR_INVALID_ARGUMENT,
+                                   rog.ROG_ERR_OVERLAP, rog.ROG_ERR_TOO_LARGE)
+
+
+def st(srcs, count, out, dtype=F32, path=rog.ROG_PATH_AUTO, W=None):
+    info = rog.rog_plan_info()
+    arr = None if srcs is None else rog._ptr_array(srcs)
+    return int(rog.lib().rog_reduce_plan(arr, len(srcs) if W is None else W, count, dtype,
+                                         ctypes.c_void_p(out), path, ctypes.byref(info)))
+
+
+def test_declared_and_exported():
+    lib = rog.lib()
+    for name in ("rog_reduce", "rog_reduce_ex", "rog_reduce_plan", "rog_reduce_single_wg_max_bytes"):
+        assert hasattr(lib, name), name
+    assert rog.rog_reduce_single_wg_max_bytes() > 0
+
+
+def test_invalid_arguments():
+    assert st(None, 16, A, W=2) == INVALID
+    assert st([A], 16, A + 4096, W=0) == INVALID
+    M = rog.rog_max_peers()
+    assert st([A + 256 * i for i in range(M + 1)], 16, 2 * A) == INVALID
+    assert st([A + 256 * i for i in range(M)], 16, 2 * A) == OK
+    assert st([A, 0], 16, 2 * A) == INVALID
+    assert st([A, A + 64], 16, 0) == INVALID
+    assert st([A], 16, 2 * A, dtype=2) == INVALID            # unknown dtype
+    assert st([A], 16, 2 * A, dtype=-1) == INVALID
+    assert st([A], 16, 2 * A, path=5) == INVALID
+    assert rog.lib().rog_reduce_plan(rog._ptr_array([A]), 1, 16, F32, ctypes.c_void_p(2 * A), 0, None) == INVALID
+
+
+def test_element_alignment():
+    # binary32 elements need 4-byte addresses, bf16 2-byte ones; nothing more
+    assert st([A + 2], 16, 2 * A, F32) == INVALID
+    assert st([A], 16, 2 * A + 2, F32) == INVALID
+    assert st([A + 4, A + 4096 + 12], 16, 2 * A + 8, F32) == OK
+    assert st([A + 1], 16, 2 * A, BF16) == INVALID
+    assert st([A], 16, 2 * A + 3, BF16) == INVALID
+    assert st([A + 2, A + 4096 + 6], 16, 2 * A + 14, BF16) == OK
+
+
+def test_zero_count_is_a_no_op_even_with_null_pointers():
+    assert st([0, 0], 0, 0) == OK
+    p = rog.rog_reduce_plan_ptrs([0, 0, 0], 0, F32, 0)
+    assert p["kernel"] == "none" and p["grid"] == 0
+    rog.rog_reduce_ptrs([0, 0], 0, BF16, 0)                  # nothing enqueued, no HIP call
+
+
+def test_too_large():
+    big = (1 << 64) - 1
+    assert st([A], big // 2 + 1, 1 << 40, F32) == TOO_LARGE  # count * 4 overflows
+    assert st([A], 1 << 34, 1 << 40, F32) == TOO_LARGE       # 2^36 bytes
+    assert st([A], (1 << 34) - 4, 1 << 40, F32) == OK
+    assert st([A], 1 << 35, 1 << 40, BF16) == TOO_LARGE
+
+
+def test_address_wrap_is_invalid():
+    top = (1 << 64) - 64
+    assert st([top], 128, A) == INVALID
+    assert st([A], 128, top) == INVALID
+
+
+def test_in_place_and_overlap_rules():
+    n = 1000                                                  # 4000 bytes of binary32
+    out = 1 << 24
+    assert st([out, A], n, out) == OK                         # out is srcs[0]
+    assert st([A, out, out], n, out) == OK                    # out is two of the sources
+    assert st([A, out + 4], n, out) == OVERLAP                # shifted by one element
+    assert st([out - 4000, A], n, out) == OK                  # touching, not overlapping
+    assert st([out - 3996, A], n, out) == OVERLAP
+    assert st([A, A, A], n, out) == OK                        # aliased sources
+
+
+def test_auto_path_follows_the_bound_inclusively():
+    bound = rog.rog_reduce_single_wg_max_bytes()
+    for dtype, es in ((F32, 4), (BF16, 2)):
+        n = bound // es
+        assert rog.rog_reduce_plan_ptrs([A, A + (1 << 28)], n, dtype, 1 << 34)["path"] == "single_wg"
+        assert rog.rog_reduce_plan_ptrs([A, A + (1 << 28)], n + 1, dtype, 1 << 34)["path"] == "multi_wg"
+
+
+@pytest.mark.parametrize("count,dtype", [(1, F32), (4096, F32), (100001, BF16), (1 << 24, BF16), (7, BF16)])
+def test_grid_sizes(count, dtype):
+    es = 4 if dtype == F32 else 2
+    srcs = [A + 2, A + (1 << 30) + 6] if dtype == BF16 else [A, A + (1 << 30)]
+    p = rog.rog_reduce_plan_ptrs(srcs, count, dtype, 1 << 34, rog.ROG_PATH_MULTI_WG)
+    assert p["kernel"] == "reduce" and p["block"] == 64 and p["units"] == count
+    # one wave per 1 KiB chunk of the at most count * es / 16 body vectors
+    assert p["grid"] == max(1, -(-(count * es // 16) // 64))
+    s = rog.rog_reduce_plan_ptrs(srcs, count, dtype, 1 << 34, rog.ROG_PATH_SINGLE_WG)
+    assert s["grid"] == 1 and s["block"] == min(1024, max(64, -(-(-(-count * es // 16)) // 64) * 64))
+
+
+def test_nt_loads_follow_source_bytes():
+    # 8 sources of 48 MiB = 384 MiB of source bytes: loads stream past the caches
+    n = (48 << 20) // 2
+    srcs = [A + i * (1 << 27) for i in range(8)]
+    assert rog.rog_reduce_plan_ptrs(srcs, n, BF16, 1 << 40)["nt_loads"]
+    assert not rog.rog_reduce_plan_ptrs(srcs, n - 8, BF16, 1 << 40)["nt_loads"]
+
+
+def test_binding_errors_map_to_exceptions():
+    with pytest.raises(rog.RogArgumentError):
+        rog.rog_reduce_ptrs([A + 1], 16, F32, 2 * A)
+    with pytest.raises(rog.RogArgumentError):
+        rog.rog_reduce_ptrs([A, A + 8], 16, F32, A + 8)

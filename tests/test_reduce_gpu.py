@@ -1,0 +1,128 @@
+"""The rank-ordered sum on the GPU against the CPU oracle, bit for bit (a NaN
+matches any NaN), through the C ABI, on every path: the pages' per-rank sizes
+across their 256 KiB single-block bound, element alignments and ragged tails,
+random bit patterns (NaNs, infinities, subnormals), in place, aliased sources,
+the largest W, and the full bandwidth case."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from deterministic_collective_movement_amd import rog
+from deterministic_collective_movement_amd import workloads as wl
+from oracle import oracle
+from tests import gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+
+
+def test_two_1k_payloads(gpu):
+    case = wl.reduce_config1()[0]
+    gc.run_reduce_all_paths(gc.place_reduce(case, gpu), case.label())
+
+
+@pytest.mark.parametrize("case", wl.reduce_config2(), ids=lambda c: c.label())
+def test_size_sweep(gpu, case):
+    gc.run_reduce_all_paths(gc.place_reduce(case, gpu), case.label())
+
+
+@pytest.mark.parametrize("case", wl.reduce_config3(), ids=lambda c: c.label())
+def test_alignment_tails_and_bit_patterns(gpu, case):
+    gc.run_reduce_all_paths(gc.place_reduce(case, gpu), case.label())
+
+
+def test_bandwidth_case_full_output(gpu):
+    """W = 8 bf16 payloads of 64 MiB: every element against the oracle."""
+    case = wl.reduce_config4()
+    placed = gc.place_reduce(case, gpu)
+    plan = rog.rog_reduce_plan(placed.srcs, placed.out)
+    assert plan["path"] == "multi_wg" and plan["nt_loads"]
+    gc.run_reduce_all_paths(placed, case.label(), paths=(rog.ROG_PATH_AUTO,))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("W", [1, 5, 64])
+def test_every_W_up_to_the_maximum(gpu, dtype, W):
+    assert W <= rog.rog_max_peers()
+    for n in (1, 1000, 70001):
+        payloads = wl.reduce_payloads(wl.case_seed(15, W * 10 + n % 7), W, n, dtype)
+        placed = gc.PlacedReduce(payloads, [r % 4 for r in range(W)], 3, dtype, gpu)
+        gc.run_reduce_all_paths(placed, "W=%d n=%d %s" % (W, n, dtype))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("which", [0, 2])
+def test_in_place(gpu, dtype, which):
+    """out is srcs[which] itself (an in-place all-reduce)."""
+    n = 50_003
+    payloads = wl.reduce_payloads(wl.case_seed(16, which), 3, n, dtype)
+    placed = gc.PlacedReduce(payloads, [1, 0, 2], 0, dtype, gpu, in_place=which)
+    gc.run_reduce_all_paths(placed, "in place srcs[%d] %s" % (which, dtype))
+
+
+def test_aliased_sources(gpu):
+    """The same buffer passed as several ranks: x + x + y, in that order."""
+    n = 40_000
+    x, y = wl.reduce_payloads(wl.case_seed(17, 0), 2, n, "bf16")
+    placed = gc.PlacedReduce([x, y], [0, 0], 0, "bf16", gpu)
+    srcs = [placed.srcs[0], placed.srcs[0], placed.srcs[1]]
+    want = np.empty(n, np.uint16)
+    oracle.reduce_c([x, x, y], want, "bf16")
+    for path in gc.PATHS:
+        placed.reset()
+        rog.rog_reduce_ex(srcs, placed.out, path)
+        torch.cuda.synchronize()
+        got = placed.out.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, want), rog.PATH_NAMES[path]
+
+
+def test_repeated_calls_give_identical_bits(gpu):
+    """Determinism: the same call on both paths, many times, the same bits."""
+    n = 1 << 20
+    payloads = wl.reduce_payloads(wl.case_seed(18, 0), 8, n, "bf16")
+    placed = gc.PlacedReduce(payloads, [0] * 8, 0, "bf16", gpu)
+    outs = []
+    for k in range(10):
+        path = (rog.ROG_PATH_MULTI_WG, rog.ROG_PATH_SINGLE_WG)[k % 2]
+        outs.append(rog.rog_reduce_ex(placed.srcs, None, path))
+    torch.cuda.synchronize()
+    first = outs[0].view(torch.int16)
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), first)
+    placed.reset()
+    rog.rog_reduce(placed.srcs, placed.out)
+    placed.check("determinism reference")
+
+
+def test_reduce_scatter_shares(gpu):
+    """rog_reduce_scatter: rank r gets the sum of every input's shard r."""
+    W, n = 4, 12_345
+    inputs = wl.reduce_payloads(wl.case_seed(19, 0), W, W * n, "f32")
+    dev = [torch.from_numpy(x).to(gpu) for x in inputs]
+    for rank in range(W):
+        got = rog.rog_reduce_scatter(dev, rank)
+        want = np.empty(n, np.float32)
+        oracle.reduce_c([x[rank * n:(rank + 1) * n] for x in inputs], want, "f32")
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy().view(np.uint32), want.view(np.uint32)), rank
+
+
+def test_zero_elements_writes_nothing(gpu):
+    placed = gc.PlacedReduce([np.zeros(0, np.float32)] * 2, [0, 0], 0, "f32", gpu)
+    rog.rog_reduce(placed.srcs, placed.out)
+    placed.check("n = 0")
+
+
+def test_binding_rejects_bad_tensors(gpu):
+    a = torch.zeros(16, dtype=torch.float32, device=gpu)
+    with pytest.raises(ValueError):
+        rog.rog_reduce([a, torch.zeros(16, dtype=torch.bfloat16, device=gpu)])
+    with pytest.raises(ValueError):
+        rog.rog_reduce([a, torch.zeros(15, dtype=torch.float32, device=gpu)])
+    with pytest.raises(ValueError):
+        rog.rog_reduce([torch.zeros(16, dtype=torch.int32, device=gpu)])
+    with pytest.raises(ValueError):
+        rog.rog_reduce([a], torch.zeros(16, dtype=torch.float32))          # output on the CPU
+    with pytest.raises(rog.RogArgumentError):
+        rog.rog_reduce([a[:8], a[4:12]], a[4:12])                           # partial overlap
