@@ -19,8 +19,10 @@ pages' 1 - 128 KiB per-rank sizes at 2 and 8 payloads), per call and replayed
 from a HIP graph of 100 calls, next to the eager floor of one tiny torch
 kernel timed the same way; the batched gather (16 tensors, W = 4, one launch);
 the device-to-device copy ceiling; aligned gathers with 64 - 512 MiB outputs,
-warm and with rotating buffer sets (cold); and the CPU oracle on a bounded
-sample of the headline workload.
+warm and with rotating buffer sets (cold); the rank-ordered sum (rog_reduce:
+W = 8 bf16 payloads of 64 MiB, and the pages' per-rank sizes of 1 KiB - 4 MiB
+at W = 2 and 8); and the CPU oracle on a bounded sample of the headline
+workload.
 
 Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
 """
@@ -424,6 +426,111 @@ def crossover(torch, rog, device, steps, warmup, totals=CROSSOVER_TOTALS):
     return rows
 
 
+# ---------------------------------------------------------------------------
+# Rank-ordered sum (rog_reduce)
+# ---------------------------------------------------------------------------
+
+class ReduceCall:
+    """A prepared rog_reduce_ex call: ctypes arguments built once."""
+
+    def __init__(self, rog, srcs, out, stream, path=0):
+        self.lib = rog.lib()
+        self.W = len(srcs)
+        self.n = srcs[0].numel()
+        self.dtype = rog.DTYPES[srcs[0].dtype]
+        self.ptrs = (ctypes.c_void_p * self.W)(*[s.data_ptr() for s in srcs])
+        self.out = ctypes.c_void_p(out.data_ptr())
+        self.stream = ctypes.c_void_p(stream)
+        self.path = path
+
+    def __call__(self):
+        st = self.lib.rog_reduce_ex(self.ptrs, self.W, self.n, self.dtype, self.out, self.stream, self.path)
+        if st != 0:
+            raise RuntimeError("rog_reduce failed with status %d" % st)
+
+
+def _reduce_tensors(torch, case, device):
+    import numpy as np
+    tdt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    payloads = case.payloads()
+    srcs = [torch.from_numpy(p.view(np.int16) if case.dtype == "bf16" else p).to(device).view(tdt)
+            for p in payloads]
+    return payloads, srcs, torch.empty(case.n, dtype=tdt, device=device)
+
+
+def reduce_bench(torch, rog, wl, device, steps, warmup):
+    """The rank-ordered sum: the W = 8 bf16 x 64 MiB bandwidth case (timed
+    region and per-call p50, sampled elements checked against the CPU oracle)
+    and the pages' per-rank sizes 1 KiB - 4 MiB at W = 2 and 8 (per-call p50)."""
+    import numpy as np
+    from oracle import oracle
+    stream = torch.cuda.current_stream(device).cuda_stream
+    case = wl.reduce_config4()
+    payloads, srcs, out = _reduce_tensors(torch, case, device)
+    call = ReduceCall(rog, srcs, out, stream)
+    region_ms = time_region(torch, call, steps, warmup)
+    per_call, _ = time_calls(torch, call, steps, 0)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for lo in (0, case.n // 2, case.n - 4096):
+        want = np.empty(4096, np.uint16)
+        oracle.reduce_c([p[lo:lo + 4096] for p in payloads], want, "bf16")
+        if not np.array_equal(got[lo:lo + 4096], want):
+            raise AssertionError("reduce bandwidth case differs from the oracle at element %d" % lo)
+    moved = (case.W + 1) * case.n * case.esize
+    plan = rog.rog_reduce_plan(srcs, out)
+    big = {"W": case.W, "dtype": case.dtype, "bytes_per_rank": case.n * case.esize, "bytes_moved": moved,
+           "path": plan["path"], "grid": plan["grid"], "block": plan["block"],
+           "mean_launch_us": round(1e3 * region_ms / steps, 2),
+           "p50_us": round(1e3 * statistics.median(per_call), 2),
+           "GBps": round(gbps(moved * steps, region_ms), 1),
+           "pct_of_peak": round(100 * gbps(moved * steps, region_ms) / PEAK_HBM_GBPS, 2)}
+    del srcs, out
+    rows = []
+    for c in wl.reduce_config2():
+        _, srcs, out = _reduce_tensors(torch, c, device)
+        p = rog.rog_reduce_plan(srcs, out)
+        per_call, _ = time_calls(torch, ReduceCall(rog, srcs, out, stream), steps, warmup)
+        sm = summarize_ms(per_call)
+        rows.append({"W": c.W, "KiB_per_rank": c.n * c.esize // 1024, "path": p["path"],
+                     "p10_us": round(sm["p10_us"], 2), "p50_us": round(sm["p50_us"], 2),
+                     "p90_us": round(sm["p90_us"], 2)})
+    return {"bandwidth": big, "latency": rows}
+
+
+REDUCE_CROSSOVER_KIB = (1, 2, 4, 8, 16, 24, 32, 48, 64, 128, 256)
+
+
+def reduce_crossover(torch, rog, device, steps, warmup, sizes_kib=REDUCE_CROSSOVER_KIB):
+    """Both forced paths of rog_reduce on bf16 outputs of the given sizes at W = 2
+    and 8, each call event-timed (the bound is chosen from the kernel-only
+    durations of the same command under rocprofv3 --kernel-trace).  Call order
+    per case: one checked call, ``warmup`` calls, ``steps`` timed calls;
+    single-WG first, then multi-WG."""
+    stream = torch.cuda.current_stream(device).cuda_stream
+    g = torch.Generator(device=device)
+    g.manual_seed(8)
+    rows = []
+    for W in (2, 8):
+        for kib in sizes_kib:
+            n = kib * 512
+            srcs = [(torch.rand(n, device=device, generator=g) * 2 - 1).to(torch.bfloat16) for _ in range(W)]
+            outs = {}
+            row = {"W": W, "output_bytes": 2 * n}
+            for path, name in ((rog.ROG_PATH_SINGLE_WG, "single_wg"), (rog.ROG_PATH_MULTI_WG, "multi_wg")):
+                out = torch.empty(n, dtype=torch.bfloat16, device=device)
+                call = ReduceCall(rog, srcs, out, stream, path)
+                call()
+                torch.cuda.synchronize()
+                outs[name] = out
+                per_call, _ = time_calls(torch, call, steps, warmup)
+                row[name + "_p50_us"] = round(1e3 * statistics.median(per_call), 2)
+            if not torch.equal(outs["single_wg"].view(torch.int16), outs["multi_wg"].view(torch.int16)):
+                raise AssertionError("reduce paths disagree at W=%d, %d KiB" % (W, kib))
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+    return rows
+
+
 def cpu_baseline(case, payloads, budget_s):
     """The CPU oracle, single-threaded, on the full headline gather repeated for
     about ``budget_s`` seconds of CPU work."""
@@ -454,6 +561,8 @@ def main(argv=None):
                     help="time only the headline gather and its misaligned variant (for counter runs)")
     ap.add_argument("--calibrate-bytes", type=int, default=0,
                     help="also run a plain elementwise copy of this many bytes, for counter scaling")
+    ap.add_argument("--reduce-crossover", action="store_true",
+                    help="time both forced rog_reduce paths over small outputs instead")
     ap.add_argument("--crossover", action="store_true",
                     help="time both forced paths over small outputs instead (one JSON line per case)")
     args = ap.parse_args(argv)
@@ -473,6 +582,9 @@ def main(argv=None):
         return 2
     device = torch.device("cuda:0")
     torch.cuda.set_device(device)
+    if args.reduce_crossover:
+        reduce_crossover(torch, rog, device, args.steps, args.warmup)
+        return 0
     if args.crossover:
         crossover(torch, rog, device, args.steps, args.warmup)
         return 0
@@ -506,6 +618,7 @@ def main(argv=None):
                                             max(1, args.warmup // 5))
         extras["d2d_copy_ceiling"] = d2d_ceiling(torch, device, case.W * case.S, 20, 3)
         extras["bandwidth_sweep"] = bandwidth_sweep(torch, rog, device, 20)
+        extras["reduce"] = reduce_bench(torch, rog, wl, device, args.steps, args.warmup)
         cpu = cpu_baseline(case, payloads, args.cpu_budget)
     else:
         cpu = None

@@ -25,7 +25,7 @@ constexpr int kMaxBatchPtrs = 192;
 #define ROG_SINGLE_WG_MAX_BYTES (32 * 1024)
 #endif
 #ifndef ROG_REDUCE_SINGLE_WG_MAX_BYTES
-#define ROG_REDUCE_SINGLE_WG_MAX_BYTES (32 * 1024)
+#define ROG_REDUCE_SINGLE_WG_MAX_BYTES (64 * 1024)
 #endif
 #ifndef ROG_FLAT_BLOCK
 #define ROG_FLAT_BLOCK 64
@@ -55,7 +55,9 @@ constexpr int kMaxBatchPtrs = 192;
 // Output bytes up to which ROG_PATH_AUTO uses the single-workgroup path
 // (inclusive), measured by sweeping both forced paths.
 constexpr size_t kSingleWgMaxBytes = ROG_SINGLE_WG_MAX_BYTES;
-// The same bound for rog_reduce, on its output bytes.
+// The bound for rog_reduce, on its source bytes W * count * esize: the measured
+// crossover sits at the same source bytes for W = 2 (32 KiB out) and W = 8
+// (8 KiB out), as the pages' all-reduce bound is tested on input bytes.
 constexpr size_t kReduceSingleWgMaxBytes = ROG_REDUCE_SINGLE_WG_MAX_BYTES;
 
 // Launch shapes.  A multi-WG wave copies a chunk of 64 * unroll consecutive

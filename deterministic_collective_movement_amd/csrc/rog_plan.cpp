@@ -214,7 +214,7 @@ rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype d
         if (ranges_overlap(s, bytes, o, bytes) && s != o) return ROG_ERR_OVERLAP;
     }
     if (path == ROG_PATH_AUTO)
-        path = bytes <= kReduceSingleWgMaxBytes ? ROG_PATH_SINGLE_WG : ROG_PATH_MULTI_WG;
+        path = uint64_t(W) * bytes <= kReduceSingleWgMaxBytes ? ROG_PATH_SINGLE_WG : ROG_PATH_MULTI_WG;
     info.path = path;
     info.kernel = ROG_KERNEL_REDUCE;
     info.units = count;

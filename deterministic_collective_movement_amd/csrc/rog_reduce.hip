@@ -70,7 +70,13 @@ __device__ __forceinline__ vec16 narrow(const float (&a)[Elem<BF16>::kPerVec]) {
     return v;
 }
 
-constexpr uint32_t kGroup = 8;   // source loads in flight per lane
+#ifndef ROG_REDUCE_GROUP
+#define ROG_REDUCE_GROUP 8
+#endif
+#ifndef ROG_REDUCE_XCD
+#define ROG_REDUCE_XCD 1
+#endif
+constexpr uint32_t kGroup = ROG_REDUCE_GROUP;   // source loads in flight per lane
 
 // The rank-ordered sum of the 16-byte vectors at byte offset off of every source.
 template <bool BF16, bool NTL>
@@ -125,7 +131,7 @@ __global__ __launch_bounds__(kWaveBlock) void rog_reduce_kernel(ReduceArgs a) {
     const PeerSplit cut = split_payload(reinterpret_cast<uintptr_t>(a.out), bytes);
     uint8_t *o = static_cast<uint8_t *>(a.out);
     for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x) {
-        const uint32_t j = xcd_grouped(vb, a.n_chunks);
+        const uint32_t j = ROG_REDUCE_XCD ? xcd_grouped(vb, a.n_chunks) : vb;
         if (j == 0) {
             for (uint64_t i = lane; i < cut.lo / Elem<BF16>::kSize; i += 64) sum_elem<BF16>(a.src, a.W, i, a.out);
             for (uint64_t i = cut.hi / Elem<BF16>::kSize + lane; i < a.count; i += 64)

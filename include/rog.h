@@ -208,8 +208,10 @@ ROG_API size_t rog_single_wg_max_bytes(void);
  *         overlap with a source is an error.  Sources may alias each other.
  * stream  HIP stream of the current device.
  *
- * Path: single-workgroup when count * element size <= rog_reduce_single_wg_max_bytes()
- * (inclusive, measured on gfx950), multi-workgroup otherwise.
+ * Path: single-workgroup when the source bytes W * count * element size are
+ * <= rog_reduce_single_wg_max_bytes() (inclusive, measured on gfx950; the
+ * pages test their all-reduce bound on input bytes too), multi-workgroup
+ * otherwise.
  * Errors (nothing enqueued):
  *   ROG_ERR_INVALID_ARGUMENT  srcs NULL; W out of range; dtype or path unknown;
  *                             count > 0 and out or some srcs[r] NULL or not
@@ -231,8 +233,8 @@ ROG_API rog_status rog_reduce_ex(const void *const *srcs, int W, size_t count, r
 ROG_API rog_status rog_reduce_plan(const void *const *srcs, int W, size_t count, rog_dtype dtype,
                                    const void *out, rog_path path, rog_plan_info *info);
 
-/* Output bytes up to which ROG_PATH_AUTO runs rog_reduce on one workgroup
- * (inclusive), measured on MI355X. */
+/* Source bytes (W * count * element size) up to which ROG_PATH_AUTO runs
+ * rog_reduce on one workgroup (inclusive), measured on MI355X. */
 ROG_API size_t rog_reduce_single_wg_max_bytes(void);
 
 /* Largest W accepted (kernel-argument capacity). */

@@ -86,12 +86,14 @@ def test_in_place_and_overlap_rules():
     assert st([A, A, A], n, out) == OK                        # aliased sources
 
 
-def test_auto_path_follows_the_bound_inclusively():
+def test_auto_path_follows_the_bound_on_source_bytes_inclusively():
     bound = rog.rog_reduce_single_wg_max_bytes()
-    for dtype, es in ((F32, 4), (BF16, 2)):
-        n = bound // es
-        assert rog.rog_reduce_plan_ptrs([A, A + (1 << 28)], n, dtype, 1 << 34)["path"] == "single_wg"
-        assert rog.rog_reduce_plan_ptrs([A, A + (1 << 28)], n + 1, dtype, 1 << 34)["path"] == "multi_wg"
+    for W in (1, 2, 8):
+        srcs = [A + r * (1 << 28) for r in range(W)]
+        for dtype, es in ((F32, 4), (BF16, 2)):
+            n = bound // (W * es)              # W * n * es == bound exactly
+            assert rog.rog_reduce_plan_ptrs(srcs, n, dtype, 1 << 40)["path"] == "single_wg", (W, es)
+            assert rog.rog_reduce_plan_ptrs(srcs, n + 1, dtype, 1 << 40)["path"] == "multi_wg", (W, es)
 
 
 @pytest.mark.parametrize("count,dtype", [(1, F32), (4096, F32), (100001, BF16), (1 << 24, BF16), (7, BF16)])
