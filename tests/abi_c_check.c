@@ -7,7 +7,8 @@
  *
  * Cases: aligned (flat) and misaligned (per-payload) gathers on every path,
  * a batch of three tensors in one launch, S = 0, and the argument errors that
- * must be reported before anything is enqueued.
+ * must be reported before anything is enqueued; rank-ordered sums (bf16 and
+ * binary32, every path, element offsets, in place) against the oracle's sum.
  * Exit status 0 = every check passed; the first failure is printed.
  */
 #include <hip/hip_runtime_api.h>
@@ -18,6 +19,8 @@
 #include "rog.h"
 
 void rog_oracle_gather(const unsigned char *const *srcs, int W, size_t S, unsigned char *out);
+void rog_oracle_reduce_f32(const float *const *srcs, int W, size_t count, float *out);
+void rog_oracle_reduce_bf16(const uint16_t *const *srcs, int W, size_t count, uint16_t *out);
 
 #define GUARD 64
 #define FILL 0xA5
@@ -173,6 +176,75 @@ static void error_cases(hipStream_t st) {
     CHECK_HIP(hipFree(buf));
 }
 
+/* Element i of payload r for the sums: finite bf16 / binary32 values spread over
+ * a few binades, of both signs. */
+static uint32_t elem_bits(unsigned seed, size_t i, int bf16) {
+    unsigned x = seed * 2246822519u + (unsigned)i * 3266489917u;
+    x ^= x >> 15;
+    x *= 0x2c1b3c6du;
+    x ^= x >> 12;
+    const uint32_t sign = (x & 1u) << 31;
+    const uint32_t expo = 120u + ((x >> 1) % 12u);          /* 2^-7 .. 2^4 */
+    const uint32_t mant = (x >> 5) & 0x7FFFFFu;
+    const uint32_t f = sign | (expo << 23) | mant;
+    return bf16 ? (f >> 16) : f;
+}
+
+/* One sum of W payloads of n elements; payload r at element offset r % 4 of its
+ * buffer, out at element offset out_off (or out = payload `in_place`). */
+static void reduce_case(int W, size_t n, int bf16, size_t out_off, int in_place, rog_path path, hipStream_t st) {
+    const size_t es = bf16 ? 2 : 4;
+    unsigned char *host[64], *dev[64];
+    const void *dsrc[64];
+    const void *hsrc[64];
+    for (int r = 0; r < W; ++r) {
+        const size_t off = (size_t)(r % 4) * es;
+        host[r] = (unsigned char *)malloc(off + n * es + 16);
+        for (size_t i = 0; i < n; ++i) {
+            const uint32_t b = elem_bits(31u * (unsigned)r + 7u, i, bf16);
+            memcpy(host[r] + off + i * es, &b, es);           /* little-endian: low bytes */
+        }
+        CHECK_HIP(hipMalloc((void **)&dev[r], off + n * es + 16));
+        CHECK_HIP(hipMemcpy(dev[r], host[r], off + n * es, hipMemcpyHostToDevice));
+        dsrc[r] = dev[r] + off;
+        hsrc[r] = host[r] + off;
+    }
+    unsigned char *want = (unsigned char *)malloc(n * es + 1);
+    unsigned char *got = (unsigned char *)malloc(n * es + 1);
+    if (bf16) rog_oracle_reduce_bf16((const uint16_t *const *)hsrc, W, n, (uint16_t *)want);
+    else rog_oracle_reduce_f32((const float *const *)hsrc, W, n, (float *)want);
+    unsigned char *dout = NULL;
+    void *out;
+    if (in_place >= 0) {
+        out = (void *)dsrc[in_place];
+    } else {
+        CHECK_HIP(hipMalloc((void **)&dout, (out_off + n) * es));
+        out = dout + out_off * es;
+    }
+    const rog_status s = rog_reduce_ex(dsrc, W, n, bf16 ? ROG_DTYPE_BF16 : ROG_DTYPE_F32, out, st, path);
+    if (s != ROG_OK) {
+        fprintf(stderr, "FAIL reduce W=%d n=%zu bf16=%d path=%d: %s\n", W, n, bf16, (int)path, rog_status_string(s));
+        ++failures;
+    } else {
+        CHECK_HIP(hipStreamSynchronize(st));
+        CHECK_HIP(hipMemcpy(got, out, n * es, hipMemcpyDeviceToHost));
+        if (memcmp(got, want, n * es) != 0) {
+            size_t k = 0;
+            while (got[k] == want[k]) ++k;
+            fprintf(stderr, "FAIL reduce W=%d n=%zu bf16=%d out_off=%zu in_place=%d path=%d: element %zu\n", W, n,
+                    bf16, out_off, in_place, (int)path, k / es);
+            ++failures;
+        }
+    }
+    if (dout) CHECK_HIP(hipFree(dout));
+    for (int r = 0; r < W; ++r) {
+        CHECK_HIP(hipFree(dev[r]));
+        free(host[r]);
+    }
+    free(want);
+    free(got);
+}
+
 int main(void) {
     hipStream_t st;
     CHECK_HIP(hipStreamCreate(&st));
@@ -187,6 +259,15 @@ int main(void) {
                     gather_case(Ws[w], sizes[s], offs[o][0], offs[o][1], paths[p], st);
     batch_case(st);
     error_cases(st);
+    const size_t counts[] = {1, 9, 1000, 32769, 300001};
+    const int rWs[] = {1, 3, 8};
+    for (int p = 0; p < 3; ++p)
+        for (int bf16 = 0; bf16 < 2; ++bf16)
+            for (unsigned w = 0; w < sizeof rWs / sizeof rWs[0]; ++w)
+                for (unsigned c = 0; c < sizeof counts / sizeof counts[0]; ++c) {
+                    reduce_case(rWs[w], counts[c], bf16, (size_t)c % 4, -1, paths[p], st);
+                    if (rWs[w] > 1) reduce_case(rWs[w], counts[c], bf16, 0, rWs[w] - 1, paths[p], st);
+                }
     CHECK_HIP(hipStreamDestroy(st));
     printf("abi_c_check: %d failures; single-WG bound %zu bytes, max W %d\n", failures,
            rog_single_wg_max_bytes(), rog_max_peers());
