@@ -458,10 +458,9 @@ def _reduce_tensors(torch, case, device):
     return payloads, srcs, torch.empty(case.n, dtype=tdt, device=device)
 
 
-def reduce_bench(torch, rog, wl, device, steps, warmup):
-    """The rank-ordered sum: the W = 8 bf16 x 64 MiB bandwidth case (timed
-    region and per-call p50, sampled elements checked against the CPU oracle)
-    and the pages' per-rank sizes 1 KiB - 4 MiB at W = 2 and 8 (per-call p50)."""
+def reduce_bandwidth(torch, rog, wl, device, steps, warmup):
+    """The rank-ordered sum of W = 8 bf16 payloads of 64 MiB: timed region and
+    per-call p50; sampled elements checked against the CPU oracle."""
     import numpy as np
     from oracle import oracle
     stream = torch.cuda.current_stream(device).cuda_stream
@@ -485,6 +484,13 @@ def reduce_bench(torch, rog, wl, device, steps, warmup):
            "GBps": round(gbps(moved * steps, region_ms), 1),
            "pct_of_peak": round(100 * gbps(moved * steps, region_ms) / PEAK_HBM_GBPS, 2)}
     del srcs, out
+    torch.cuda.empty_cache()
+    return big
+
+
+def reduce_latency(torch, rog, wl, device, steps, warmup):
+    """The pages' per-rank sizes 1 KiB - 4 MiB at W = 2 and 8: per-call p50."""
+    stream = torch.cuda.current_stream(device).cuda_stream
     rows = []
     for c in wl.reduce_config2():
         _, srcs, out = _reduce_tensors(torch, c, device)
@@ -494,7 +500,7 @@ def reduce_bench(torch, rog, wl, device, steps, warmup):
         rows.append({"W": c.W, "KiB_per_rank": c.n * c.esize // 1024, "path": p["path"],
                      "p10_us": round(sm["p10_us"], 2), "p50_us": round(sm["p50_us"], 2),
                      "p90_us": round(sm["p90_us"], 2)})
-    return {"bandwidth": big, "latency": rows}
+    return rows
 
 
 REDUCE_CROSSOVER_KIB = (1, 2, 4, 8, 16, 24, 32, 48, 64, 128, 256)
@@ -558,7 +564,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
     ap.add_argument("--headline-only", action="store_true",
-                    help="time only the headline gather and its misaligned variant (for counter runs)")
+                    help="time only the headline gather, its misaligned variant and the large "
+                         "rank-ordered sum (for counter runs)")
     ap.add_argument("--calibrate-bytes", type=int, default=0,
                     help="also run a plain elementwise copy of this many bytes, for counter scaling")
     ap.add_argument("--reduce-crossover", action="store_true",
@@ -618,9 +625,12 @@ def main(argv=None):
                                             max(1, args.warmup // 5))
         extras["d2d_copy_ceiling"] = d2d_ceiling(torch, device, case.W * case.S, 20, 3)
         extras["bandwidth_sweep"] = bandwidth_sweep(torch, rog, device, 20)
-        extras["reduce"] = reduce_bench(torch, rog, wl, device, args.steps, args.warmup)
+        extras["reduce"] = {"bandwidth": reduce_bandwidth(torch, rog, wl, device, args.steps, args.warmup),
+                            "latency": reduce_latency(torch, rog, wl, device, args.steps, args.warmup)}
         cpu = cpu_baseline(case, payloads, args.cpu_budget)
     else:
+        extras["reduce"] = {"bandwidth": reduce_bandwidth(torch, rog, wl, device, max(10, args.steps // 2),
+                                                          max(2, args.warmup // 2))}
         cpu = None
     extras["device"] = torch.cuda.get_device_name(device)
     config = {"workload": "rank-ordered gather of W=8 aligned bf16 payloads of 64 MiB into a 512 MiB "
