@@ -1,4 +1,4 @@
-"""rog_gather and rog_gather_many inside a captured HIP graph.
+"""rog_gather, rog_gather_many and rog_reduce inside a captured HIP graph.
 
 Each call is one kernel launch on the caller's stream with every argument in
 the kernel arguments -- no allocation, no memset, no synchronisation -- so a
@@ -91,3 +91,40 @@ def test_graph_captures_a_batched_gather(gpu):
         torch.cuda.synchronize()
         for srcs, o in zip(batch, outs):
             assert np.array_equal(o.cpu().numpy(), _expected(srcs)), replay
+
+
+def test_graph_captures_rank_ordered_sums(gpu):
+    """rog_reduce on both paths (single-WG and multi-WG), bf16 and binary32, in
+    one captured graph; the sources change between replays and every replay
+    matches the oracle bit for bit."""
+    specs = [(2, 1000, "bf16"), (8, 70_001, "bf16"), (3, 40_000, "f32")]
+    cases = []
+    for W, n, dt in specs:
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        srcs = [torch.zeros(n, dtype=tdt, device=gpu) for _ in range(W)]
+        cases.append((W, n, dt, srcs, torch.zeros(n, dtype=tdt, device=gpu)))
+    for _, _, _, srcs, out in cases:
+        rog.rog_reduce(srcs, out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _, _, _, srcs, out in cases:
+            rog.rog_reduce(srcs, out)
+    for replay in range(4):
+        wants = []
+        for W, n, dt, srcs, out in cases:
+            payloads = wl.reduce_payloads(wl.case_seed(20, replay * 10 + W), W, n, dt)
+            for s, p in zip(srcs, payloads):
+                s.copy_(torch.from_numpy(p.view(np.int16) if dt == "bf16" else p).to(gpu).view(s.dtype))
+            out.zero_()
+            want = np.empty(n, oracle.REDUCE_DTYPES[dt])
+            oracle.reduce_c(payloads, want, dt)
+            wants.append(want)
+        torch.cuda.synchronize()
+        print("graph replay %d (sums)" % replay, flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        for (W, n, dt, _, out), want in zip(cases, wants):
+            bits = torch.int16 if dt == "bf16" else torch.int32
+            got = out.view(bits).cpu().numpy().view(want.dtype)
+            assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), (replay, W, n, dt)
