@@ -40,15 +40,5 @@ __device__ __forceinline__ uint32_t divide(uint32_t v, const Divider &d) {
     return (t + ((v - t) >> d.sh1)) >> d.sh2;
 }
 
-// Workgroups go to the 8 XCDs round-robin (b mod 8).  Hand each XCD runs of
-// kXcdRun consecutive chunks, so that neighbouring chunks -- which share the
-// cache line a misaligned chunk straddles -- meet in the same L2.  A bijection
-// on [0, n): whole spans of 8 * kXcdRun are permuted, the rest is left as is.
-__device__ __forceinline__ uint32_t xcd_grouped(uint32_t b, uint32_t n) {
-    constexpr uint32_t kSpan = kXcds * kXcdRun;
-    if (kXcdRun <= 1 || b >= n - n % kSpan) return b;
-    const uint32_t x = b % kXcds, k = b / kXcds;
-    return (k / kXcdRun) * kSpan + x * kXcdRun + k % kXcdRun;
-}
 
 }  // namespace rog

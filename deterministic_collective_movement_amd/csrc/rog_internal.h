@@ -116,6 +116,17 @@ __host__ __device__ inline PeerSplit split_payload(uint64_t da, uint64_t S) {
     return PeerSplit{to_line, to_line + ((S - to_line) & ~uint64_t(15))};
 }
 
+// Workgroups go to the 8 XCDs round-robin (b mod 8).  Hand each XCD runs of
+// kXcdRun consecutive chunks, so that neighbouring chunks -- which share the
+// cache line a misaligned chunk straddles -- meet in the same L2.  A bijection
+// on [0, n): whole spans of 8 * kXcdRun are permuted, the rest is left as is.
+__host__ __device__ inline uint32_t xcd_grouped(uint32_t b, uint32_t n) {
+    constexpr uint32_t kSpan = kXcds * kXcdRun;
+    if (kXcdRun <= 1 || b >= n - n % kSpan) return b;
+    const uint32_t x = b % kXcds, k = b / kXcds;
+    return (k / kXcdRun) * kSpan + x * kXcdRun + k % kXcdRun;
+}
+
 // ---------------------------------------------------------------------------
 // Kernel arguments
 // ---------------------------------------------------------------------------

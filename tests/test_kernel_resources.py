@@ -17,13 +17,19 @@ from deterministic_collective_movement_amd import build as b
 @pytest.fixture(scope="module")
 def kernels(tmp_path_factory):
     hipcc = shutil.which("hipcc") or os.path.join(b.ROCM, "bin", "hipcc")
-    out = str(tmp_path_factory.mktemp("asm") / "rog.s")
-    subprocess.check_call([hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "--offload-device-only",
-                           "-S", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                           "-Wno-unused-command-line-argument", "-I", b.INCLUDE, "-I", b.CSRC,
-                           os.path.join(b.CSRC, "rog_kernels.hip"), "-o", out],
-                          stderr=subprocess.DEVNULL)
-    text = open(out).read()
+    ks = {}
+    for src in ("rog_kernels.hip", "rog_reduce.hip"):
+        out = str(tmp_path_factory.mktemp("asm") / (src + ".s"))
+        subprocess.check_call([hipcc, "-O3", "-std=c++17", "--offload-arch=gfx950", "--offload-device-only",
+                               "-S", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                               "-Wno-unused-command-line-argument", "-I", b.INCLUDE, "-I", b.CSRC,
+                               os.path.join(b.CSRC, src), "-o", out],
+                              stderr=subprocess.DEVNULL)
+        ks.update(_parse(open(out).read()))
+    return ks
+
+
+def _parse(text):
     meta = text[text.index("amdhsa.kernels:"):]
     ks = {}
     for block in meta.split("  - .")[1:]:
@@ -33,17 +39,16 @@ def kernels(tmp_path_factory):
         get = lambda k: int(re.search(r"\.%s:\s+(\d+)" % k, block).group(1))  # noqa: E731
         ks[name.group(1)] = {"scratch": get("private_segment_fixed_size"), "vgpr": get("vgpr_count"),
                              "max_wg": get("max_flat_workgroup_size"),
-                             "dyn_stack": "uses_dynamic_stack:  true" in block or
-                                          re.search(r"uses_dynamic_stack:\s+true", block) is not None}
+                             "dyn_stack": re.search(r"uses_dynamic_stack:\s+true", block) is not None}
     return ks
 
 
 def test_every_kernel_is_present(kernels):
     names = " ".join(kernels)
     for k in ("rog_flat_kernel", "rog_flat_single_kernel", "rog_peer_kernel", "rog_peer_single_kernel",
-              "rog_batch_kernel"):
+              "rog_batch_kernel", "rog_reduce_kernel", "rog_reduce_single_kernel"):
         assert k in names, k
-    assert len(kernels) >= 10
+    assert len(kernels) >= 18
 
 
 def test_no_scratch_and_vgprs_fit(kernels):

@@ -82,3 +82,48 @@ def test_a_concrete_cut(split):
 def test_aligned_destination_has_no_head(split):
     lo, hi = split(1 << 40, 4096 + 5)
     assert lo == 0 and hi == 4096
+
+
+# ---------------------------------------------------------------------------
+# XCD-grouped chunk order
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def xcd(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or os.path.join(b.ROCM, "bin", "hipcc")
+    so = str(tmp_path_factory.mktemp("xcd") / "libxcd.so")
+    subprocess.check_call([hipcc, "-x", "hip", "-O2", "-std=c++17", "-fPIC", "-shared",
+                           "--offload-arch=gfx950", "-Wno-unused-command-line-argument",
+                           "-I", b.INCLUDE, "-I", b.CSRC, os.path.join(HERE, "split_shim.cpp"), "-o", so],
+                          stderr=subprocess.DEVNULL)
+    lib = ctypes.CDLL(so)
+    lib.rog_test_xcd_run.restype = ctypes.c_uint32
+    lib.rog_test_xcd_grouped.argtypes = [ctypes.c_uint32, ctypes.c_void_p]
+
+    def f(n):
+        import numpy as np
+        out = np.empty(max(1, n), np.uint32)
+        lib.rog_test_xcd_grouped(n, out.ctypes.data)
+        return out[:n]
+    f.run = int(lib.rog_test_xcd_run())
+    return f
+
+
+def test_xcd_grouping_is_a_bijection_with_runs(xcd):
+    """Every launch size: each chunk is visited exactly once; within whole spans
+    of 8 runs, workgroup b (on XCD b mod 8) handles chunks in runs of kXcdRun
+    consecutive chunks per XCD; the remainder keeps its order."""
+    import numpy as np
+    R = xcd.run
+    span = 8 * R
+    sizes = sorted(set(list(range(0, 3 * span + 9, 7)) + [span - 1, span, span + 1, 5 * span + 3, 65536, 1 << 20]))
+    for n in sizes:
+        m = xcd(n)
+        assert np.array_equal(np.sort(m), np.arange(n, dtype=np.uint32)), n
+        full = n - n % span
+        b = np.arange(full, dtype=np.int64)
+        if full:
+            # XCD x = b % 8 works on consecutive chunks x*R + k (mod R) within span b // span
+            x, k = b % 8, b // 8
+            assert np.array_equal(m[:full], (k // R) * span + x * R + k % R)
+        assert np.array_equal(m[full:], np.arange(full, n, dtype=np.uint32)), n
