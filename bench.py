@@ -75,11 +75,22 @@ def gbps(nbytes, ms):
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def code_only(text):
+    """C/C++ source with comments removed and whitespace runs collapsed, so
+    that edits to comments alone leave the digest of the code unchanged.  (The
+    sources hold no string literal with a comment marker in it.)"""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest(paths=KERNEL_SOURCES):
+    """sha256 over the code (comments and layout stripped) of the sources the
+    headline kernel is built from, in order."""
     h = hashlib.sha256()
     for p in paths:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()
 
 

@@ -1,4 +1,5 @@
-"""deterministic_collective_movement_amd -- rank-ordered gather (rog) for MI355X.
+"""deterministic_collective_movement_amd -- rank-ordered gather and rank-ordered
+sum (rog) for MI355X.
 
 The library is the C-ABI shared object ``librog.so`` (declared in
 ``include/rog.h``) built from the hand-written HIP kernels under ``csrc/``.

@@ -60,13 +60,14 @@ constexpr size_t kSingleWgMaxBytes = ROG_SINGLE_WG_MAX_BYTES;
 // (8 KiB out), as the pages' all-reduce bound is tested on input bytes.
 constexpr size_t kReduceSingleWgMaxBytes = ROG_REDUCE_SINGLE_WG_MAX_BYTES;
 
-// Launch shapes.  A multi-WG wave copies a chunk of 64 * unroll consecutive
-// 16-byte vectors; each of its loads and stores is one dwordx4 instruction over
-// 64 consecutive vectors (1 KiB).  Small workgroups of one wave, one 1 KiB chunk
-// each, measured fastest for HBM-bound gathers (FLAT, PEER and BATCH alike).
+// Launch shapes.  A multi-WG wave works on a chunk of 64 * unroll consecutive
+// 16-byte output vectors; each of its loads and stores is one dwordx4
+// instruction over 64 consecutive vectors (1 KiB).  Small workgroups of one
+// wave, one 1 KiB chunk each, measured fastest for the HBM-bound launches
+// (FLAT, PEER, BATCH and REDUCE alike).
 constexpr int kFlatBlock = ROG_FLAT_BLOCK;        // multi-WG FLAT workgroup (threads)
 constexpr int kFlatUnroll = ROG_FLAT_UNROLL;      // vectors per lane per chunk
-constexpr int kWaveBlock = 64;                    // multi-WG PEER and BATCH workgroup
+constexpr int kWaveBlock = 64;                    // multi-WG PEER, BATCH and REDUCE workgroup
 constexpr int kSingleBlock = 1024;                // the single workgroup (16 waves)
 constexpr int kSingleUnroll = ROG_SINGLE_UNROLL;  // single-WG FLAT vectors per lane
 constexpr int kSinglePeerUnroll = 4;              // single-WG PEER vectors per thread
@@ -80,10 +81,10 @@ constexpr uint32_t kGridCap = ROG_GRID_CAP;       // workgroups of one launch, a
 // 256 measured best (vs 16: +4.7 % on 8 x 64 MiB at offsets 1/3).
 constexpr uint64_t kBodyAlign = ROG_BODY_ALIGN;
 static_assert(kBodyAlign >= 16 && (kBodyAlign & (kBodyAlign - 1)) == 0, "body alignment");
-// Workgroups are dispatched to the 8 XCDs round-robin.  PEER and BATCH
+// Workgroups are dispatched to the 8 XCDs round-robin.  PEER, BATCH and REDUCE
 // launches hand each XCD runs of kXcdRun consecutive 1 KiB chunks (128 measured
-// best of 1..1024: a misaligned chunk straddles one cache line with its
-// neighbour, which then sits in the same L2).
+// best of 1..1024 for PEER: a misaligned chunk straddles one cache line with
+// its neighbour, which then sits in the same L2).
 constexpr uint32_t kXcds = 8;
 constexpr uint32_t kXcdRun = ROG_XCD_RUN;
 
@@ -99,12 +100,13 @@ struct Divider {
 
 Divider make_divider(uint32_t d);
 
-// How the PEER path cuts a payload that is not 16-byte aligned on both sides
-// (destination address da, S bytes): bytes [0, lo) and [hi, S) move one by one,
-// bytes [lo, hi) as aligned 16-byte stores, each fed by one 16-byte load from
-// the source at the same payload offset (aligned or not).  The body starts at
-// the first kBodyAlign-aligned destination byte, so every read lies inside
-// [sa, sa + S) and every store is aligned.
+// How the PEER path cuts a payload, and the REDUCE path its output
+// (destination address da, S bytes): bytes [0, lo) and [hi, S) move one by one
+// (one element at a time for REDUCE), bytes [lo, hi) as aligned 16-byte
+// stores, each fed by 16-byte loads of the source bytes at the same offset
+// (aligned or not).  The body starts at the first kBodyAlign-aligned
+// destination byte; every read lies inside the source's S bytes and every
+// store is aligned.
 struct PeerSplit {
     uint64_t lo;      // first byte of the body (da + lo is kBodyAlign-aligned)
     uint64_t hi;      // end of the body; (hi - lo) % 16 == 0; lo == hi: no body

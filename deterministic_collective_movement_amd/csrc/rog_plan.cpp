@@ -1,6 +1,7 @@
 // rog_plan.cpp -- argument validation, alignment classification, path dispatch
-// and grid sizing for the rank-ordered gather.  Pure host code: no HIP calls,
-// so every decision here can be checked on a machine without a GPU.
+// and grid sizing for the rank-ordered gather and the rank-ordered sum.  Pure
+// host code: no HIP calls, so every decision here can be checked on a machine
+// without a GPU.
 //
 // Decisions follow RL-Align/RL-Kernel PR #491 ("perf(cuda): vectorize the
 // deterministic all-gather copy and right-size its single-block path"):
@@ -11,6 +12,9 @@
 //    chosen by output size, inclusive; the bound here is measured on MI355X.
 //  * review thread on grid sizing: size the multi-block grid from the vector
 //    count when the aligned path applies, from the per-peer work otherwise.
+//  * author's reply on the benchmark sizes: the all-reduce's single-block
+//    bound is tested on input bytes; rog_reduce's bound likewise counts source
+//    bytes (W * count * element size).
 #include <limits.h>
 #include <string.h>
 

@@ -24,6 +24,9 @@ Semantics follow RL-Align/RL-Kernel PR #491 ("perf(cuda): vectorize the
 deterministic all-gather copy and right-size its single-block path"):
 ``all_gather(input, out=)`` returns ``out`` itself and hands offset views to
 the kernel without copying them (author's replies to the size-test review).
+The sum is the reduction of the same PR's deterministic all_reduce /
+reduce_scatter ("Not in this PR"); its order and precision are stated in
+include/rog.h.
 """
 from __future__ import annotations
 

@@ -124,3 +124,13 @@ def test_time_calls_attributes_each_interval_to_its_call():
     assert per_call == durations
     assert region == pytest.approx(sum(durations))
     assert len(calls) == 6
+
+
+def test_source_digest_ignores_comments_but_not_code(tmp_path):
+    a = tmp_path / "a.hip"
+    a.write_text("// header\nint f(int x) {  /* twice */ return 2 * x; }  // tail\n")
+    d0 = bench.kernel_source_digest([str(a)])
+    a.write_text("// a new header\n\nint f(int x) {\n    /* doubled */\n    return 2 * x;\n}\n")
+    assert bench.kernel_source_digest([str(a)]) == d0
+    a.write_text("int f(int x) { return 3 * x; }\n")
+    assert bench.kernel_source_digest([str(a)]) != d0
