@@ -15,7 +15,9 @@
  *     out[r*S + i] = srcs[r][i]     for 0 <= r < W, 0 <= i < S,
  *
  * byte-identical to a plain concatenation for every alignment and size.  On one
- * GPU the W "peer payloads" are W caller-owned device buffers.
+ * GPU the W "peer payloads" are W caller-owned device buffers.  Beside it,
+ * rog_reduce computes the rank-ordered sum at the heart of the same pages'
+ * deterministic all-reduce and reduce-scatter (declared and defined below).
  *
  * Common rules for every entry point:
  *  - Pointers to data (srcs[r], out, the descriptors' buffers) are device
@@ -27,11 +29,15 @@
  *    enqueued on `stream` has completed.
  *  - All argument errors are returned before anything is enqueued: on error no
  *    byte of any output is written and no HIP call has been made.
- *  - Success means the copy has been enqueued on `stream` (asynchronous).
+ *  - Success means the work has been enqueued on `stream` (asynchronous), as
+ *    exactly one kernel launch; nothing else is enqueued, so calls can be
+ *    captured into a HIP graph.
  *  - The library allocates no device or host memory, keeps no state except a
  *    thread-local copy of the last HIP error, and may be called from any thread.
- *  - Bytes outside [out, out + W*S) are never written.  Source bytes are never
- *    written.  Every read lies inside a source range [srcs[r], srcs[r] + S).
+ *  - Bytes outside the output range (out, W*S bytes for a gather; count
+ *    elements for a sum) are never written.  Source bytes are never written,
+ *    except by an in-place call where out is itself a source.  Every read lies
+ *    inside a source range (S bytes for a gather, count elements for a sum).
  */
 #ifndef ROG_H
 #define ROG_H
