@@ -20,9 +20,9 @@ from a HIP graph of 100 calls, next to the eager floor of one tiny torch
 kernel timed the same way; the batched gather (16 tensors, W = 4, one launch);
 the device-to-device copy ceiling; aligned gathers with 64 - 512 MiB outputs,
 warm and with rotating buffer sets (cold); the rank-ordered sum (rog_reduce:
-W = 8 bf16 payloads of 64 MiB, and the pages' per-rank sizes of 1 KiB - 4 MiB
-at W = 2 and 8); and the CPU oracle on a bounded sample of the headline
-workload.
+W = 8 bf16 payloads of 64 MiB, the pages' per-rank sizes of 1 KiB - 4 MiB at
+W = 2 and 8, and a 16-tensor rog_reduce_many); and the CPU oracle on a bounded
+sample of the headline workload.
 
 Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
 """
@@ -514,6 +514,48 @@ def reduce_latency(torch, rog, wl, device, steps, warmup):
     return rows
 
 
+def reduce_batch(torch, rog, wl, device, steps, warmup):
+    """rog_reduce_many over the batched gather's 16 tensor shapes (rows x cols
+    bf16, W = 4) in one launch; every tensor's first elements checked against
+    the CPU oracle."""
+    import numpy as np
+    from oracle import oracle
+    case = wl.config5(0)
+    counts = [x.rows * x.cols for x in case.tensors]
+    batch, payloads_all, outs = [], [], []
+    for t, n in enumerate(counts):
+        payloads = wl.reduce_payloads(wl.case_seed(26, t), case.W, n, "bf16")
+        batch.append([torch.from_numpy(p.view(np.int16)).to(device).view(torch.bfloat16) for p in payloads])
+        payloads_all.append(payloads)
+        outs.append(torch.empty(n, dtype=torch.bfloat16, device=device))
+    rog.rog_reduce_many(batch, outs)
+    torch.cuda.synchronize()
+    for payloads, o in zip(payloads_all, outs):
+        k = min(4096, o.numel())
+        want = np.empty(k, np.uint16)
+        oracle.reduce_c([p[:k] for p in payloads], want, "bf16")
+        if not np.array_equal(o[:k].view(torch.int16).cpu().numpy().view(np.uint16), want):
+            raise AssertionError("batched sum differs from the oracle")
+    del payloads_all
+    lib = rog.lib()
+    keep = [(ctypes.c_void_p * case.W)(*[s.data_ptr() for s in srcs]) for srcs in batch]
+    descs = (rog.rog_reduce_desc * len(batch))()
+    for t, (o, n) in enumerate(zip(outs, counts)):
+        descs[t].srcs = ctypes.cast(keep[t], ctypes.POINTER(ctypes.c_void_p))
+        descs[t].out = ctypes.c_void_p(o.data_ptr())
+        descs[t].count = n
+    stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+    def call():
+        if lib.rog_reduce_many(descs, len(batch), case.W, rog.ROG_DTYPE_BF16, stream) != 0:
+            raise RuntimeError("rog_reduce_many failed")
+    per_call, _ = time_calls(torch, call, steps, warmup)
+    moved = sum((case.W + 1) * n * 2 for n in counts)
+    p50 = statistics.median(per_call)
+    return {"W": case.W, "n": len(counts), "elements": sum(counts), "bytes_moved": moved,
+            "p50_us": round(1e3 * p50, 1), "GBps": round(gbps(moved, p50), 1)}
+
+
 REDUCE_CROSSOVER_KIB = (1, 2, 4, 8, 16, 24, 32, 48, 64, 128, 256)
 
 
@@ -637,7 +679,9 @@ def main(argv=None):
         extras["d2d_copy_ceiling"] = d2d_ceiling(torch, device, case.W * case.S, 20, 3)
         extras["bandwidth_sweep"] = bandwidth_sweep(torch, rog, device, 20)
         extras["reduce"] = {"bandwidth": reduce_bandwidth(torch, rog, wl, device, args.steps, args.warmup),
-                            "latency": reduce_latency(torch, rog, wl, device, args.steps, args.warmup)}
+                            "latency": reduce_latency(torch, rog, wl, device, args.steps, args.warmup),
+                            "batched": reduce_batch(torch, rog, wl, device, max(5, args.steps // 5),
+                                                    max(1, args.warmup // 5))}
         cpu = cpu_baseline(case, payloads, args.cpu_budget)
     else:
         extras["reduce"] = {"bandwidth": reduce_bandwidth(torch, rog, wl, device, max(10, args.steps // 2),

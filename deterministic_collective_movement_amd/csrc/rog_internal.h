@@ -218,9 +218,34 @@ extern thread_local int g_last_hip_error;
 rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out,
                        rog_path path, Plan *plan);
 
+// One tensor of a batched sum: chunks [first_chunk, first_chunk + n_chunks) of
+// the launch, each 64 body vectors of its output (chunk 0 also sums the head
+// and tail elements).
+struct ReduceTensor {
+    uint64_t out;
+    uint64_t count;             // elements
+    uint32_t first_chunk;
+    uint32_t n_chunks;
+};
+
+struct ReduceBatchArgs {
+    const void *src[kMaxBatchPtrs];   // tensor t's payloads at [t*W, t*W + W)
+    ReduceTensor t[kMaxBatch];
+    uint32_t n;
+    uint32_t W;
+    uint32_t n_chunks;                // all tensors' chunks
+};
+
+static_assert(sizeof(ReduceBatchArgs) <= 4096, "kernel arguments must stay below 4 KiB");
+
 // Validate and plan one rank-ordered sum (no HIP calls).
 rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype dtype,
                        const void *out, rog_path path, Plan *plan);
+
+// Validate and plan a batch of rank-ordered sums (no HIP calls).  grid == 0
+// means nothing to launch.
+rog_status plan_reduce_batch(const rog_reduce_desc *descs, int n, int W, rog_dtype dtype,
+                             ReduceBatchArgs *args, uint32_t *grid, bool *nt_loads);
 
 // Validate and plan a batch (no HIP calls).  grid == 0 means nothing to launch.
 // *nt_loads: the launch streams its loads past the caches.

@@ -185,21 +185,15 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
     return ROG_OK;
 }
 
-rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype dtype,
-                       const void *out, rog_path path, Plan *plan) {
-    if (path != ROG_PATH_AUTO && path != ROG_PATH_SINGLE_WG && path != ROG_PATH_MULTI_WG)
-        return ROG_ERR_INVALID_ARGUMENT;
-    if (dtype != ROG_DTYPE_F32 && dtype != ROG_DTYPE_BF16) return ROG_ERR_INVALID_ARGUMENT;
+namespace {
+
+// Shared checks of one rank-ordered sum: pointers, element alignment, limits,
+// address wrap, overlap (out may be exactly a source).  *bytes_out = count * esize.
+rog_status validate_reduce(const void *const *srcs, int W, size_t count, size_t esize, const void *out,
+                           uint64_t *bytes_out) {
     if (!srcs || W < 1 || W > kMaxPeers) return ROG_ERR_INVALID_ARGUMENT;
-    const size_t esize = dtype == ROG_DTYPE_F32 ? 4 : 2;
-    rog_plan_info &info = plan->info;
-    memset(&info, 0, sizeof(info));
-    plan->dtype = dtype;
-    if (count == 0) {
-        info.path = path == ROG_PATH_AUTO ? ROG_PATH_SINGLE_WG : path;
-        info.kernel = ROG_KERNEL_NONE;
-        return ROG_OK;
-    }
+    *bytes_out = 0;
+    if (count == 0) return ROG_OK;
     if (!out) return ROG_ERR_INVALID_ARGUMENT;
     for (int r = 0; r < W; ++r)
         if (!srcs[r]) return ROG_ERR_INVALID_ARGUMENT;
@@ -216,6 +210,38 @@ rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype d
         // In place (out is exactly this source) is allowed: every element is
         // read from every source before the one thread that owns it writes it.
         if (ranges_overlap(s, bytes, o, bytes) && s != o) return ROG_ERR_OVERLAP;
+    }
+    *bytes_out = bytes;
+    return ROG_OK;
+}
+
+inline size_t dtype_size(rog_dtype dtype) { return dtype == ROG_DTYPE_F32 ? 4 : 2; }
+
+inline bool dtype_ok(rog_dtype dtype) { return dtype == ROG_DTYPE_F32 || dtype == ROG_DTYPE_BF16; }
+
+// Multi-WG REDUCE: one wave per 1 KiB chunk of the body (at most bytes / 16
+// vectors).  bytes < 2^36, so the count fits 26 bits.
+uint32_t reduce_chunks(uint64_t bytes) {
+    return uint32_t(std::max<uint64_t>(1, ceil_div(bytes / 16, 64)));
+}
+
+}  // namespace
+
+rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype dtype,
+                       const void *out, rog_path path, Plan *plan) {
+    if (path != ROG_PATH_AUTO && path != ROG_PATH_SINGLE_WG && path != ROG_PATH_MULTI_WG)
+        return ROG_ERR_INVALID_ARGUMENT;
+    if (!dtype_ok(dtype)) return ROG_ERR_INVALID_ARGUMENT;
+    uint64_t bytes = 0;
+    const rog_status st = validate_reduce(srcs, W, count, dtype_size(dtype), out, &bytes);
+    if (st != ROG_OK) return st;
+    rog_plan_info &info = plan->info;
+    memset(&info, 0, sizeof(info));
+    plan->dtype = dtype;
+    if (count == 0) {
+        info.path = path == ROG_PATH_AUTO ? ROG_PATH_SINGLE_WG : path;
+        info.kernel = ROG_KERNEL_NONE;
+        return ROG_OK;
     }
     if (path == ROG_PATH_AUTO)
         path = uint64_t(W) * bytes <= kReduceSingleWgMaxBytes ? ROG_PATH_SINGLE_WG : ROG_PATH_MULTI_WG;
@@ -235,11 +261,58 @@ rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype d
         info.block = round_up_64(ceil_div(bytes, 16));
         info.grid = 1;
     } else {
-        // One wave per 1 KiB chunk of the body (at most bytes / 16 vectors).
-        a.n_chunks = uint32_t(std::max<uint64_t>(1, ceil_div(bytes / 16, 64)));
+        a.n_chunks = reduce_chunks(bytes);
         info.block = kWaveBlock;
         info.grid = std::min(a.n_chunks, max_grid(kWaveBlock));
     }
+    return ROG_OK;
+}
+
+rog_status plan_reduce_batch(const rog_reduce_desc *descs, int n, int W, rog_dtype dtype,
+                             ReduceBatchArgs *args, uint32_t *grid, bool *nt_loads) {
+    *grid = 0;
+    *nt_loads = false;
+    if (n < 0 || W < 1 || W > kMaxPeers || !dtype_ok(dtype)) return ROG_ERR_INVALID_ARGUMENT;
+    if (n > 0 && !descs) return ROG_ERR_INVALID_ARGUMENT;
+    if (n > kMaxBatch || n * W > kMaxBatchPtrs) return ROG_ERR_TOO_LARGE;
+    const size_t esize = dtype_size(dtype);
+    uint64_t bytes[kMaxBatch];
+    for (int t = 0; t < n; ++t) {
+        const rog_status st = validate_reduce(descs[t].srcs, W, descs[t].count, esize, descs[t].out, &bytes[t]);
+        if (st != ROG_OK) return st;
+    }
+    // Tensors are summed concurrently: no output may overlap another tensor's
+    // output or another tensor's sources.
+    for (int t = 0; t < n; ++t) {
+        if (!bytes[t]) continue;
+        const uintptr_t o = addr(descs[t].out);
+        for (int u = 0; u < n; ++u) {
+            if (u == t || !bytes[u]) continue;
+            if (ranges_overlap(o, bytes[t], addr(descs[u].out), bytes[u])) return ROG_ERR_OVERLAP;
+            for (int r = 0; r < W; ++r)
+                if (ranges_overlap(o, bytes[t], addr(descs[u].srcs[r]), bytes[u])) return ROG_ERR_OVERLAP;
+        }
+    }
+    memset(args, 0, sizeof(*args));
+    args->W = uint32_t(W);
+    uint64_t next = 0, source_bytes = 0;
+    uint32_t k = 0;
+    for (int t = 0; t < n; ++t) {
+        if (!bytes[t]) continue;            // empty tensors get no chunks
+        ReduceTensor &rt = args->t[k];
+        for (int r = 0; r < W; ++r) args->src[k * uint32_t(W) + uint32_t(r)] = descs[t].srcs[r];
+        rt.out = addr(descs[t].out);
+        rt.count = descs[t].count;
+        rt.first_chunk = uint32_t(next);
+        rt.n_chunks = reduce_chunks(bytes[t]);
+        next += rt.n_chunks;
+        source_bytes += uint64_t(W) * bytes[t];
+        ++k;
+    }
+    args->n = k;
+    args->n_chunks = uint32_t(next);   // 32 tensors of < 2^26 chunks each
+    *grid = uint32_t(std::min<uint64_t>(next, max_grid(kWaveBlock)));
+    *nt_loads = source_bytes >= kNtLoadMinBytes;
     return ROG_OK;
 }
 

@@ -16,8 +16,9 @@
 // with up to 8 loads in flight, accumulates them in rank order and stores one
 // aligned 16-byte vector.  Multi-WG: one wave per 1 KiB chunk of the body,
 // chunks handed to the XCDs in runs (xcd_grouped); single-WG: one workgroup
-// strides over the whole output.  Bandwidth bound: (W + 1) * count * esize
-// bytes per call.
+// strides over the whole output; batch (rog_reduce_many): every tensor's
+// chunks in one launch.  Bandwidth bound: (W + 1) * count * esize bytes per
+// sum.
 #include <hip/hip_runtime.h>
 
 #include "rog_device.h"
@@ -122,23 +123,44 @@ __device__ __forceinline__ void sum_elem(const void *const *src, uint32_t W, uin
     else static_cast<float *>(out)[i] = acc;
 }
 
-// Multi-WG: one wave per workgroup and per 1 KiB chunk of the body; chunk 0
-// also sums the head and tail elements.
+// One wave: body chunk j (body vectors [64j, 64j + 64)) of a sum of `count`
+// elements into out; chunk 0 also sums the head and tail elements.
+template <bool BF16, bool NTL>
+__device__ __forceinline__ void sum_chunk(const void *const *src, uint32_t W, void *out, uint64_t count,
+                                          uint32_t j) {
+    const uint32_t lane = __lane_id();
+    const PeerSplit cut = split_payload(reinterpret_cast<uintptr_t>(out), count * Elem<BF16>::kSize);
+    if (j == 0) {
+        for (uint64_t i = lane; i < cut.lo / Elem<BF16>::kSize; i += 64) sum_elem<BF16>(src, W, i, out);
+        for (uint64_t i = cut.hi / Elem<BF16>::kSize + lane; i < count; i += 64) sum_elem<BF16>(src, W, i, out);
+    }
+    const uint64_t off = cut.lo + 16 * (uint64_t(j) * 64 + lane);
+    if (off < cut.hi)
+        st16(reinterpret_cast<vec16 *>(static_cast<uint8_t *>(out) + off), sum_vec<BF16, NTL>(src, W, off));
+}
+
+// Multi-WG: one wave per workgroup and per 1 KiB chunk of the body, chunks
+// handed to the XCDs in runs, grid-strided over a capped grid.
 template <bool BF16, bool NTL>
 __global__ __launch_bounds__(kWaveBlock) void rog_reduce_kernel(ReduceArgs a) {
-    const uint32_t lane = __lane_id();
-    const uint64_t bytes = a.count * Elem<BF16>::kSize;
-    const PeerSplit cut = split_payload(reinterpret_cast<uintptr_t>(a.out), bytes);
-    uint8_t *o = static_cast<uint8_t *>(a.out);
+    for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x)
+        sum_chunk<BF16, NTL>(a.src, a.W, a.out, a.count, ROG_REDUCE_XCD ? xcd_grouped(vb, a.n_chunks) : vb);
+}
+
+// Batch: the tensors' chunks laid end to end; a wave finds its tensor by a
+// scalar binary search over the tensors' first chunks.
+template <bool BF16, bool NTL>
+__global__ __launch_bounds__(kWaveBlock) void rog_reduce_batch_kernel(ReduceBatchArgs a) {
     for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x) {
-        const uint32_t j = ROG_REDUCE_XCD ? xcd_grouped(vb, a.n_chunks) : vb;
-        if (j == 0) {
-            for (uint64_t i = lane; i < cut.lo / Elem<BF16>::kSize; i += 64) sum_elem<BF16>(a.src, a.W, i, a.out);
-            for (uint64_t i = cut.hi / Elem<BF16>::kSize + lane; i < a.count; i += 64)
-                sum_elem<BF16>(a.src, a.W, i, a.out);
+        const uint32_t c = ROG_REDUCE_XCD ? xcd_grouped(vb, a.n_chunks) : vb;
+        uint32_t lo = 0, hi = a.n;          // last tensor whose first chunk is <= c
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) / 2;
+            if (a.t[mid].first_chunk <= c) lo = mid;
+            else hi = mid;
         }
-        const uint64_t off = cut.lo + 16 * (uint64_t(j) * 64 + lane);
-        if (off < cut.hi) st16(reinterpret_cast<vec16 *>(o + off), sum_vec<BF16, NTL>(a.src, a.W, off));
+        const ReduceTensor &t = a.t[lo];
+        sum_chunk<BF16, NTL>(a.src + lo * a.W, a.W, reinterpret_cast<void *>(t.out), t.count, c - t.first_chunk);
     }
 }
 
@@ -179,6 +201,11 @@ rog_status launch_reduce(Plan &p, hipStream_t stream) {
     return ROG_OK;
 }
 
+template <bool BF16>
+const void *reduce_batch_kernel(bool ntl) {
+    return ntl ? kfn(&rog_reduce_batch_kernel<BF16, true>) : kfn(&rog_reduce_batch_kernel<BF16, false>);
+}
+
 }  // namespace
 }  // namespace rog
 
@@ -210,5 +237,22 @@ ROG_API rog_status rog_reduce_plan(const void *const *srcs, int W, size_t count,
 }
 
 ROG_API size_t rog_reduce_single_wg_max_bytes(void) { return rog::kReduceSingleWgMaxBytes; }
+
+ROG_API rog_status rog_reduce_many(const rog_reduce_desc *descs, int n, int W, rog_dtype dtype,
+                                   hipStream_t stream) {
+    rog::ReduceBatchArgs args;
+    uint32_t grid = 0;
+    bool ntl = false;
+    const rog_status st = rog::plan_reduce_batch(descs, n, W, dtype, &args, &grid, &ntl);
+    if (st != ROG_OK || grid == 0) return st;
+    const void *k = dtype == ROG_DTYPE_BF16 ? rog::reduce_batch_kernel<true>(ntl) : rog::reduce_batch_kernel<false>(ntl);
+    void *params[] = {&args};
+    const hipError_t e = hipLaunchKernel(k, dim3(grid), dim3(rog::kWaveBlock), params, 0, stream);
+    if (e != hipSuccess) {
+        rog::g_last_hip_error = int(e);
+        return ROG_ERR_LAUNCH;
+    }
+    return ROG_OK;
+}
 
 }  // extern "C"

@@ -13,6 +13,8 @@ Entry points keep the C names.  Tensor forms:
 * ``rog_reduce(srcs, out=None, stream=None)`` -> ``out``: the rank-ordered sum
   of W float32 or bfloat16 tensors;
 * ``rog_reduce_ex(srcs, out, path, stream=None)``, ``rog_reduce_plan(srcs, out, path)``;
+* ``rog_reduce_many(batch, outs=None, stream=None)`` -> list of outputs (one
+  launch);
 * ``rog_reduce_scatter(inputs, rank, out=None, stream=None)`` -> ``out``: rank
   ``rank``'s share of a reduce-scatter, i.e. ``rog_reduce`` over shard
   ``rank`` of each input (views; nothing is copied).
@@ -82,6 +84,12 @@ class rog_gather_desc(ctypes.Structure):
                 ("bytes_per_rank", ctypes.c_size_t)]
 
 
+class rog_reduce_desc(ctypes.Structure):
+    _fields_ = [("srcs", ctypes.POINTER(ctypes.c_void_p)),
+                ("out", ctypes.c_void_p),
+                ("count", ctypes.c_size_t)]
+
+
 class rog_plan_info(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("kernel", ctypes.c_int32),
                 ("grid", ctypes.c_uint32), ("block", ctypes.c_uint32),
@@ -119,8 +127,9 @@ def _load() -> ctypes.CDLL:
     lib.rog_reduce.argtypes = [ptrs, i32, sz, i32, vp, vp]
     lib.rog_reduce_ex.argtypes = [ptrs, i32, sz, i32, vp, vp, i32]
     lib.rog_reduce_plan.argtypes = [ptrs, i32, sz, i32, vp, i32, ctypes.POINTER(rog_plan_info)]
+    lib.rog_reduce_many.argtypes = [ctypes.POINTER(rog_reduce_desc), i32, i32, i32, vp]
     for name in ("rog_gather", "rog_gather_ex", "rog_gather_many", "rog_plan", "rog_reduce", "rog_reduce_ex",
-                 "rog_reduce_plan"):
+                 "rog_reduce_plan", "rog_reduce_many"):
         getattr(lib, name).restype = i32
     for name in ("rog_single_wg_max_bytes", "rog_reduce_single_wg_max_bytes"):
         getattr(lib, name).argtypes = []
@@ -247,6 +256,20 @@ def rog_reduce_plan_ptrs(src_ptrs: Optional[Sequence[int]], count: int, dtype: i
                               ctypes.c_void_p(out_ptr), path, ctypes.byref(info))
     _check(st, "rog_reduce_plan")
     return _plan_dict(info)
+
+
+def rog_reduce_many_ptrs(batch_ptrs: Sequence[Sequence[int]], counts: Sequence[int],
+                         out_ptrs: Sequence[int], W: int, dtype: int, stream: int = 0) -> None:
+    """rog_reduce_many on raw addresses: tensor t sums the W sources batch_ptrs[t]."""
+    n = len(out_ptrs)
+    keep = [_ptr_array(p) for p in batch_ptrs]
+    descs = (rog_reduce_desc * max(1, n))()
+    for t in range(n):
+        descs[t].srcs = ctypes.cast(keep[t], ctypes.POINTER(ctypes.c_void_p))
+        descs[t].out = ctypes.c_void_p(out_ptrs[t])
+        descs[t].count = counts[t]
+    st = _lib.rog_reduce_many(descs, n, W, dtype, ctypes.c_void_p(stream))
+    _check(st, "rog_reduce_many")
 
 
 def rog_gather_many_ptrs(batch_ptrs: Sequence[Sequence[int]], sizes: Sequence[int],
@@ -436,3 +459,35 @@ def rog_reduce_scatter(inputs: Sequence[torch.Tensor], rank: int, out: Optional[
     for i, t in enumerate(inputs):
         _check_tensor(t, "inputs[%d]" % i, inputs[0].device)
     return rog_reduce([t.reshape(-1)[rank * n:(rank + 1) * n] for t in inputs], out, stream)
+
+
+def rog_reduce_many(batch: Sequence[Sequence[torch.Tensor]],
+                    outs: Optional[Sequence[Optional[torch.Tensor]]] = None,
+                    stream=None) -> List[torch.Tensor]:
+    """Rank-ordered sums of every tensor list ``batch[t]`` (W tensors each, one
+    dtype for the batch) into ``outs[t]``, in one launch."""
+    n = len(batch)
+    if outs is None:
+        outs = [None] * n
+    if len(outs) != n:
+        raise ValueError("one output per tensor")
+    if n == 0:
+        return []
+    W = len(batch[0])
+    if any(len(b) != W for b in batch):
+        raise ValueError("every tensor of a batch has the same number of sources")
+    device = batch[0][0].device
+    ready, counts, dt0 = [], [], None
+    for t in range(n):
+        dev, count, dt, o = _prepare_reduce(batch[t], outs[t])
+        if dev != device:
+            raise ValueError("all tensors of a batch must be on one device")
+        if dt0 is not None and dt != dt0:
+            raise ValueError("all tensors of a batch must have one dtype")
+        dt0 = dt
+        ready.append(o)
+        counts.append(count)
+    with _on_device(device):
+        rog_reduce_many_ptrs([[s.data_ptr() for s in b] for b in batch], counts,
+                             [o.data_ptr() for o in ready], W, dt0, _stream_handle(stream, device))
+    return ready

@@ -243,6 +243,31 @@ ROG_API rog_status rog_reduce_plan(const void *const *srcs, int W, size_t count,
  * rog_reduce on one workgroup (inclusive), measured on MI355X. */
 ROG_API size_t rog_reduce_single_wg_max_bytes(void);
 
+/* One tensor of a batched sum: W source pointers, its output, its count. */
+typedef struct {
+    const void *const *srcs;   /* W device pointers (host array)                  */
+    void *out;                 /* device pointer to `count` elements              */
+    size_t count;              /* elements of this tensor; 0 is allowed           */
+} rog_reduce_desc;
+
+/*
+ * rog_reduce_many -- n independent rank-ordered sums sharing W and dtype, in one
+ * kernel launch: tensor t gets out_t[i] = the rank-ordered sum of srcs_t[r][i]
+ * (exactly as rog_reduce).  The pages' reduce_scatter_many / all_gather_many
+ * (PR #491, "Tests" and the review threads on the benchmark) batch a list of
+ * tensors behind one handshake; here every tensor keeps its own
+ * caller-provided output and the whole batch is one launch.
+ *
+ * descs  host array of n descriptors (each with a host array of W pointers).
+ * n      0 <= n <= rog_max_batch(); n == 0 or all counts 0: ROG_OK, nothing
+ *        enqueued.  n*W must not exceed rog_max_batch_pointers().
+ * Errors: as rog_reduce for each tensor; besides, a tensor's output must not
+ * overlap another tensor's output or sources (ROG_ERR_OVERLAP); limits
+ * exceeded: ROG_ERR_TOO_LARGE.  Always the multi-workgroup shape.
+ */
+ROG_API rog_status rog_reduce_many(const rog_reduce_desc *descs, int n, int W, rog_dtype dtype,
+                                   hipStream_t stream);
+
 /* Largest W accepted (kernel-argument capacity). */
 ROG_API int rog_max_peers(void);
 

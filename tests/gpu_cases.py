@@ -214,3 +214,22 @@ def run_reduce_all_paths(placed: PlacedReduce, label: str, paths=PATHS) -> None:
         ret = rog.rog_reduce_ex(placed.srcs, placed.out, path)
         assert ret is placed.out
         placed.check("%s path=%s" % (label, rog.PATH_NAMES[path]))
+
+
+class PlacedReduceBatch:
+    """A batch of rank-ordered sums: tensor t's W payloads and output, each in
+    guarded buffers at element offsets."""
+
+    def __init__(self, items: Sequence[PlacedReduce]):
+        self.items = list(items)
+
+    def run(self, label: str) -> None:
+        for it in self.items:
+            it.reset()
+        print(label, flush=True)
+        outs = rog.rog_reduce_many([it.srcs for it in self.items], [it.out for it in self.items])
+        for o, it in zip(outs, self.items):
+            assert o is it.out
+        for t, it in enumerate(self.items):
+            it.check("%s tensor %d (n=%d, %s)" % (label, t, it.n, it.dtype))
+

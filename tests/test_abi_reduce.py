@@ -121,3 +121,38 @@ def test_binding_errors_map_to_exceptions():
         rog.rog_reduce_ptrs([A + 1], 16, F32, 2 * A)
     with pytest.raises(rog.RogArgumentError):
         rog.rog_reduce_ptrs([A, A + 8], 16, F32, A + 8)
+
+
+# ---------------------------------------------------------------------------
+# rog_reduce_many validation (every case returns before any HIP call)
+# ---------------------------------------------------------------------------
+
+def many_status(batch, counts, outs, W, dtype=F32, n=None):
+    keep = [rog._ptr_array(p) for p in batch]
+    descs = (rog.rog_reduce_desc * max(1, len(outs)))()
+    for t in range(len(outs)):
+        descs[t].srcs = ctypes.cast(keep[t], ctypes.POINTER(ctypes.c_void_p))
+        descs[t].out = ctypes.c_void_p(outs[t])
+        descs[t].count = counts[t]
+    return int(rog.lib().rog_reduce_many(descs, len(outs) if n is None else n, W, dtype, None))
+
+
+def test_reduce_many_validation():
+    assert rog.lib().rog_reduce_many(None, 0, 2, F32, None) == OK           # empty batch
+    assert rog.lib().rog_reduce_many(None, 1, 2, F32, None) == INVALID      # NULL descriptors
+    assert many_status([[A, A + 4096]], [16], [1 << 36], 2, dtype=7) == INVALID
+    assert many_status([[A]], [16], [1 << 36], 0) == INVALID
+    n_max, p_max = rog.rog_max_batch(), rog.rog_max_batch_pointers()
+    assert many_status([[A]] * (n_max + 1), [0] * (n_max + 1), [0] * (n_max + 1), 1) == TOO_LARGE
+    W = p_max // 4 + 1
+    assert many_status([[A] * W] * 4, [0] * 4, [0] * 4, W) == TOO_LARGE
+    # per-tensor rules: alignment, partial overlap with its own output
+    assert many_status([[A + 2]], [16], [1 << 36], 1, F32) == INVALID
+    assert many_status([[A, (1 << 36) + 4]], [16], [1 << 36], 2) == OVERLAP
+    # across tensors: outputs, and an output over another tensor's source
+    o1, o2 = 1 << 36, (1 << 36) + (1 << 20)
+    assert many_status([[A], [A + 64]], [16, 16], [o1, o1 + 32], 1) == OVERLAP
+    assert many_status([[A], [o1 + 8]], [16, 16], [o1, o2], 1) == OVERLAP
+    assert many_status([[A, o2], [A, A]], [16, 16], [o1, o2], 2) == OVERLAP  # o2 is tensor 0's source
+    assert many_status([[0, 0], [0, 0]], [0, 0], [0, 0], 2) == OK           # all empty: nothing enqueued
+    # (valid non-empty batches launch a kernel: the GPU tests run them)

@@ -128,3 +128,31 @@ def test_graph_captures_rank_ordered_sums(gpu):
             bits = torch.int16 if dt == "bf16" else torch.int32
             got = out.view(bits).cpu().numpy().view(want.dtype)
             assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), (replay, W, n, dt)
+
+
+def test_graph_captures_a_batched_sum(gpu):
+    W = 3
+    counts = [5, 4097, 30_000, 0, 123_457]
+    batch = [[torch.zeros(n, dtype=torch.bfloat16, device=gpu) for _ in range(W)] for n in counts]
+    outs = [torch.zeros(n, dtype=torch.bfloat16, device=gpu) for n in counts]
+    rog.rog_reduce_many(batch, outs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rog.rog_reduce_many(batch, outs)
+    for replay in range(3):
+        wants = []
+        for t, (srcs, n) in enumerate(zip(batch, counts)):
+            payloads = wl.reduce_payloads(wl.case_seed(25, replay * 10 + t), W, n, "bf16")
+            for s, p in zip(srcs, payloads):
+                s.copy_(torch.from_numpy(p.view(np.int16)).to(gpu).view(torch.bfloat16))
+            want = np.empty(n, np.uint16)
+            oracle.reduce_c(payloads, want, "bf16")
+            wants.append(want)
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, want in zip(outs, wants):
+            assert np.array_equal(o.view(torch.int16).cpu().numpy().view(np.uint16), want), replay

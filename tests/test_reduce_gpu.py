@@ -126,3 +126,69 @@ def test_binding_rejects_bad_tensors(gpu):
         rog.rog_reduce([a], torch.zeros(16, dtype=torch.float32))          # output on the CPU
     with pytest.raises(rog.RogArgumentError):
         rog.rog_reduce([a[:8], a[4:12]], a[4:12])                           # partial overlap
+
+
+# ---------------------------------------------------------------------------
+# rog_reduce_many: one launch for a batch
+# ---------------------------------------------------------------------------
+
+def _batch(seed, W, counts, dtype, offs=None, kinds=None, in_place=None):
+    items = []
+    for t, n in enumerate(counts):
+        kind = kinds[t] if kinds else "uniform"
+        payloads = wl.reduce_payloads(wl.case_seed(23, seed * 100 + t), W, n, dtype, kind)
+        io = offs[t] if offs else [0] * W
+        ip = in_place[t] if in_place else -1
+        items.append(gc.PlacedReduce(payloads, io, t % 4, dtype, gpu_device(), in_place=ip))
+    return gc.PlacedReduceBatch(items)
+
+
+def gpu_device():
+    return torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("W", [1, 3, 8])
+def test_batched_sums_mixed_sizes(gpu, dtype, W):
+    counts = [0, 1, 7, 513, 4096, 0, 70_001, 262_147, 9]
+    offs = [[(t + r) % 4 for r in range(W)] for t in range(len(counts))]
+    kinds = ["bits" if t % 3 == 0 else "uniform" for t in range(len(counts))]
+    _batch(W, W, counts, dtype, offs, kinds).run("batched sums W=%d %s" % (W, dtype))
+
+
+def test_batched_sums_maximum_batch(gpu):
+    n = rog.rog_max_batch()
+    W = rog.rog_max_batch_pointers() // n
+    rng = np.random.default_rng(31)
+    counts = [int(rng.integers(1, 20_000)) for _ in range(n)]
+    _batch(40, W, counts, "bf16").run("batched sums max n=%d W=%d" % (n, W))
+
+
+def test_batched_sums_in_place(gpu):
+    counts = [1000, 33_333, 5]
+    _batch(41, 4, counts, "f32", in_place=[0, 3, 1]).run("batched sums in place")
+
+
+def test_batched_sums_large(gpu):
+    """Sixteen bf16 tensors of the batched gather's shapes (rows up to 3000 x
+    cols in {128, 1024, 8192}), W = 4, summed in one launch."""
+    case = wl.config5(0, max_rows=3000)
+    counts = [x.rows * x.cols for x in case.tensors]
+    offs = [[(x.in_off // 2) % 4] * case.W for x in case.tensors]
+    b = _batch(42, case.W, counts, "bf16", offs)
+    b.run("batched sums, config-5 shapes")
+
+
+def test_batched_sums_sharing_sources(gpu):
+    """Two tensors summing the same source buffers into separate outputs, and
+    an empty tensor whose output pointer lies inside another's output."""
+    W, n = 3, 50_000
+    payloads = wl.reduce_payloads(wl.case_seed(24, 0), W, n, "f32")
+    a = gc.PlacedReduce(payloads, [0, 1, 2], 0, "f32", gpu)
+    b = gc.PlacedReduce(payloads, [0, 0, 0], 3, "f32", gpu)
+    srcs = a.srcs
+    empty_out = a.out[10:10]
+    outs = rog.rog_reduce_many([srcs, srcs, [s[:0] for s in srcs]], [a.out, b.out, empty_out])
+    assert outs[0] is a.out and outs[1] is b.out
+    a.check("shared sources, tensor 0")
+    b.check("shared sources, tensor 1")
