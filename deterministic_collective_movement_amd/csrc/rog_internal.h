@@ -72,6 +72,11 @@ constexpr int kSingleBlock = 1024;                // the single workgroup (16 wa
 constexpr int kSingleUnroll = ROG_SINGLE_UNROLL;  // single-WG FLAT vectors per lane
 constexpr int kSinglePeerUnroll = 4;              // single-WG PEER vectors per thread
 constexpr bool kNtStore = ROG_NT_STORE != 0;      // non-temporal 16-byte stores
+// Vectors per lane of the single-WG FLAT kernel for an output of n_vec vectors:
+// 1 while one pass of 16 waves covers the output (1 KiB wave chunks then line
+// up with payloads of 1 KiB or more, so no chunk takes the per-lane payload
+// lookup), kSingleUnroll beyond.
+inline int single_flat_unroll(uint64_t n_vec) { return n_vec <= uint64_t(kSingleBlock) ? 1 : kSingleUnroll; }
 // Source bytes from which 16-byte loads are non-temporal: below it the payloads
 // may still sit in the 256 MB Infinity Cache, and cached loads then win.
 constexpr uint64_t kNtLoadMinBytes = ROG_NT_LOAD_MIN_BYTES;

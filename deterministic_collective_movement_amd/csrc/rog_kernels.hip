@@ -162,10 +162,11 @@ __global__ __launch_bounds__(BLOCK) void rog_flat_kernel(FlatArgs a) {
     flat_copy<kFlatUnroll, NTL>(a.src, a.out, a.n_vec, a.vpr, a.div, blockIdx.x, gridDim.x, BLOCK / 64);
 }
 
-// Single-WG FLAT: one workgroup of as many waves as there are chunks (<= 16).
-template <bool NTL>
+// Single-WG FLAT: one workgroup of as many waves as there are chunks (<= 16),
+// U = single_flat_unroll(n_vec) vectors per lane.
+template <int U, bool NTL>
 __global__ __launch_bounds__(kSingleBlock) void rog_flat_single_kernel(FlatArgs a) {
-    flat_copy<kSingleUnroll, NTL>(a.src, a.out, a.n_vec, a.vpr, a.div, 0, 1, blockDim.x / 64);
+    flat_copy<U, NTL>(a.src, a.out, a.n_vec, a.vpr, a.div, 0, 1, blockDim.x / 64);
 }
 
 // Multi-WG PEER: one wave per workgroup and per body chunk, chunks grouped by
@@ -247,7 +248,10 @@ rog_status launch_plan(Plan &p, hipStream_t stream) {
     case ROG_KERNEL_NONE:
         return ROG_OK;
     case ROG_KERNEL_FLAT:
-        if (single) k = ntl ? kfn(&rog_flat_single_kernel<true>) : kfn(&rog_flat_single_kernel<false>);
+        if (single && single_flat_unroll(p.flat.n_vec) == 1)
+            k = ntl ? kfn(&rog_flat_single_kernel<1, true>) : kfn(&rog_flat_single_kernel<1, false>);
+        else if (single)
+            k = ntl ? kfn(&rog_flat_single_kernel<kSingleUnroll, true>) : kfn(&rog_flat_single_kernel<kSingleUnroll, false>);
         else        k = ntl ? kfn(&rog_flat_kernel<kFlatBlock, true>) : kfn(&rog_flat_kernel<kFlatBlock, false>);
         return launch(k, i.grid, i.block, p.flat, stream);
     case ROG_KERNEL_PEER:

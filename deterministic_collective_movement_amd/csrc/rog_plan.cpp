@@ -113,10 +113,10 @@ uint32_t round_up_64(uint64_t threads) {
     return uint32_t(std::min<uint64_t>(kSingleBlock, std::max<uint64_t>(64, (threads + 63) / 64 * 64)));
 }
 
-// Single-WG FLAT workgroup: one wave per chunk of 64*kSingleUnroll vectors, at
-// most 16 waves (idle waves only cost launch time).
+// Single-WG FLAT workgroup: one wave per chunk of 64 * single_flat_unroll
+// vectors, at most 16 waves (idle waves only cost launch time).
 uint32_t flat_single_block(uint64_t n_vec) {
-    return round_up_64(ceil_div(n_vec, 64 * uint64_t(kSingleUnroll)) * 64);
+    return round_up_64(ceil_div(n_vec, 64 * uint64_t(single_flat_unroll(n_vec))) * 64);
 }
 
 // Single-WG PEER workgroup: enough threads for one tile of the largest payload.

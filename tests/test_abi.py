@@ -232,7 +232,9 @@ def test_grid_sizes():
         assert p["kernel"] == "flat" and p["block"] == FLAT_BLOCK
         assert p["grid"] == max(1, -(-chunks // (FLAT_BLOCK // 64)))
         s = rog.rog_plan_ptrs(srcs, S, out, rog.ROG_PATH_SINGLE_WG)
-        single_chunks = -(-n_vec // (64 * SINGLE_UNROLL))
+        # 1 KiB wave chunks while 16 waves cover the output, 4 KiB beyond
+        u = 1 if n_vec <= 1024 else SINGLE_UNROLL
+        single_chunks = -(-n_vec // (64 * u))
         assert s["grid"] == 1 and s["block"] == min(1024, max(64, 64 * single_chunks))
     # PEER multi-WG: W payloads, each cut into 1 KiB body chunks (enough for
     # the longest possible body, S // 16 vectors), one wave per chunk.
