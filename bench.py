@@ -24,7 +24,7 @@ W = 8 bf16 payloads of 64 MiB, the pages' per-rank sizes of 1 KiB - 4 MiB at
 W = 2 and 8, and a 16-tensor rog_reduce_many); and the CPU oracle on a bounded
 sample of the headline workload.
 
-Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
+Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: the benchmark measures one GPU.
 """
 from __future__ import annotations
 
