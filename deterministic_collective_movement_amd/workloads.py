@@ -17,7 +17,7 @@ calibration", the reproduction command and its results table).
 from __future__ import annotations
 
 from dataclasses import dataclass, field
-from typing import List, Sequence, Tuple
+from typing import List, Tuple
 
 import numpy as np
 

@@ -12,7 +12,6 @@ import subprocess
 import numpy as np
 import pytest
 
-import deterministic_collective_movement_amd as dcm
 from deterministic_collective_movement_amd import rog
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

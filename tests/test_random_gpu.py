@@ -8,7 +8,6 @@ from __future__ import annotations
 import numpy as np
 import pytest
 
-from deterministic_collective_movement_amd import rog
 from deterministic_collective_movement_amd import workloads as wl
 from tests import gpu_cases as gc
 
