@@ -253,6 +253,8 @@ def misaligned(torch, rog, case, payloads, srcs, device, steps, warmup, in_off=1
 
 
 def latency_sweep(torch, rog, wl, device, steps, warmup):
+    """The two-payload case and the size sweep's 1 - 128 KiB payloads: every
+    call event-timed; p10 / p50 / p90 and all samples (µs)."""
     rows = []
     cases = wl.config1() + [c for c in wl.config2() if c.S <= 128 * wl.KiB]
     stream = torch.cuda.current_stream(device).cuda_stream
@@ -262,10 +264,12 @@ def latency_sweep(torch, rog, wl, device, steps, warmup):
         plan = rog.rog_plan(srcs, out)
         per_call, _ = time_calls(torch, Call(rog, srcs, out, stream), steps, warmup)
         s = summarize_ms(per_call)
-        rows.append({"W": case.W, "S_KiB": case.S // wl.KiB, "path": plan["path"], "kernel": plan["kernel"],
+        rows.append({"case": "c%d#%d" % (case.config, case.index), "W": case.W, "S_KiB": case.S // wl.KiB,
+                     "path": plan["path"], "kernel": plan["kernel"],
                      "p10_us": round(s["p10_us"], 2), "p50_us": round(s["p50_us"], 2),
                      "p90_us": round(s["p90_us"], 2),
-                     "eff_GBps": round(gbps(2 * case.W * case.S, s["p50_us"] * 1e-3), 1)})
+                     "eff_GBps": round(gbps(2 * case.W * case.S, s["p50_us"] * 1e-3), 1),
+                     "samples_us": [round(1e3 * x, 2) for x in per_call]})
     return rows
 
 
