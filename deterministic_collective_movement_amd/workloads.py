@@ -215,16 +215,19 @@ def config5(index: int = 0, n: int = 16, W: int = 4, max_rows: int = CONFIG5_MAX
 # ---------------------------------------------------------------------------
 
 #: Bytes of one element of each element type of the sum.
-REDUCE_ESIZE = {"f32": 4, "bf16": 2}
+REDUCE_ESIZE = {"f32": 4, "bf16": 2, "f16": 2}
 
 
 def reduce_payloads(seed: int, W: int, n: int, dtype: str, kind: str = "uniform") -> List[np.ndarray]:
     """W payloads of n elements, reproducible from (seed, payload index).
 
-    dtype "f32": float32 arrays; "bf16": uint16 arrays of bf16 bit patterns.
+    dtype "f32": float32 arrays; "bf16" / "f16": uint16 arrays of bf16 /
+    binary16 bit patterns.
     kind "uniform": values uniform in [-1, 1) (bf16: the float32 draw cut to its
-    top 16 bits, i.e. rounded toward zero); "bits": uniformly random bit
-    patterns (NaNs, infinities and subnormals included).
+    top 16 bits, i.e. rounded toward zero; f16: a random sign, a random
+    significand and an exponent uniform over 2^-14 .. 2^0, i.e. normal
+    binary16 values of magnitude below 2, built bit by bit); "bits": uniformly
+    random bit patterns (NaNs, infinities and subnormals included).
     """
     out = []
     for r in range(W):
@@ -232,6 +235,12 @@ def reduce_payloads(seed: int, W: int, n: int, dtype: str, kind: str = "uniform"
         if kind == "bits":
             b = rng.bytes(n * REDUCE_ESIZE[dtype])
             out.append(np.frombuffer(b, np.float32 if dtype == "f32" else np.uint16).copy())
+            continue
+        if dtype == "f16":
+            sign = rng.integers(0, 2, n, dtype=np.uint16) << np.uint16(15)
+            expo = rng.integers(1, 16, n, dtype=np.uint16) << np.uint16(10)
+            mant = rng.integers(0, 1 << 10, n, dtype=np.uint16)
+            out.append((sign | expo | mant).astype(np.uint16))
             continue
         f = rng.random(n, dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
         out.append(f if dtype == "f32" else (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16))

@@ -14,8 +14,9 @@ The rank-ordered sum (the reduction of a deterministic all-reduce or
 reduce-scatter) likewise has a C form, ``reduce_c``, and a pure-Python form,
 ``reduce_py``, which rounds every binary32 addition through ``struct`` (an
 addition of two binary32 numbers in binary64 followed by one rounding to
-binary32 is the correctly rounded binary32 sum: 53 >= 2*24 + 2) and rounds to
-bf16 with its own integer arithmetic.  The reading of the pages it follows is
+binary32 is the correctly rounded binary32 sum: 53 >= 2*24 + 2), rounds to
+bf16 with its own integer arithmetic and to binary16 through ``struct``'s half
+format.  The reading of the pages it follows is
 stated in ``rog_oracle.c``.
 
 Definition (RL-Align/RL-Kernel PR #491, "perf(cuda): vectorize the deterministic
@@ -67,12 +68,14 @@ def _load():
                                                ctypes.POINTER(ctypes.c_void_p),
                                                ctypes.POINTER(ctypes.c_size_t),
                                                ctypes.c_int, ctypes.c_int]
-        for name, ct in (("rog_oracle_reduce_f32", ctypes.c_void_p), ("rog_oracle_reduce_bf16", ctypes.c_void_p)):
+        for name, ct in (("rog_oracle_reduce_f32", ctypes.c_void_p), ("rog_oracle_reduce_bf16", ctypes.c_void_p),
+                         ("rog_oracle_reduce_f16", ctypes.c_void_p)):
             f = getattr(lib, name)
             f.restype = None
             f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_size_t, ct]
-        lib.rog_oracle_f32_to_bf16.restype = ctypes.c_uint16
-        lib.rog_oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        for name in ("rog_oracle_f32_to_bf16", "rog_oracle_f32_to_f16"):
+            getattr(lib, name).restype = ctypes.c_uint16
+            getattr(lib, name).argtypes = [ctypes.c_float]
         _lib = lib
     return _lib
 
@@ -144,13 +147,14 @@ def gather_py(srcs: Sequence[bytes], S: int) -> bytearray:
 # ---------------------------------------------------------------------------
 
 #: Element types of the sum: numpy storage dtype of one element.
-REDUCE_DTYPES = {"f32": np.dtype(np.float32), "bf16": np.dtype(np.uint16)}
+REDUCE_DTYPES = {"f32": np.dtype(np.float32), "bf16": np.dtype(np.uint16), "f16": np.dtype(np.uint16)}
 
 
 def reduce_c(srcs: Sequence[np.ndarray], out: np.ndarray, dtype: str) -> np.ndarray:
     """out[i] = rank-ordered binary32 sum of srcs[r][i], rounded to ``dtype``.
 
-    ``dtype`` "f32": float32 arrays; "bf16": uint16 arrays holding bf16 bits.
+    ``dtype`` "f32": float32 arrays; "bf16" / "f16": uint16 arrays holding
+    bf16 / IEEE binary16 bits.
     All arrays 1-D, equal length, aligned to their element size.
     """
     want = REDUCE_DTYPES[dtype]
@@ -166,7 +170,8 @@ def reduce_c(srcs: Sequence[np.ndarray], out: np.ndarray, dtype: str) -> np.ndar
     if not out.flags.writeable:
         raise ValueError("out must be writeable")
     ptrs = (ctypes.c_void_p * W)(*[a.ctypes.data for a in srcs])
-    fn = _load().rog_oracle_reduce_f32 if dtype == "f32" else _load().rog_oracle_reduce_bf16
+    fn = {"f32": _load().rog_oracle_reduce_f32, "bf16": _load().rog_oracle_reduce_bf16,
+          "f16": _load().rog_oracle_reduce_f16}[dtype]
     fn(ptrs, W, n, out.ctypes.data)
     return out
 
@@ -181,6 +186,32 @@ def f32_to_bf16_c(x: np.ndarray) -> np.ndarray:
 #: between the largest binary32 number, (2 - 2^-23) 2^127, and 2^128; that
 #: largest number has an odd significand, so the tie itself rounds up.
 _F32_OVERFLOW = 2.0 ** 128 - 2.0 ** 103
+
+
+def f32_to_f16_c(x: np.ndarray) -> np.ndarray:
+    """The C oracle's binary32 -> binary16 rounding, element by element (uint16 bits)."""
+    lib = _load()
+    return np.array([lib.rog_oracle_f32_to_f16(float(v)) for v in np.asarray(x, np.float32)], np.uint16)
+
+
+#: Magnitudes from which rounding to binary16 gives infinity: the midpoint
+#: between the largest binary16 number, 65504 (odd significand), and 2^16.
+_F16_OVERFLOW = 65520.0
+
+
+def f16_bits_to_float(h: int) -> float:
+    return struct.unpack("<e", struct.pack("<H", h & 0xFFFF))[0]
+
+
+def f32_to_f16_py(x: float) -> int:
+    """binary32 value -> binary16 bits, nearest-even (struct's half format
+    rounds half to even; overflow to infinity handled here); a NaN becomes a
+    quiet NaN with the same sign."""
+    if math.isnan(x):
+        return 0xFE00 if math.copysign(1.0, x) < 0 else 0x7E00
+    if abs(x) >= _F16_OVERFLOW:
+        return 0xFC00 if x < 0 else 0x7C00
+    return struct.unpack("<H", struct.pack("<e", x))[0]
 
 
 def _f32(x: float) -> float:
@@ -214,8 +245,11 @@ def reduce_py(srcs: Sequence[Sequence], dtype: str) -> List:
     """Pure-Python rank-ordered sum, element by element (tiny inputs only).
 
     "f32": sequences of Python floats that are binary32 values; returns floats.
-    "bf16": sequences of bf16 bit patterns (ints); returns bf16 bit patterns.
+    "bf16" / "f16": sequences of bf16 / binary16 bit patterns (ints); returns
+    bit patterns of the same type.
     """
+    widen = {"bf16": bf16_bits_to_float, "f16": f16_bits_to_float}.get(dtype)
+    narrow = {"bf16": f32_to_bf16_py, "f16": f32_to_f16_py}.get(dtype)
     W = len(srcs)
     n = len(srcs[0])
     out = []
@@ -226,8 +260,8 @@ def reduce_py(srcs: Sequence[Sequence], dtype: str) -> List:
                 acc = _f32(acc + _f32(float(srcs[r][i])))
             out.append(acc)
         else:
-            acc = bf16_bits_to_float(int(srcs[0][i]))
+            acc = widen(int(srcs[0][i]))
             for r in range(1, W):
-                acc = _f32(acc + bf16_bits_to_float(int(srcs[r][i])))
-            out.append(f32_to_bf16_py(acc))
+                acc = _f32(acc + widen(int(srcs[r][i])))
+            out.append(narrow(acc))
     return out

@@ -2,8 +2,9 @@
 by IEEE-754 arithmetic, independent of any implementation under test.
 
 A ``reduce`` under test has the signature ``reduce(srcs, dtype) -> array``:
-``srcs`` are W equal-length 1-D arrays (float32 for "f32", uint16 bf16 bit
-patterns for "bf16"); it returns the n results in the same storage type.
+``srcs`` are W equal-length 1-D arrays (float32 for "f32", uint16 bf16 /
+binary16 bit patterns for "bf16" / "f16"); it returns the n results in the
+same storage type.
 
 The reading (the pages -- RL-Align/RL-Kernel PR #491, "Not in this PR" -- name
 deterministic all_reduce / reduce_scatter but print no arithmetic): the sum is
@@ -25,7 +26,12 @@ taken as it is, and the result rounded once to the element type
 * special values -- infinities, NaN, signed zeros, overflow, subnormals, by
   IEEE-754 rules;
 * bf16 rounding -- torch's CPU float32 -> bfloat16 conversion (a library
-  routine, round to nearest-even) and hand-worked ties.
+  routine, round to nearest-even) and hand-worked ties;
+* binary16 -- the same integer, order, accumulation and special-value pins
+  worked for binary16, the identity over every pattern, pairs against numpy's
+  binary16 conversions, and the rounding against numpy's and torch's CPU
+  float32 -> float16 conversions and hand-worked ties (overflow at 65520,
+  gradual underflow).
 """
 from __future__ import annotations
 
@@ -78,10 +84,108 @@ def same_bits(got: np.ndarray, want: np.ndarray, dtype: str) -> bool:
         g, w = got.astype(np.float32), want.astype(np.float32)
         gn, wn = np.isnan(g), np.isnan(w)
         return bool(np.array_equal(gn, wn) and np.array_equal(g.view(np.uint32)[~gn], w.view(np.uint32)[~wn]))
+    inf = 0x7F80 if dtype == "bf16" else 0x7C00
     g, w = got.astype(np.uint16), want.astype(np.uint16)
-    gn = ((g & 0x7FFF) > 0x7F80)
-    wn = ((w & 0x7FFF) > 0x7F80)
+    gn = ((g & 0x7FFF) > inf)
+    wn = ((w & 0x7FFF) > inf)
     return bool(np.array_equal(gn, wn) and np.array_equal(g[~gn], w[~wn]))
+
+
+# ---------------------------------------------------------------------------
+# binary16 pins
+# ---------------------------------------------------------------------------
+
+def f16_of_exact(x: float) -> int:
+    """binary16 bits of a value known to be exactly representable in binary16."""
+    h = int(np.array([x], np.float16).view(np.uint16)[0])
+    assert float(np.array([h], np.uint16).view(np.float16)[0]) == x, x
+    return h
+
+
+def pin_f16_sums(reduce):
+    """Integer sums, rank order, binary32 accumulation and special values for
+    binary16 elements (worked by hand)."""
+    rng = np.random.default_rng(13)
+    for W in (1, 2, 8, 16):
+        y = rng.integers(-8, 9, size=(W, 129))
+        hs = [np.array([f16_of_exact(float(v)) for v in row], np.uint16) for row in y]
+        want = np.array([f16_of_exact(float(v)) for v in y.sum(axis=0)], np.uint16)
+        assert np.array_equal(reduce(hs, "f16"), want), W
+    # rank order: 2^15 + 2^-9 is a binary32 tie (ulp 2^-8) and rounds to the even
+    # 2^15; - 2^15 then gives 0.  Reversed: -2^15 + 2^-9 is exact, + 2^15 = 2^-9.
+    big, small = 2.0 ** 15, 2.0 ** -9
+    for xs, want in (([big, small, -big], 0.0), ([-big, small, big], small)):
+        got = reduce([np.array([f16_of_exact(v)], np.uint16) for v in xs], "f16")
+        assert got[0] == f16_of_exact(want), (xs, hex(int(got[0])))
+    # binary32 accumulation: 1 + 2^-11 + 2^-11 = 1 + 2^-10 exactly (0x3C01); rounding
+    # to binary16 after every add would give 1 + 2^-11 -> 1 (tie, even), twice: 0x3C00
+    got = reduce([np.array([h], np.uint16) for h in (0x3C00, f16_of_exact(2.0 ** -11), f16_of_exact(2.0 ** -11))],
+                 "f16")
+    assert got[0] == 0x3C01
+    cases = [
+        ([0x7C00, 0x3C00], 0x7C00),               # +inf + 1
+        ([0x7C00, 0xFC00], None),                 # +inf + -inf = NaN
+        ([0x7E00, 0x3C00], None),                 # NaN + 1
+        ([0x7BFF, 0x7BFF], 0x7C00),               # 65504 + 65504 overflows binary16
+        ([0x7BFF, f16_of_exact(16.0)], 0x7C00),   # 65520: a tie above 65504 (odd): up to +inf
+        ([0x7BFF, f16_of_exact(8.0)], 0x7BFF),    # 65512: below the tie, stays 65504
+        ([0x0001, 0x0001], 0x0002),               # subnormals add exactly
+        ([0x8001, 0x0001], 0x0000),               # x + (-x) = +0
+        ([0x8000, 0x8000], 0x8000),               # -0 + -0 = -0
+        ([0x3C00, f16_of_exact(2.0 ** -11)], 0x3C00),      # 1 + 2^-11: tie, to even (1)
+        ([0x3C01, f16_of_exact(2.0 ** -11)], 0x3C02),      # (1 + 2^-10) + 2^-11: tie, to even
+        ([0x0400, 0x8001], 0x03FF),               # smallest normal - smallest subnormal
+    ]
+    for hs, want in cases:
+        got = reduce([np.array([h], np.uint16) for h in hs], "f16")
+        if want is None:
+            assert (got[0] & 0x7FFF) > 0x7C00, (hs, hex(int(got[0])))
+        else:
+            assert got[0] == want, (hs, hex(int(got[0])), hex(want))
+    # W = 1 is the identity on every binary16 pattern (NaNs by class)
+    every = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    assert same_bits(reduce([every.copy()], "f16"), every, "f16")
+    # pairs against numpy's own binary16 widening and binary32 -> binary16
+    # rounding (library routines): x + y in binary32, rounded once
+    bits = rng.integers(0, 1 << 16, size=(2, 20000), dtype=np.uint32).astype(np.uint16)
+    with np.errstate(over="ignore", invalid="ignore"):
+        want = (bits[0].view(np.float16).astype(np.float32) + bits[1].view(np.float16).astype(np.float32))
+        want = want.astype(np.float16).view(np.uint16)
+    assert same_bits(reduce([bits[0].copy(), bits[1].copy()], "f16"), want, "f16")
+
+
+def pin_f16_rounding(round_fn):
+    """``round_fn(float32 array) -> uint16 binary16 bits`` against hand-worked
+    ties and numpy's and torch's CPU conversions."""
+    import torch
+    hand = {0x3F801000: 0x3C00,     # 1 + 2^-11: tie, even stays
+            0x3F803000: 0x3C02,     # 1 + 3*2^-11: tie, odd rounds up
+            0x3F801001: 0x3C01,     # just above the tie
+            0x477FE000: 0x7BFF,     # 65504, the largest binary16, exactly
+            0x477FE800: 0x7BFF,     # 65512: below the tie, down to 65504
+            0x477FF000: 0x7C00,     # 65520: the tie above 65504 (odd) -> +inf
+            0x477FEFFF: 0x7BFF,     # just below 65520
+            0x477FF800: 0x7C00,     # 65528: above the tie -> +inf
+            0x33000000: 0x0000,     # 2^-25: tie with 0 and 2^-24, to even (0)
+            0x33400000: 0x0001,     # 1.5 * 2^-25 -> 2^-24
+            0x33C00000: 0x0002,     # 3 * 2^-25: tie, to even (2 * 2^-24)
+            0x387FE000: 0x0400,     # 2^-14 - 2^-25: tie between 0x03FF (odd) and 0x0400
+            0x7F800000: 0x7C00, 0xFF800000: 0xFC00, 0x80000000: 0x8000, 0x00000001: 0x0000}
+    xs = np.array(list(hand), dtype=np.uint32).view(np.float32)
+    got = np.asarray(round_fn(xs))
+    for k, (u, want) in enumerate(hand.items()):
+        assert got[k] == want, (hex(u), hex(int(got[k])), hex(want))
+    rng = np.random.default_rng(19)
+    bits = rng.integers(0, 1 << 32, size=20000, dtype=np.uint64).astype(np.uint32)
+    bits[:5000] = (bits[:5000] & 0xFFFFE000) | 0x1000          # ties at the normal quantum
+    bits[5000:6000] = (bits[5000:6000] & 0x807FFFFF) | (np.uint32(100) << 23)   # subnormal range
+    xs = bits.view(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        want_np = xs.astype(np.float16).view(np.uint16)
+    want_t = torch.from_numpy(xs.copy()).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    got = np.asarray(round_fn(xs))
+    assert same_bits(got, want_np, "f16")
+    assert same_bits(got, want_t, "f16")
 
 
 # ---------------------------------------------------------------------------

@@ -23,7 +23,7 @@ def c_reduce(srcs, dtype):
 def py_reduce(srcs, dtype):
     if dtype == "f32":
         return np.array(oracle.reduce_py([s.tolist() for s in srcs], "f32"), dtype=np.float32)
-    return np.array(oracle.reduce_py([[int(v) for v in s] for s in srcs], "bf16"), dtype=np.uint16)
+    return np.array(oracle.reduce_py([[int(v) for v in s] for s in srcs], dtype), dtype=np.uint16)
 
 
 ORACLES = {"c": c_reduce, "py": py_reduce}
@@ -127,3 +127,24 @@ def test_the_mistake_harness_itself_passes_when_correct():
     correct = _mistake()
     for pin in PINS + [pins.pin_identity]:
         pin(correct)
+
+
+# ---------------------------------------------------------------------------
+# binary16
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("which", sorted(ORACLES))
+def test_oracle_passes_f16_pins(which):
+    pins.pin_f16_sums(ORACLES[which])
+
+
+def test_f16_rounding_of_both_oracles():
+    pins.pin_f16_rounding(oracle.f32_to_f16_c)
+    pins.pin_f16_rounding(lambda xs: np.array([oracle.f32_to_f16_py(float(v)) for v in xs], np.uint16))
+
+
+@pytest.mark.parametrize("W", [1, 2, 5, 8])
+def test_c_and_python_oracles_agree_f16(W):
+    for kind in ("uniform", "bits"):
+        srcs = wl.reduce_payloads(wl.case_seed(8, W), W, 97, "f16", kind)
+        assert pins.same_bits(c_reduce(srcs, "f16"), py_reduce(srcs, "f16"), "f16"), (W, kind)
