@@ -217,7 +217,9 @@ rog_status validate_reduce(const void *const *srcs, int W, size_t count, size_t 
 
 inline size_t dtype_size(rog_dtype dtype) { return dtype == ROG_DTYPE_F32 ? 4 : 2; }
 
-inline bool dtype_ok(rog_dtype dtype) { return dtype == ROG_DTYPE_F32 || dtype == ROG_DTYPE_BF16; }
+inline bool dtype_ok(rog_dtype dtype) {
+    return dtype == ROG_DTYPE_F32 || dtype == ROG_DTYPE_BF16 || dtype == ROG_DTYPE_F16;
+}
 
 // Multi-WG REDUCE: one wave per 1 KiB chunk of the body (at most bytes / 16
 // vectors).  bytes < 2^36, so the count fits 26 bits.

@@ -7,7 +7,8 @@
 // paths have the same size cliff as the gather had).  Every element is summed
 // by exactly one lane, in rank order, in binary32 (v_add_f32, round to
 // nearest-even, subnormals kept), and rounded once to the element type
-// (v_cvt_pk_bf16_f32 for bf16), so the bits never depend on the launch.
+// (v_cvt_pk_bf16_f32 for bf16, v_cvt_pk_f16_f32 for binary16), so the bits
+// never depend on the launch.
 //
 // The output is cut like a PEER payload (split_payload): an element head up to
 // the first 256-byte boundary of out, a body of 16-byte vectors, an element
@@ -28,42 +29,58 @@ namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-template <bool BF16>
+// Element type DT (a rog_dtype value).
+template <int DT>
 struct Elem {
-    static constexpr int kPerVec = BF16 ? 8 : 4;   // elements per 16-byte vector
-    static constexpr uint32_t kSize = BF16 ? 2 : 4;
+    static constexpr bool kHalf = DT != ROG_DTYPE_F32;  // 2-byte elements
+    static constexpr int kPerVec = kHalf ? 8 : 4;       // elements per 16-byte vector
+    static constexpr uint32_t kSize = kHalf ? 2 : 4;
 };
 
 __device__ __forceinline__ float from_bits(uint32_t u) { return __builtin_bit_cast(float, u); }
 
-// Two binary32 values -> two bf16 (element 0 in the low half), nearest-even.
-__device__ __forceinline__ uint32_t to_bf16x2(float lo, float hi) {
+// Two binary32 values -> two 2-byte elements (element 0 in the low half),
+// nearest-even: v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32.
+template <int DT>
+__device__ __forceinline__ uint32_t narrow2(float lo, float hi) {
     const f32x2 v = {lo, hi};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    if constexpr (DT == ROG_DTYPE_BF16) return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    else return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// Two 2-byte elements (element 0 in the low half) -> binary32, exactly.
+template <int DT>
+__device__ __forceinline__ void widen2(uint32_t w, float &lo, float &hi) {
+    if constexpr (DT == ROG_DTYPE_BF16) {
+        lo = from_bits(w << 16);
+        hi = from_bits(w & 0xFFFF0000u);
+    } else {
+        const f32x2 f = __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+        lo = f.x;
+        hi = f.y;
+    }
 }
 
 // The elements of one 16-byte vector, widened to binary32.
-template <bool BF16>
-__device__ __forceinline__ void widen(const vec16 &v, float (&x)[Elem<BF16>::kPerVec]) {
-    if constexpr (BF16) {
+template <int DT>
+__device__ __forceinline__ void widen(const vec16 &v, float (&x)[Elem<DT>::kPerVec]) {
+    if constexpr (Elem<DT>::kHalf) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            x[2 * k] = from_bits(v[k] << 16);
-            x[2 * k + 1] = from_bits(v[k] & 0xFFFF0000u);
-        }
+        for (int k = 0; k < 4; ++k) widen2<DT>(v[k], x[2 * k], x[2 * k + 1]);
     } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k) x[k] = from_bits(v[k]);
     }
 }
 
-template <bool BF16>
-__device__ __forceinline__ vec16 narrow(const float (&a)[Elem<BF16>::kPerVec]) {
+template <int DT>
+__device__ __forceinline__ vec16 narrow(const float (&a)[Elem<DT>::kPerVec]) {
     vec16 v;
-    if constexpr (BF16) {
+    if constexpr (Elem<DT>::kHalf) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = to_bf16x2(a[2 * k], a[2 * k + 1]);
+        for (int k = 0; k < 4; ++k) v[k] = narrow2<DT>(a[2 * k], a[2 * k + 1]);
     } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k) v[k] = __builtin_bit_cast(uint32_t, a[k]);
@@ -80,9 +97,9 @@ __device__ __forceinline__ vec16 narrow(const float (&a)[Elem<BF16>::kPerVec]) {
 constexpr uint32_t kGroup = ROG_REDUCE_GROUP;   // source loads in flight per lane
 
 // The rank-ordered sum of the 16-byte vectors at byte offset off of every source.
-template <bool BF16, bool NTL>
+template <int DT, bool NTL>
 __device__ __forceinline__ vec16 sum_vec(const void *const *src, uint32_t W, uint64_t off) {
-    constexpr int E = Elem<BF16>::kPerVec;
+    constexpr int E = Elem<DT>::kPerVec;
     float acc[E];
     for (uint32_t r0 = 0; r0 < W; r0 += kGroup) {
         const uint32_t g = min(W - r0, kGroup);
@@ -94,7 +111,7 @@ __device__ __forceinline__ vec16 sum_vec(const void *const *src, uint32_t W, uin
         for (uint32_t q = 0; q < kGroup; ++q) {
             if (q < g) {
                 float x[E];
-                widen<BF16>(v[q], x);
+                widen<DT>(v[q], x);
                 if (r0 + q == 0) {
 #pragma unroll
                     for (int e = 0; e < E; ++e) acc[e] = x[e];       // the first term as it is
@@ -105,51 +122,56 @@ __device__ __forceinline__ vec16 sum_vec(const void *const *src, uint32_t W, uin
             }
         }
     }
-    return narrow<BF16>(acc);
+    return narrow<DT>(acc);
 }
 
-template <bool BF16>
+template <int DT>
 __device__ __forceinline__ float load_elem(const void *p, uint64_t i) {
-    if constexpr (BF16) return from_bits(uint32_t(static_cast<const uint16_t *>(p)[i]) << 16);
-    else return static_cast<const float *>(p)[i];
+    if constexpr (Elem<DT>::kHalf) {
+        float lo, hi;
+        widen2<DT>(static_cast<const uint16_t *>(p)[i], lo, hi);
+        return lo;
+    } else {
+        return static_cast<const float *>(p)[i];
+    }
 }
 
 // One element: the rank-ordered sum of element i of every source, stored to out.
-template <bool BF16>
+template <int DT>
 __device__ __forceinline__ void sum_elem(const void *const *src, uint32_t W, uint64_t i, void *out) {
-    float acc = load_elem<BF16>(src[0], i);
-    for (uint32_t r = 1; r < W; ++r) acc += load_elem<BF16>(src[r], i);
-    if constexpr (BF16) static_cast<uint16_t *>(out)[i] = uint16_t(to_bf16x2(acc, 0.0f) & 0xFFFFu);
+    float acc = load_elem<DT>(src[0], i);
+    for (uint32_t r = 1; r < W; ++r) acc += load_elem<DT>(src[r], i);
+    if constexpr (Elem<DT>::kHalf) static_cast<uint16_t *>(out)[i] = uint16_t(narrow2<DT>(acc, 0.0f) & 0xFFFFu);
     else static_cast<float *>(out)[i] = acc;
 }
 
 // One wave: body chunk j (body vectors [64j, 64j + 64)) of a sum of `count`
 // elements into out; chunk 0 also sums the head and tail elements.
-template <bool BF16, bool NTL>
+template <int DT, bool NTL>
 __device__ __forceinline__ void sum_chunk(const void *const *src, uint32_t W, void *out, uint64_t count,
                                           uint32_t j) {
     const uint32_t lane = __lane_id();
-    const PeerSplit cut = split_payload(reinterpret_cast<uintptr_t>(out), count * Elem<BF16>::kSize);
+    const PeerSplit cut = split_payload(reinterpret_cast<uintptr_t>(out), count * Elem<DT>::kSize);
     if (j == 0) {
-        for (uint64_t i = lane; i < cut.lo / Elem<BF16>::kSize; i += 64) sum_elem<BF16>(src, W, i, out);
-        for (uint64_t i = cut.hi / Elem<BF16>::kSize + lane; i < count; i += 64) sum_elem<BF16>(src, W, i, out);
+        for (uint64_t i = lane; i < cut.lo / Elem<DT>::kSize; i += 64) sum_elem<DT>(src, W, i, out);
+        for (uint64_t i = cut.hi / Elem<DT>::kSize + lane; i < count; i += 64) sum_elem<DT>(src, W, i, out);
     }
     const uint64_t off = cut.lo + 16 * (uint64_t(j) * 64 + lane);
     if (off < cut.hi)
-        st16(reinterpret_cast<vec16 *>(static_cast<uint8_t *>(out) + off), sum_vec<BF16, NTL>(src, W, off));
+        st16(reinterpret_cast<vec16 *>(static_cast<uint8_t *>(out) + off), sum_vec<DT, NTL>(src, W, off));
 }
 
 // Multi-WG: one wave per workgroup and per 1 KiB chunk of the body, chunks
 // handed to the XCDs in runs, grid-strided over a capped grid.
-template <bool BF16, bool NTL>
+template <int DT, bool NTL>
 __global__ __launch_bounds__(kWaveBlock) void rog_reduce_kernel(ReduceArgs a) {
     for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x)
-        sum_chunk<BF16, NTL>(a.src, a.W, a.out, a.count, ROG_REDUCE_XCD ? xcd_grouped(vb, a.n_chunks) : vb);
+        sum_chunk<DT, NTL>(a.src, a.W, a.out, a.count, ROG_REDUCE_XCD ? xcd_grouped(vb, a.n_chunks) : vb);
 }
 
 // Batch: the tensors' chunks laid end to end; a wave finds its tensor by a
 // scalar binary search over the tensors' first chunks.
-template <bool BF16, bool NTL>
+template <int DT, bool NTL>
 __global__ __launch_bounds__(kWaveBlock) void rog_reduce_batch_kernel(ReduceBatchArgs a) {
     for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x) {
         const uint32_t c = ROG_REDUCE_XCD ? xcd_grouped(vb, a.n_chunks) : vb;
@@ -160,30 +182,30 @@ __global__ __launch_bounds__(kWaveBlock) void rog_reduce_batch_kernel(ReduceBatc
             else hi = mid;
         }
         const ReduceTensor &t = a.t[lo];
-        sum_chunk<BF16, NTL>(a.src + lo * a.W, a.W, reinterpret_cast<void *>(t.out), t.count, c - t.first_chunk);
+        sum_chunk<DT, NTL>(a.src + lo * a.W, a.W, reinterpret_cast<void *>(t.out), t.count, c - t.first_chunk);
     }
 }
 
 // Single-WG: one workgroup over the whole output.
-template <bool BF16, bool NTL>
+template <int DT, bool NTL>
 __global__ __launch_bounds__(kSingleBlock) void rog_reduce_single_kernel(ReduceArgs a) {
     const uint32_t tid = threadIdx.x, nt = blockDim.x;
-    const uint64_t bytes = a.count * Elem<BF16>::kSize;
+    const uint64_t bytes = a.count * Elem<DT>::kSize;
     const PeerSplit cut = split_payload(reinterpret_cast<uintptr_t>(a.out), bytes);
     uint8_t *o = static_cast<uint8_t *>(a.out);
-    for (uint64_t i = tid; i < cut.lo / Elem<BF16>::kSize; i += nt) sum_elem<BF16>(a.src, a.W, i, a.out);
-    for (uint64_t i = cut.hi / Elem<BF16>::kSize + tid; i < a.count; i += nt) sum_elem<BF16>(a.src, a.W, i, a.out);
+    for (uint64_t i = tid; i < cut.lo / Elem<DT>::kSize; i += nt) sum_elem<DT>(a.src, a.W, i, a.out);
+    for (uint64_t i = cut.hi / Elem<DT>::kSize + tid; i < a.count; i += nt) sum_elem<DT>(a.src, a.W, i, a.out);
     for (uint64_t off = cut.lo + 16 * uint64_t(tid); off < cut.hi; off += 16 * uint64_t(nt))
-        st16(reinterpret_cast<vec16 *>(o + off), sum_vec<BF16, NTL>(a.src, a.W, off));
+        st16(reinterpret_cast<vec16 *>(o + off), sum_vec<DT, NTL>(a.src, a.W, off));
 }
 
 template <typename K>
 const void *kfn(K *k) { return reinterpret_cast<const void *>(k); }
 
-template <bool BF16>
+template <int DT>
 const void *reduce_kernel(bool single, bool ntl) {
-    if (single) return ntl ? kfn(&rog_reduce_single_kernel<BF16, true>) : kfn(&rog_reduce_single_kernel<BF16, false>);
-    return ntl ? kfn(&rog_reduce_kernel<BF16, true>) : kfn(&rog_reduce_kernel<BF16, false>);
+    if (single) return ntl ? kfn(&rog_reduce_single_kernel<DT, true>) : kfn(&rog_reduce_single_kernel<DT, false>);
+    return ntl ? kfn(&rog_reduce_kernel<DT, true>) : kfn(&rog_reduce_kernel<DT, false>);
 }
 
 rog_status launch_reduce(Plan &p, hipStream_t stream) {
@@ -191,7 +213,9 @@ rog_status launch_reduce(Plan &p, hipStream_t stream) {
     if (i.kernel == ROG_KERNEL_NONE) return ROG_OK;
     const bool single = i.path == ROG_PATH_SINGLE_WG;
     const bool ntl = (i.flags & ROG_PLAN_NT_LOADS) != 0;
-    const void *k = p.dtype == ROG_DTYPE_BF16 ? reduce_kernel<true>(single, ntl) : reduce_kernel<false>(single, ntl);
+    const void *k = p.dtype == ROG_DTYPE_BF16  ? reduce_kernel<ROG_DTYPE_BF16>(single, ntl)
+                    : p.dtype == ROG_DTYPE_F16 ? reduce_kernel<ROG_DTYPE_F16>(single, ntl)
+                                               : reduce_kernel<ROG_DTYPE_F32>(single, ntl);
     void *params[] = {&p.reduce};
     const hipError_t e = hipLaunchKernel(k, dim3(i.grid), dim3(i.block), params, 0, stream);
     if (e != hipSuccess) {
@@ -201,9 +225,9 @@ rog_status launch_reduce(Plan &p, hipStream_t stream) {
     return ROG_OK;
 }
 
-template <bool BF16>
+template <int DT>
 const void *reduce_batch_kernel(bool ntl) {
-    return ntl ? kfn(&rog_reduce_batch_kernel<BF16, true>) : kfn(&rog_reduce_batch_kernel<BF16, false>);
+    return ntl ? kfn(&rog_reduce_batch_kernel<DT, true>) : kfn(&rog_reduce_batch_kernel<DT, false>);
 }
 
 }  // namespace
@@ -245,7 +269,9 @@ ROG_API rog_status rog_reduce_many(const rog_reduce_desc *descs, int n, int W, r
     bool ntl = false;
     const rog_status st = rog::plan_reduce_batch(descs, n, W, dtype, &args, &grid, &ntl);
     if (st != ROG_OK || grid == 0) return st;
-    const void *k = dtype == ROG_DTYPE_BF16 ? rog::reduce_batch_kernel<true>(ntl) : rog::reduce_batch_kernel<false>(ntl);
+    const void *k = dtype == ROG_DTYPE_BF16  ? rog::reduce_batch_kernel<ROG_DTYPE_BF16>(ntl)
+                    : dtype == ROG_DTYPE_F16 ? rog::reduce_batch_kernel<ROG_DTYPE_F16>(ntl)
+                                             : rog::reduce_batch_kernel<ROG_DTYPE_F32>(ntl);
     void *params[] = {&args};
     const hipError_t e = hipLaunchKernel(k, dim3(grid), dim3(rog::kWaveBlock), params, 0, stream);
     if (e != hipSuccess) {

@@ -11,7 +11,7 @@ Entry points keep the C names.  Tensor forms:
 * ``rog_gather_many(batch, outs=None, stream=None)`` -> list of outputs;
 * ``rog_plan(srcs, out, path=ROG_PATH_AUTO)`` -> dict (no GPU work);
 * ``rog_reduce(srcs, out=None, stream=None)`` -> ``out``: the rank-ordered sum
-  of W float32 or bfloat16 tensors;
+  of W float32, bfloat16 or float16 tensors;
 * ``rog_reduce_ex(srcs, out, path, stream=None)``, ``rog_reduce_plan(srcs, out, path)``;
 * ``rog_reduce_many(batch, outs=None, stream=None)`` -> list of outputs (one
   launch);
@@ -59,11 +59,12 @@ ROG_KERNEL_REDUCE = 3
 
 ROG_DTYPE_F32 = 0
 ROG_DTYPE_BF16 = 1
+ROG_DTYPE_F16 = 2
 
 PATH_NAMES = {ROG_PATH_AUTO: "auto", ROG_PATH_SINGLE_WG: "single_wg", ROG_PATH_MULTI_WG: "multi_wg"}
 KERNEL_NAMES = {ROG_KERNEL_NONE: "none", ROG_KERNEL_FLAT: "flat", ROG_KERNEL_PEER: "peer",
                 ROG_KERNEL_REDUCE: "reduce"}
-DTYPES = {torch.float32: ROG_DTYPE_F32, torch.bfloat16: ROG_DTYPE_BF16}
+DTYPES = {torch.float32: ROG_DTYPE_F32, torch.bfloat16: ROG_DTYPE_BF16, torch.float16: ROG_DTYPE_F16}
 
 
 class RogError(RuntimeError):
@@ -405,7 +406,7 @@ def _prepare_reduce(srcs: Sequence[torch.Tensor], out: Optional[torch.Tensor]):
     device = srcs[0].device
     dtype = srcs[0].dtype
     if dtype not in DTYPES:
-        raise ValueError("rog_reduce sums float32 or bfloat16 tensors (got %s)" % dtype)
+        raise ValueError("rog_reduce sums float32, bfloat16 or float16 tensors (got %s)" % dtype)
     n = srcs[0].numel()
     for i, s in enumerate(srcs):
         _check_tensor(s, "srcs[%d]" % i, device)
@@ -432,7 +433,8 @@ def rog_reduce_ex(srcs: Sequence[torch.Tensor], out: Optional[torch.Tensor] = No
 def rog_reduce(srcs: Sequence[torch.Tensor], out: Optional[torch.Tensor] = None,
                stream=None) -> torch.Tensor:
     """out[i] = rank-ordered binary32 sum of srcs[r][i], rounded to the tensors'
-    dtype (float32 or bfloat16).  ``out`` may be one of ``srcs`` (in place)."""
+    dtype (float32, bfloat16 or float16).  ``out`` may be one of ``srcs`` (in
+    place)."""
     return rog_reduce_ex(srcs, out, ROG_PATH_AUTO, stream)
 
 

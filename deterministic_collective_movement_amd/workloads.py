@@ -301,11 +301,11 @@ REDUCE_ELEM_OFFSETS = (0, 1, 3, 8)
 
 
 def reduce_config3() -> List[ReduceCase]:
-    """Alignment / tail sweep: bf16 and f32 x W in {2, 3, 8} x n x element
-    offsets of the sources (all alike) and of the output, plus a mixed-offset
-    case per (dtype, W, n) and random-bit-pattern cases."""
+    """Alignment / tail sweep: bf16, binary16 and binary32 x W in {2, 3, 8} x n x
+    element offsets of the sources (all alike) and of the output, plus a
+    mixed-offset case per (dtype, W, n) and random-bit-pattern cases."""
     cases = []
-    for dtype in ("bf16", "f32"):
+    for dtype in ("bf16", "f16", "f32"):
         for W in (2, 3, 8):
             for n in REDUCE_TAIL_N:
                 for io in REDUCE_ELEM_OFFSETS:

@@ -79,7 +79,8 @@ typedef enum {
 /* Element types of the rank-ordered sum. */
 typedef enum {
     ROG_DTYPE_F32 = 0,       /* IEEE binary32, 4 bytes                               */
-    ROG_DTYPE_BF16 = 1       /* bfloat16 (top 16 bits of a binary32), 2 bytes       */
+    ROG_DTYPE_BF16 = 1,      /* bfloat16 (top 16 bits of a binary32), 2 bytes       */
+    ROG_DTYPE_F16 = 2        /* IEEE binary16, 2 bytes                               */
 } rog_dtype;
 
 /* One tensor of a batch: W source pointers, its output, its per-rank bytes. */
@@ -190,9 +191,10 @@ ROG_API size_t rog_single_wg_max_bytes(void);
  *     out[i] = round( ((x_0[i] + x_1[i]) + x_2[i]) + ... + x_{W-1}[i] ),
  *
  * x_r = srcs[r], the sum taken in rank order with every addition an IEEE
- * binary32 addition rounded to nearest-even, bf16 elements widened to binary32
- * exactly, the first term taken as it is (a lone -0 stays -0), and the result
- * rounded once to `dtype` (bf16: nearest-even; a NaN stays a NaN, its payload
+ * binary32 addition rounded to nearest-even, bf16 and binary16 elements
+ * widened to binary32 exactly, the first term taken as it is (a lone -0 stays
+ * -0), and the result rounded once to `dtype` (nearest-even; binary16 with
+ * gradual underflow and overflow to infinity; a NaN stays a NaN, its payload
  * unspecified).  Every element is summed by one thread in that fixed order, so
  * the result is the same bits on every call, whatever the launch shape.
  *
@@ -208,7 +210,7 @@ ROG_API size_t rog_single_wg_max_bytes(void);
  *         aligned to the element size (any alignment beyond that).
  * W       1 <= W <= rog_max_peers().
  * count   elements per payload (and in out).
- * dtype   ROG_DTYPE_F32 or ROG_DTYPE_BF16.
+ * dtype   ROG_DTYPE_F32, ROG_DTYPE_BF16 or ROG_DTYPE_F16.
  * out     device pointer to `count` writable elements, element-aligned.  out
  *         may be exactly one (or several) of the srcs (in place); any other
  *         overlap with a source is an error.  Sources may alias each other.

@@ -116,7 +116,7 @@ def place_batch(case: wl.BatchCase, device) -> PlacedBatch:
 # Rank-ordered sum
 # ---------------------------------------------------------------------------
 
-TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def _same_elements(got: np.ndarray, want: np.ndarray, dtype: str) -> np.ndarray:
@@ -126,9 +126,10 @@ def _same_elements(got: np.ndarray, want: np.ndarray, dtype: str) -> np.ndarray:
         gn = (g & 0x7FFFFFFF) > 0x7F800000
         wn = (w & 0x7FFFFFFF) > 0x7F800000
     else:
+        inf = 0x7F80 if dtype == "bf16" else 0x7C00
         g, w = got.view(np.uint16), want.view(np.uint16)
-        gn = (g & 0x7FFF) > 0x7F80
-        wn = (w & 0x7FFF) > 0x7F80
+        gn = (g & 0x7FFF) > inf
+        wn = (w & 0x7FFF) > inf
     return (g == w) | (gn & wn)
 
 

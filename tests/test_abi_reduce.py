@@ -11,7 +11,7 @@ import pytest
 from deterministic_collective_movement_amd import rog
 
 A = 1 << 33
-F32, BF16 = rog.ROG_DTYPE_F32, rog.ROG_DTYPE_BF16
+F32, BF16, F16 = rog.ROG_DTYPE_F32, rog.ROG_DTYPE_BF16, rog.ROG_DTYPE_F16
 OK, INVALID, OVERLAP, TOO_LARGE = (rog.ROG_OK, rog.ROG_ERR_INVALID_ARGUMENT,
                                    rog.ROG_ERR_OVERLAP, rog.ROG_ERR_TOO_LARGE)
 
@@ -38,7 +38,7 @@ def test_invalid_arguments():
     assert st([A + 256 * i for i in range(M)], 16, 2 * A) == OK
     assert st([A, 0], 16, 2 * A) == INVALID
     assert st([A, A + 64], 16, 0) == INVALID
-    assert st([A], 16, 2 * A, dtype=2) == INVALID            # unknown dtype
+    assert st([A], 16, 2 * A, dtype=3) == INVALID            # unknown dtype
     assert st([A], 16, 2 * A, dtype=-1) == INVALID
     assert st([A], 16, 2 * A, path=5) == INVALID
     assert rog.lib().rog_reduce_plan(rog._ptr_array([A]), 1, 16, F32, ctypes.c_void_p(2 * A), 0, None) == INVALID
@@ -52,6 +52,8 @@ def test_element_alignment():
     assert st([A + 1], 16, 2 * A, BF16) == INVALID
     assert st([A], 16, 2 * A + 3, BF16) == INVALID
     assert st([A + 2, A + 4096 + 6], 16, 2 * A + 14, BF16) == OK
+    assert st([A + 1], 16, 2 * A, F16) == INVALID
+    assert st([A + 2, A + 4096 + 6], 16, 2 * A + 14, F16) == OK
 
 
 def test_zero_count_is_a_no_op_even_with_null_pointers():

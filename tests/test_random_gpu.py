@@ -38,7 +38,7 @@ def test_random_gather(gpu, seed):
 def test_random_sum(gpu, seed):
     rng = np.random.default_rng([4343, seed])
     W = int(rng.choice([1, 2, 3, 4, 6, 8, 11, 32, 64]))
-    dtype = str(rng.choice(["bf16", "f32"]))
+    dtype = str(rng.choice(["bf16", "f16", "f32"]))
     n = _size(rng, 0, 6.0 if W <= 8 else 4.5)
     in_offs = [int(rng.integers(0, 16)) if rng.random() < 0.5 else 0 for _ in range(W)]
     out_off = int(rng.integers(0, 16)) if rng.random() < 0.5 else 0

@@ -41,7 +41,7 @@ def test_bandwidth_case_full_output(gpu):
     gc.run_reduce_all_paths(placed, case.label(), paths=(rog.ROG_PATH_AUTO,))
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("W", [1, 5, 64])
 def test_every_W_up_to_the_maximum(gpu, dtype, W):
     assert W <= rog.rog_max_peers()
@@ -51,7 +51,7 @@ def test_every_W_up_to_the_maximum(gpu, dtype, W):
         gc.run_reduce_all_paths(placed, "W=%d n=%d %s" % (W, n, dtype))
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("which", [0, 2])
 def test_in_place(gpu, dtype, which):
     """out is srcs[which] itself (an in-place all-reduce)."""
@@ -123,6 +123,8 @@ def test_binding_rejects_bad_tensors(gpu):
     with pytest.raises(ValueError):
         rog.rog_reduce([torch.zeros(16, dtype=torch.int32, device=gpu)])
     with pytest.raises(ValueError):
+        rog.rog_reduce([a.half(), a])                                        # mixed dtypes
+    with pytest.raises(ValueError):
         rog.rog_reduce([a], torch.zeros(16, dtype=torch.float32))          # output on the CPU
     with pytest.raises(rog.RogArgumentError):
         rog.rog_reduce([a[:8], a[4:12]], a[4:12])                           # partial overlap
@@ -147,7 +149,7 @@ def gpu_device():
     return torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("W", [1, 3, 8])
 def test_batched_sums_mixed_sizes(gpu, dtype, W):
     counts = [0, 1, 7, 513, 4096, 0, 70_001, 262_147, 9]
