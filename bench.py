@@ -21,8 +21,9 @@ kernel timed the same way; the batched gather (16 tensors, W = 4, one launch);
 the device-to-device copy ceiling; aligned gathers with 64 - 512 MiB outputs,
 warm and with rotating buffer sets (cold); the rank-ordered sum (rog_reduce:
 W = 8 bf16 payloads of 64 MiB, the pages' per-rank sizes of 1 KiB - 4 MiB at
-W = 2 and 8, and a 16-tensor rog_reduce_many); and the CPU oracle on a bounded
-sample of the headline workload.
+W = 2 and 8, and a 16-tensor rog_reduce_many); and the CPU oracle on bounded
+samples of the headline gather and of the large sum (the CPU-baseline legs,
+the only ones that call the oracle).
 
 Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: the benchmark measures one GPU.
 """
@@ -475,9 +476,9 @@ def _reduce_tensors(torch, case, device):
 
 def reduce_bandwidth(torch, rog, wl, device, steps, warmup):
     """The rank-ordered sum of W = 8 bf16 payloads of 64 MiB: timed region and
-    per-call p50; sampled elements checked against the CPU oracle."""
+    per-call p50.  Returns the result line, the payloads and the output (on the
+    host) for the CPU-baseline leg, which checks a sample of it."""
     import numpy as np
-    from oracle import oracle
     stream = torch.cuda.current_stream(device).cuda_stream
     case = wl.reduce_config4()
     payloads, srcs, out = _reduce_tensors(torch, case, device)
@@ -485,11 +486,6 @@ def reduce_bandwidth(torch, rog, wl, device, steps, warmup):
     region_ms = time_region(torch, call, steps, warmup)
     per_call, _ = time_calls(torch, call, steps, 0)
     got = out.view(torch.int16).cpu().numpy().view(np.uint16)
-    for lo in (0, case.n // 2, case.n - 4096):
-        want = np.empty(4096, np.uint16)
-        oracle.reduce_c([p[lo:lo + 4096] for p in payloads], want, "bf16")
-        if not np.array_equal(got[lo:lo + 4096], want):
-            raise AssertionError("reduce bandwidth case differs from the oracle at element %d" % lo)
     moved = (case.W + 1) * case.n * case.esize
     plan = rog.rog_reduce_plan(srcs, out)
     big = {"W": case.W, "dtype": case.dtype, "bytes_per_rank": case.n * case.esize, "bytes_moved": moved,
@@ -500,7 +496,31 @@ def reduce_bandwidth(torch, rog, wl, device, steps, warmup):
            "pct_of_peak": round(100 * gbps(moved * steps, region_ms) / PEAK_HBM_GBPS, 2)}
     del srcs, out
     torch.cuda.empty_cache()
-    return big
+    return big, payloads, got
+
+
+def reduce_cpu_baseline(payloads, got, budget_s, sample=1 << 22):
+    """The CPU oracle, single-threaded, on a bounded sample of the large sum
+    (its first ``sample`` elements of all W payloads) repeated for about
+    ``budget_s`` seconds; the sample of the GPU's output must equal it."""
+    import numpy as np
+    from oracle import oracle
+    srcs = [p[:sample] for p in payloads]
+    want = np.empty(sample, np.uint16)
+    oracle.reduce_c(srcs, want, "bf16")
+    if not np.array_equal(got[:sample], want):
+        raise AssertionError("the GPU's rank-ordered sum differs from the oracle's on the sample")
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.reduce_c(srcs, want, "bf16")
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    moved = (len(srcs) + 1) * sample * 2 * reps
+    return {"value": round(moved / el / 1e9, 2), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d x the first %d elements of the W=%d bf16 sum (%.1f s, single-threaded C loop)"
+                      % (reps, sample, len(srcs), el)}
 
 
 def reduce_latency(torch, rog, wl, device, steps, warmup):
@@ -520,27 +540,18 @@ def reduce_latency(torch, rog, wl, device, steps, warmup):
 
 def reduce_batch(torch, rog, wl, device, steps, warmup):
     """rog_reduce_many over the batched gather's 16 tensor shapes (rows x cols
-    bf16, W = 4) in one launch; every tensor's first elements checked against
-    the CPU oracle."""
+    bf16, W = 4) in one launch (the GPU tests check these shapes against the
+    oracle)."""
     import numpy as np
-    from oracle import oracle
     case = wl.config5(0)
     counts = [x.rows * x.cols for x in case.tensors]
-    batch, payloads_all, outs = [], [], []
+    batch, outs = [], []
     for t, n in enumerate(counts):
         payloads = wl.reduce_payloads(wl.case_seed(26, t), case.W, n, "bf16")
         batch.append([torch.from_numpy(p.view(np.int16)).to(device).view(torch.bfloat16) for p in payloads])
-        payloads_all.append(payloads)
         outs.append(torch.empty(n, dtype=torch.bfloat16, device=device))
     rog.rog_reduce_many(batch, outs)
     torch.cuda.synchronize()
-    for payloads, o in zip(payloads_all, outs):
-        k = min(4096, o.numel())
-        want = np.empty(k, np.uint16)
-        oracle.reduce_c([p[:k] for p in payloads], want, "bf16")
-        if not np.array_equal(o[:k].view(torch.int16).cpu().numpy().view(np.uint16), want):
-            raise AssertionError("batched sum differs from the oracle")
-    del payloads_all
     lib = rog.lib()
     keep = [(ctypes.c_void_p * case.W)(*[s.data_ptr() for s in srcs]) for srcs in batch]
     descs = (rog.rog_reduce_desc * len(batch))()
@@ -682,14 +693,17 @@ def main(argv=None):
                                             max(1, args.warmup // 5))
         extras["d2d_copy_ceiling"] = d2d_ceiling(torch, device, case.W * case.S, 20, 3)
         extras["bandwidth_sweep"] = bandwidth_sweep(torch, rog, device, 20)
-        extras["reduce"] = {"bandwidth": reduce_bandwidth(torch, rog, wl, device, args.steps, args.warmup),
+        big, rpayloads, rgot = reduce_bandwidth(torch, rog, wl, device, args.steps, args.warmup)
+        extras["reduce"] = {"bandwidth": big,
                             "latency": reduce_latency(torch, rog, wl, device, args.steps, args.warmup),
                             "batched": reduce_batch(torch, rog, wl, device, max(5, args.steps // 5),
                                                     max(1, args.warmup // 5))}
         cpu = cpu_baseline(case, payloads, args.cpu_budget)
+        extras["reduce"]["cpu_baseline"] = reduce_cpu_baseline(rpayloads, rgot, min(5.0, args.cpu_budget))
+        del rpayloads, rgot
     else:
         extras["reduce"] = {"bandwidth": reduce_bandwidth(torch, rog, wl, device, max(10, args.steps // 2),
-                                                          max(2, args.warmup // 2))}
+                                                          max(2, args.warmup // 2))[0]}
         cpu = None
     extras["device"] = torch.cuda.get_device_name(device)
     config = {"workload": "rank-ordered gather of W=8 aligned bf16 payloads of 64 MiB into a 512 MiB "

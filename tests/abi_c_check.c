@@ -8,7 +8,8 @@
  * Cases: aligned (flat) and misaligned (per-payload) gathers on every path,
  * a batch of three tensors in one launch, S = 0, and the argument errors that
  * must be reported before anything is enqueued; rank-ordered sums (bf16 and
- * binary32, every path, element offsets, in place) against the oracle's sum.
+ * binary32, every path, element offsets, in place) against the oracle's sum,
+ * and a batch of binary16 sums in one launch.
  * Exit status 0 = every check passed; the first failure is printed.
  */
 #include <hip/hip_runtime_api.h>
@@ -21,6 +22,7 @@
 void rog_oracle_gather(const unsigned char *const *srcs, int W, size_t S, unsigned char *out);
 void rog_oracle_reduce_f32(const float *const *srcs, int W, size_t count, float *out);
 void rog_oracle_reduce_bf16(const uint16_t *const *srcs, int W, size_t count, uint16_t *out);
+void rog_oracle_reduce_f16(const uint16_t *const *srcs, int W, size_t count, uint16_t *out);
 
 #define GUARD 64
 #define FILL 0xA5
@@ -245,6 +247,60 @@ static void reduce_case(int W, size_t n, int bf16, size_t out_off, int in_place,
     free(got);
 }
 
+/* A batch of binary16 sums (W = 3) in one launch: counts 0, 1, 1000, 65537. */
+static void reduce_batch_case(hipStream_t st) {
+    enum { N = 4, W = 3 };
+    const size_t counts[N] = {0, 1, 1000, 65537};
+    uint16_t *h[N][W], *want[N], *got[N];
+    uint16_t *d[N][W], *dout[N];
+    const void *ptrs[N][W];
+    rog_reduce_desc desc[N];
+    for (int t = 0; t < N; ++t) {
+        const size_t n = counts[t];
+        for (int r = 0; r < W; ++r) {
+            h[t][r] = (uint16_t *)malloc(n * 2 + 2);
+            for (size_t i = 0; i < n; ++i) {
+                /* normal binary16 values of magnitude below 2, from the element hash */
+                const uint32_t x = elem_bits(53u * (unsigned)t + (unsigned)r, i, 0);
+                h[t][r][i] = (uint16_t)(((x >> 16) & 0x8000u) | ((1u + (x >> 3) % 15u) << 10) | (x & 0x3FFu));
+            }
+            CHECK_HIP(hipMalloc((void **)&d[t][r], n * 2 + 2));
+            CHECK_HIP(hipMemcpy(d[t][r], h[t][r], n * 2, hipMemcpyHostToDevice));
+            ptrs[t][r] = d[t][r];
+        }
+        want[t] = (uint16_t *)malloc(n * 2 + 2);
+        got[t] = (uint16_t *)malloc(n * 2 + 2);
+        rog_oracle_reduce_f16((const uint16_t *const *)h[t], W, n, want[t]);
+        CHECK_HIP(hipMalloc((void **)&dout[t], n * 2 + 2));
+        desc[t].srcs = ptrs[t];
+        desc[t].out = dout[t];
+        desc[t].count = n;
+    }
+    const rog_status s = rog_reduce_many(desc, N, W, ROG_DTYPE_F16, st);
+    if (s != ROG_OK) {
+        fprintf(stderr, "FAIL reduce batch: %s\n", rog_status_string(s));
+        ++failures;
+    } else {
+        CHECK_HIP(hipStreamSynchronize(st));
+        for (int t = 0; t < N; ++t) {
+            CHECK_HIP(hipMemcpy(got[t], dout[t], counts[t] * 2, hipMemcpyDeviceToHost));
+            if (memcmp(got[t], want[t], counts[t] * 2) != 0) {
+                fprintf(stderr, "FAIL reduce batch tensor %d\n", t);
+                ++failures;
+            }
+        }
+    }
+    for (int t = 0; t < N; ++t) {
+        for (int r = 0; r < W; ++r) {
+            CHECK_HIP(hipFree(d[t][r]));
+            free(h[t][r]);
+        }
+        CHECK_HIP(hipFree(dout[t]));
+        free(want[t]);
+        free(got[t]);
+    }
+}
+
 int main(void) {
     hipStream_t st;
     CHECK_HIP(hipStreamCreate(&st));
@@ -268,6 +324,7 @@ int main(void) {
                     reduce_case(rWs[w], counts[c], bf16, (size_t)c % 4, -1, paths[p], st);
                     if (rWs[w] > 1) reduce_case(rWs[w], counts[c], bf16, 0, rWs[w] - 1, paths[p], st);
                 }
+    reduce_batch_case(st);
     CHECK_HIP(hipStreamDestroy(st));
     printf("abi_c_check: %d failures; single-WG bound %zu bytes, max W %d\n", failures,
            rog_single_wg_max_bytes(), rog_max_peers());
