@@ -58,16 +58,15 @@ def bf16_random_bits(seed: int, stream: int, n_elems: int) -> np.ndarray:
 
 
 def bf16_uniform(seed: int, stream: int, n_elems: int) -> np.ndarray:
-    """n_elems bf16 values uniform in [-1, 1] (float32 rounded to nearest even), as bytes."""
+    """n_elems bf16 values uniform in [-1, 1] as bytes: float32 draws cut to their
+    top 16 bits (rounded toward zero; no rounding of either method here)."""
     rng = _rng(seed, stream)
     out = np.empty(n_elems, dtype=np.uint16)
     step = 1 << 24
     for lo in range(0, n_elems, step):
         hi = min(n_elems, lo + step)
         f = rng.random(hi - lo, dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
-        u = f.view(np.uint32)
-        u = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
-        out[lo:hi] = (u >> np.uint32(16)).astype(np.uint16)
+        out[lo:hi] = (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
     return out.view(np.uint8)
 
 
