@@ -34,6 +34,38 @@ __device__ __forceinline__ uint32_t uniform(uint32_t x) {
     return __builtin_amdgcn_readfirstlane(x);
 }
 
+// The low 32 bits of the 64-bit pair hi:lo shifted right by b = 0..3 bytes:
+// one v_alignbyte_b32 on the device, the same shift written out on the host
+// (where the CPU tests run it).
+__host__ __device__ inline uint32_t align_bytes(uint32_t hi, uint32_t lo, uint32_t b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_alignbyte(hi, lo, b);
+#else
+    return uint32_t(((uint64_t(hi) << 32) | lo) >> (8 * b));
+#endif
+}
+
+// Bytes [m, m + 16) of the 32 bytes lo then hi (little-endian), m = 0..15:
+// dword k joins dwords q + k and q + k + 1 (q = m / 4) shifted by m % 4 bytes.
+// m is wave-uniform in the kernels, so the switch is a scalar branch.
+__host__ __device__ inline vec16 cut16(vec16 lo, vec16 hi, uint32_t m) {
+    const uint32_t b = m & 3;
+    switch (m >> 2) {
+    case 0:
+        return vec16{align_bytes(lo.y, lo.x, b), align_bytes(lo.z, lo.y, b), align_bytes(lo.w, lo.z, b),
+                     align_bytes(hi.x, lo.w, b)};
+    case 1:
+        return vec16{align_bytes(lo.z, lo.y, b), align_bytes(lo.w, lo.z, b), align_bytes(hi.x, lo.w, b),
+                     align_bytes(hi.y, hi.x, b)};
+    case 2:
+        return vec16{align_bytes(lo.w, lo.z, b), align_bytes(hi.x, lo.w, b), align_bytes(hi.y, hi.x, b),
+                     align_bytes(hi.z, hi.y, b)};
+    default:
+        return vec16{align_bytes(hi.x, lo.w, b), align_bytes(hi.y, hi.x, b), align_bytes(hi.z, hi.y, b),
+                     align_bytes(hi.w, hi.z, b)};
+    }
+}
+
 // floor(v / d) by the host-built multiplier (exact for every 32-bit v).
 __device__ __forceinline__ uint32_t divide(uint32_t v, const Divider &d) {
     const uint32_t t = __umulhi(v, d.magic);

@@ -48,6 +48,9 @@ constexpr int kMaxBatchPtrs = 192;
 #ifndef ROG_XCD_RUN
 #define ROG_XCD_RUN 128
 #endif
+#ifndef ROG_PEER_SHIFT
+#define ROG_PEER_SHIFT 1
+#endif
 #ifndef ROG_GRID_CAP
 #define ROG_GRID_CAP (1u << 30)
 #endif
@@ -92,6 +95,13 @@ static_assert(kBodyAlign >= 16 && (kBodyAlign & (kBodyAlign - 1)) == 0, "body al
 // its neighbour, which then sits in the same L2).
 constexpr uint32_t kXcds = 8;
 constexpr uint32_t kXcdRun = ROG_XCD_RUN;
+// Multi-WG PEER body loads at a source misaligned by m = 1..15 bytes from its
+// 16-byte granule: 0 = one unaligned 16-byte load per lane; 1 = for m not a
+// multiple of 4, one aligned load per lane, the next granule taken from the
+// next lane and the 16 bytes cut out of the pair; 2 = the same for every m.
+// 1 measured best on 8 x 64 MiB: +2-4 % over 0 at odd and 2-mod-4 offsets,
+// equal at multiples of 4 (where 2 loses 1-2 %).
+constexpr int kPeerShift = ROG_PEER_SHIFT;
 
 // Exact floor(v / d) for every 32-bit v by one 32x32 high multiply:
 // t = mulhi(v, magic); q = (t + ((v - t) >> sh1)) >> sh2.

@@ -17,14 +17,17 @@
 //    boundary walks the few payloads it touches with per-lane range masks.
 //  * PEER kernel (anything else): each payload on its own -- a byte head up to
 //    a 256-byte boundary of its destination, a body of aligned 16-byte stores,
-//    a byte tail.  Every body store is fed by one 16-byte load from the source
-//    at the same payload offset, at whatever byte alignment the source has
-//    (gfx950 global loads run in unaligned-access mode under the HSA runtime:
-//    still one global_load_dwordx4).  The pages' fallback copies such payloads
-//    byte by byte ("vectors where aligned, byte-wise tail"); the bytes written
-//    are the same.  Multi-WG, the body is cut into 1 KiB chunks, one wave per
-//    chunk, all payloads at once; single-WG, the one workgroup takes the
-//    payloads in turn.
+//    a byte tail.  Every body store takes the 16 source bytes at the same
+//    payload offset, whatever byte alignment the source has.  At a multiple of
+//    4 bytes that is one unaligned global_load_dwordx4 (gfx950 global loads
+//    run in unaligned-access mode under the HSA runtime).  Otherwise the
+//    multi-WG lanes load aligned granules and rebuild their bytes from their
+//    own granule and the next lane's (a lane shuffle and v_alignbyte), which
+//    streams faster than split unaligned loads.  The pages' fallback copies
+//    such payloads byte by byte ("vectors where aligned, byte-wise tail"); the
+//    bytes written are the same.  Multi-WG, the body is cut into 1 KiB chunks,
+//    one wave per chunk, all payloads at once; single-WG, the one workgroup
+//    takes the payloads in turn.
 //  * BATCH kernel (rog_gather_many): one launch; every wave finds its tensor by
 //    a scalar binary search over the tensors' first chunks and does one FLAT
 //    or PEER chunk of that tensor.
@@ -112,6 +115,14 @@ __device__ __forceinline__ void flat_copy(const void *const *src, void *out, uin
 
 // One wave: body chunk j (body vectors [64j, 64j + 64)); chunk 0 also moves the
 // head and tail bytes (at most kBodyAlign - 1 and 15 of them).
+//
+// Body source bytes sit m = (s + lo) % 16 bytes past a 16-byte granule, the
+// same m for every lane.  Unless kPeerShift takes this m, each lane reads its
+// 16 bytes with one unaligned load.  Otherwise each lane loads the aligned
+// granule g holding its first byte; the granule after g is the next lane's
+// g, passed across by a lane shuffle, and only the last lane of the wave or
+// of the body loads it itself.  Every granule read holds at least one byte
+// of the payload, so it lies in the payload's pages.
 template <bool NTL>
 __device__ __forceinline__ void peer_chunk(const uint8_t *s, uint8_t *d, uint64_t S, uint32_t j) {
     const uint32_t lane = __lane_id();
@@ -121,7 +132,22 @@ __device__ __forceinline__ void peer_chunk(const uint8_t *s, uint8_t *d, uint64_
         for (uint64_t i = cut.hi + lane; i < S; i += 64) d[i] = s[i];
     }
     const uint64_t off = cut.lo + 16 * (uint64_t(j) * 64 + lane);
-    if (off < cut.hi) st16(reinterpret_cast<vec16 *>(d + off), ldu16<NTL>(s + off));
+    const bool live = off < cut.hi;
+    const uint32_t m = uniform(uint32_t(reinterpret_cast<uintptr_t>(s + cut.lo)) & 15);
+    const bool shift = kPeerShift == 2 ? m != 0 : (kPeerShift == 1 && (m & 3) != 0);
+    if (!shift) {
+        if (live) st16(reinterpret_cast<vec16 *>(d + off), ldu16<NTL>(s + off));
+        return;
+    }
+    const vec16 *g = reinterpret_cast<const vec16 *>(s + off - m);
+    const bool own_hi = live && (lane == 63 || off + 16 >= cut.hi);
+    vec16 lo = vec16{0, 0, 0, 0}, hi = lo;
+    if (live) lo = ld16<NTL>(g);
+    if (own_hi) hi = ld16<NTL>(g + 1);  // in flight beside lo
+    // Lane l + 1's granule; all 64 lanes take part in the shuffle.
+    const vec16 next = vec16{__shfl_down(lo.x, 1u), __shfl_down(lo.y, 1u), __shfl_down(lo.z, 1u),
+                             __shfl_down(lo.w, 1u)};
+    if (live) st16(reinterpret_cast<vec16 *>(d + off), cut16(lo, own_hi ? hi : next, m));
 }
 
 // One workgroup of nt threads, the whole payload: head and tail bytes, then the

@@ -17,3 +17,17 @@ extern "C" void rog_test_xcd_grouped(uint32_t n, uint32_t *out) {
 }
 
 extern "C" uint32_t rog_test_xcd_run(void) { return rog::kXcdRun; }
+
+// The PEER body's byte-window cut (cut16 in csrc/rog_device.h): bytes
+// [m, m + 16) of the 32 bytes lo then hi.
+#include "rog_device.h"
+
+extern "C" void rog_test_cut16(const uint8_t *lo16, const uint8_t *hi16, uint32_t m, uint8_t *out16) {
+    rog::vec16 lo, hi;
+    __builtin_memcpy(&lo, lo16, 16);
+    __builtin_memcpy(&hi, hi16, 16);
+    const rog::vec16 v = rog::cut16(lo, hi, m);
+    __builtin_memcpy(out16, &v, 16);
+}
+
+extern "C" int rog_test_peer_shift(void) { return rog::kPeerShift; }

@@ -127,3 +127,44 @@ def test_xcd_grouping_is_a_bijection_with_runs(xcd):
             x, k = b % 8, b // 8
             assert np.array_equal(m[:full], (k // R) * span + x * R + k % R)
         assert np.array_equal(m[full:], np.arange(full, n, dtype=np.uint32)), n
+
+
+# ---------------------------------------------------------------------------
+# Byte-window cut of the PEER body (misaligned sources)
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def cut16(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or os.path.join(b.ROCM, "bin", "hipcc")
+    so = str(tmp_path_factory.mktemp("cut16") / "libcut16.so")
+    subprocess.check_call([hipcc, "-x", "hip", "-O2", "-std=c++17", "-fPIC", "-shared",
+                           "--offload-arch=gfx950", "-Wno-unused-command-line-argument",
+                           "-I", b.INCLUDE, "-I", b.CSRC, os.path.join(HERE, "split_shim.cpp"), "-o", so],
+                          stderr=subprocess.DEVNULL)
+    lib = ctypes.CDLL(so)
+    lib.rog_test_cut16.argtypes = [ctypes.c_char_p, ctypes.c_char_p, ctypes.c_uint32, ctypes.c_void_p]
+    out = ctypes.create_string_buffer(16)
+
+    def f(window, m):
+        lib.rog_test_cut16(bytes(window[:16]), bytes(window[16:]), m, out)
+        return out.raw
+    f.shift = int(lib.rog_test_peer_shift())
+    return f
+
+
+def test_cut16_takes_bytes_m_to_m_plus_16(cut16):
+    """For every shift m the cut returns bytes [m, m + 16) of the 32-byte pair:
+    the unaligned payload bytes a lane stores, rebuilt from two aligned granules."""
+    import random
+    rng = random.Random(7)
+    for m in range(16):
+        for _ in range(50):
+            w = bytes(rng.randrange(256) for _ in range(32))
+            assert cut16(w, m) == w[m:m + 16], m
+        # distinct bytes: a swapped or repeated dword would show
+        w = bytes(range(32))
+        assert cut16(w, m) == w[m:m + 16], m
+
+
+def test_peer_shift_mode_is_a_known_one(cut16):
+    assert cut16.shift in (0, 1, 2)
