@@ -51,6 +51,9 @@ constexpr int kMaxBatchPtrs = 192;
 #ifndef ROG_PEER_SHIFT
 #define ROG_PEER_SHIFT 1
 #endif
+#ifndef ROG_REDUCE_SHIFT
+#define ROG_REDUCE_SHIFT 2
+#endif
 #ifndef ROG_GRID_CAP
 #define ROG_GRID_CAP (1u << 30)
 #endif
@@ -102,6 +105,18 @@ constexpr uint32_t kXcdRun = ROG_XCD_RUN;
 // 1 measured best on 8 x 64 MiB: +2-4 % over 0 at odd and 2-mod-4 offsets,
 // equal at multiples of 4 (where 2 loses 1-2 %).
 constexpr int kPeerShift = ROG_PEER_SHIFT;
+// The same choice for the multi-WG rank-ordered sum's body loads (same modes).
+// 2 measured best on W = 8 bf16 x 32 Mi elements: +16-19 % over 0 at 2-mod-4
+// sources, +3-4 % at multiples of 4 (eight unaligned streams at once cost
+// more than the one of a gather), equal when aligned.
+constexpr int kReduceShift = ROG_REDUCE_SHIFT;
+
+// Whether a body whose source bytes sit m = 0..15 bytes past a 16-byte
+// granule is read as aligned granules shared between neighbouring lanes,
+// under mode 0, 1 or 2 above.
+__host__ __device__ inline bool shift_granules(uint32_t m, int mode) {
+    return mode == 2 ? m != 0 : (mode == 1 && (m & 3) != 0);
+}
 
 // Exact floor(v / d) for every 32-bit v by one 32x32 high multiply:
 // t = mulhi(v, magic); q = (t + ((v - t) >> sh1)) >> sh2.
@@ -258,9 +273,10 @@ rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype d
                        const void *out, rog_path path, Plan *plan);
 
 // Validate and plan a batch of rank-ordered sums (no HIP calls).  grid == 0
-// means nothing to launch.
+// means nothing to launch.  *shifted: some tensor's body is read as shared
+// aligned granules (the launch takes the kernel that can).
 rog_status plan_reduce_batch(const rog_reduce_desc *descs, int n, int W, rog_dtype dtype,
-                             ReduceBatchArgs *args, uint32_t *grid, bool *nt_loads);
+                             ReduceBatchArgs *args, uint32_t *grid, bool *nt_loads, bool *shifted);
 
 // Validate and plan a batch (no HIP calls).  grid == 0 means nothing to launch.
 // *nt_loads: the launch streams its loads past the caches.

@@ -134,8 +134,7 @@ __device__ __forceinline__ void peer_chunk(const uint8_t *s, uint8_t *d, uint64_
     const uint64_t off = cut.lo + 16 * (uint64_t(j) * 64 + lane);
     const bool live = off < cut.hi;
     const uint32_t m = uniform(uint32_t(reinterpret_cast<uintptr_t>(s + cut.lo)) & 15);
-    const bool shift = kPeerShift == 2 ? m != 0 : (kPeerShift == 1 && (m & 3) != 0);
-    if (!shift) {
+    if (!shift_granules(m, kPeerShift)) {
         if (live) st16(reinterpret_cast<vec16 *>(d + off), ldu16<NTL>(s + off));
         return;
     }

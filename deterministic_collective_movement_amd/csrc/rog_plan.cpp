@@ -119,6 +119,14 @@ uint32_t flat_single_block(uint64_t n_vec) {
     return round_up_64(ceil_div(n_vec, 64 * uint64_t(single_flat_unroll(n_vec))) * 64);
 }
 
+// Whether the multi-WG body of a payload of S bytes from src to the output
+// address d is read as shared aligned granules (mode as kPeerShift).
+bool shifted_body(const void *src, uint64_t d, uint64_t S, int mode) {
+    const PeerSplit cut = split_payload(d, S);
+    if (cut.hi == cut.lo) return false;
+    return shift_granules(uint32_t(addr(src) + cut.lo) & 15, mode);
+}
+
 // Single-WG PEER workgroup: enough threads for one tile of the largest payload.
 uint32_t peer_single_block(size_t S) {
     return round_up_64(ceil_div(S / 16, kSinglePeerUnroll));
@@ -180,6 +188,9 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
             a.cdiv = make_divider(a.chunks_per_peer);
             info.block = kWaveBlock;
             info.grid = std::min(a.n_chunks, max_grid(kWaveBlock));
+            for (int r = 0; r < W; ++r)
+                if (shifted_body(srcs[r], addr(out) + uint64_t(r) * S, S, kPeerShift))
+                    info.flags |= ROG_PLAN_SHIFTED_LOADS;
         }
     }
     return ROG_OK;
@@ -266,14 +277,17 @@ rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype d
         a.n_chunks = reduce_chunks(bytes);
         info.block = kWaveBlock;
         info.grid = std::min(a.n_chunks, max_grid(kWaveBlock));
+        for (int r = 0; r < W; ++r)
+            if (shifted_body(srcs[r], addr(out), bytes, kReduceShift)) info.flags |= ROG_PLAN_SHIFTED_LOADS;
     }
     return ROG_OK;
 }
 
 rog_status plan_reduce_batch(const rog_reduce_desc *descs, int n, int W, rog_dtype dtype,
-                             ReduceBatchArgs *args, uint32_t *grid, bool *nt_loads) {
+                             ReduceBatchArgs *args, uint32_t *grid, bool *nt_loads, bool *shifted) {
     *grid = 0;
     *nt_loads = false;
+    *shifted = false;
     if (n < 0 || W < 1 || W > kMaxPeers || !dtype_ok(dtype)) return ROG_ERR_INVALID_ARGUMENT;
     if (n > 0 && !descs) return ROG_ERR_INVALID_ARGUMENT;
     if (n > kMaxBatch || n * W > kMaxBatchPtrs) return ROG_ERR_TOO_LARGE;
@@ -307,6 +321,8 @@ rog_status plan_reduce_batch(const rog_reduce_desc *descs, int n, int W, rog_dty
         rt.count = descs[t].count;
         rt.first_chunk = uint32_t(next);
         rt.n_chunks = reduce_chunks(bytes[t]);
+        for (int r = 0; r < W; ++r)
+            if (shifted_body(descs[t].srcs[r], rt.out, bytes[t], kReduceShift)) *shifted = true;
         next += rt.n_chunks;
         source_bytes += uint64_t(W) * bytes[t];
         ++k;

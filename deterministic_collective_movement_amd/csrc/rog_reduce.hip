@@ -12,10 +12,13 @@
 //
 // The output is cut like a PEER payload (split_payload): an element head up to
 // the first 256-byte boundary of out, a body of 16-byte vectors, an element
-// tail.  A body lane loads the 16 bytes at the same offset of every source --
-// one global_load_dwordx4 each, at whatever element alignment the source has --
+// tail.  A body lane loads the 16 bytes at the same offset of every source,
 // with up to 8 loads in flight, accumulates them in rank order and stores one
-// aligned 16-byte vector.  Multi-WG: one wave per 1 KiB chunk of the body,
+// aligned 16-byte vector.  An aligned source takes one global_load_dwordx4 per
+// lane; where the plan finds a misaligned source (ROG_PLAN_SHIFTED_LOADS), the
+// launch takes the kernel form that reads such sources as aligned granules,
+// each lane rebuilding its bytes from its own granule and the next lane's, as
+// the PEER gather does.  Multi-WG: one wave per 1 KiB chunk of the body,
 // chunks handed to the XCDs in runs (xcd_grouped); single-WG: one workgroup
 // strides over the whole output; batch (rog_reduce_many): every tensor's
 // chunks in one launch.  Bandwidth bound: (W + 1) * count * esize bytes per
@@ -125,6 +128,64 @@ __device__ __forceinline__ vec16 sum_vec(const void *const *src, uint32_t W, uin
     return narrow<DT>(acc);
 }
 
+// sum_vec for a whole wave of a multi-WG chunk whose plan found a source read
+// as shared granules (shift_granules under kReduceShift, the PEER gather's
+// scheme): every lane calls it, since the shuffle needs all 64; `live` lanes
+// own a body vector at byte offset off; `own_hi` lanes (lane 63 and the body's
+// last lane) load the granule after their own themselves.  body is the body's
+// first byte offset: source r's bytes sit m_r = (src_r + body) % 16 bytes past
+// a granule in every lane.  Sources that are not shifted keep the unaligned
+// load.  This form holds twice the loaded registers of sum_vec, so the plan
+// takes it only where a source needs it.
+template <int DT, bool NTL>
+__device__ __forceinline__ vec16 sum_vec_wave(const void *const *src, uint32_t W, uint64_t off, uint64_t body,
+                                              bool live, bool own_hi) {
+    constexpr int E = Elem<DT>::kPerVec;
+    float acc[E];
+    for (uint32_t r0 = 0; r0 < W; r0 += kGroup) {
+        const uint32_t g = min(W - r0, kGroup);
+        vec16 v[kGroup], h[kGroup];
+#pragma unroll
+        for (uint32_t q = 0; q < kGroup; ++q) {
+            if (q < g) {
+                const uint8_t *s = static_cast<const uint8_t *>(src[r0 + q]);
+                const uint32_t m = uniform(uint32_t(reinterpret_cast<uintptr_t>(s) + body) & 15);
+                v[q] = h[q] = vec16{0, 0, 0, 0};
+                if (shift_granules(m, kReduceShift)) {
+                    const vec16 *gp = reinterpret_cast<const vec16 *>(s + off - m);
+                    if (live) v[q] = ld16<NTL>(gp);
+                    if (own_hi) h[q] = ld16<NTL>(gp + 1);
+                } else if (live) {
+                    v[q] = ldu16<NTL>(s + off);
+                }
+            }
+        }
+#pragma unroll
+        for (uint32_t q = 0; q < kGroup; ++q) {
+            if (q < g) {
+                const uint32_t m =
+                    uniform(uint32_t(reinterpret_cast<uintptr_t>(src[r0 + q]) + body) & 15);
+                vec16 w = v[q];
+                if (shift_granules(m, kReduceShift)) {
+                    const vec16 next = vec16{__shfl_down(w.x, 1u), __shfl_down(w.y, 1u), __shfl_down(w.z, 1u),
+                                             __shfl_down(w.w, 1u)};
+                    w = cut16(w, own_hi ? h[q] : next, m);
+                }
+                float x[E];
+                widen<DT>(w, x);
+                if (r0 + q == 0) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[e] = x[e];       // the first term as it is
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[e] += x[e];
+                }
+            }
+        }
+    }
+    return narrow<DT>(acc);
+}
+
 template <int DT>
 __device__ __forceinline__ float load_elem(const void *p, uint64_t i) {
     if constexpr (Elem<DT>::kHalf) {
@@ -146,8 +207,9 @@ __device__ __forceinline__ void sum_elem(const void *const *src, uint32_t W, uin
 }
 
 // One wave: body chunk j (body vectors [64j, 64j + 64)) of a sum of `count`
-// elements into out; chunk 0 also sums the head and tail elements.
-template <int DT, bool NTL>
+// elements into out; chunk 0 also sums the head and tail elements.  SH: the
+// launch holds a source read as shared granules.
+template <int DT, bool NTL, bool SH>
 __device__ __forceinline__ void sum_chunk(const void *const *src, uint32_t W, void *out, uint64_t count,
                                           uint32_t j) {
     const uint32_t lane = __lane_id();
@@ -157,21 +219,27 @@ __device__ __forceinline__ void sum_chunk(const void *const *src, uint32_t W, vo
         for (uint64_t i = cut.hi / Elem<DT>::kSize + lane; i < count; i += 64) sum_elem<DT>(src, W, i, out);
     }
     const uint64_t off = cut.lo + 16 * (uint64_t(j) * 64 + lane);
-    if (off < cut.hi)
+    const bool live = off < cut.hi;
+    if constexpr (SH) {
+        const bool own_hi = live && (lane == 63 || off + 16 >= cut.hi);
+        const vec16 v = sum_vec_wave<DT, NTL>(src, W, off, cut.lo, live, own_hi);
+        if (live) st16(reinterpret_cast<vec16 *>(static_cast<uint8_t *>(out) + off), v);
+    } else if (live) {
         st16(reinterpret_cast<vec16 *>(static_cast<uint8_t *>(out) + off), sum_vec<DT, NTL>(src, W, off));
+    }
 }
 
 // Multi-WG: one wave per workgroup and per 1 KiB chunk of the body, chunks
 // handed to the XCDs in runs, grid-strided over a capped grid.
-template <int DT, bool NTL>
+template <int DT, bool NTL, bool SH>
 __global__ __launch_bounds__(kWaveBlock) void rog_reduce_kernel(ReduceArgs a) {
     for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x)
-        sum_chunk<DT, NTL>(a.src, a.W, a.out, a.count, ROG_REDUCE_XCD ? xcd_grouped(vb, a.n_chunks) : vb);
+        sum_chunk<DT, NTL, SH>(a.src, a.W, a.out, a.count, ROG_REDUCE_XCD ? xcd_grouped(vb, a.n_chunks) : vb);
 }
 
 // Batch: the tensors' chunks laid end to end; a wave finds its tensor by a
 // scalar binary search over the tensors' first chunks.
-template <int DT, bool NTL>
+template <int DT, bool NTL, bool SH>
 __global__ __launch_bounds__(kWaveBlock) void rog_reduce_batch_kernel(ReduceBatchArgs a) {
     for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x) {
         const uint32_t c = ROG_REDUCE_XCD ? xcd_grouped(vb, a.n_chunks) : vb;
@@ -182,7 +250,7 @@ __global__ __launch_bounds__(kWaveBlock) void rog_reduce_batch_kernel(ReduceBatc
             else hi = mid;
         }
         const ReduceTensor &t = a.t[lo];
-        sum_chunk<DT, NTL>(a.src + lo * a.W, a.W, reinterpret_cast<void *>(t.out), t.count, c - t.first_chunk);
+        sum_chunk<DT, NTL, SH>(a.src + lo * a.W, a.W, reinterpret_cast<void *>(t.out), t.count, c - t.first_chunk);
     }
 }
 
@@ -203,9 +271,10 @@ template <typename K>
 const void *kfn(K *k) { return reinterpret_cast<const void *>(k); }
 
 template <int DT>
-const void *reduce_kernel(bool single, bool ntl) {
+const void *reduce_kernel(bool single, bool ntl, bool sh) {
     if (single) return ntl ? kfn(&rog_reduce_single_kernel<DT, true>) : kfn(&rog_reduce_single_kernel<DT, false>);
-    return ntl ? kfn(&rog_reduce_kernel<DT, true>) : kfn(&rog_reduce_kernel<DT, false>);
+    if (sh) return ntl ? kfn(&rog_reduce_kernel<DT, true, true>) : kfn(&rog_reduce_kernel<DT, false, true>);
+    return ntl ? kfn(&rog_reduce_kernel<DT, true, false>) : kfn(&rog_reduce_kernel<DT, false, false>);
 }
 
 rog_status launch_reduce(Plan &p, hipStream_t stream) {
@@ -213,9 +282,10 @@ rog_status launch_reduce(Plan &p, hipStream_t stream) {
     if (i.kernel == ROG_KERNEL_NONE) return ROG_OK;
     const bool single = i.path == ROG_PATH_SINGLE_WG;
     const bool ntl = (i.flags & ROG_PLAN_NT_LOADS) != 0;
-    const void *k = p.dtype == ROG_DTYPE_BF16  ? reduce_kernel<ROG_DTYPE_BF16>(single, ntl)
-                    : p.dtype == ROG_DTYPE_F16 ? reduce_kernel<ROG_DTYPE_F16>(single, ntl)
-                                               : reduce_kernel<ROG_DTYPE_F32>(single, ntl);
+    const bool sh = (i.flags & ROG_PLAN_SHIFTED_LOADS) != 0;
+    const void *k = p.dtype == ROG_DTYPE_BF16  ? reduce_kernel<ROG_DTYPE_BF16>(single, ntl, sh)
+                    : p.dtype == ROG_DTYPE_F16 ? reduce_kernel<ROG_DTYPE_F16>(single, ntl, sh)
+                                               : reduce_kernel<ROG_DTYPE_F32>(single, ntl, sh);
     void *params[] = {&p.reduce};
     const hipError_t e = hipLaunchKernel(k, dim3(i.grid), dim3(i.block), params, 0, stream);
     if (e != hipSuccess) {
@@ -226,8 +296,9 @@ rog_status launch_reduce(Plan &p, hipStream_t stream) {
 }
 
 template <int DT>
-const void *reduce_batch_kernel(bool ntl) {
-    return ntl ? kfn(&rog_reduce_batch_kernel<DT, true>) : kfn(&rog_reduce_batch_kernel<DT, false>);
+const void *reduce_batch_kernel(bool ntl, bool sh) {
+    if (sh) return ntl ? kfn(&rog_reduce_batch_kernel<DT, true, true>) : kfn(&rog_reduce_batch_kernel<DT, false, true>);
+    return ntl ? kfn(&rog_reduce_batch_kernel<DT, true, false>) : kfn(&rog_reduce_batch_kernel<DT, false, false>);
 }
 
 }  // namespace
@@ -266,12 +337,12 @@ ROG_API rog_status rog_reduce_many(const rog_reduce_desc *descs, int n, int W, r
                                    hipStream_t stream) {
     rog::ReduceBatchArgs args;
     uint32_t grid = 0;
-    bool ntl = false;
-    const rog_status st = rog::plan_reduce_batch(descs, n, W, dtype, &args, &grid, &ntl);
+    bool ntl = false, sh = false;
+    const rog_status st = rog::plan_reduce_batch(descs, n, W, dtype, &args, &grid, &ntl, &sh);
     if (st != ROG_OK || grid == 0) return st;
-    const void *k = dtype == ROG_DTYPE_BF16  ? rog::reduce_batch_kernel<ROG_DTYPE_BF16>(ntl)
-                    : dtype == ROG_DTYPE_F16 ? rog::reduce_batch_kernel<ROG_DTYPE_F16>(ntl)
-                                             : rog::reduce_batch_kernel<ROG_DTYPE_F32>(ntl);
+    const void *k = dtype == ROG_DTYPE_BF16  ? rog::reduce_batch_kernel<ROG_DTYPE_BF16>(ntl, sh)
+                    : dtype == ROG_DTYPE_F16 ? rog::reduce_batch_kernel<ROG_DTYPE_F16>(ntl, sh)
+                                             : rog::reduce_batch_kernel<ROG_DTYPE_F32>(ntl, sh);
     void *params[] = {&args};
     const hipError_t e = hipLaunchKernel(k, dim3(grid), dim3(rog::kWaveBlock), params, 0, stream);
     if (e != hipSuccess) {

@@ -51,6 +51,7 @@ ROG_PATH_SINGLE_WG = 1
 ROG_PATH_MULTI_WG = 2
 
 ROG_PLAN_NT_LOADS = 1
+ROG_PLAN_SHIFTED_LOADS = 2
 
 ROG_KERNEL_NONE = 0
 ROG_KERNEL_FLAT = 1
@@ -236,7 +237,8 @@ def _plan_dict(info) -> dict:
     return {"path": PATH_NAMES[info.path], "kernel": KERNEL_NAMES[info.kernel],
             "grid": info.grid, "block": info.block, "vec_ok_mask": info.vec_ok_mask,
             "units": info.units, "peer_magic": info.peer_magic, "peer_sh1": info.peer_sh1,
-            "peer_sh2": info.peer_sh2, "nt_loads": bool(info.flags & ROG_PLAN_NT_LOADS)}
+            "peer_sh2": info.peer_sh2, "nt_loads": bool(info.flags & ROG_PLAN_NT_LOADS),
+            "shifted_loads": bool(info.flags & ROG_PLAN_SHIFTED_LOADS)}
 
 
 def rog_reduce_ptrs(src_ptrs: Sequence[int], count: int, dtype: int, out_ptr: int,

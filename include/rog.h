@@ -112,6 +112,13 @@ typedef struct {
  * past the caches); set when the W*S source bytes are too many to stay in the
  * 256 MB Infinity Cache.  Stores are always non-temporal.  Affects speed only. */
 #define ROG_PLAN_NT_LOADS 1u
+/* rog_plan_info.flags: the multi-workgroup PEER or REDUCE kernel reads at least
+ * one source body as aligned 16-byte granules, each lane taking the granule
+ * after its own from the next lane.  Set when the body (from the first
+ * 256-byte boundary of the payload's output) is not empty and a source sits m
+ * bytes past a 16-byte granule there, with m odd or 2 mod 4 (PEER) or m != 0
+ * (REDUCE).  Affects speed only; the bytes are the same. */
+#define ROG_PLAN_SHIFTED_LOADS 2u
 
 /*
  * rog_gather -- out[r*S + i] = srcs[r][i] for r < W, i < S, enqueued on `stream`.
