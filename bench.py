@@ -494,9 +494,32 @@ def reduce_bandwidth(torch, rog, wl, device, steps, warmup):
            "p50_us": round(1e3 * statistics.median(per_call), 2),
            "GBps": round(gbps(moved * steps, region_ms), 1),
            "pct_of_peak": round(100 * gbps(moved * steps, region_ms) / PEAK_HBM_GBPS, 2)}
+    big["misaligned"] = reduce_misaligned(torch, rog, srcs, out, stream, steps, warmup)
     del srcs, out
     torch.cuda.empty_cache()
     return big, payloads, got
+
+
+def reduce_misaligned(torch, rog, srcs, aligned_out, stream, steps, warmup, in_off=1, out_off=0):
+    """The same sum with every source at element offset ``in_off`` of its own
+    buffer and the output at element offset ``out_off``: 2-byte source shifts,
+    read as aligned granules shared between lanes.  Its output must equal the
+    aligned sum's bit for bit."""
+    n = aligned_out.numel()
+    views = []
+    for s in srcs:
+        buf = torch.empty(in_off + n, dtype=s.dtype, device=s.device)
+        buf[in_off:].copy_(s)
+        views.append(buf[in_off:])
+    obuf = torch.empty(out_off + n, dtype=aligned_out.dtype, device=aligned_out.device)
+    out = obuf[out_off:]
+    plan = rog.rog_reduce_plan(views, out)
+    region_ms = time_region(torch, ReduceCall(rog, views, out, stream), steps, warmup)
+    if not torch.equal(out.view(torch.int16), aligned_out.view(torch.int16)):
+        raise AssertionError("the misaligned sum differs from the aligned one")
+    moved = (len(srcs) + 1) * n * out.element_size()
+    return {"src_elem_offset": in_off, "out_elem_offset": out_off, "shifted_loads": plan["shifted_loads"],
+            "GBps": round(gbps(moved * steps, region_ms), 1), "mean_launch_us": round(1e3 * region_ms / steps, 2)}
 
 
 def reduce_cpu_baseline(payloads, got, budget_s, sample=1 << 22):
