@@ -52,7 +52,7 @@ constexpr int kMaxBatchPtrs = 192;
 #define ROG_PEER_SHIFT 1
 #endif
 #ifndef ROG_REDUCE_SHIFT
-#define ROG_REDUCE_SHIFT 2
+#define ROG_REDUCE_SHIFT 1
 #endif
 #ifndef ROG_GRID_CAP
 #define ROG_GRID_CAP (1u << 30)
@@ -98,17 +98,23 @@ static_assert(kBodyAlign >= 16 && (kBodyAlign & (kBodyAlign - 1)) == 0, "body al
 // its neighbour, which then sits in the same L2).
 constexpr uint32_t kXcds = 8;
 constexpr uint32_t kXcdRun = ROG_XCD_RUN;
-// Multi-WG PEER body loads at a source misaligned by m = 1..15 bytes from its
-// 16-byte granule: 0 = one unaligned 16-byte load per lane; 1 = for m not a
-// multiple of 4, one aligned load per lane, the next granule taken from the
-// next lane and the 16 bytes cut out of the pair; 2 = the same for every m.
-// 1 measured best on 8 x 64 MiB: +2-4 % over 0 at odd and 2-mod-4 offsets,
-// equal at multiples of 4 (where 2 loses 1-2 %).
+// Multi-WG PEER body loads, where the loads stream past the caches, at a
+// source misaligned by m = 1..15 bytes from its 16-byte granule: 0 = one
+// unaligned 16-byte load per lane; 1 = for m not a multiple of 4, one aligned
+// load per lane, the next granule taken from the next lane and the 16 bytes
+// cut out of the pair; 2 = the same for every m.  1 measured best on
+// 8 x 64 MiB: +2-4 % over 0 at odd and 2-mod-4 offsets, equal at multiples of
+// 4 (where 2 loses 1-2 %).  With cached loads (2 or 4 x 64 MiB) unaligned
+// loads win at every offset (+7 %), so the kernel keeps them there.
 constexpr int kPeerShift = ROG_PEER_SHIFT;
-// The same choice for the multi-WG rank-ordered sum's body loads (same modes).
-// 2 measured best on W = 8 bf16 x 32 Mi elements: +16-19 % over 0 at 2-mod-4
-// sources, +3-4 % at multiples of 4 (eight unaligned streams at once cost
-// more than the one of a gather), equal when aligned.
+// When the multi-WG rank-ordered sum reads every source as shared granules
+// (its granule form) instead of one unaligned 16-byte load per lane and
+// source: 0 never; 1 whenever the launch streams its loads past the caches
+// (ROG_PLAN_NT_LOADS), whatever the alignment.  Measured on MI355X: with
+// streamed loads (W = 8 x 64 MiB) the granule form runs 6.55-6.6 TB/s aligned
+// or misaligned, against 6.2-6.3 aligned and 5.4-6.0 misaligned for unaligned
+// loads; with cached loads (W = 2-4 x 64 MiB, 8 x 8 MiB) the unaligned loads
+// are as fast or faster at every offset (up to +20 %).
 constexpr int kReduceShift = ROG_REDUCE_SHIFT;
 
 // Whether a body whose source bytes sit m = 0..15 bytes past a 16-byte

@@ -117,11 +117,13 @@ __device__ __forceinline__ void flat_copy(const void *const *src, void *out, uin
 // head and tail bytes (at most kBodyAlign - 1 and 15 of them).
 //
 // Body source bytes sit m = (s + lo) % 16 bytes past a 16-byte granule, the
-// same m for every lane.  Unless kPeerShift takes this m, each lane reads its
-// 16 bytes with one unaligned load.  Otherwise each lane loads the aligned
+// same m for every lane.  Unless the loads stream past the caches (NTL) and
+// kPeerShift takes this m, each lane reads its 16 bytes with one unaligned
+// load.  Otherwise each lane loads the aligned
 // granule g holding its first byte; the granule after g is the next lane's
 // g, passed across by a lane shuffle, and only the last lane of the wave or
-// of the body loads it itself.  Every granule read holds at least one byte
+// of the body loads it itself (a cached load: that granule is the next
+// chunk's first).  Every granule read holds at least one byte
 // of the payload, so it lies in the payload's pages.
 template <bool NTL>
 __device__ __forceinline__ void peer_chunk(const uint8_t *s, uint8_t *d, uint64_t S, uint32_t j) {
@@ -134,15 +136,17 @@ __device__ __forceinline__ void peer_chunk(const uint8_t *s, uint8_t *d, uint64_
     const uint64_t off = cut.lo + 16 * (uint64_t(j) * 64 + lane);
     const bool live = off < cut.hi;
     const uint32_t m = uniform(uint32_t(reinterpret_cast<uintptr_t>(s + cut.lo)) & 15);
-    if (!shift_granules(m, kPeerShift)) {
+    if (!NTL || !shift_granules(m, kPeerShift)) {
         if (live) st16(reinterpret_cast<vec16 *>(d + off), ldu16<NTL>(s + off));
         return;
     }
     const vec16 *g = reinterpret_cast<const vec16 *>(s + off - m);
-    const bool own_hi = live && (lane == 63 || off + 16 >= cut.hi);
+    // The granule after the body's end is read only if it holds payload bytes
+    // (m != 0); the last lane of a wave inside the body always may.
+    const bool own_hi = live && (lane == 63 || off + 16 >= cut.hi) && (m != 0 || off + 16 < cut.hi);
     vec16 lo = vec16{0, 0, 0, 0}, hi = lo;
     if (live) lo = ld16<NTL>(g);
-    if (own_hi) hi = ld16<NTL>(g + 1);  // in flight beside lo
+    if (own_hi) hi = ld16<false>(g + 1);  // cached; in flight beside lo
     // Lane l + 1's granule; all 64 lanes take part in the shuffle.
     const vec16 next = vec16{__shfl_down(lo.x, 1u), __shfl_down(lo.y, 1u), __shfl_down(lo.z, 1u),
                              __shfl_down(lo.w, 1u)};

@@ -188,9 +188,10 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
             a.cdiv = make_divider(a.chunks_per_peer);
             info.block = kWaveBlock;
             info.grid = std::min(a.n_chunks, max_grid(kWaveBlock));
-            for (int r = 0; r < W; ++r)
-                if (shifted_body(srcs[r], addr(out) + uint64_t(r) * S, S, kPeerShift))
-                    info.flags |= ROG_PLAN_SHIFTED_LOADS;
+            if (info.flags & ROG_PLAN_NT_LOADS)
+                for (int r = 0; r < W; ++r)
+                    if (shifted_body(srcs[r], addr(out) + uint64_t(r) * S, S, kPeerShift))
+                        info.flags |= ROG_PLAN_SHIFTED_LOADS;
         }
     }
     return ROG_OK;
@@ -277,8 +278,8 @@ rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype d
         a.n_chunks = reduce_chunks(bytes);
         info.block = kWaveBlock;
         info.grid = std::min(a.n_chunks, max_grid(kWaveBlock));
-        for (int r = 0; r < W; ++r)
-            if (shifted_body(srcs[r], addr(out), bytes, kReduceShift)) info.flags |= ROG_PLAN_SHIFTED_LOADS;
+        // The granule form where loads stream past the caches (kReduceShift).
+        if (kReduceShift == 1 && (info.flags & ROG_PLAN_NT_LOADS)) info.flags |= ROG_PLAN_SHIFTED_LOADS;
     }
     return ROG_OK;
 }
@@ -321,8 +322,6 @@ rog_status plan_reduce_batch(const rog_reduce_desc *descs, int n, int W, rog_dty
         rt.count = descs[t].count;
         rt.first_chunk = uint32_t(next);
         rt.n_chunks = reduce_chunks(bytes[t]);
-        for (int r = 0; r < W; ++r)
-            if (shifted_body(descs[t].srcs[r], rt.out, bytes[t], kReduceShift)) *shifted = true;
         next += rt.n_chunks;
         source_bytes += uint64_t(W) * bytes[t];
         ++k;
@@ -331,6 +330,7 @@ rog_status plan_reduce_batch(const rog_reduce_desc *descs, int n, int W, rog_dty
     args->n_chunks = uint32_t(next);   // 32 tensors of < 2^26 chunks each
     *grid = uint32_t(std::min<uint64_t>(next, max_grid(kWaveBlock)));
     *nt_loads = source_bytes >= kNtLoadMinBytes;
+    *shifted = *nt_loads && kReduceShift == 1;
     return ROG_OK;
 }
 

@@ -128,51 +128,42 @@ __device__ __forceinline__ vec16 sum_vec(const void *const *src, uint32_t W, uin
     return narrow<DT>(acc);
 }
 
-// sum_vec for a whole wave of a multi-WG chunk whose plan found a source read
-// as shared granules (shift_granules under kReduceShift, the PEER gather's
-// scheme): every lane calls it, since the shuffle needs all 64; `live` lanes
-// own a body vector at byte offset off; `own_hi` lanes (lane 63 and the body's
-// last lane) load the granule after their own themselves.  body is the body's
-// first byte offset: source r's bytes sit m_r = (src_r + body) % 16 bytes past
-// a granule in every lane.  Sources that are not shifted keep the unaligned
-// load.  This form holds twice the loaded registers of sum_vec, so the plan
-// takes it only where a source needs it.
+// sum_vec for a whole wave of a multi-WG chunk, reading every source as
+// aligned 16-byte granules shared between neighbouring lanes (the PEER
+// gather's scheme): every lane calls it, since the shuffle needs all 64.
+// `live` lanes own a body vector at byte offset off; `own_hi` lanes (lane 63
+// and the body's last lane) load the granule after their own themselves, as
+// a cached load.  body is the body's first byte offset: source r's bytes sit
+// m_r = (src_r + body) % 16 bytes past a granule in every lane.
 template <int DT, bool NTL>
 __device__ __forceinline__ vec16 sum_vec_wave(const void *const *src, uint32_t W, uint64_t off, uint64_t body,
-                                              bool live, bool own_hi) {
+                                              bool live, bool own_hi, bool next_in_body) {
     constexpr int E = Elem<DT>::kPerVec;
     float acc[E];
     for (uint32_t r0 = 0; r0 < W; r0 += kGroup) {
         const uint32_t g = min(W - r0, kGroup);
         vec16 v[kGroup], h[kGroup];
+        uint32_t m[kGroup];
 #pragma unroll
         for (uint32_t q = 0; q < kGroup; ++q) {
+            v[q] = h[q] = vec16{0, 0, 0, 0};
+            m[q] = 0;
             if (q < g) {
                 const uint8_t *s = static_cast<const uint8_t *>(src[r0 + q]);
-                const uint32_t m = uniform(uint32_t(reinterpret_cast<uintptr_t>(s) + body) & 15);
-                v[q] = h[q] = vec16{0, 0, 0, 0};
-                if (shift_granules(m, kReduceShift)) {
-                    const vec16 *gp = reinterpret_cast<const vec16 *>(s + off - m);
-                    if (live) v[q] = ld16<NTL>(gp);
-                    if (own_hi) h[q] = ld16<NTL>(gp + 1);
-                } else if (live) {
-                    v[q] = ldu16<NTL>(s + off);
-                }
+                m[q] = uniform(uint32_t(reinterpret_cast<uintptr_t>(s) + body) & 15);
+                const vec16 *gp = reinterpret_cast<const vec16 *>(s + off - m[q]);
+                if (live) v[q] = ld16<NTL>(gp);
+                // past the body's end only where that granule holds payload bytes
+                if (own_hi && (m[q] != 0 || next_in_body)) h[q] = ld16<false>(gp + 1);
             }
         }
 #pragma unroll
         for (uint32_t q = 0; q < kGroup; ++q) {
             if (q < g) {
-                const uint32_t m =
-                    uniform(uint32_t(reinterpret_cast<uintptr_t>(src[r0 + q]) + body) & 15);
-                vec16 w = v[q];
-                if (shift_granules(m, kReduceShift)) {
-                    const vec16 next = vec16{__shfl_down(w.x, 1u), __shfl_down(w.y, 1u), __shfl_down(w.z, 1u),
-                                             __shfl_down(w.w, 1u)};
-                    w = cut16(w, own_hi ? h[q] : next, m);
-                }
+                const vec16 next = vec16{__shfl_down(v[q].x, 1u), __shfl_down(v[q].y, 1u),
+                                         __shfl_down(v[q].z, 1u), __shfl_down(v[q].w, 1u)};
                 float x[E];
-                widen<DT>(w, x);
+                widen<DT>(cut16(v[q], own_hi ? h[q] : next, m[q]), x);
                 if (r0 + q == 0) {
 #pragma unroll
                     for (int e = 0; e < E; ++e) acc[e] = x[e];       // the first term as it is
@@ -222,7 +213,7 @@ __device__ __forceinline__ void sum_chunk(const void *const *src, uint32_t W, vo
     const bool live = off < cut.hi;
     if constexpr (SH) {
         const bool own_hi = live && (lane == 63 || off + 16 >= cut.hi);
-        const vec16 v = sum_vec_wave<DT, NTL>(src, W, off, cut.lo, live, own_hi);
+        const vec16 v = sum_vec_wave<DT, NTL>(src, W, off, cut.lo, live, own_hi, off + 16 < cut.hi);
         if (live) st16(reinterpret_cast<vec16 *>(static_cast<uint8_t *>(out) + off), v);
     } else if (live) {
         st16(reinterpret_cast<vec16 *>(static_cast<uint8_t *>(out) + off), sum_vec<DT, NTL>(src, W, off));

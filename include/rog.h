@@ -114,10 +114,11 @@ typedef struct {
 #define ROG_PLAN_NT_LOADS 1u
 /* rog_plan_info.flags: the multi-workgroup PEER or REDUCE kernel reads at least
  * one source body as aligned 16-byte granules, each lane taking the granule
- * after its own from the next lane.  Set when the body (from the first
- * 256-byte boundary of the payload's output) is not empty and a source sits m
- * bytes past a 16-byte granule there, with m odd or 2 mod 4 (PEER) or m != 0
- * (REDUCE).  Affects speed only; the bytes are the same. */
+ * after its own from the next lane.  Only with ROG_PLAN_NT_LOADS.  PEER: set
+ * when a payload's body (from the first 256-byte boundary of its output) is
+ * not empty and its source sits an odd or 2-mod-4 number of bytes past a
+ * 16-byte granule there.  REDUCE: set with ROG_PLAN_NT_LOADS, for every
+ * source.  Affects speed only; the bytes are the same. */
 #define ROG_PLAN_SHIFTED_LOADS 2u
 
 /*

@@ -122,16 +122,16 @@ def test_gather_plan_matches_the_rules(W, S, path, data):
         mask = sum(1 << r for r, s in enumerate(srcs) if ((s | (out + r * S)) & 15) == 0)
         assert info.vec_ok_mask == mask
     assert bool(info.flags & rog.ROG_PLAN_NT_LOADS) == (total >= 384 << 20)
-    shifted = (not flat and info.path == 2
+    shifted = (not flat and info.path == 2 and total >= 384 << 20
                and any(shared_granules(s, out + r * S, S, PEER_MODE) for r, s in enumerate(srcs)))
     assert bool(info.flags & rog.ROG_PLAN_SHIFTED_LOADS) == shifted
 
 
-# The multi-WG PEER and REDUCE bodies start at the first 256-byte boundary of
-# their output; a source sitting m bytes past a 16-byte granule there is read
-# as aligned granules shared between lanes when m is odd or 2 mod 4 (the
-# gather's PEER kernel as built, mode 1) or whenever m != 0 (the sum as built,
-# mode 2).
+# The multi-WG PEER body starts at the first 256-byte boundary of its output;
+# where the loads stream past the caches, a source sitting m bytes past a
+# 16-byte granule there is read as aligned granules shared between lanes when
+# m is odd or 2 mod 4 (mode 1, as built); mode 2 would take every m != 0.
+# (The sum takes its granule form exactly when its loads stream.)
 PEER_MODE, REDUCE_MODE = 1, 2
 
 
@@ -173,8 +173,8 @@ def test_reduce_plan_matches_the_rules(W, n, dt, path, data):
     else:
         assert info.grid == 1 and info.block == min(1024, max(64, -(-(-(-nb // 16)) // 64) * 64))
     assert bool(info.flags & rog.ROG_PLAN_NT_LOADS) == (W * nb >= 384 << 20)
-    shifted = resolved == 2 and any(shared_granules(s, out, nb, REDUCE_MODE) for s in srcs)
-    assert bool(info.flags & rog.ROG_PLAN_SHIFTED_LOADS) == shifted
+    nt = W * nb >= 384 << 20
+    assert bool(info.flags & rog.ROG_PLAN_SHIFTED_LOADS) == (resolved == 2 and nt)
 
 
 def test_shared_granule_examples():
@@ -187,7 +187,7 @@ def test_shared_granule_examples():
         assert not shared_granules(g + 1, g + 3, 253 + 15, mode)  # body empty
         assert shared_granules(g, g + 255, 1 << 20, mode)        # head 1: m = 1
     assert not shared_granules(g + 4, g, 1 << 20, PEER_MODE)     # m = 4: the gather keeps the unaligned load
-    assert shared_granules(g + 4, g, 1 << 20, REDUCE_MODE)       # the sum shares granules
+    assert shared_granules(g + 4, g, 1 << 20, REDUCE_MODE)
 
 
 def test_bad_dtype_is_invalid():
