@@ -279,3 +279,43 @@ def test_chunk_counts_beyond_whole_xcd_spans(gpu, W, S):
     placed = gc.Placed(payloads, offs, 5, gpu)
     gc.run_all_paths(placed, "chunk spans W=%d S=%d" % (W, S),
                      paths=(rog.ROG_PATH_AUTO, rog.ROG_PATH_MULTI_WG))
+
+
+@pytest.fixture(scope="module")
+def streamed_payloads():
+    """8 payloads of 48 MiB + 5 bytes: 384 MiB of sources, enough for the
+    kernels to stream their loads past the caches."""
+    S = (48 << 20) + 5
+    rng = np.random.default_rng(77)
+    return [np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(8)]
+
+
+def _shares_granules(placed):
+    """The PEER kernel's rule for streamed loads: some payload's source sits an
+    odd or 2-mod-4 number of bytes past a 16-byte granule where its body (from
+    the first 256-byte boundary of its output) starts."""
+    o = placed.out.data_ptr()
+    for r, s in enumerate(placed.srcs):
+        head = (256 - (o + r * placed.S) % 256) % 256
+        if placed.S >= head + 16 and ((s.data_ptr() + head) % 16) % 4:
+            return True
+    return False
+
+
+@pytest.mark.parametrize("io,oo", [(1, 3), (0, 1), (2, 0), (4, 0), (5, 5)])
+def test_misaligned_streamed_payloads(gpu, streamed_payloads, io, oo):
+    """Misaligned payloads with streamed loads, where the PEER body reads
+    aligned granules shared between lanes at odd and 2-mod-4 shifts (and
+    unaligned loads at the others): every byte against the oracle."""
+    placed = gc.Placed(streamed_payloads, [io] * 8, oo, gpu)
+    plan = rog.rog_plan(placed.srcs, placed.out)
+    assert plan["kernel"] == "peer" and plan["path"] == "multi_wg" and plan["nt_loads"]
+    assert plan["shifted_loads"] == _shares_granules(placed)
+    gc.run_all_paths(placed, "streamed misaligned in=%d out=%d" % (io, oo), paths=(rog.ROG_PATH_AUTO,))
+
+
+def test_streamed_payloads_each_misaligned_differently(gpu, streamed_payloads):
+    placed = gc.Placed(streamed_payloads, list(range(1, 9)), 7, gpu)
+    plan = rog.rog_plan(placed.srcs, placed.out)
+    assert plan["nt_loads"] and plan["shifted_loads"]
+    gc.run_all_paths(placed, "streamed misaligned, source offsets 1..8, out 7", paths=(rog.ROG_PATH_AUTO,))

@@ -194,3 +194,28 @@ def test_batched_sums_sharing_sources(gpu):
     assert outs[0] is a.out and outs[1] is b.out
     a.check("shared sources, tensor 0")
     b.check("shared sources, tensor 1")
+
+
+_STREAMED = {}
+
+
+def _streamed_payloads(dtype, n):
+    if dtype not in _STREAMED:
+        _STREAMED.clear()           # one element type's 384 MiB at a time
+        _STREAMED[dtype] = wl.reduce_payloads(606, 8, n, dtype, "bits" if dtype == "f16" else "uniform")
+    return _STREAMED[dtype]
+
+
+@pytest.mark.parametrize("offs", [((0,) * 8, 0), ((1,) * 8, 0), ((0,) * 8, 1), ((2,) * 8, 0), ((3,) * 8, 5),
+                                  (tuple(range(8)), 3)], ids=lambda o: "in%s_out%d" % (o[0][:2], o[1]))
+@pytest.mark.parametrize("dtype,n", [("bf16", 24 << 20), ("f32", 12 << 20), ("f16", 24 << 20)])
+def test_streamed_sums_take_the_granule_form(gpu, dtype, n, offs):
+    """Sums over 384 MiB of sources stream their loads and read every source as
+    aligned granules shared between lanes, at any element offset: every
+    element against the oracle."""
+    in_offs, out_off = offs
+    placed = gc.PlacedReduce(_streamed_payloads(dtype, n), in_offs, out_off, dtype, gpu)
+    plan = rog.rog_reduce_plan(placed.srcs, placed.out)
+    assert plan["path"] == "multi_wg" and plan["nt_loads"] and plan["shifted_loads"]
+    gc.run_reduce_all_paths(placed, "streamed %s in=%s out=%d" % (dtype, in_offs, out_off),
+                            paths=(rog.ROG_PATH_AUTO,))
