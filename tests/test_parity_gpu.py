@@ -319,3 +319,17 @@ def test_streamed_payloads_each_misaligned_differently(gpu, streamed_payloads):
     plan = rog.rog_plan(placed.srcs, placed.out)
     assert plan["nt_loads"] and plan["shifted_loads"]
     gc.run_all_paths(placed, "streamed misaligned, source offsets 1..8, out 7", paths=(rog.ROG_PATH_AUTO,))
+
+
+def test_streamed_batch_with_small_misaligned_tensors(gpu):
+    """A batch whose sources total 384 MiB or more streams its loads, so its
+    misaligned tensors take the shuffled PEER body, down to tensors of a few
+    bytes and bodies shorter than one wave: one 100 MiB tensor (W = 4) beside
+    small and empty tensors at odd offsets."""
+    rng = np.random.default_rng(88)
+    W = 4
+    sizes = [100 << 20, 0, 1, 17, 255, 256 + 5, 1040, 4096 + 3, 65536 + 7, 1 << 20]
+    in_offs = [1, 0, 3, 1, 2, 1, 5, 3, 1, 2]
+    out_offs = [3, 0, 0, 1, 0, 3, 7, 2, 9, 0]
+    payloads = [[np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(W)] for S in sizes]
+    gc.PlacedBatch(W, payloads, in_offs, out_offs, gpu).run("streamed batch, small misaligned tensors")

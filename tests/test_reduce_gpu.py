@@ -219,3 +219,16 @@ def test_streamed_sums_take_the_granule_form(gpu, dtype, n, offs):
     assert plan["path"] == "multi_wg" and plan["nt_loads"] and plan["shifted_loads"]
     gc.run_reduce_all_paths(placed, "streamed %s in=%s out=%d" % (dtype, in_offs, out_off),
                             paths=(rog.ROG_PATH_AUTO,))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_streamed_batch_with_small_tensors(gpu, dtype):
+    """A batch of sums over 384 MiB or more of sources takes the granule form
+    for every tensor, down to single elements, bodies shorter than one wave and
+    empty tensors: one 100 MiB-per-source tensor (W = 4) beside small ones at
+    element offsets."""
+    big = (100 << 20) // wl.REDUCE_ESIZE[dtype]
+    counts = [big, 0, 1, 7, 127, 129, 520, 2049, 33_333, 0, 262_147]
+    offs = [[(t + r) % 5 for r in range(4)] for t in range(len(counts))]
+    b = _batch(43, 4, counts, dtype, offs)
+    b.run("streamed batch of sums %s" % dtype)
