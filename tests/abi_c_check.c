@@ -9,7 +9,8 @@
  * a batch of three tensors in one launch, S = 0, and the argument errors that
  * must be reported before anything is enqueued; rank-ordered sums (bf16 and
  * binary32, every path, element offsets, in place) against the oracle's sum,
- * and a batch of binary16 sums in one launch.
+ * and a batch of binary16 sums in one launch; the plans' cache-policy and
+ * shared-granule flags.
  * Exit status 0 = every check passed; the first failure is printed.
  */
 #include <hip/hip_runtime_api.h>
@@ -301,7 +302,43 @@ static void reduce_batch_case(hipStream_t st) {
     }
 }
 
+/* Plan flags from the header's rules (no launch: addresses are never touched). */
+static void plan_flag_cases(void) {
+    const void *srcs[8];
+    const uintptr_t base = (uintptr_t)1 << 40;
+    rog_plan_info info;
+    /* streamed (8 x 48 MiB + 5 >= 384 MiB), sources 1 byte and output 3 bytes past
+     * 256-byte boundaries: body head 253, m = (1 + 253) % 16 = 14 -> shared granules */
+    const size_t S = ((size_t)48 << 20) + 5;
+    for (int r = 0; r < 8; ++r) srcs[r] = (const void *)(base + ((uintptr_t)r << 30) + 1);
+    const void *out = (const void *)(base + ((uintptr_t)16 << 30) + 3);
+    if (rog_plan(srcs, 8, S, out, ROG_PATH_AUTO, &info) != ROG_OK || info.kernel != ROG_KERNEL_PEER ||
+        info.flags != (ROG_PLAN_NT_LOADS | ROG_PLAN_SHIFTED_LOADS)) {
+        fprintf(stderr, "plan flags: streamed misaligned gather got kernel %d flags %u\n", info.kernel, info.flags);
+        ++failures;
+    }
+    /* the same layout at 8 MiB per payload: cached loads, unaligned loads kept */
+    if (rog_plan(srcs, 8, (size_t)8 << 20, out, ROG_PATH_AUTO, &info) != ROG_OK || info.flags != 0) {
+        fprintf(stderr, "plan flags: cached misaligned gather got flags %u\n", info.flags);
+        ++failures;
+    }
+    /* sums: 8 x 24 Mi bf16 (384 MiB) -> granule form; 2 x 1 Mi -> plain */
+    for (int r = 0; r < 8; ++r) srcs[r] = (const void *)(base + ((uintptr_t)r << 30));
+    out = (const void *)(base + ((uintptr_t)16 << 30));
+    if (rog_reduce_plan(srcs, 8, (size_t)24 << 20, ROG_DTYPE_BF16, out, ROG_PATH_AUTO, &info) != ROG_OK ||
+        info.flags != (ROG_PLAN_NT_LOADS | ROG_PLAN_SHIFTED_LOADS)) {
+        fprintf(stderr, "plan flags: streamed sum got flags %u\n", info.flags);
+        ++failures;
+    }
+    if (rog_reduce_plan(srcs, 2, (size_t)1 << 20, ROG_DTYPE_BF16, out, ROG_PATH_AUTO, &info) != ROG_OK ||
+        info.flags != 0) {
+        fprintf(stderr, "plan flags: cached sum got flags %u\n", info.flags);
+        ++failures;
+    }
+}
+
 int main(void) {
+    plan_flag_cases();
     hipStream_t st;
     CHECK_HIP(hipStreamCreate(&st));
     const rog_path paths[3] = {ROG_PATH_AUTO, ROG_PATH_SINGLE_WG, ROG_PATH_MULTI_WG};
