@@ -628,6 +628,49 @@ def reduce_crossover(torch, rog, device, steps, warmup, sizes_kib=REDUCE_CROSSOV
     return rows
 
 
+# hipDeviceAttribute_t values (hip_runtime_api.h): global memory bus width in
+# bits, peak memory clock in kHz.
+HIP_ATTR_MEMORY_BUS_WIDTH = 59
+HIP_ATTR_MEMORY_CLOCK_RATE = 60
+
+
+def hbm_from_runtime(device_index):
+    """The HBM peak the HIP runtime's own figures imply, through the HIP
+    runtime torch mapped: bus width x memory clock x transfers per clock.  On
+    MI355X HIP reports 8192 bits and 2 GHz; two transfers per clock would give
+    4.1 TB/s, less than the kernels here measure, so the figure takes four
+    (8 Gb/s per pin, 8.2 TB/s: AMD's published 8 TB/s)."""
+    from deterministic_collective_movement_amd import rog
+    paths = sorted(rog._hip_runtimes_mapped())
+    if len(paths) != 1:
+        return {"error": "HIP runtimes mapped: %d" % len(paths)}
+    hip = ctypes.CDLL(paths[0])
+    vals = {}
+    for name, attr in (("bus_width_bits", HIP_ATTR_MEMORY_BUS_WIDTH), ("memory_clock_khz", HIP_ATTR_MEMORY_CLOCK_RATE)):
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, device_index) != 0:
+            return {"error": "hipDeviceGetAttribute(%d) failed" % attr}
+        vals[name] = v.value
+    vals["transfers_per_clock"] = 4
+    vals["GBps"] = round(4 * vals["memory_clock_khz"] * 1e3 * vals["bus_width_bits"] / 8 / 1e9, 1)
+    vals["denominator_used"] = "AMD's published %.0f GB/s, not this figure" % PEAK_HBM_GBPS
+    return vals
+
+
+def host_cpu():
+    """Model name and the number of cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "cores_available": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(case, payloads, budget_s):
     """The CPU oracle, single-threaded, on the full headline gather repeated for
     about ``budget_s`` seconds of CPU work."""
@@ -645,7 +688,7 @@ def cpu_baseline(case, payloads, budget_s):
     moved = 2 * case.W * case.S * reps
     return {"value": round(moved / el / 1e9, 2), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "%d x the full W=8 x 64 MiB gather (%.1f s, single-threaded C per-byte loop)"
-                      % (reps, el)}
+                      % (reps, el), "host": host_cpu()}
 
 
 def main(argv=None):
@@ -729,6 +772,7 @@ def main(argv=None):
                                                           max(2, args.warmup // 2))[0]}
         cpu = None
     extras["device"] = torch.cuda.get_device_name(device)
+    extras["hbm_from_runtime"] = hbm_from_runtime(device.index or 0)
     config = {"workload": "rank-ordered gather of W=8 aligned bf16 payloads of 64 MiB into a 512 MiB "
                           "output (1 GiB moved per step)",
               "W": case.W, "bytes_per_rank": case.S, "bytes_moved_per_step": alg_bytes}

@@ -5,6 +5,7 @@ benchmark tests)."""
 from __future__ import annotations
 
 import json
+import os
 
 import pytest
 
@@ -133,3 +134,25 @@ def test_source_digest_ignores_comments_but_not_code(tmp_path):
     assert bench.kernel_source_digest([str(a)]) == d0
     a.write_text("int f(int x) { return 3 * x; }\n")
     assert bench.kernel_source_digest([str(a)]) != d0
+
+
+def test_hip_attribute_numbers_match_the_header(tmp_path):
+    """The bench reads the memory bus width and clock with hipDeviceGetAttribute;
+    its enum numbers must be the ones the installed HIP header defines."""
+    import shutil
+    import subprocess
+    if not os.path.exists("/opt/rocm/include/hip/hip_runtime_api.h") or not shutil.which("gcc"):
+        pytest.skip("no HIP header or gcc")
+    src = tmp_path / "attr.c"
+    src.write_text('#include <hip/hip_runtime_api.h>\n#include <stdio.h>\n'
+                   'int main(void) { printf("%d %d", (int)hipDeviceAttributeMemoryBusWidth, '
+                   '(int)hipDeviceAttributeMemoryClockRate); return 0; }\n')
+    exe = tmp_path / "attr"
+    subprocess.check_call(["gcc", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", str(src), "-o", str(exe)])
+    bus, clock = map(int, subprocess.check_output([str(exe)]).split())
+    assert (bench.HIP_ATTR_MEMORY_BUS_WIDTH, bench.HIP_ATTR_MEMORY_CLOCK_RATE) == (bus, clock)
+
+
+def test_host_cpu_reports_model_and_cores():
+    h = bench.host_cpu()
+    assert h["cores_available"] >= 1
