@@ -334,12 +334,13 @@ def d2d_ceiling(torch, device, nbytes, steps, warmup):
 
 
 SWEEP_OUT_MIB = (64, 128, 256, 512)
+SWEEP_MID_OUT_MIB = (2, 8, 32)
 SWEEP_FOOTPRINT = 2 << 30      # bytes of rotating buffer sets per cold case (8 x the 256 MB cache)
 
 
 def bandwidth_sweep(torch, rog, device, calls, out_mib=SWEEP_OUT_MIB, footprint=SWEEP_FOOTPRINT):
-    """Aligned gathers with outputs of 64 - 512 MiB at W = 2 and 8 (the north
-    star's "outputs >= 64 MiB"), timed two ways over ``calls`` back-to-back
+    """Aligned gathers with outputs of ``out_mib`` (64 - 512 MiB by default,
+    the "outputs >= 64 MiB" of the headline target) at W = 2 and 8, timed two ways over ``calls`` back-to-back
     launches: warm, the same buffers every call (as the pages time a call), and
     cold, rotating through K buffer sets that together span ``footprint`` bytes,
     so that no call finds its sources in the 256 MB Infinity Cache.  Sampled
@@ -759,6 +760,8 @@ def main(argv=None):
                                             max(1, args.warmup // 5))
         extras["d2d_copy_ceiling"] = d2d_ceiling(torch, device, case.W * case.S, 20, 3)
         extras["bandwidth_sweep"] = bandwidth_sweep(torch, rog, device, 20)
+        # the size sweep's 1 and 4 MiB payloads (outputs of 2 - 32 MiB), warm and cold
+        extras["bandwidth_sweep_mid"] = bandwidth_sweep(torch, rog, device, 50, out_mib=SWEEP_MID_OUT_MIB)
         big, rpayloads, rgot = reduce_bandwidth(torch, rog, wl, device, args.steps, args.warmup)
         extras["reduce"] = {"bandwidth": big,
                             "latency": reduce_latency(torch, rog, wl, device, args.steps, args.warmup),
