@@ -203,7 +203,6 @@ struct PeerArgs {
 struct BatchTensor {
     uint64_t out;
     uint64_t S;
-    uint32_t first_chunk;
     uint32_t n_chunks;
     uint32_t flat;              // 1: FLAT tensor, 0: PEER tensor
     uint32_t vpr;               // FLAT: vectors per rank
@@ -214,10 +213,12 @@ struct BatchTensor {
 
 struct BatchArgs {
     const void *src[kMaxBatchPtrs];   // tensor t's payloads at [t*W, t*W + W)
+    uint32_t first[kMaxBatch];        // tensor t's first chunk (strictly increasing over [0, n))
     BatchTensor t[kMaxBatch];
     uint32_t n;
     uint32_t W;
     uint32_t n_chunks;                // all tensors' chunks
+    uint32_t flat_chunks;             // chunks of the FLAT tensors, which come first
 };
 
 static_assert(sizeof(BatchArgs) <= 4096, "kernel arguments must stay below 4 KiB");
@@ -260,12 +261,12 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
 struct ReduceTensor {
     uint64_t out;
     uint64_t count;             // elements
-    uint32_t first_chunk;
     uint32_t n_chunks;
 };
 
 struct ReduceBatchArgs {
     const void *src[kMaxBatchPtrs];   // tensor t's payloads at [t*W, t*W + W)
+    uint32_t first[kMaxBatch];        // tensor t's first chunk (strictly increasing over [0, n))
     ReduceTensor t[kMaxBatch];
     uint32_t n;
     uint32_t W;

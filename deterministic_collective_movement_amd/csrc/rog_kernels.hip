@@ -220,21 +220,20 @@ __global__ __launch_bounds__(kSingleBlock) void rog_peer_single_kernel(PeerArgs 
                                            static_cast<uint8_t *>(a.out) + uint64_t(r) * a.S, a.S, blockDim.x);
 }
 
-// BATCH: one wave per workgroup and per chunk of some tensor, chunks grouped by
-// XCD over the whole launch.
+// BATCH: one wave per workgroup and per chunk of some tensor.  The FLAT
+// tensors' chunks come first and go to the XCDs round-robin, as in the FLAT
+// kernel; the PEER tensors' chunks follow, handed out in XCD runs as in the
+// PEER kernel.  (Runs over the FLAT chunks too measured 5 % slower on an
+// aligned batch; no runs at all, 9 % slower on 8 x 64 MiB PEER payloads.)
 template <bool NTL>
 __global__ __launch_bounds__(kWaveBlock) void rog_batch_kernel(BatchArgs a) {
     for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x) {
-        const uint32_t c = xcd_grouped(vb, a.n_chunks);
-        // Last tensor whose first chunk is <= c (first_chunk strictly increases).
-        uint32_t lo = 0, hi = a.n;
-        while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) / 2;
-            if (a.t[mid].first_chunk <= c) lo = mid;
-            else hi = mid;
-        }
+        const uint32_t c = vb < a.flat_chunks
+                               ? vb
+                               : a.flat_chunks + xcd_grouped(vb - a.flat_chunks, a.n_chunks - a.flat_chunks);
+        const uint32_t lo = batch_tensor(a.first, a.n, c);
         const BatchTensor &t = a.t[lo];
-        const uint32_t lc = c - t.first_chunk;
+        const uint32_t lc = c - a.first[lo];
         const void *const *src = a.src + lo * a.W;
         if (t.flat) {
             flat_chunk<kFlatUnroll, NTL>(src, reinterpret_cast<vec16 *>(t.out), t.n_vec, t.vpr, t.div, lc);

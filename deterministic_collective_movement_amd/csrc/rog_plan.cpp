@@ -320,7 +320,7 @@ rog_status plan_reduce_batch(const rog_reduce_desc *descs, int n, int W, rog_dty
         for (int r = 0; r < W; ++r) args->src[k * uint32_t(W) + uint32_t(r)] = descs[t].srcs[r];
         rt.out = addr(descs[t].out);
         rt.count = descs[t].count;
-        rt.first_chunk = uint32_t(next);
+        args->first[k] = uint32_t(next);
         rt.n_chunks = reduce_chunks(bytes[t]);
         next += rt.n_chunks;
         source_bytes += uint64_t(W) * bytes[t];
@@ -366,32 +366,39 @@ rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *arg
     args->W = uint32_t(W);
     // One chunk per wave: 64 * kFlatUnroll output vectors of a FLAT tensor, 64
     // body vectors of one payload of a PEER tensor.  Each tensor has fewer than
-    // 2^26 + W chunks, so the batch's chunk count fits 32 bits.
+    // 2^26 + W chunks, so the batch's chunk count fits 32 bits.  FLAT tensors
+    // come first: their chunks go to the XCDs round-robin, the PEER tensors'
+    // chunks that follow in XCD runs.
+    bool flat[kMaxBatch];
+    for (int t = 0; t < n; ++t) flat[t] = totals[t] && is_flat(descs[t].srcs, W, descs[t].bytes_per_rank, descs[t].out);
     uint64_t next = 0;
     uint32_t k = 0;
-    for (int t = 0; t < n; ++t) {
-        if (!totals[t]) continue;           // empty tensors get no chunks
-        const rog_gather_desc &d = descs[t];
-        const size_t S = d.bytes_per_rank;
-        BatchTensor &bt = args->t[k];
-        for (int r = 0; r < W; ++r) args->src[k * uint32_t(W) + uint32_t(r)] = d.srcs[r];
-        bt.out = addr(d.out);
-        bt.S = S;
-        bt.first_chunk = uint32_t(next);
-        if (is_flat(d.srcs, W, S, d.out)) {
-            bt.flat = 1;
-            bt.n_vec = uint32_t(totals[t] / 16);
-            bt.vpr = uint32_t(S / 16);
-            bt.div = make_divider(bt.vpr);
-            bt.n_chunks = uint32_t(ceil_div(bt.n_vec, 64 * uint64_t(kFlatUnroll)));
-        } else {
-            bt.flat = 0;
-            bt.chunks_per_peer = peer_chunks_per_peer(S);
-            bt.div = make_divider(bt.chunks_per_peer);
-            bt.n_chunks = bt.chunks_per_peer * uint32_t(W);
+    for (int pass = 0; pass < 2; ++pass) {
+        if (pass == 1) args->flat_chunks = uint32_t(next);
+        for (int t = 0; t < n; ++t) {
+            if (!totals[t] || flat[t] != (pass == 0)) continue;   // empty tensors get no chunks
+            const rog_gather_desc &d = descs[t];
+            const size_t S = d.bytes_per_rank;
+            BatchTensor &bt = args->t[k];
+            for (int r = 0; r < W; ++r) args->src[k * uint32_t(W) + uint32_t(r)] = d.srcs[r];
+            bt.out = addr(d.out);
+            bt.S = S;
+            args->first[k] = uint32_t(next);
+            if (flat[t]) {
+                bt.flat = 1;
+                bt.n_vec = uint32_t(totals[t] / 16);
+                bt.vpr = uint32_t(S / 16);
+                bt.div = make_divider(bt.vpr);
+                bt.n_chunks = uint32_t(ceil_div(bt.n_vec, 64 * uint64_t(kFlatUnroll)));
+            } else {
+                bt.flat = 0;
+                bt.chunks_per_peer = peer_chunks_per_peer(S);
+                bt.div = make_divider(bt.chunks_per_peer);
+                bt.n_chunks = bt.chunks_per_peer * uint32_t(W);
+            }
+            next += bt.n_chunks;
+            ++k;
         }
-        next += bt.n_chunks;
-        ++k;
     }
     if (next > UINT32_MAX) return ROG_ERR_TOO_LARGE;
     args->n = k;

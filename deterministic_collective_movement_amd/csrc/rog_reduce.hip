@@ -236,14 +236,9 @@ template <int DT, bool NTL, bool SH>
 __global__ __launch_bounds__(kWaveBlock) void rog_reduce_batch_kernel(ReduceBatchArgs a) {
     for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x) {
         const uint32_t c = ROG_REDUCE_XCD ? xcd_grouped(vb, a.n_chunks) : vb;
-        uint32_t lo = 0, hi = a.n;          // last tensor whose first chunk is <= c
-        while (hi - lo > 1) {
-            const uint32_t mid = (lo + hi) / 2;
-            if (a.t[mid].first_chunk <= c) lo = mid;
-            else hi = mid;
-        }
+        const uint32_t lo = batch_tensor(a.first, a.n, c);
         const ReduceTensor &t = a.t[lo];
-        sum_chunk<DT, NTL, SH>(a.src + lo * a.W, a.W, reinterpret_cast<void *>(t.out), t.count, c - t.first_chunk);
+        sum_chunk<DT, NTL, SH>(a.src + lo * a.W, a.W, reinterpret_cast<void *>(t.out), t.count, c - a.first[lo]);
     }
 }
 
