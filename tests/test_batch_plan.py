@@ -1,0 +1,146 @@
+"""The batch planners' chunk layout, checked on the CPU through a shim
+compiled from the planner's own source (csrc/rog_plan.cpp): every non-empty
+tensor planned once, FLAT tensors first (their chunks go to the XCDs
+round-robin, the PEER tensors' after them in XCD runs), first chunks laid end
+to end, chunk counts as the kernels expect, and the sum batch's tensors in
+the caller's order."""
+from __future__ import annotations
+
+import ctypes
+import os
+import shutil
+import subprocess
+
+import pytest
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+from deterministic_collective_movement_amd import build as b
+from deterministic_collective_movement_amd import rog
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+MAXB = 32
+
+
+@pytest.fixture(scope="module")
+def shim(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or os.path.join(b.ROCM, "bin", "hipcc")
+    so = str(tmp_path_factory.mktemp("plan") / "libplanshim.so")
+    subprocess.check_call([hipcc, "-x", "hip", "-O2", "-std=c++17", "-fPIC", "-shared",
+                           "--offload-arch=gfx950", "-Wno-unused-command-line-argument",
+                           "-I", b.INCLUDE, "-I", b.CSRC, os.path.join(HERE, "plan_shim.cpp"),
+                           os.path.join(b.CSRC, "rog_plan.cpp"), "-o", so],
+                          stderr=subprocess.DEVNULL)
+    return ctypes.CDLL(so)
+
+
+U64 = ctypes.c_uint64 * 64
+U32 = ctypes.c_uint32 * 64
+
+
+def plan_batch(shim, tensors, W):
+    """tensors: [(src addresses, out address, S)] -> (status, planned list, meta)."""
+    keep = [(ctypes.c_void_p * W)(*srcs) for srcs, _, _ in tensors]
+    descs = (rog.rog_gather_desc * max(1, len(tensors)))()
+    for i, (srcs, o, S) in enumerate(tensors):
+        descs[i].srcs = ctypes.cast(keep[i], ctypes.POINTER(ctypes.c_void_p))
+        descs[i].out = ctypes.c_void_p(o)
+        descs[i].bytes_per_rank = S
+    n_out = ctypes.c_uint32()
+    out, S, flat, nch, first = U64(), U64(), U32(), U32(), U32()
+    srcs = (ctypes.c_uint64 * (MAXB * 8))()
+    meta = (ctypes.c_uint32 * 4)()
+    status = shim.rog_test_plan_batch(descs, len(tensors), W, ctypes.byref(n_out), out, S, flat, nch, first,
+                                      srcs, meta)
+    planned = [dict(out=out[k], S=S[k], flat=flat[k], n_chunks=nch[k], first=first[k],
+                    srcs=tuple(srcs[k * W + r] for r in range(W))) for k in range(n_out.value)]
+    return status, planned, list(meta)
+
+
+def _chunks(srcs, o, S, W):
+    flat = ((o | S | _or(srcs)) & 15) == 0
+    if flat:
+        return True, -(-(W * S // 16) // 64)
+    return False, max(1, -(-(S // 16) // 64)) * W
+
+
+def _or(xs):
+    v = 0
+    for x in xs:
+        v |= x
+    return v
+
+
+BASE = 1 << 40
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(data=st.data(), n=st.integers(0, 12), W=st.sampled_from([1, 2, 4, 8]))
+def test_gather_batch_layout(shim, data, n, W):
+    tensors = []
+    for t in range(n):
+        S = data.draw(st.one_of(st.just(0), st.integers(1, 5000), st.sampled_from([16, 1024, 4096, 65536, 1 << 20])))
+        off = data.draw(st.sampled_from([0, 0, 16, 1, 3, 8]))
+        base = BASE + t * (1 << 32)
+        srcs = [base + r * (1 << 28) + off for r in range(W)]
+        o = base + (W + 1) * (1 << 28) + data.draw(st.sampled_from([0, 16, 1, 5]))
+        tensors.append((srcs, o, S))
+    status, planned, meta = plan_batch(shim, tensors, W)
+    assert status == 0
+    want = [(tuple(s), o, S) + _chunks(s, o, S, W) for s, o, S in tensors if S]
+    # FLAT tensors first, each group in the caller's order
+    order = [x for x in want if x[3]] + [x for x in want if not x[3]]
+    assert [(p["srcs"], p["out"], p["S"], bool(p["flat"]), p["n_chunks"]) for p in planned] == order
+    nxt = 0
+    for p in planned:
+        assert p["first"] == nxt
+        nxt += p["n_chunks"]
+    assert meta[0] == nxt
+    assert meta[1] == sum(p["n_chunks"] for p in planned if p["flat"])
+    assert meta[2] == nxt            # one wave per chunk while the grid is not capped
+
+
+def test_gather_batch_all_empty(shim):
+    status, planned, meta = plan_batch(shim, [([BASE], BASE + (1 << 30), 0)] * 3, 1)
+    assert status == 0 and planned == [] and meta[0] == 0 and meta[2] == 0
+
+
+def plan_reduce_batch(shim, tensors, W, dtype):
+    keep = [(ctypes.c_void_p * W)(*srcs) for srcs, _, _ in tensors]
+    descs = (rog.rog_reduce_desc * max(1, len(tensors)))()
+    for i, (srcs, o, cnt) in enumerate(tensors):
+        descs[i].srcs = ctypes.cast(keep[i], ctypes.POINTER(ctypes.c_void_p))
+        descs[i].out = ctypes.c_void_p(o)
+        descs[i].count = cnt
+    n_out = ctypes.c_uint32()
+    out, count, nch, first = U64(), U64(), U32(), U32()
+    meta = (ctypes.c_uint32 * 4)()
+    status = shim.rog_test_plan_reduce_batch(descs, len(tensors), W, dtype, ctypes.byref(n_out), out, count, nch,
+                                             first, meta)
+    planned = [dict(out=out[k], count=count[k], n_chunks=nch[k], first=first[k]) for k in range(n_out.value)]
+    return status, planned, list(meta)
+
+
+@settings(max_examples=200, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(data=st.data(), n=st.integers(0, 12), W=st.sampled_from([1, 3, 4]), dtype=st.sampled_from([0, 1, 2]))
+def test_reduce_batch_layout(shim, data, n, W, dtype):
+    es = 4 if dtype == 0 else 2
+    tensors = []
+    for t in range(n):
+        cnt = data.draw(st.one_of(st.just(0), st.integers(1, 100_000), st.just(24 << 20)))
+        base = BASE + t * (1 << 33)
+        srcs = [base + r * (1 << 29) + es * data.draw(st.integers(0, 7)) for r in range(W)]
+        o = base + (W + 1) * (1 << 29) + es * data.draw(st.integers(0, 7))
+        tensors.append((srcs, o, cnt))
+    status, planned, meta = plan_reduce_batch(shim, tensors, W, dtype)
+    assert status == 0
+    want = [(o, cnt, max(1, -(-(cnt * es // 16) // 64))) for _, o, cnt in tensors if cnt]
+    assert [(p["out"], p["count"], p["n_chunks"]) for p in planned] == want   # the caller's order
+    nxt = 0
+    for p in planned:
+        assert p["first"] == nxt
+        nxt += p["n_chunks"]
+    assert meta[0] == nxt and meta[1] == nxt
+    source_bytes = sum(W * cnt * es for _, _, cnt in tensors)
+    nt = source_bytes >= 384 << 20
+    assert meta[2] == int(nt) and meta[3] == int(nt)   # the granule form exactly with streamed loads
