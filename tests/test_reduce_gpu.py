@@ -232,3 +232,14 @@ def test_streamed_batch_with_small_tensors(gpu, dtype):
     offs = [[(t + r) % 5 for r in range(4)] for t in range(len(counts))]
     b = _batch(43, 4, counts, dtype, offs)
     b.run("streamed batch of sums %s" % dtype)
+
+
+def test_streamed_sum_of_random_bit_patterns(gpu):
+    """The granule form on bf16 random bit patterns (NaNs, infinities,
+    subnormals) at element offsets: 8 x 24 Mi elements, every element against
+    the oracle (NaNs compared by class)."""
+    payloads = wl.reduce_payloads(607, 8, 24 << 20, "bf16", "bits")
+    placed = gc.PlacedReduce(payloads, (1, 0, 3, 2, 5, 4, 7, 6), 1, "bf16", gpu)
+    plan = rog.rog_reduce_plan(placed.srcs, placed.out)
+    assert plan["nt_loads"] and plan["shifted_loads"]
+    gc.run_reduce_all_paths(placed, "streamed bf16 bit patterns", paths=(rog.ROG_PATH_AUTO,))
