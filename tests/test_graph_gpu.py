@@ -156,3 +156,48 @@ def test_graph_captures_a_batched_sum(gpu):
         torch.cuda.synchronize()
         for o, want in zip(outs, wants):
             assert np.array_equal(o.view(torch.int16).cpu().numpy().view(np.uint16), want), replay
+
+
+def test_graph_captures_streamed_forms(gpu):
+    """The streamed-load forms in one graph: a 384 MiB sum at element offsets
+    (granule form, lane shuffles) and a 384 MiB gather at byte offsets 1 / 3
+    (shuffled PEER body); sources change between replays, every replay
+    against the oracle."""
+    W, n = 8, 24 << 20
+    S = 2 * n + 3
+    sum_bufs = [torch.zeros(n + 1, dtype=torch.bfloat16, device=gpu) for _ in range(W)]
+    sum_srcs = [b[1:] for b in sum_bufs]
+    sum_out = torch.zeros(n, dtype=torch.bfloat16, device=gpu)
+    g_bufs = [torch.zeros(S + 1, dtype=torch.uint8, device=gpu) for _ in range(W)]
+    g_srcs = [b[1:] for b in g_bufs]
+    g_obuf = torch.zeros(W * S + 3, dtype=torch.uint8, device=gpu)
+    g_out = g_obuf[3:]
+    assert rog.rog_reduce_plan(sum_srcs, sum_out)["shifted_loads"]
+    assert rog.rog_plan(g_srcs, g_out)["shifted_loads"]
+    rog.rog_reduce(sum_srcs, sum_out)
+    rog.rog_gather(g_srcs, g_out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rog.rog_reduce(sum_srcs, sum_out)
+        rog.rog_gather(g_srcs, g_out)
+    rng = np.random.default_rng(91)
+    for replay in range(3):
+        payloads = wl.reduce_payloads(wl.case_seed(27, replay), W, n, "bf16")
+        for s, p in zip(sum_srcs, payloads):
+            s.copy_(torch.from_numpy(p.view(np.int16)).to(gpu).view(torch.bfloat16))
+        want_sum = np.empty(n, np.uint16)
+        oracle.reduce_c(payloads, want_sum, "bf16")
+        gp = [np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(W)]
+        for s, p in zip(g_srcs, gp):
+            s.copy_(torch.from_numpy(p).to(gpu))
+        sum_out.zero_()
+        g_out.zero_()
+        torch.cuda.synchronize()
+        print("graph replay %d (streamed forms)" % replay, flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(sum_out.view(torch.int16).cpu().numpy().view(np.uint16), want_sum), replay
+        want_g = np.empty(W * S, np.uint8)
+        oracle.gather_c(gp, want_g)
+        assert np.array_equal(g_out.cpu().numpy(), want_g), replay
