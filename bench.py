@@ -49,6 +49,39 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flat_kernel_w8x64MiB_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "deterministic_collective_movement_amd", "csrc", f)
                   for f in ("rog_kernels.hip", "rog_internal.h", "rog_plan.cpp", "rog_device.h")]
 LATENCY_SIZES_KIB = (1, 8, 32, 128)
+NATIVE_SRC = os.path.join(ROOT, "bench_native.c")
+NATIVE_BIN = os.path.join(ROOT, "_build", "bench_native")
+
+
+def build_native() -> str:
+    """Compile bench_native.c (the small-gather latency timed from C) against
+    librog.so and the HIP runtime into _build/bench_native."""
+    import subprocess
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    pkg = os.path.join(ROOT, "deterministic_collective_movement_amd")
+    os.makedirs(os.path.dirname(NATIVE_BIN), exist_ok=True)
+    tmp = NATIVE_BIN + ".tmp%d" % os.getpid()
+    subprocess.check_call([
+        "gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+        "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"), NATIVE_SRC,
+        os.path.join(pkg, "librog.so"), "-Wl,-rpath,$ORIGIN/../deterministic_collective_movement_amd",
+        "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", tmp])
+    os.replace(tmp, NATIVE_BIN)
+    return NATIVE_BIN
+
+
+def latency_native(timeout_s=120):
+    """Run the native latency harness in a child process; its JSON, or why not."""
+    import subprocess
+    if not os.path.exists(NATIVE_BIN):
+        return {"error": "bench_native not built"}
+    try:
+        r = subprocess.run([NATIVE_BIN], capture_output=True, text=True, timeout=timeout_s)
+    except subprocess.TimeoutExpired:
+        return {"error": "timed out"}
+    if r.returncode != 0:
+        return {"error": "exit %d: %s" % (r.returncode, r.stderr.strip()[-200:])}
+    return json.loads(r.stdout)
 
 
 # ---------------------------------------------------------------------------
@@ -755,6 +788,7 @@ def main(argv=None):
     if not args.headline_only:
         extras["latency"] = latency_sweep(torch, rog, wl, device, args.steps, args.warmup)
         extras["latency_floor"] = launch_floor(torch, device, args.steps, args.warmup)
+        extras["latency_native"] = latency_native()
         extras["latency_in_graph"] = graph_latency(torch, rog, wl, device)
         extras["gather_many"] = batch_bench(torch, rog, wl, device, max(5, args.steps // 5),
                                             max(1, args.warmup // 5))

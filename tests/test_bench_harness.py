@@ -156,3 +156,14 @@ def test_hip_attribute_numbers_match_the_header(tmp_path):
 def test_host_cpu_reports_model_and_cores():
     h = bench.host_cpu()
     assert h["cores_available"] >= 1
+
+
+def test_native_latency_harness_builds():
+    """bench_native.c (small-gather latency timed from C) compiles against the
+    installed header and librog.so; bench.py runs the binary on the GPU."""
+    import shutil
+    if not shutil.which("gcc") or not os.path.exists(os.path.join(bench.ROOT, "deterministic_collective_movement_amd",
+                                                                  "librog.so")):
+        pytest.skip("no gcc or librog.so not built")
+    path = bench.build_native()
+    assert os.access(path, os.X_OK)
