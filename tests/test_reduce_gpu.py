@@ -243,3 +243,15 @@ def test_streamed_sum_of_random_bit_patterns(gpu):
     plan = rog.rog_reduce_plan(placed.srcs, placed.out)
     assert plan["nt_loads"] and plan["shifted_loads"]
     gc.run_reduce_all_paths(placed, "streamed bf16 bit patterns", paths=(rog.ROG_PATH_AUTO,))
+
+
+@pytest.mark.parametrize("W,n,dtype", [(12, 16 << 20, "bf16"), (64, 3 << 20, "f16"), (9, 11 << 20, "f32")])
+def test_streamed_sums_over_several_source_groups(gpu, W, n, dtype):
+    """The granule form with more sources than one group of loads in flight
+    (8): W = 12, 64 and 9 over 384 MiB or more of sources, each source at its
+    own element offset; every element against the oracle."""
+    payloads = wl.reduce_payloads(608 + W, W, n, dtype)
+    placed = gc.PlacedReduce(payloads, [r % 7 for r in range(W)], 2, dtype, gpu)
+    plan = rog.rog_reduce_plan(placed.srcs, placed.out)
+    assert plan["nt_loads"] and plan["shifted_loads"]
+    gc.run_reduce_all_paths(placed, "streamed W=%d %s" % (W, dtype), paths=(rog.ROG_PATH_AUTO,))
