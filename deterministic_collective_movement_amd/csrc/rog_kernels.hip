@@ -109,8 +109,9 @@ __device__ __forceinline__ void flat_copy(const void *const *src, void *out, uin
 // ---------------------------------------------------------------------------
 // PEER: one payload of S bytes from s to d, cut by split_payload into a byte
 // head [0, lo), a body [lo, hi) of aligned 16-byte stores -- each fed by the
-// 16 source bytes at the same payload offset, read inside [s, s + S) -- and a
-// byte tail [hi, S).  Every output byte is written exactly once.
+// 16 source bytes at the same payload offset, read inside [s, s + S) or, in
+// the shuffled form, inside the 16-byte granules that hold those bytes -- and
+// a byte tail [hi, S).  Every output byte is written exactly once.
 // ---------------------------------------------------------------------------
 
 // One wave: body chunk j (body vectors [64j, 64j + 64)); chunk 0 also moves the
@@ -119,12 +120,12 @@ __device__ __forceinline__ void flat_copy(const void *const *src, void *out, uin
 // Body source bytes sit m = (s + lo) % 16 bytes past a 16-byte granule, the
 // same m for every lane.  Unless the loads stream past the caches (NTL) and
 // kPeerShift takes this m, each lane reads its 16 bytes with one unaligned
-// load.  Otherwise each lane loads the aligned
-// granule g holding its first byte; the granule after g is the next lane's
-// g, passed across by a lane shuffle, and only the last lane of the wave or
-// of the body loads it itself (a cached load: that granule is the next
-// chunk's first).  Every granule read holds at least one byte
-// of the payload, so it lies in the payload's pages.
+// load.  Otherwise (the shuffled form) each lane loads the aligned granule g
+// holding its first byte; the granule after g is the next lane's g, passed
+// across by a lane shuffle, and only the last lane of the wave or of the body
+// loads it itself (a cached load: that granule is the next chunk's first).
+// Every granule read holds at least one byte of the payload, so it lies in
+// the payload's pages.
 template <bool NTL>
 __device__ __forceinline__ void peer_chunk(const uint8_t *s, uint8_t *d, uint64_t S, uint32_t j) {
     const uint32_t lane = __lane_id();
