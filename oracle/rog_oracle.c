@@ -1,5 +1,5 @@
 /*
- * rog_oracle.c -- CPU oracle for the rank-ordered gather.
+ * rog_oracle.c -- CPU oracle for the rank-ordered gather and the rank-ordered sum.
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously correct
  * definition that the GPU library is checked against.  Only the test suite,
