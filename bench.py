@@ -731,6 +731,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
+    ap.add_argument("--no-native", action="store_true",
+                    help="skip the C-timed small gathers (a child process), e.g. under a tracer")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline gather, its misaligned variant and the large "
                          "rank-ordered sum (for counter runs)")
@@ -788,7 +790,7 @@ def main(argv=None):
     if not args.headline_only:
         extras["latency"] = latency_sweep(torch, rog, wl, device, args.steps, args.warmup)
         extras["latency_floor"] = launch_floor(torch, device, args.steps, args.warmup)
-        extras["latency_native"] = latency_native()
+        extras["latency_native"] = {"skipped": "--no-native"} if args.no_native else latency_native()
         extras["latency_in_graph"] = graph_latency(torch, rog, wl, device)
         extras["gather_many"] = batch_bench(torch, rog, wl, device, max(5, args.steps // 5),
                                             max(1, args.warmup // 5))
