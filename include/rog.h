@@ -37,7 +37,10 @@
  *  - Bytes outside the output range (out, W*S bytes for a gather; count
  *    elements for a sum) are never written.  Source bytes are never written,
  *    except by an in-place call where out is itself a source.  Every read lies
- *    inside a source range (S bytes for a gather, count elements for a sum).
+ *    inside a source range (S bytes for a gather, count elements for a sum) or,
+ *    in the forms flagged ROG_PLAN_SHIFTED_LOADS, inside an aligned 16-byte
+ *    granule that holds bytes of one (so within that range's own pages); the
+ *    bytes read beyond a range are never used.
  */
 #ifndef ROG_H
 #define ROG_H
@@ -138,9 +141,11 @@ typedef struct {
  * srcs[r] are 16-byte aligned, else PEER (PR #491 "What", copy_rank_ordered).
  * PEER copies each payload as a byte head up to a 256-byte boundary of its
  * destination, a body of aligned 16-byte stores, each fed by one 16-byte load
- * of the source bytes at the same payload offset (at any source alignment),
- * and a byte tail: the pages' fallback ("vectors where aligned, byte-wise
- * tail") extended to misaligned payloads, same bytes as a byte-by-byte copy.
+ * of the source bytes at the same payload offset (at any source alignment; or,
+ * where the loads stream past the caches, by aligned granules shared between
+ * neighbouring lanes, see ROG_PLAN_SHIFTED_LOADS), and a byte tail: the pages'
+ * fallback ("vectors where aligned, byte-wise tail") extended to misaligned
+ * payloads, same bytes as a byte-by-byte copy.
  *
  * Errors (nothing enqueued):
  *   ROG_ERR_INVALID_ARGUMENT  srcs NULL; W < 1 or W > rog_max_peers(); S > 0 and
