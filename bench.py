@@ -15,15 +15,17 @@ calls), for the per-call p50.
 
 Besides the headline line the run measures: the same gather with every payload
 and the output at odd byte offsets (the per-payload path); small gathers (the
-pages' 1 - 128 KiB per-rank sizes at 2 and 8 payloads), per call and replayed
-from a HIP graph of 100 calls, next to the eager floor of one tiny torch
-kernel timed the same way; the batched gather (16 tensors, W = 4, one launch);
-the device-to-device copy ceiling; aligned gathers with 64 - 512 MiB outputs,
-warm and with rotating buffer sets (cold); the rank-ordered sum (rog_reduce:
-W = 8 bf16 payloads of 64 MiB, the pages' per-rank sizes of 1 KiB - 4 MiB at
-W = 2 and 8, and a 16-tensor rog_reduce_many); and the CPU oracle on bounded
-samples of the headline gather and of the large sum (the CPU-baseline legs,
-the only ones that call the oracle).
+pages' 1 - 128 KiB per-rank sizes at 2 and 8 payloads), per call, replayed
+from a HIP graph of 100 calls, and timed from C by bench_native.c (a child
+process), next to the eager floor of one tiny torch kernel timed the same way;
+the batched gather (16 tensors, W = 4, one launch); the device-to-device copy
+ceiling and the HBM figure the HIP runtime reports; aligned gathers with
+2 - 512 MiB outputs, warm and with rotating buffer sets (cold); the
+rank-ordered sum (rog_reduce: W = 8 bf16 payloads of 64 MiB, aligned and one
+element off, the pages' per-rank sizes of 1 KiB - 4 MiB at W = 2 and 8, and a
+16-tensor rog_reduce_many); and the CPU oracle on bounded samples of the
+headline gather and of the large sum (the CPU-baseline legs, the only ones
+that call the oracle).
 
 Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: the benchmark measures one GPU.
 """
