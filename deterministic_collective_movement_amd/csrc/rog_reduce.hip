@@ -10,9 +10,10 @@
 // (v_cvt_pk_bf16_f32 for bf16, v_cvt_pk_f16_f32 for binary16), so the bits
 // never depend on the launch.
 //
-// The output is cut like a PEER payload (split_payload): an element head up to
-// the first 256-byte boundary of out, a body of 16-byte vectors, an element
-// tail.  A body lane loads the 16 bytes at the same offset of every source,
+// The output is cut like a PEER payload: an element head, a body of 16-byte
+// vectors, an element tail.  The body starts at out's first 256-byte boundary
+// (split_payload), or in the granule form where source 0 is read in whole
+// 128-byte lines (split_anchored).  A body lane loads the 16 bytes at the same offset of every source,
 // with up to 8 loads in flight, accumulates them in rank order and stores one
 // aligned 16-byte vector.  Where the loads stay cached, each source takes one
 // global_load_dwordx4 per lane at its own alignment; where they stream past
@@ -201,13 +202,17 @@ __device__ __forceinline__ void sum_elem(const void *const *src, uint32_t W, uin
 
 // One wave: body chunk j (body vectors [64j, 64j + 64)) of a sum of `count`
 // elements into out; chunk 0 also sums the head and tail elements.  SH: the
-// granule form (the plan's ROG_PLAN_SHIFTED_LOADS), else one unaligned load
-// per lane and source.
+// granule form (the plan's ROG_PLAN_SHIFTED_LOADS), its body cut so that
+// source 0 is read in whole 128-byte lines (split_anchored); else one
+// unaligned load per lane and source, the body cut at out's first 256-byte
+// boundary (split_payload).
 template <int DT, bool NTL, bool SH>
 __device__ __forceinline__ void sum_chunk(const void *const *src, uint32_t W, void *out, uint64_t count,
                                           uint32_t j) {
     const uint32_t lane = __lane_id();
-    const PeerSplit cut = split_payload(reinterpret_cast<uintptr_t>(out), count * Elem<DT>::kSize);
+    const uint64_t bytes = count * Elem<DT>::kSize;
+    const PeerSplit cut = SH ? split_anchored(reinterpret_cast<uintptr_t>(out), bytes, reinterpret_cast<uintptr_t>(src[0]))
+                             : split_payload(reinterpret_cast<uintptr_t>(out), bytes);
     if (j == 0) {
         for (uint64_t i = lane; i < cut.lo / Elem<DT>::kSize; i += 64) sum_elem<DT>(src, W, i, out);
         for (uint64_t i = cut.hi / Elem<DT>::kSize + lane; i < count; i += 64) sum_elem<DT>(src, W, i, out);

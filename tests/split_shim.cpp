@@ -10,6 +10,13 @@ extern "C" void rog_test_split(uint64_t da, uint64_t S, uint64_t *out2) {
 
 extern "C" uint64_t rog_test_body_align(void) { return rog::kBodyAlign; }
 
+// The sum's granule-form cut (split_anchored).
+extern "C" void rog_test_split_anchored(uint64_t da, uint64_t S, uint64_t anchor, uint64_t *out2) {
+    const rog::PeerSplit p = rog::split_anchored(da, S, anchor);
+    out2[0] = p.lo;
+    out2[1] = p.hi;
+}
+
 // The workgroup-to-chunk remapping of the PEER, BATCH and REDUCE kernels,
 // over a whole launch of n chunks: out[b] = xcd_grouped(b, n).
 extern "C" void rog_test_xcd_grouped(uint32_t n, uint32_t *out) {

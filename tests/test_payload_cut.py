@@ -168,3 +168,46 @@ def test_cut16_takes_bytes_m_to_m_plus_16(cut16):
 
 def test_peer_shift_mode_is_a_known_one(cut16):
     assert cut16.shift in (0, 1, 2)
+
+
+# ---------------------------------------------------------------------------
+# The sum's granule-form cut, anchored on source 0's 128-byte lines
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def anchored(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or os.path.join(b.ROCM, "bin", "hipcc")
+    so = str(tmp_path_factory.mktemp("anch") / "libanch.so")
+    subprocess.check_call([hipcc, "-x", "hip", "-O2", "-std=c++17", "-fPIC", "-shared",
+                           "--offload-arch=gfx950", "-Wno-unused-command-line-argument",
+                           "-I", b.INCLUDE, "-I", b.CSRC, os.path.join(HERE, "split_shim.cpp"), "-o", so],
+                          stderr=subprocess.DEVNULL)
+    lib = ctypes.CDLL(so)
+    lib.rog_test_split_anchored.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                            ctypes.POINTER(ctypes.c_uint64)]
+    out = (ctypes.c_uint64 * 2)()
+
+    def f(da, S, anchor):
+        lib.rog_test_split_anchored(da, S, anchor, out)
+        return out[0], out[1]
+    return f
+
+
+def test_split_anchored_every_alignment(anchored):
+    """For every output and anchor alignment (mod 256, in 2-byte steps as for
+    2-byte elements) and sizes around the body's start: the body starts at the
+    smallest offset where the output is 16-byte aligned and the anchor's granule
+    run starts a 128-byte line, holds whole 16-byte vectors, and leaves a tail
+    under 16 bytes; sizes too small for a body leave it empty."""
+    base = 1 << 40
+    for do in range(0, 256, 2):
+        for ao in range(0, 256, 2):
+            want_lo = next(l for l in range(0, 256) if (do + l) % 16 == 0 and (ao + l) % 128 < 16)
+            assert want_lo < 128
+            for S in (0, 1, want_lo + 14, want_lo + 15, want_lo + 16, want_lo + 17, 1000, 4096 + 7):
+                lo, hi = anchored(base + do, S, base + 512 + ao)
+                if S < want_lo + 16:
+                    assert (lo, hi) == (S, S), (do, ao, S)
+                    continue
+                assert lo == want_lo, (do, ao, S, lo)
+                assert (hi - lo) % 16 == 0 and hi <= S and S - hi < 16, (do, ao, S, lo, hi)
