@@ -203,7 +203,7 @@ def rog_status_string(status: int) -> str:
 # ---------------------------------------------------------------------------
 
 def _ptr_array(addrs: Sequence[int]):
-    return (ctypes.c_void_p * max(1, len(addrs)))(*[ctypes.c_void_p(a) for a in addrs])
+    return (ctypes.c_void_p * max(1, len(addrs)))(*addrs)
 
 
 def rog_gather_ptrs(src_ptrs: Sequence[int], bytes_per_rank: int, out_ptr: int,
@@ -300,16 +300,23 @@ def _nbytes(t: torch.Tensor) -> int:
 def _check_tensor(t: torch.Tensor, what: str, device: torch.device) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % what)
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("%s must be on a GPU (got %s)" % (what, t.device))
-    if t.device != device:
+    if t.get_device() != device.index:
         raise ValueError("%s is on %s, expected %s" % (what, t.device, device))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % what)
 
 
+# torch's current stream of a device as a raw handle, without building a
+# Stream object (a few microseconds per call otherwise).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(stream, device) -> int:
     if stream is None:
+        if _raw_stream is not None:
+            return int(_raw_stream(device.index if device.index is not None else torch.cuda.current_device()))
         stream = torch.cuda.current_stream(device)
     if isinstance(stream, torch.cuda.Stream):
         return int(stream.cuda_stream)
@@ -319,12 +326,16 @@ def _stream_handle(stream, device) -> int:
 def _prepare(srcs: Sequence[torch.Tensor], out: Optional[torch.Tensor]):
     if len(srcs) == 0:
         raise ValueError("need at least one source tensor")
+    _check_tensor(srcs[0], "srcs[0]", srcs[0].device if isinstance(srcs[0], torch.Tensor) else None)
     device = srcs[0].device
-    for i, s in enumerate(srcs):
-        _check_tensor(s, "srcs[%d]" % i, device)
+    idx = device.index
     S = _nbytes(srcs[0])
-    if any(_nbytes(s) != S for s in srcs):
-        raise ValueError("every source must hold the same number of bytes")
+    for i, s in enumerate(srcs):
+        # one pass of cheap checks; the full check names the first failure
+        if not (isinstance(s, torch.Tensor) and s.is_cuda and s.get_device() == idx and s.is_contiguous()):
+            _check_tensor(s, "srcs[%d]" % i, device)
+        if s.numel() * s.element_size() != S:
+            raise ValueError("every source must hold the same number of bytes")
     if out is None:
         out = torch.empty(len(srcs) * S, dtype=torch.uint8, device=device)
     _check_tensor(out, "out", device)
@@ -333,16 +344,20 @@ def _prepare(srcs: Sequence[torch.Tensor], out: Optional[torch.Tensor]):
     return device, S, out
 
 
+# The calling thread's current device index, without torch's lazy-init checks.
+_current_device = getattr(torch._C, "_cuda_getDevice", None) or torch.cuda.current_device
+
+
 class _on_device:
     """Make ``device`` the calling thread's current HIP device for the call (the
     library launches on the current device), restoring the previous one."""
 
     def __init__(self, device: torch.device):
-        self.index = device.index if device.index is not None else torch.cuda.current_device()
+        self.index = device.index if device.index is not None else _current_device()
         self.prev = None
 
     def __enter__(self):
-        cur = torch.cuda.current_device()
+        cur = _current_device()
         if cur != self.index:
             self.prev = cur
             torch.cuda.set_device(self.index)
@@ -410,8 +425,10 @@ def _prepare_reduce(srcs: Sequence[torch.Tensor], out: Optional[torch.Tensor]):
     if dtype not in DTYPES:
         raise ValueError("rog_reduce sums float32, bfloat16 or float16 tensors (got %s)" % dtype)
     n = srcs[0].numel()
+    idx = device.index
     for i, s in enumerate(srcs):
-        _check_tensor(s, "srcs[%d]" % i, device)
+        if not (isinstance(s, torch.Tensor) and s.is_cuda and s.get_device() == idx and s.is_contiguous()):
+            _check_tensor(s, "srcs[%d]" % i, device)
         if s.dtype != dtype or s.numel() != n:
             raise ValueError("every source must have the dtype and element count of srcs[0]")
     if out is None:
