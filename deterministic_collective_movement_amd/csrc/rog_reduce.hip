@@ -147,6 +147,9 @@ __device__ __forceinline__ vec16 sum_vec_wave(const void *const *src, uint32_t W
         const uint32_t g = min(W - r0, kGroup);
         vec16 v[kGroup], h[kGroup];
         uint32_t m[kGroup];
+        // The few cached loads of the granules after the wave's last go out
+        // before the group's streamed loads: issued after them, they waited
+        // behind them and the sum ran 3-6% slower.
 #pragma unroll
         for (uint32_t q = 0; q < kGroup; ++q) {
             v[q] = h[q] = vec16{0, 0, 0, 0};
@@ -155,9 +158,15 @@ __device__ __forceinline__ vec16 sum_vec_wave(const void *const *src, uint32_t W
                 const uint8_t *s = static_cast<const uint8_t *>(src[r0 + q]);
                 m[q] = uniform(uint32_t(reinterpret_cast<uintptr_t>(s) + body) & 15);
                 const vec16 *gp = reinterpret_cast<const vec16 *>(s + off - m[q]);
-                if (live) v[q] = ld16<NTL>(gp);
                 // past the body's end only where that granule holds payload bytes
                 if (own_hi && (m[q] != 0 || next_in_body)) h[q] = ld16<false>(gp + 1);
+            }
+        }
+#pragma unroll
+        for (uint32_t q = 0; q < kGroup; ++q) {
+            if (q < g && live) {
+                const uint8_t *s = static_cast<const uint8_t *>(src[r0 + q]);
+                v[q] = ld16<NTL>(reinterpret_cast<const vec16 *>(s + off - m[q]));
             }
         }
 #pragma unroll
