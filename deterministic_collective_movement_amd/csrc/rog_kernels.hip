@@ -13,17 +13,19 @@
 //    vectors; each of its U loads and U stores is one dwordx4 instruction over
 //    64 consecutive vectors (1 KiB, fully coalesced).  The payload of a chunk
 //    is found once per chunk, in scalar registers, by one 32-bit multiply-high
-//    (no division on the device at all); a chunk that crosses a payload
-//    boundary walks the few payloads it touches with per-lane range masks.
+//    (no division on the device at all); in a chunk that crosses a payload
+//    boundary each lane finds its own payload with the same multiply-high.
 //  * PEER kernel (anything else): each payload on its own -- a byte head up to
 //    a 256-byte boundary of its destination, a body of aligned 16-byte stores,
 //    a byte tail.  Every body store takes the 16 source bytes at the same
 //    payload offset, whatever byte alignment the source has.  At a multiple of
 //    4 bytes that is one unaligned global_load_dwordx4 (gfx950 global loads
-//    run in unaligned-access mode under the HSA runtime).  Otherwise the
-//    multi-WG lanes load aligned granules and rebuild their bytes from their
-//    own granule and the next lane's (a lane shuffle and v_alignbyte), which
-//    streams faster than split unaligned loads.  The pages' fallback copies
+//    run in unaligned-access mode under the HSA runtime), and so it is with
+//    cached loads at any alignment.  Where the loads stream past the caches
+//    and the source sits an odd or 2-mod-4 number of bytes past a 16-byte
+//    granule, the multi-WG lanes load aligned granules instead and rebuild
+//    their bytes from their own granule and the next lane's (a lane shuffle
+//    and v_alignbyte), which streams faster than split unaligned loads.  The pages' fallback copies
 //    such payloads byte by byte ("vectors where aligned, byte-wise tail"); the
 //    bytes written are the same.  Multi-WG, the body is cut into 1 KiB chunks,
 //    one wave per chunk, all payloads at once; single-WG, the one workgroup

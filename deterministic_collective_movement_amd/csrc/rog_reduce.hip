@@ -12,10 +12,10 @@
 //
 // The output is cut like a PEER payload: an element head, a body of 16-byte
 // vectors, an element tail.  The body starts at out's first 256-byte boundary
-// (split_payload), or in the granule form where source 0 is read in whole
-// 128-byte lines (split_anchored).  A body lane loads the 16 bytes at the same offset of every source,
-// with up to 8 loads in flight, accumulates them in rank order and stores one
-// aligned 16-byte vector.  Where the loads stay cached, each source takes one
+// (split_payload), or, in the granule form, where source 0 is read in whole
+// 128-byte lines (split_anchored).  A body lane loads the 16 bytes at the same
+// offset of every source, with up to 8 loads in flight, accumulates them in
+// rank order and stores one aligned 16-byte vector.  Where the loads stay cached, each source takes one
 // global_load_dwordx4 per lane at its own alignment; where they stream past
 // the caches (ROG_PLAN_NT_LOADS, then ROG_PLAN_SHIFTED_LOADS), the launch
 // takes the granule form, which reads every source as aligned granules, each
