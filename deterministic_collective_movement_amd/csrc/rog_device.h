@@ -25,9 +25,30 @@ __device__ __forceinline__ vec16 ldu16(const uint8_t *p) {
     else return *q;
 }
 
-__device__ __forceinline__ void st16(vec16 *p, vec16 v) {
-    if constexpr (kNtStore) __builtin_nontemporal_store(v, p);
-    else *p = v;
+// Word 3 of a buffer resource for raw (untyped, unswizzled, unstrided) buffer
+// accesses on CDNA: a 32-bit data format and nothing else set.
+constexpr int kBufferWord3 = 0x00020000;
+
+// A window [base, base + bytes) of an output, written by 16-byte buffer stores
+// at byte offsets from base under the cache policy AUX.  base and bytes are
+// wave-uniform (the resource lives in scalar registers), bytes < 2^31 and a
+// multiple of 16; the hardware drops any store that would leave the window.
+template <int AUX>
+class OutWindow {
+public:
+    __device__ __forceinline__ OutWindow(void *base, uint32_t bytes)
+        : r_(__builtin_amdgcn_make_buffer_rsrc(base, 0, int(bytes), kBufferWord3)) {}
+    __device__ __forceinline__ void st16(uint32_t off, vec16 v) const {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r_, int(off), 0, AUX);
+    }
+
+private:
+    __amdgpu_buffer_rsrc_t r_;
+};
+
+// Bytes of [lo, hi) that a window starting at lo and at most cap long holds.
+__device__ __forceinline__ uint32_t window_bytes(uint64_t lo, uint64_t hi, uint64_t cap) {
+    return uint32_t(lo < hi ? (hi - lo < cap ? hi - lo : cap) : 0);
 }
 
 __device__ __forceinline__ uint32_t uniform(uint32_t x) {

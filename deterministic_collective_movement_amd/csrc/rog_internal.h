@@ -27,17 +27,17 @@ constexpr int kMaxBatchPtrs = 192;
 #ifndef ROG_REDUCE_SINGLE_WG_MAX_BYTES
 #define ROG_REDUCE_SINGLE_WG_MAX_BYTES (64 * 1024)
 #endif
-#ifndef ROG_FLAT_BLOCK
-#define ROG_FLAT_BLOCK 64
-#endif
 #ifndef ROG_FLAT_UNROLL
 #define ROG_FLAT_UNROLL 1
 #endif
 #ifndef ROG_SINGLE_UNROLL
 #define ROG_SINGLE_UNROLL 4
 #endif
-#ifndef ROG_NT_STORE
-#define ROG_NT_STORE 1
+#ifndef ROG_STORE_AUX
+#define ROG_STORE_AUX 18
+#endif
+#ifndef ROG_SUM_STORE_AUX
+#define ROG_SUM_STORE_AUX 2
 #endif
 #ifndef ROG_NT_LOAD_MIN_BYTES
 #define ROG_NT_LOAD_MIN_BYTES (384ull << 20)
@@ -71,13 +71,23 @@ constexpr size_t kReduceSingleWgMaxBytes = ROG_REDUCE_SINGLE_WG_MAX_BYTES;
 // instruction over 64 consecutive vectors (1 KiB).  Small workgroups of one
 // wave, one 1 KiB chunk each, measured fastest for the HBM-bound launches
 // (FLAT, PEER, BATCH and REDUCE alike).
-constexpr int kFlatBlock = ROG_FLAT_BLOCK;        // multi-WG FLAT workgroup (threads)
 constexpr int kFlatUnroll = ROG_FLAT_UNROLL;      // vectors per lane per chunk
-constexpr int kWaveBlock = 64;                    // multi-WG PEER, BATCH and REDUCE workgroup
+constexpr int kWaveBlock = 64;                    // multi-WG workgroup (FLAT, PEER, BATCH, REDUCE)
 constexpr int kSingleBlock = 1024;                // the single workgroup (16 waves)
 constexpr int kSingleUnroll = ROG_SINGLE_UNROLL;  // single-WG FLAT vectors per lane
 constexpr int kSinglePeerUnroll = 4;              // single-WG PEER vectors per thread
-constexpr bool kNtStore = ROG_NT_STORE != 0;      // non-temporal 16-byte stores
+// Cache-policy bits of the gathers' 16-byte output stores (the buffer
+// instructions' aux operand: 1 = sc0, 2 = nt, 16 = sc1).  18 = nt sc1:
+// streamed, and written through each XCD's L2 at device scope, so the end of
+// a launch finds no dirty output lines there to write back.  Against nt alone
+// it measured 3 % faster on 8 x 64 MiB gathers (FLAT and PEER alike).  It
+// loses where neighbouring chunks split output lines between them, since two
+// partial writes then go out instead of one merged line.
+constexpr int kStoreAux = ROG_STORE_AUX;
+// The rank-ordered sum's stores: nt alone.  Its granule form starts the body
+// where source 0's lines start, so output lines may be split between chunks;
+// there nt sc1 measured 3-7 % slower, and it gained nothing where aligned.
+constexpr int kSumStoreAux = ROG_SUM_STORE_AUX;
 // Vectors per lane of the single-WG FLAT kernel for an output of n_vec vectors:
 // 1 while one pass of 16 waves covers the output (1 KiB wave chunks then line
 // up with payloads of 1 KiB or more, so no chunk takes the per-lane payload
@@ -179,18 +189,44 @@ __host__ __device__ inline uint32_t xcd_grouped(uint32_t b, uint32_t n) {
     return (k / kXcdRun) * kSpan + x * kXcdRun + k % kXcdRun;
 }
 
+// FLAT chunks of `chunk` output vectors, shifted back by `shift` vectors:
+// chunk c covers vectors [c * chunk - shift, (c + 1) * chunk - shift) clipped
+// to [0, n_vec).  With shift = (out % 128) / 16 every chunk after the first
+// starts on one of the output's 128-byte lines, so no two chunks write parts
+// of one line.  The host keeps shift = 0 unless n_vec < 2^31, so c * chunk
+// never wraps (c * chunk < n_vec + shift, and 2^32 is a multiple of chunk).
+struct ChunkSpan {
+    uint32_t b;   // first vector
+    uint32_t n;   // vectors, >= 1 for c < flat_chunk_count(...)
+};
+__host__ __device__ inline ChunkSpan flat_span(uint32_t c, uint32_t chunk, uint32_t shift, uint32_t n_vec) {
+    const uint32_t b = c == 0 ? 0 : c * chunk - shift;
+    const uint32_t cap = c == 0 ? chunk - shift : chunk;
+    const uint32_t left = n_vec - b;
+    return ChunkSpan{b, left < cap ? left : cap};
+}
+__host__ __device__ inline uint32_t flat_chunk_count(uint32_t n_vec, uint32_t chunk, uint32_t shift) {
+    return uint32_t((uint64_t(n_vec) + shift + chunk - 1) / chunk);
+}
+// The shift for an output at address out of n_vec vectors (out 16-byte aligned).
+inline uint32_t flat_shift(uint64_t out, uint64_t n_vec) {
+    return n_vec < (uint64_t(1) << 31) ? uint32_t((out & 127) >> 4) : 0;
+}
+
 // ---------------------------------------------------------------------------
 // Kernel arguments
 // ---------------------------------------------------------------------------
 
 // FLAT: the whole output is one space of n_vec 16-byte vectors; vector v comes
-// from payload r = v / vpr at index v - r*vpr.
+// from payload r = v / vpr at index v - r*vpr.  Chunks as flat_span cuts them.
 struct FlatArgs {
     const void *src[kMaxPeers];
     void *out;
     uint32_t n_vec;
     uint32_t vpr;
     Divider div;
+    uint32_t shift;   // flat_span's shift: 0..7 (multi-WG), 0 (single-WG)
+    uint32_t runs;    // multi-WG: 1 = chunks to the XCDs in runs, 0 = round-robin
 };
 
 // PEER: each payload is its own copy job, cut by split_payload into a byte
@@ -209,11 +245,11 @@ struct PeerArgs {
     Divider cdiv;
 };
 
-// One tensor of a batch.  Chunks [first_chunk, first_chunk + n_chunks) of the
-// launch belong to it.  FLAT tensors: chunk c covers output vectors
-// [64c, 64c + 64), the payload found by div (divides by vpr).  PEER tensors:
-// chunk c is chunk c % chunks_per_peer of payload c / chunks_per_peer (div
-// divides by chunks_per_peer).
+// One tensor of a batch.  Chunks [first, first + n_chunks) of the launch
+// belong to it.  FLAT tensors: chunk c is flat_span(c, 64, shift, n_vec), the
+// payload found by div (divides by vpr).  PEER tensors: chunk c is chunk
+// c % chunks_per_peer of payload c / chunks_per_peer (div divides by
+// chunks_per_peer).
 struct BatchTensor {
     uint64_t out;
     uint64_t S;
@@ -221,6 +257,7 @@ struct BatchTensor {
     uint32_t flat;              // 1: FLAT tensor, 0: PEER tensor
     uint32_t vpr;               // FLAT: vectors per rank
     uint32_t n_vec;             // FLAT: W * vpr
+    uint32_t shift;             // FLAT: flat_span's shift
     uint32_t chunks_per_peer;   // PEER
     Divider div;
 };
@@ -232,7 +269,7 @@ struct BatchArgs {
     uint32_t n;
     uint32_t W;
     uint32_t n_chunks;                // all tensors' chunks
-    uint32_t flat_chunks;             // chunks of the FLAT tensors, which come first
+    uint32_t aligned_chunks;          // chunks of the line-aligned FLAT tensors, which come first
 };
 
 static_assert(sizeof(BatchArgs) <= 4096, "kernel arguments must stay below 4 KiB");
@@ -269,7 +306,7 @@ extern thread_local int g_last_hip_error;
 rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out,
                        rog_path path, Plan *plan);
 
-// One tensor of a batched sum: chunks [first_chunk, first_chunk + n_chunks) of
+// One tensor of a batched sum: chunks [first, first + n_chunks) of
 // the launch, each 64 body vectors of its output (chunk 0 also sums the head
 // and tail elements).
 struct ReduceTensor {

@@ -45,35 +45,39 @@ namespace rog {
 
 // ---------------------------------------------------------------------------
 // FLAT: vectors [0, n_vec) of one gather.  Vector v comes from payload
-// r = v / vpr at index v - r*vpr.  Chunk c is vectors [64*U*c, 64*U*(c + 1)).
+// r = v / vpr at index v - r*vpr.  Chunk c is flat_span(c, 64*U, shift, n_vec):
+// 64*U vectors, the first chunk shorter by shift so that the others start on
+// the output's 128-byte lines.
 // ---------------------------------------------------------------------------
 template <int U, bool NTL>
 __device__ __forceinline__ void flat_chunk(const void *const *src, vec16 *o, uint32_t n_vec,
-                                           uint32_t vpr, const Divider &div, uint32_t c) {
+                                           uint32_t vpr, const Divider &div, uint32_t shift, uint32_t c) {
     constexpr uint32_t kChunk = 64 * U;
     const uint32_t lane = __lane_id();
-    // n_vec < 2^32 and b is a multiple of kChunk below n_vec, so no expression
-    // below wraps (b + kChunk - 1 <= 2^32 - 1; seg_lo + vpr <= n_vec).
-    const uint32_t b = c * kChunk;                  // first vector of the chunk
-    const uint32_t n = min(n_vec - b, kChunk);      // vectors in the chunk
+    // b < e = b + n <= n_vec < 2^32, and b + kChunk - 1 <= 2^32 - 1 (shift is
+    // 0 unless n_vec < 2^31, else b is a multiple of kChunk), so no
+    // expression below wraps (seg_lo + vpr <= n_vec).
+    const ChunkSpan span = flat_span(c, kChunk, shift, n_vec);
+    const uint32_t b = span.b;                      // first vector of the chunk
+    const uint32_t n = span.n;                      // vectors in the chunk
     const uint32_t e = b + n;                       // chunk end
     const uint32_t r = divide(b, div);              // payload of b (scalar)
     const uint32_t seg_lo = r * vpr;
+    const OutWindow<kStoreAux> w(o + b, n * 16);    // the chunk's output
     if (e <= seg_lo + vpr) {
         // The whole chunk lies in payload r: scalar bases, lane offsets.
         const vec16 *s = static_cast<const vec16 *>(src[r]) + (b - seg_lo);
-        vec16 *d = o + b;
         if (n == kChunk) {
             vec16 v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) v[u] = ld16<NTL>(s + u * 64 + lane);
 #pragma unroll
-            for (int u = 0; u < U; ++u) st16(d + u * 64 + lane, v[u]);
+            for (int u = 0; u < U; ++u) w.st16(16 * (u * 64 + lane), v[u]);
         } else {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint32_t k = u * 64 + lane;
-                if (k < n) st16(d + k, ld16<NTL>(s + k));
+                if (k < n) w.st16(16 * k, ld16<NTL>(s + k));
             }
         }
     } else {
@@ -87,25 +91,20 @@ __device__ __forceinline__ void flat_chunk(const void *const *src, vec16 *o, uin
             if (k < e) {
                 const uint32_t rk = divide(k, div);
                 const vec16 *s = static_cast<const vec16 *>(src[rk]);
-                st16(o + k, ld16<NTL>(s + (k - rk * vpr)));
+                w.st16(16 * (k - b), ld16<NTL>(s + (k - rk * vpr)));
             }
         }
     }
 }
 
-// FLAT by workgroups `block` of `nblocks`, each of `waves` waves: a wave owns
-// chunks wave_id, wave_id + stride, ... (grid-stride over a capped grid).
+// FLAT by one workgroup of `waves` waves: wave w owns chunks w, w + waves, ...
 template <int U, bool NTL>
-__device__ __forceinline__ void flat_copy(const void *const *src, void *out, uint32_t n_vec,
-                                          uint32_t vpr, const Divider &div, uint32_t block,
-                                          uint32_t nblocks, uint32_t waves) {
+__device__ __forceinline__ void flat_copy(const FlatArgs &a, uint32_t waves) {
     constexpr uint32_t kChunk = 64 * U;
     const uint32_t wave = uniform(threadIdx.x / 64);
-    const uint32_t n_chunks = n_vec / kChunk + (n_vec % kChunk != 0);
-    const uint32_t stride = nblocks * waves;
-    vec16 *o = static_cast<vec16 *>(out);
-    for (uint32_t c = block * waves + wave; c < n_chunks; c += stride)
-        flat_chunk<U, NTL>(src, o, n_vec, vpr, div, c);
+    const uint32_t n_chunks = flat_chunk_count(a.n_vec, kChunk, a.shift);
+    for (uint32_t c = wave; c < n_chunks; c += waves)
+        flat_chunk<U, NTL>(a.src, static_cast<vec16 *>(a.out), a.n_vec, a.vpr, a.div, a.shift, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -136,11 +135,13 @@ __device__ __forceinline__ void peer_chunk(const uint8_t *s, uint8_t *d, uint64_
         for (uint64_t i = lane; i < cut.lo; i += 64) d[i] = s[i];
         for (uint64_t i = cut.hi + lane; i < S; i += 64) d[i] = s[i];
     }
-    const uint64_t off = cut.lo + 16 * (uint64_t(j) * 64 + lane);
+    const uint64_t w0 = cut.lo + uint64_t(j) * 1024;  // the wave's first body byte
+    const OutWindow<kStoreAux> w(d + w0, window_bytes(w0, cut.hi, 1024));
+    const uint64_t off = w0 + 16 * lane;
     const bool live = off < cut.hi;
     const uint32_t m = uniform(uint32_t(reinterpret_cast<uintptr_t>(s + cut.lo)) & 15);
     if (!NTL || !shift_granules(m, kPeerShift)) {
-        if (live) st16(reinterpret_cast<vec16 *>(d + off), ldu16<NTL>(s + off));
+        if (live) w.st16(16 * lane, ldu16<NTL>(s + off));
         return;
     }
     const vec16 *g = reinterpret_cast<const vec16 *>(s + off - m);
@@ -153,7 +154,7 @@ __device__ __forceinline__ void peer_chunk(const uint8_t *s, uint8_t *d, uint64_
     // Lane l + 1's granule; all 64 lanes take part in the shuffle.
     const vec16 next = vec16{__shfl_down(lo.x, 1u), __shfl_down(lo.y, 1u), __shfl_down(lo.z, 1u),
                              __shfl_down(lo.w, 1u)};
-    if (live) st16(reinterpret_cast<vec16 *>(d + off), cut16(lo, own_hi ? hi : next, m));
+    if (live) w.st16(16 * lane, cut16(lo, own_hi ? hi : next, m));
 }
 
 // One workgroup of nt threads, the whole payload: head and tail bytes, then the
@@ -165,21 +166,22 @@ __device__ __forceinline__ void peer_whole(const uint8_t *s, uint8_t *d, uint64_
     for (uint64_t i = tid; i < cut.lo; i += nt) d[i] = s[i];
     for (uint64_t i = cut.hi + tid; i < S; i += nt) d[i] = s[i];
     const uint8_t *sb = s + cut.lo;
-    vec16 *db = reinterpret_cast<vec16 *>(d + cut.lo);
+    uint8_t *db = d + cut.lo;
     const uint64_t count = (cut.hi - cut.lo) >> 4;
     const uint64_t tile = uint64_t(nt) * U;
     for (uint64_t base = 0; base < count; base += tile) {
+        const OutWindow<kStoreAux> w(db + 16 * base, window_bytes(16 * base, 16 * count, 16 * tile));
         if (base + tile <= count) {
             vec16 v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) v[u] = ldu16<NTL>(sb + 16 * (base + u * nt + tid));
 #pragma unroll
-            for (int u = 0; u < U; ++u) st16(db + base + u * nt + tid, v[u]);
+            for (int u = 0; u < U; ++u) w.st16(16 * (u * nt + tid), v[u]);
         } else {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint64_t k = base + u * nt + tid;
-                if (k < count) st16(db + k, ldu16<NTL>(sb + 16 * k));
+                if (k < count) w.st16(uint32_t(16 * (k - base)), ldu16<NTL>(sb + 16 * k));
             }
         }
     }
@@ -188,17 +190,26 @@ __device__ __forceinline__ void peer_whole(const uint8_t *s, uint8_t *d, uint64_
 // ---------------------------------------------------------------------------
 // Kernels
 // ---------------------------------------------------------------------------
-// Multi-WG FLAT: workgroups of BLOCK threads over the whole output.
-template <int BLOCK, bool NTL>
-__global__ __launch_bounds__(BLOCK) void rog_flat_kernel(FlatArgs a) {
-    flat_copy<kFlatUnroll, NTL>(a.src, a.out, a.n_vec, a.vpr, a.div, blockIdx.x, gridDim.x, BLOCK / 64);
+// Multi-WG FLAT: one wave per workgroup and per chunk, grid-strided over a
+// capped grid.  Where the output, the payload size and every source sit on
+// 128-byte lines, chunks go to the XCDs round-robin.  Otherwise neighbouring
+// chunks read parts of the same source lines, and they go to the XCDs in runs
+// (xcd_grouped) that keep those lines in one L2: 17-26 % faster there, 1-1.5 %
+// slower on aligned gathers.
+template <bool NTL>
+__global__ __launch_bounds__(kWaveBlock) void rog_flat_kernel(FlatArgs a) {
+    constexpr uint32_t kChunk = 64 * kFlatUnroll;
+    const uint32_t n_chunks = flat_chunk_count(a.n_vec, kChunk, a.shift);
+    for (uint32_t vb = blockIdx.x; vb < n_chunks; vb += gridDim.x)
+        flat_chunk<kFlatUnroll, NTL>(a.src, static_cast<vec16 *>(a.out), a.n_vec, a.vpr, a.div, a.shift,
+                                     a.runs ? xcd_grouped(vb, n_chunks) : vb);
 }
 
 // Single-WG FLAT: one workgroup of as many waves as there are chunks (<= 16),
 // U = single_flat_unroll(n_vec) vectors per lane.
 template <int U, bool NTL>
 __global__ __launch_bounds__(kSingleBlock) void rog_flat_single_kernel(FlatArgs a) {
-    flat_copy<U, NTL>(a.src, a.out, a.n_vec, a.vpr, a.div, 0, 1, blockDim.x / 64);
+    flat_copy<U, NTL>(a, blockDim.x / 64);
 }
 
 // Multi-WG PEER: one wave per workgroup and per body chunk, chunks grouped by
@@ -223,23 +234,24 @@ __global__ __launch_bounds__(kSingleBlock) void rog_peer_single_kernel(PeerArgs 
                                            static_cast<uint8_t *>(a.out) + uint64_t(r) * a.S, a.S, blockDim.x);
 }
 
-// BATCH: one wave per workgroup and per chunk of some tensor.  The FLAT
-// tensors' chunks come first and go to the XCDs round-robin, as in the FLAT
-// kernel; the PEER tensors' chunks follow, handed out in XCD runs as in the
-// PEER kernel.  (Runs over the FLAT chunks too measured 5 % slower on an
-// aligned batch; no runs at all, 9 % slower on 8 x 64 MiB PEER payloads.)
+// BATCH: one wave per workgroup and per chunk of some tensor.  The chunks of
+// the FLAT tensors whose output, size and sources all sit on 128-byte lines
+// come first and go to the XCDs round-robin; the other tensors' chunks (FLAT
+// or PEER) follow, handed out in XCD runs as in the FLAT and PEER kernels.
+// (Runs over the aligned FLAT chunks too measured 5 % slower on an aligned
+// batch; no runs at all, 9 % slower on 8 x 64 MiB PEER payloads.)
 template <bool NTL>
 __global__ __launch_bounds__(kWaveBlock) void rog_batch_kernel(BatchArgs a) {
     for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x) {
-        const uint32_t c = vb < a.flat_chunks
+        const uint32_t c = vb < a.aligned_chunks
                                ? vb
-                               : a.flat_chunks + xcd_grouped(vb - a.flat_chunks, a.n_chunks - a.flat_chunks);
+                               : a.aligned_chunks + xcd_grouped(vb - a.aligned_chunks, a.n_chunks - a.aligned_chunks);
         const uint32_t lo = batch_tensor(a.first, a.n, c);
         const BatchTensor &t = a.t[lo];
         const uint32_t lc = c - a.first[lo];
         const void *const *src = a.src + lo * a.W;
         if (t.flat) {
-            flat_chunk<kFlatUnroll, NTL>(src, reinterpret_cast<vec16 *>(t.out), t.n_vec, t.vpr, t.div, lc);
+            flat_chunk<kFlatUnroll, NTL>(src, reinterpret_cast<vec16 *>(t.out), t.n_vec, t.vpr, t.div, t.shift, lc);
         } else {
             const uint32_t r = divide(lc, t.div);
             peer_chunk<NTL>(static_cast<const uint8_t *>(src[r]), reinterpret_cast<uint8_t *>(t.out) + uint64_t(r) * t.S,
@@ -283,7 +295,7 @@ rog_status launch_plan(Plan &p, hipStream_t stream) {
             k = ntl ? kfn(&rog_flat_single_kernel<1, true>) : kfn(&rog_flat_single_kernel<1, false>);
         else if (single)
             k = ntl ? kfn(&rog_flat_single_kernel<kSingleUnroll, true>) : kfn(&rog_flat_single_kernel<kSingleUnroll, false>);
-        else        k = ntl ? kfn(&rog_flat_kernel<kFlatBlock, true>) : kfn(&rog_flat_kernel<kFlatBlock, false>);
+        else        k = ntl ? kfn(&rog_flat_kernel<true>) : kfn(&rog_flat_kernel<false>);
         return launch(k, i.grid, i.block, p.flat, stream);
     case ROG_KERNEL_PEER:
         if (single) k = ntl ? kfn(&rog_peer_single_kernel<true>) : kfn(&rog_peer_single_kernel<false>);

@@ -95,11 +95,17 @@ uint32_t max_grid(int block) {
     return std::min<uint32_t>(kGridCap, 0xFFFFFFFFu / uint32_t(block));
 }
 
-// Multi-WG FLAT grid: one wave per chunk of 64*unroll vectors.
-uint32_t flat_blocks(uint64_t n_vec, int block, int unroll, uint32_t cap) {
-    const uint64_t chunks = ceil_div(n_vec, 64 * uint64_t(unroll));
-    const uint64_t blocks = ceil_div(chunks, uint64_t(block) / 64);
-    return uint32_t(std::max<uint64_t>(1, std::min<uint64_t>(blocks, cap)));
+// Multi-WG FLAT grid: one one-wave workgroup per chunk (flat_span).
+uint32_t flat_blocks(uint32_t n_vec, uint32_t shift) {
+    const uint32_t chunks = flat_chunk_count(n_vec, 64 * uint32_t(kFlatUnroll), shift);
+    return std::max<uint32_t>(1, std::min<uint32_t>(chunks, max_grid(kWaveBlock)));
+}
+
+// Whether the output, the payload size and every source sit on 128-byte lines.
+bool line_aligned(const void *const *srcs, int W, size_t S, const void *out) {
+    uint64_t bits = addr(out) | uint64_t(S);
+    for (int r = 0; r < W; ++r) bits |= addr(srcs[r]);
+    return (bits & 127) == 0;
 }
 
 // Multi-WG PEER: 1 KiB body chunks per payload, enough for the largest body
@@ -162,10 +168,12 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
         a.n_vec = uint32_t(total / 16);
         a.vpr = uint32_t(S / 16);
         a.div = make_divider(a.vpr);
+        a.shift = single ? 0 : flat_shift(addr(out), a.n_vec);
+        a.runs = !single && !line_aligned(srcs, W, S, out);
         info.kernel = ROG_KERNEL_FLAT;
         info.units = a.n_vec;
-        info.block = single ? flat_single_block(a.n_vec) : kFlatBlock;
-        info.grid = single ? 1 : flat_blocks(a.n_vec, kFlatBlock, kFlatUnroll, max_grid(kFlatBlock));
+        info.block = single ? flat_single_block(a.n_vec) : kWaveBlock;
+        info.grid = single ? 1 : flat_blocks(a.n_vec, a.shift);
         info.peer_magic = a.div.magic;
         info.peer_sh1 = a.div.sh1;
         info.peer_sh2 = a.div.sh2;
@@ -364,19 +372,23 @@ rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *arg
 
     memset(args, 0, sizeof(*args));
     args->W = uint32_t(W);
-    // One chunk per wave: 64 * kFlatUnroll output vectors of a FLAT tensor, 64
-    // body vectors of one payload of a PEER tensor.  Each tensor has fewer than
-    // 2^26 + W chunks, so the batch's chunk count fits 32 bits.  FLAT tensors
-    // come first: their chunks go to the XCDs round-robin, the PEER tensors'
-    // chunks that follow in XCD runs.
-    bool flat[kMaxBatch];
-    for (int t = 0; t < n; ++t) flat[t] = totals[t] && is_flat(descs[t].srcs, W, descs[t].bytes_per_rank, descs[t].out);
+    // One chunk per wave: 64 * kFlatUnroll output vectors of a FLAT tensor
+    // (flat_span), 64 body vectors of one payload of a PEER tensor.  Each
+    // tensor has fewer than 2^26 + W chunks, so the batch's chunk count fits
+    // 32 bits.  The line-aligned FLAT tensors come first: their chunks go to
+    // the XCDs round-robin, the other tensors' chunks that follow in XCD runs.
+    bool flat[kMaxBatch], aligned[kMaxBatch];
+    for (int t = 0; t < n; ++t) {
+        const rog_gather_desc &d = descs[t];
+        flat[t] = totals[t] && is_flat(d.srcs, W, d.bytes_per_rank, d.out);
+        aligned[t] = flat[t] && line_aligned(d.srcs, W, d.bytes_per_rank, d.out);
+    }
     uint64_t next = 0;
     uint32_t k = 0;
     for (int pass = 0; pass < 2; ++pass) {
-        if (pass == 1) args->flat_chunks = uint32_t(next);
+        if (pass == 1) args->aligned_chunks = uint32_t(next);
         for (int t = 0; t < n; ++t) {
-            if (!totals[t] || flat[t] != (pass == 0)) continue;   // empty tensors get no chunks
+            if (!totals[t] || aligned[t] != (pass == 0)) continue;   // empty tensors get no chunks
             const rog_gather_desc &d = descs[t];
             const size_t S = d.bytes_per_rank;
             BatchTensor &bt = args->t[k];
@@ -389,7 +401,8 @@ rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *arg
                 bt.n_vec = uint32_t(totals[t] / 16);
                 bt.vpr = uint32_t(S / 16);
                 bt.div = make_divider(bt.vpr);
-                bt.n_chunks = uint32_t(ceil_div(bt.n_vec, 64 * uint64_t(kFlatUnroll)));
+                bt.shift = flat_shift(bt.out, bt.n_vec);
+                bt.n_chunks = flat_chunk_count(bt.n_vec, 64 * uint32_t(kFlatUnroll), bt.shift);
             } else {
                 bt.flat = 0;
                 bt.chunks_per_peer = peer_chunks_per_peer(S);

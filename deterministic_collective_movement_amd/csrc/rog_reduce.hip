@@ -226,14 +226,16 @@ __device__ __forceinline__ void sum_chunk(const void *const *src, uint32_t W, vo
         for (uint64_t i = lane; i < cut.lo / Elem<DT>::kSize; i += 64) sum_elem<DT>(src, W, i, out);
         for (uint64_t i = cut.hi / Elem<DT>::kSize + lane; i < count; i += 64) sum_elem<DT>(src, W, i, out);
     }
-    const uint64_t off = cut.lo + 16 * (uint64_t(j) * 64 + lane);
+    const uint64_t w0 = cut.lo + uint64_t(j) * 1024;  // the wave's first body byte
+    const OutWindow<kSumStoreAux> w(static_cast<uint8_t *>(out) + w0, window_bytes(w0, cut.hi, 1024));
+    const uint64_t off = w0 + 16 * lane;
     const bool live = off < cut.hi;
     if constexpr (SH) {
         const bool own_hi = live && (lane == 63 || off + 16 >= cut.hi);
         const vec16 v = sum_vec_wave<DT, NTL>(src, W, off, cut.lo, live, own_hi, off + 16 < cut.hi);
-        if (live) st16(reinterpret_cast<vec16 *>(static_cast<uint8_t *>(out) + off), v);
+        if (live) w.st16(16 * lane, v);
     } else if (live) {
-        st16(reinterpret_cast<vec16 *>(static_cast<uint8_t *>(out) + off), sum_vec<DT, NTL>(src, W, off));
+        w.st16(16 * lane, sum_vec<DT, NTL>(src, W, off));
     }
 }
 
@@ -268,8 +270,12 @@ __global__ __launch_bounds__(kSingleBlock) void rog_reduce_single_kernel(ReduceA
     uint8_t *o = static_cast<uint8_t *>(a.out);
     for (uint64_t i = tid; i < cut.lo / Elem<DT>::kSize; i += nt) sum_elem<DT>(a.src, a.W, i, a.out);
     for (uint64_t i = cut.hi / Elem<DT>::kSize + tid; i < a.count; i += nt) sum_elem<DT>(a.src, a.W, i, a.out);
-    for (uint64_t off = cut.lo + 16 * uint64_t(tid); off < cut.hi; off += 16 * uint64_t(nt))
-        st16(reinterpret_cast<vec16 *>(o + off), sum_vec<DT, NTL>(a.src, a.W, off));
+    const uint64_t step = 16 * uint64_t(nt);
+    for (uint64_t t0 = cut.lo; t0 < cut.hi; t0 += step) {
+        const OutWindow<kSumStoreAux> w(o + t0, window_bytes(t0, cut.hi, step));
+        const uint64_t off = t0 + 16 * uint64_t(tid);
+        if (off < cut.hi) w.st16(16 * tid, sum_vec<DT, NTL>(a.src, a.W, off));
+    }
 }
 
 template <typename K>

@@ -72,6 +72,26 @@ int main(int argc, char **argv) {
         if (st == ROG_OK && p.info.kernel != ROG_KERNEL_NONE &&
             (p.info.grid == 0 || p.info.block == 0 || uint64_t(p.info.grid) * p.info.block >= (uint64_t(1) << 32)))
             fail("plan_gather: bad launch", i);
+        if (st == ROG_OK && p.info.kernel == ROG_KERNEL_FLAT) {
+            // The chunks tile [0, n_vec) and, shifted, start on the output's lines.
+            const rog::FlatArgs &a = p.flat;
+            const uint32_t chunk = 64 * uint32_t(p.info.path == ROG_PATH_SINGLE_WG ? 1 : rog::kFlatUnroll);
+            const uint32_t nc = rog::flat_chunk_count(a.n_vec, chunk, a.shift);
+            if (a.shift > 7 || (a.n_vec >= (uint32_t(1) << 31) && a.shift) ||
+                (p.info.path == ROG_PATH_SINGLE_WG && (a.shift || a.runs)))
+                fail("plan_gather: FLAT shift", i);
+            uint64_t bits = out | S;
+            for (int r = 0; r < W; ++r) bits |= uint64_t(reinterpret_cast<uintptr_t>(srcs[r]));
+            if (p.info.path == ROG_PATH_MULTI_WG && a.runs != ((bits & 127) != 0))
+                fail("plan_gather: FLAT runs", i);
+            const rog::ChunkSpan c0 = rog::flat_span(0, chunk, a.shift, a.n_vec);
+            const rog::ChunkSpan cl = rog::flat_span(nc - 1, chunk, a.shift, a.n_vec);
+            if (c0.b != 0 || c0.n == 0 || cl.n == 0 || uint64_t(cl.b) + cl.n != a.n_vec)
+                fail("plan_gather: FLAT chunks", i);
+            if (nc > 1 && a.n_vec < (uint32_t(1) << 31) && p.info.path == ROG_PATH_MULTI_WG &&
+                ((out + 16 * uint64_t(rog::flat_span(1, chunk, a.shift, a.n_vec).b)) & 127) != 0)
+                fail("plan_gather: FLAT chunk 1 off the output's lines", i);
+        }
 
         const rog_dtype dt = rog_dtype(pick(4));                  // 3 is not a type
         st = rog::plan_reduce(srcs, W, size_t(S >> pick(4)), dt, reinterpret_cast<const void *>(out), path, &p);
@@ -105,7 +125,19 @@ int main(int argc, char **argv) {
             if (ba.n == 0 || ba.first[0] != 0) fail("plan_batch: first chunk", i);
             for (uint32_t k = 1; k < ba.n; ++k)
                 if (ba.first[k] != ba.first[k - 1] + ba.t[k - 1].n_chunks) fail("plan_batch: chunk layout", i);
-            if (ba.flat_chunks > ba.n_chunks) fail("plan_batch: flat chunks", i);
+            if (ba.aligned_chunks > ba.n_chunks) fail("plan_batch: aligned chunks", i);
+            for (uint32_t k = 0; k < ba.n; ++k) {
+                const rog::BatchTensor &t = ba.t[k];
+                if (t.flat && (t.shift != rog::flat_shift(t.out, t.n_vec) ||
+                               t.n_chunks != rog::flat_chunk_count(t.n_vec, 64 * uint32_t(rog::kFlatUnroll), t.shift)))
+                    fail("plan_batch: FLAT tensor chunks", i);
+                if (ba.first[k] < ba.aligned_chunks) {     // round-robin group: all on 128-byte lines
+                    uint64_t bits = t.out | t.S;
+                    for (uint32_t r = 0; r < ba.W; ++r)
+                        bits |= uint64_t(reinterpret_cast<uintptr_t>(ba.src[k * ba.W + r]));
+                    if (!t.flat || (bits & 127) != 0) fail("plan_batch: aligned group", i);
+                }
+            }
         }
         st = rog::plan_reduce_batch(pick(16) ? rd : nullptr, nb, Wb, rog_dtype(pick(4)), &ra, &grid, &nt, &sh);
         if (!status_ok(st)) fail("plan_reduce_batch: unknown status", i);

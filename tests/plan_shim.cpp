@@ -7,7 +7,7 @@
 
 // Gather batch: per planned tensor k (k < *n_out): out[k], S[k], flat[k],
 // n_chunks[k], first[k], and its W source pointers at srcs[k * W ...].
-// meta: n_chunks, flat_chunks, grid, nt_loads.
+// meta: n_chunks, aligned_chunks, grid, nt_loads.
 extern "C" int rog_test_plan_batch(const rog_gather_desc *descs, int n, int W, uint32_t *n_out,
                                    uint64_t *out, uint64_t *S, uint32_t *flat, uint32_t *n_chunks,
                                    uint32_t *first, uint64_t *srcs, uint32_t *meta) {
@@ -27,7 +27,7 @@ extern "C" int rog_test_plan_batch(const rog_gather_desc *descs, int n, int W, u
         for (int r = 0; r < W; ++r) srcs[k * uint32_t(W) + uint32_t(r)] = uint64_t(uintptr_t(a.src[k * uint32_t(W) + uint32_t(r)]));
     }
     meta[0] = a.n_chunks;
-    meta[1] = a.flat_chunks;
+    meta[1] = a.aligned_chunks;
     meta[2] = grid;
     meta[3] = nt ? 1u : 0u;
     return 0;

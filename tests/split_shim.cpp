@@ -17,13 +17,25 @@ extern "C" void rog_test_split_anchored(uint64_t da, uint64_t S, uint64_t anchor
     out2[1] = p.hi;
 }
 
-// The workgroup-to-chunk remapping of the PEER, BATCH and REDUCE kernels,
+// The workgroup-to-chunk remapping of the FLAT, PEER, BATCH and REDUCE kernels,
 // over a whole launch of n chunks: out[b] = xcd_grouped(b, n).
 extern "C" void rog_test_xcd_grouped(uint32_t n, uint32_t *out) {
     for (uint32_t b = 0; b < n; ++b) out[b] = rog::xcd_grouped(b, n);
 }
 
 extern "C" uint32_t rog_test_xcd_run(void) { return rog::kXcdRun; }
+
+// The FLAT kernels' chunk cut: chunk c = flat_span(c, chunk, shift, n_vec),
+// flat_chunk_count chunks, and the planner's shift for an output address.
+extern "C" void rog_test_flat_span(uint32_t c, uint32_t chunk, uint32_t shift, uint32_t n_vec, uint32_t *out2) {
+    const rog::ChunkSpan s = rog::flat_span(c, chunk, shift, n_vec);
+    out2[0] = s.b;
+    out2[1] = s.n;
+}
+extern "C" uint32_t rog_test_flat_chunk_count(uint32_t n_vec, uint32_t chunk, uint32_t shift) {
+    return rog::flat_chunk_count(n_vec, chunk, shift);
+}
+extern "C" uint32_t rog_test_flat_shift(uint64_t out, uint64_t n_vec) { return rog::flat_shift(out, n_vec); }
 
 // The PEER body's byte-window cut (cut16 in csrc/rog_device.h): bytes
 // [m, m + 16) of the 32 bytes lo then hi.

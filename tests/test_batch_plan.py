@@ -58,10 +58,14 @@ def plan_batch(shim, tensors, W):
 
 
 def _chunks(srcs, o, S, W):
+    """(FLAT?, chunks, line-aligned FLAT?).  A FLAT tensor's first chunk is
+    short by (o % 128) / 16 vectors so the others start on o's 128-byte lines."""
     flat = ((o | S | _or(srcs)) & 15) == 0
     if flat:
-        return True, -(-(W * S // 16) // 64)
-    return False, max(1, -(-(S // 16) // 64)) * W
+        n_vec = W * S // 16
+        shift = (o % 128) // 16
+        return True, -(-(n_vec + shift) // 64), ((o | S | _or(srcs)) & 127) == 0
+    return False, max(1, -(-(S // 16) // 64)) * W, False
 
 
 def _or(xs):
@@ -80,23 +84,24 @@ def test_gather_batch_layout(shim, data, n, W):
     tensors = []
     for t in range(n):
         S = data.draw(st.one_of(st.just(0), st.integers(1, 5000), st.sampled_from([16, 1024, 4096, 65536, 1 << 20])))
-        off = data.draw(st.sampled_from([0, 0, 16, 1, 3, 8]))
+        off = data.draw(st.sampled_from([0, 0, 16, 1, 3, 8, 48, 128]))
         base = BASE + t * (1 << 32)
         srcs = [base + r * (1 << 28) + off for r in range(W)]
-        o = base + (W + 1) * (1 << 28) + data.draw(st.sampled_from([0, 16, 1, 5]))
+        o = base + (W + 1) * (1 << 28) + data.draw(st.sampled_from([0, 16, 1, 5, 80, 128]))
         tensors.append((srcs, o, S))
     status, planned, meta = plan_batch(shim, tensors, W)
     assert status == 0
     want = [(tuple(s), o, S) + _chunks(s, o, S, W) for s, o, S in tensors if S]
-    # FLAT tensors first, each group in the caller's order
-    order = [x for x in want if x[3]] + [x for x in want if not x[3]]
+    # line-aligned FLAT tensors first (round-robin), then the rest (XCD runs),
+    # each group in the caller's order
+    order = [x[:5] for x in want if x[5]] + [x[:5] for x in want if not x[5]]
     assert [(p["srcs"], p["out"], p["S"], bool(p["flat"]), p["n_chunks"]) for p in planned] == order
     nxt = 0
     for p in planned:
         assert p["first"] == nxt
         nxt += p["n_chunks"]
     assert meta[0] == nxt
-    assert meta[1] == sum(p["n_chunks"] for p in planned if p["flat"])
+    assert meta[1] == sum(x[4] for x in want if x[5])
     assert meta[2] == nxt            # one wave per chunk while the grid is not capped
 
 

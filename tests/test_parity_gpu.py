@@ -134,6 +134,59 @@ def test_payload_boundaries_inside_wave_chunks(gpu, W, vpr):
     gc.run_all_paths(placed, "tagged W=%d vpr=%d" % (W, vpr))
 
 
+# Output offsets past the 64-byte guard: the output then sits 16 * k bytes past
+# a 128-byte line for every k in 0..7, so the multi-WG FLAT kernel cuts its
+# first chunk short by each possible shift.
+LINE_OFFSETS = [(16 * k - wl.GUARD) % 128 for k in range(8)]
+
+
+@pytest.mark.parametrize("W", [1, 3, 8])
+@pytest.mark.parametrize("S", [16, 1024, 16 * 257, 65536 + 48, (1 << 20) + 16])
+def test_flat_output_at_every_line_offset(gpu, W, S):
+    """FLAT gathers whose output sits anywhere on the 128-byte line grid, with
+    sources at other line offsets: the first chunk is short by the output's
+    offset / 16 vectors and the rest start on lines; every byte, the guards
+    and the sources against the oracle on every path."""
+    payloads = [wl.tagged_payload(r + 5, S) for r in range(W)]
+    for k, oo in enumerate(LINE_OFFSETS):
+        offs = [(16 * (3 * r + k)) % 128 for r in range(W)]
+        placed = gc.Placed(payloads, offs, oo, gpu)
+        assert rog.rog_plan(placed.srcs, placed.out)["kernel"] == "flat"
+        line = (placed.out.data_ptr() % 128) // 16
+        gc.run_all_paths(placed, "flat W=%d S=%d out line offset %d srcs %s" % (W, S, 16 * line, offs))
+
+
+def test_flat_batch_off_the_line_grid(gpu):
+    """A batch mixing FLAT tensors on the line grid (round-robin group), FLAT
+    tensors off it (shifted first chunk, XCD runs) and PEER tensors: every
+    tensor against the oracle."""
+    W = 3
+    rng = np.random.default_rng(123)
+    sizes = [4096, 16 * 1000, 65536, 48, (1 << 20) + 16, 1024, 4096 + 5, 16 * 77]
+    in_offs = [64, 16, 64, 112, 0, 80, 3, 32]
+    out_offs = [64, 80, 0, 16, 112, 64, 7, 48]
+    payloads = [[np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(W)] for S in sizes]
+    b = gc.PlacedBatch(W, payloads, in_offs, out_offs, gpu)
+    lines = [((it.out.data_ptr() | it.S | it.srcs[0].data_ptr()) % 128 == 0) for it in b.items]
+    assert any(lines) and not all(lines)
+    b.run("flat batch off the line grid")
+
+
+def test_streamed_flat_gather_off_the_line_grid(gpu):
+    """FLAT with streamed loads (384 MiB of sources), output 16 bytes past a
+    line and every source at its own line offset: every byte against the
+    oracle."""
+    S = 48 << 20
+    rng = np.random.default_rng(321)
+    payloads = [np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(8)]
+    oo = (16 - wl.GUARD) % 128
+    placed = gc.Placed(payloads, [(16 * r) % 128 for r in range(8)], oo, gpu)
+    plan = rog.rog_plan(placed.srcs, placed.out)
+    assert plan["kernel"] == "flat" and plan["path"] == "multi_wg" and plan["nt_loads"]
+    assert placed.out.data_ptr() % 128 == 16
+    gc.run_all_paths(placed, "streamed flat, out 16 past a line", paths=(rog.ROG_PATH_AUTO,))
+
+
 @pytest.mark.parametrize("S,W", [(16 * 1000, 4), (4095, 3), (1 << 20, 8)])
 def test_exact_in_place_segments(gpu, S, W):
     """Payloads 1 and 3 already sit in their own output segments."""

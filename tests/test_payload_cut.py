@@ -106,6 +106,7 @@ def xcd(tmp_path_factory):
         lib.rog_test_xcd_grouped(n, out.ctypes.data)
         return out[:n]
     f.run = int(lib.rog_test_xcd_run())
+    f.lib = lib
     return f
 
 
@@ -127,6 +128,66 @@ def test_xcd_grouping_is_a_bijection_with_runs(xcd):
             x, k = b % 8, b // 8
             assert np.array_equal(m[:full], (k // R) * span + x * R + k % R)
         assert np.array_equal(m[full:], np.arange(full, n, dtype=np.uint32)), n
+
+
+# ---------------------------------------------------------------------------
+# The FLAT kernels' chunks (flat_span): shifted so later chunks start on lines
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def flat(xcd):
+    lib = xcd.lib
+    lib.rog_test_flat_span.argtypes = [ctypes.c_uint32] * 4 + [ctypes.POINTER(ctypes.c_uint32)]
+    lib.rog_test_flat_chunk_count.restype = ctypes.c_uint32
+    lib.rog_test_flat_chunk_count.argtypes = [ctypes.c_uint32] * 3
+    lib.rog_test_flat_shift.restype = ctypes.c_uint32
+    lib.rog_test_flat_shift.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+    out = (ctypes.c_uint32 * 2)()
+
+    def span(c, chunk, shift, n_vec):
+        lib.rog_test_flat_span(c, chunk, shift, n_vec, out)
+        return out[0], out[1]
+    return span, lib.rog_test_flat_chunk_count, lib.rog_test_flat_shift
+
+
+def test_flat_chunks_tile_the_output_on_its_lines(flat):
+    """Every output size up to 600 vectors, every shift an output address can
+    give (0..7) and the chunk lengths of the FLAT kernels (64 and 256 vectors):
+    the chunks cover [0, n_vec) exactly once, in order, none empty or longer
+    than a chunk, and every chunk after the first starts where the output's
+    128-byte lines do (an output at byte 16 * shift past a line)."""
+    span, count, _ = flat
+    for chunk in (64, 128, 256):
+        for shift in range(8):
+            for n_vec in range(1, 601):
+                nc = count(n_vec, chunk, shift)
+                assert nc == -(-(n_vec + shift) // chunk)
+                pos = 0
+                for c in range(nc):
+                    b, n = span(c, chunk, shift, n_vec)
+                    assert b == pos and 1 <= n <= chunk, (chunk, shift, n_vec, c, b, n)
+                    if c:
+                        assert (16 * shift + 16 * b) % 128 == 0
+                    pos += n
+                assert pos == n_vec, (chunk, shift, n_vec)
+
+
+def test_flat_chunks_at_the_largest_outputs(flat):
+    """Near the top of the 32-bit vector range nothing wraps: shifts up to 7
+    below 2^31 vectors, no shift above (the planner's rule), first and last
+    chunks exact."""
+    span, count, shift_of = flat
+    for n_vec, shifts in (((1 << 31) - 1, range(8)), ((1 << 31) - 65, range(8)),
+                          ((1 << 32) - 1, [0]), ((1 << 32) - 64, [0]), ((1 << 32) - 65, [0])):
+        for shift in shifts:
+            nc = count(n_vec, 64, shift)
+            assert nc == -(-(n_vec + shift) // 64)
+            assert span(0, 64, shift, n_vec) == (0, 64 - shift)
+            b, n = span(nc - 1, 64, shift, n_vec)
+            assert b + n == n_vec and 1 <= n <= 64 and b == (nc - 1) * 64 - shift
+    assert shift_of((1 << 34) + 16 * 5, (1 << 31) - 1) == 5
+    assert shift_of((1 << 34) + 16 * 5, 1 << 31) == 0
+    assert [shift_of((1 << 34) + 16 * k, 1000) for k in range(16)] == [k % 8 for k in range(16)]
 
 
 # ---------------------------------------------------------------------------
