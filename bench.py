@@ -18,7 +18,7 @@ and the output at odd byte offsets (the per-payload path); small gathers (the
 pages' 1 - 128 KiB per-rank sizes at 2 and 8 payloads), per call, replayed
 from a HIP graph of 100 calls, and timed from C by bench_native.c (a child
 process), next to the eager floor of one tiny torch kernel timed the same way;
-the batched gather (16 tensors, W = 4, one launch); the device-to-device copy
+the batched gather (16 tensors, W = 4, one launch, after 40 untimed calls); the device-to-device copy
 ceiling and the HBM figure the HIP runtime reports; aligned gathers with
 2 - 512 MiB outputs, warm and with rotating buffer sets (cold); the
 rank-ordered sum (rog_reduce: W = 8 bf16 payloads of 64 MiB, aligned and one

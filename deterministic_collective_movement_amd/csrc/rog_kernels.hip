@@ -11,7 +11,9 @@
 //    over all W*S/16 vectors of the output, so every wave stays busy across
 //    payload boundaries.  A 64-lane wave owns a chunk of 64*U consecutive
 //    vectors; each of its U loads and U stores is one dwordx4 instruction over
-//    64 consecutive vectors (1 KiB, fully coalesced).  The payload of a chunk
+//    64 consecutive vectors (1 KiB, fully coalesced).  The first chunk is cut
+//    short so that the others start on the output's 128-byte lines, and off
+//    the line grid chunks go to the XCDs in runs.  The payload of a chunk
 //    is found once per chunk, in scalar registers, by one 32-bit multiply-high
 //    (no division on the device at all); in a chunk that crosses a payload
 //    boundary each lane finds its own payload with the same multiply-high.
@@ -25,9 +27,9 @@
 //    and the source sits an odd or 2-mod-4 number of bytes past a 16-byte
 //    granule, the multi-WG lanes load aligned granules instead and rebuild
 //    their bytes from their own granule and the next lane's (a lane shuffle
-//    and v_alignbyte), which streams faster than split unaligned loads.  The pages' fallback copies
-//    such payloads byte by byte ("vectors where aligned, byte-wise tail"); the
-//    bytes written are the same.  Multi-WG, the body is cut into 1 KiB chunks,
+//    and v_alignbyte), which streams faster than split unaligned loads.  The
+//    pages' fallback copies such payloads byte by byte (vectors only where
+//    both sides are aligned); the bytes written are the same.  Multi-WG, the body is cut into 1 KiB chunks,
 //    one wave per chunk, all payloads at once; single-WG, the one workgroup
 //    takes the payloads in turn.
 //  * BATCH kernel (rog_gather_many): one launch; every wave finds its tensor by
@@ -36,7 +38,8 @@
 //
 // Everything a launch needs is in its kernel arguments; there are no scratch
 // buffers, atomics or inter-workgroup synchronisation, and every output byte
-// has exactly one writer.
+// has exactly one writer.  16-byte stores go through OutWindow: buffer stores
+// that stream and write through the XCD's L2 (nt sc1).
 #include <hip/hip_runtime.h>
 
 #include "rog_device.h"

@@ -7,7 +7,8 @@
 // deterministic all-gather copy and right-size its single-block path"):
 //  * "What", copy_rank_ordered bullet: one flat loop over all peers' 16-byte
 //    vectors when the output, the size and every payload are 16-byte aligned;
-//    otherwise peers one by one, vectors where aligned, bytes for the rest.
+//    otherwise each peer on its own, 16-byte vectors only where both sides
+//    are aligned and single bytes elsewhere.
 //  * "What", kAllGatherSingleBlockMaxBytes bullet: the single-block path is
 //    chosen by output size, inclusive; the bound here is measured on MI355X.
 //  * review thread on grid sizing: size the multi-block grid from the vector

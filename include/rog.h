@@ -15,7 +15,7 @@
  *     out[r*S + i] = srcs[r][i]     for 0 <= r < W, 0 <= i < S,
  *
  * byte-identical to a plain concatenation for every alignment and size.  On one
- * GPU the W "peer payloads" are W caller-owned device buffers.  Beside it,
+ * GPU the W peers' payloads are W caller-owned device buffers.  Beside it,
  * rog_reduce computes the rank-ordered sum at the heart of the same pages'
  * deterministic all-reduce and reduce-scatter (declared and defined below).
  *
@@ -65,7 +65,7 @@ typedef enum {
 
 typedef enum {
     ROG_PATH_AUTO = 0,       /* single-WG iff W*S <= rog_single_wg_max_bytes()  */
-    ROG_PATH_SINGLE_WG = 1,  /* one 1024-thread workgroup copies the whole output */
+    ROG_PATH_SINGLE_WG = 1,  /* one workgroup of up to 1024 threads does it all */
     ROG_PATH_MULTI_WG = 2    /* a grid of small workgroups sized from the work      */
 } rog_path;
 
@@ -131,13 +131,13 @@ typedef struct {
  * srcs            host array of W device pointers (payload r = rank r).
  * W               number of payloads, 1 <= W <= rog_max_peers().
  * bytes_per_rank  S, the byte size of every payload (one S for all, as in an
- *                 all-gather; PR #491 "What": "the per-rank byte count").
+ *                 all-gather; PR #491 "What": one byte count per rank).
  * out             device pointer to W*S writable bytes.
  * stream          HIP stream (0 = null stream) of the current device.
  *
  * Path: single-workgroup when W*S <= rog_single_wg_max_bytes(), multi-workgroup
- * otherwise (PR #491 "What", kAllGatherSingleBlockMaxBytes bullet: a one-block
- * gather copies the whole output alone and wins only for small outputs; the
+ * otherwise (PR #491 "What", kAllGatherSingleBlockMaxBytes bullet: with one
+ * block doing all the work the gather is faster only for small outputs; the
  * crossover here is measured on gfx950).  Kernel: FLAT when out, S and every
  * srcs[r] are 16-byte aligned, else PEER (PR #491 "What", copy_rank_ordered).
  * PEER copies each payload as a byte head up to a 256-byte boundary of its
@@ -145,8 +145,8 @@ typedef struct {
  * of the source bytes at the same payload offset (at any source alignment; or,
  * where the loads stream past the caches, by aligned granules shared between
  * neighbouring lanes, see ROG_PLAN_SHIFTED_LOADS), and a byte tail: the pages'
- * fallback ("vectors where aligned, byte-wise tail") extended to misaligned
- * payloads, same bytes as a byte-by-byte copy.
+ * fallback (vector copies only where both sides are aligned, bytes otherwise)
+ * extended to misaligned payloads, same bytes as a byte-by-byte copy.
  *
  * Errors (nothing enqueued):
  *   ROG_ERR_INVALID_ARGUMENT  srcs NULL; W < 1 or W > rog_max_peers(); S > 0 and
@@ -216,7 +216,7 @@ ROG_API size_t rog_single_wg_max_bytes(void);
  * and reduce_scatter (RL-Align/RL-Kernel PR #491, "Not in this PR": their
  * single-block paths grow with size as the gather's did; 523 us at 256 KiB
  * per rank on 8 GPUs).  The pages print no arithmetic; the order and precision
- * above are this library's reading.  On one GPU the W "ranks" are W caller-owned
+ * above are this library's reading.  On one GPU the W ranks are W caller-owned
  * device buffers: an all-reduce is rog_reduce over the W inputs, rank r's share
  * of a reduce-scatter is rog_reduce over the W inputs' r-th shards.
  *

@@ -21,9 +21,9 @@ stated in ``rog_oracle.c``.
 
 Definition (RL-Align/RL-Kernel PR #491, "perf(cuda): vectorize the deterministic
 all-gather copy and right-size its single-block path", section "What", the
-copy_rank_ordered bullet): the copy is a pure rank-ordered copy with a
-byte-identical result, i.e. an all-gather whose output holds payload r at byte
-offset r*S.  The batched form follows the same PR's description of
+copy_rank_ordered bullet): the faster copy changes how bytes move, not which
+bytes land where, so the result is that of an all-gather: payload r at byte
+offset r*S of the output.  The batched form follows the same PR's description of
 all_gather_many: every tensor of the list gets its own gathered output.
 """
 from __future__ import annotations

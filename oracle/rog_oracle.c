@@ -9,9 +9,9 @@
  *
  * What is computed.  The pages "perf(cuda): vectorize the deterministic
  * all-gather copy and right-size its single-block path" (RL-Align/RL-Kernel
- * PR #491, section "What", the copy_rank_ordered bullet) state that the
- * optimised copy is still a plain rank-ordered copy whose result is
- * byte-identical to the old one, and the size test in the same PR ("Tests")
+ * PR #491, section "What", the copy_rank_ordered bullet) say that the faster
+ * copy moves the same bytes to the same places as the copy it replaces, and
+ * the size test in the same PR ("Tests")
  * compares it with NCCL's all-gather.  An all-gather of W payloads of S bytes
  * each places payload r at byte offset r*S of the W*S-byte output.  The oracle
  * is that definition written out as a per-peer byte loop, peers in rank order.

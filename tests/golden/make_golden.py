@@ -20,8 +20,8 @@ CASES = [(1, 1), (2, 1), (2, 7), (3, 5), (3, 16), (4, 17), (8, 3), (5, 33)]
 HEADER = """# Rank-ordered gather of peer-tagged payloads, written by make_golden.py from the
 # CPU oracle (oracle/rog_oracle.c).  Definition: RL-Align/RL-Kernel PR #491,
 # "perf(cuda): vectorize the deterministic all-gather copy and right-size its
-# single-block path", section "What" (copy_rank_ordered is a pure rank-ordered
-# copy, byte-identical to the all-gather): output = payload 0 | payload 1 | ...
+# single-block path", section "What" (copy_rank_ordered places the bytes as the
+# all-gather does): output = payload 0 | payload 1 | ...
 # Input byte i of payload r is (r*131 + i*7 + 1) mod 251.
 """
 

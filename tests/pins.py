@@ -8,8 +8,8 @@ and must leave every other byte of ``buf`` alone.
 What each pin rests on (RL-Align/RL-Kernel PR #491, "perf(cuda): vectorize the
 deterministic all-gather copy and right-size its single-block path"):
 
-* closed form -- the result is a pure rank-ordered copy, byte-identical to an
-  all-gather, i.e. the concatenation of the payloads in rank order ("What",
+* closed form -- the copy puts the same bytes where an all-gather does, i.e.
+  the output is the concatenation of the payloads in rank order ("What",
   copy_rank_ordered bullet; "Tests": compared with NCCL's all-gather);
 * per-segment invariant and peer tags -- segment r of the output is payload r;
 * guards -- bytes before and after the output are untouched (review threads on
