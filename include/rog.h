@@ -173,8 +173,9 @@ ROG_API rog_status rog_gather_ex(const void *const *srcs, int W, size_t bytes_pe
 /*
  * rog_gather_many -- n independent gathers sharing W, in one kernel launch.
  * Tensor t: out_t[r*S_t + i] = srcs_t[r][i].  The pages' all_gather_many
- * (PR #491 review threads on the benchmark) gathers a list of tensors with one
- * handshake and no packing; here every tensor keeps its own caller-provided
+ * (PR #491 review threads on the benchmark) gathers a list of tensors with a
+ * single synchronisation of the ranks and without copying them into one
+ * buffer first; here every tensor keeps its own caller-provided
  * output and its own alignment class (flat or per-peer).
  *
  * descs  host array of n descriptors (each with a host array of W pointers).
@@ -271,7 +272,7 @@ typedef struct {
  * kernel launch: tensor t gets out_t[i] = the rank-ordered sum of srcs_t[r][i]
  * (exactly as rog_reduce).  The pages' reduce_scatter_many / all_gather_many
  * (PR #491, "Tests" and the review threads on the benchmark) batch a list of
- * tensors behind one handshake; here every tensor keeps its own
+ * tensors under a single synchronisation of the ranks; here every tensor keeps its own
  * caller-provided output and the whole batch is one launch.
  *
  * descs  host array of n descriptors (each with a host array of W pointers).

@@ -41,8 +41,9 @@ void rog_oracle_gather(const unsigned char *const *srcs, int W, size_t S,
 /*
  * Batched form: n independent gathers that share W, taken in order.  The
  * pages' all_gather_many (same PR, review thread on the benchmark's
- * all_gather_many row) gathers each tensor of a list into its own output with
- * one handshake and no packing; each output is its own rank-ordered
+ * all_gather_many row) gathers each tensor of a list into an output of its
+ * own, synchronising the ranks once for the whole list and without first
+ * copying the tensors into one buffer; each output is its own rank-ordered
  * concatenation.  srcs holds n*W pointers, tensor t's payloads at
  * srcs[t*W .. t*W+W-1]; bytes_per_rank[t] is that tensor's S.
  */
