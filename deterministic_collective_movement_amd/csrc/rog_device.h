@@ -51,6 +51,17 @@ __device__ __forceinline__ uint32_t window_bytes(uint64_t lo, uint64_t hi, uint6
     return uint32_t(lo < hi ? (hi - lo < cap ? hi - lo : cap) : 0);
 }
 
+// Lane l gets lane l + 1's value, lane 63 gets 0: the whole-wave DPP shift
+// of the gfx9 family (wave_shl:1, control 0x130), one v_mov_b32_dpp with no
+// LDS traffic, where __shfl_down would take a ds_bpermute_b32.  The callers
+// run it with the whole wave active.
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t x) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x130, 0xf, 0xf, false));
+}
+__device__ __forceinline__ vec16 from_next_lane(vec16 v) {
+    return vec16{from_next_lane(v.x), from_next_lane(v.y), from_next_lane(v.z), from_next_lane(v.w)};
+}
+
 __device__ __forceinline__ uint32_t uniform(uint32_t x) {
     return __builtin_amdgcn_readfirstlane(x);
 }

@@ -155,8 +155,7 @@ __device__ __forceinline__ void peer_chunk(const uint8_t *s, uint8_t *d, uint64_
     if (live) lo = ld16<NTL>(g);
     if (own_hi) hi = ld16<false>(g + 1);  // cached; in flight beside lo
     // Lane l + 1's granule; all 64 lanes take part in the shuffle.
-    const vec16 next = vec16{__shfl_down(lo.x, 1u), __shfl_down(lo.y, 1u), __shfl_down(lo.z, 1u),
-                             __shfl_down(lo.w, 1u)};
+    const vec16 next = from_next_lane(lo);
     if (live) w.st16(16 * lane, cut16(lo, own_hi ? hi : next, m));
 }
 

@@ -172,8 +172,7 @@ __device__ __forceinline__ vec16 sum_vec_wave(const void *const *src, uint32_t W
 #pragma unroll
         for (uint32_t q = 0; q < kGroup; ++q) {
             if (q < g) {
-                const vec16 next = vec16{__shfl_down(v[q].x, 1u), __shfl_down(v[q].y, 1u),
-                                         __shfl_down(v[q].z, 1u), __shfl_down(v[q].w, 1u)};
+                const vec16 next = from_next_lane(v[q]);
                 float x[E];
                 widen<DT>(cut16(v[q], own_hi ? h[q] : next, m[q]), x);
                 if (r0 + q == 0) {
