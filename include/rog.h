@@ -100,9 +100,9 @@ typedef struct {
     uint32_t grid;             /* workgroups launched (0 when kernel == NONE)           */
     uint32_t block;            /* threads per workgroup                                 */
     uint64_t vec_ok_mask;      /* PEER kernel: bit r set iff srcs[r] and out + r*S are
-                                  both 16-byte aligned (the pages' "vectors where
-                                  aligned"); informational, every payload gets a
-                                  16-byte body whatever its alignment              */
+                                  both 16-byte aligned (where the pages' fallback
+                                  copies vectors); informational, every payload
+                                  gets a 16-byte body whatever its alignment       */
     uint64_t units;            /* FLAT: 16-byte vectors W*S/16; PEER: bytes W*S;
                                   REDUCE: elements per payload                        */
     uint32_t peer_magic;       /* FLAT: floor(v / (S/16)) = (t + ((v - t) >> peer_sh1))  */
@@ -140,6 +140,10 @@ typedef struct {
  * block doing all the work the gather is faster only for small outputs; the
  * crossover here is measured on gfx950).  Kernel: FLAT when out, S and every
  * srcs[r] are 16-byte aligned, else PEER (PR #491 "What", copy_rank_ordered).
+ * Multi-workgroup FLAT moves 1 KiB chunks, the first one shorter by
+ * k = (out mod 128) / 16 vectors so that the rest start on out's 128-byte
+ * lines (k = 0 from 2^31 vectors on): grid = ceil((W*S/16 + k) / 64) one-wave
+ * workgroups (capped).
  * PEER copies each payload as a byte head up to a 256-byte boundary of its
  * destination, a body of aligned 16-byte stores, each fed by one 16-byte load
  * of the source bytes at the same payload offset (at any source alignment; or,

@@ -230,6 +230,11 @@ def test_grid_sizes():
         chunks = -(-n_vec // (64 * FLAT_UNROLL))
         assert p["kernel"] == "flat" and p["block"] == FLAT_BLOCK
         assert p["grid"] == max(1, -(-chunks // (FLAT_BLOCK // 64)))
+        # an output 16 * k bytes past a 128-byte line: the first chunk is k
+        # vectors short, so one more chunk may be needed
+        for k in range(8):
+            q = rog.rog_plan_ptrs(srcs, S, out + 16 * k, rog.ROG_PATH_MULTI_WG)
+            assert q["kernel"] == "flat" and q["grid"] == max(1, -(-(n_vec + k) // (64 * FLAT_UNROLL))), (W, S, k)
         s = rog.rog_plan_ptrs(srcs, S, out, rog.ROG_PATH_SINGLE_WG)
         # 1 KiB wave chunks while 16 waves cover the output, 4 KiB beyond
         u = 1 if n_vec <= 1024 else SINGLE_UNROLL
