@@ -118,6 +118,13 @@ def test_gather_plan_matches_the_rules(W, S, path, data):
     assert info.grid >= 1 and info.grid * info.block < (1 << 32)
     if info.path == 1:
         assert info.grid == 1 and 64 <= info.block <= 1024 and info.block % 64 == 0
+    if flat and info.path == 2:
+        # one-wave workgroups over 1 KiB chunks, the first short by the
+        # output's vectors past a 128-byte line (none from 2^31 vectors on)
+        n_vec = total // 16
+        k = (out % 128) // 16 if n_vec < (1 << 31) else 0
+        assert info.block == 64
+        assert info.grid == min(max(1, -(-(n_vec + k) // 64)), 0xFFFFFFFF // 64), (n_vec, k, info.grid)
     if not flat:
         mask = sum(1 << r for r, s in enumerate(srcs) if ((s | (out + r * S)) & 15) == 0)
         assert info.vec_ok_mask == mask
