@@ -120,7 +120,7 @@ constexpr int kPeerShift = ROG_PEER_SHIFT;
 // When the multi-WG rank-ordered sum reads every source as shared granules
 // (its granule form) instead of one unaligned 16-byte load per lane and
 // source: 0 never; 1 whenever the launch streams its loads past the caches
-// (ROG_PLAN_NT_LOADS), whatever the alignment.  Measured on MI355X: with
+// (ROG_PLAN_NT_LOADS), whatever the alignment; 2 always.  Measured on MI355X: with
 // streamed loads (W = 8 x 64 MiB) the granule form runs 6.55-6.6 TB/s aligned
 // or misaligned, against 6.2-6.3 aligned and 5.4-6.0 misaligned for unaligned
 // loads; with cached loads (W = 2-4 x 64 MiB, 8 x 8 MiB) the unaligned loads

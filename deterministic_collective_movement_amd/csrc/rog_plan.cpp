@@ -288,7 +288,8 @@ rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype d
         info.block = kWaveBlock;
         info.grid = std::min(a.n_chunks, max_grid(kWaveBlock));
         // The granule form where loads stream past the caches (kReduceShift).
-        if (kReduceShift == 1 && (info.flags & ROG_PLAN_NT_LOADS)) info.flags |= ROG_PLAN_SHIFTED_LOADS;
+        if (kReduceShift == 2 || (kReduceShift == 1 && (info.flags & ROG_PLAN_NT_LOADS)))
+            info.flags |= ROG_PLAN_SHIFTED_LOADS;
     }
     return ROG_OK;
 }
@@ -339,7 +340,7 @@ rog_status plan_reduce_batch(const rog_reduce_desc *descs, int n, int W, rog_dty
     args->n_chunks = uint32_t(next);   // 32 tensors of < 2^26 chunks each
     *grid = uint32_t(std::min<uint64_t>(next, max_grid(kWaveBlock)));
     *nt_loads = source_bytes >= kNtLoadMinBytes;
-    *shifted = *nt_loads && kReduceShift == 1;
+    *shifted = kReduceShift == 2 || (kReduceShift == 1 && *nt_loads);
     return ROG_OK;
 }
 
