@@ -51,8 +51,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flat_kernel_w8x64MiB_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "deterministic_collective_movement_amd", "csrc", f)
                   for f in ("rog_kernels.hip", "rog_internal.h", "rog_plan.cpp", "rog_device.h")]
 LATENCY_SIZES_KIB = (1, 8, 32, 128)
+# Calls timed per small-payload latency case, whatever --steps is: the pages
+# report the median of 100 calls (RL-Align/RL-Kernel PR #491, "Results").
+LATENCY_CALLS = 100
+LATENCY_WARMUP = 10
 NATIVE_SRC = os.path.join(ROOT, "bench_native.c")
 NATIVE_BIN = os.path.join(ROOT, "_build", "bench_native")
+FLOOR_SRC = os.path.join(ROOT, "bench_floor.hip")
+FLOOR_BIN = os.path.join(ROOT, "_build", "bench_floor")
 
 
 def build_native() -> str:
@@ -69,6 +75,15 @@ def build_native() -> str:
         os.path.join(pkg, "librog.so"), "-Wl,-rpath,$ORIGIN/../deterministic_collective_movement_amd",
         "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", tmp])
     os.replace(tmp, NATIVE_BIN)
+    # the launch-floor harness (null, load-only and store-only kernels of the
+    # gathers' launch shape), for the profiles; bench.py does not run it
+    hipcc = os.path.join(rocm, "bin", "hipcc")
+    tmp = FLOOR_BIN + ".tmp%d" % os.getpid()
+    subprocess.check_call([hipcc, "-O3", "-std=c++17", "-Wall", "-Wextra", "-Werror", "--offload-arch=gfx950",
+                           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                           "-Wno-unused-command-line-argument", FLOOR_SRC, "-o", tmp],
+                          stderr=subprocess.DEVNULL)
+    os.replace(tmp, FLOOR_BIN)
     return NATIVE_BIN
 
 
@@ -288,9 +303,10 @@ def misaligned(torch, rog, case, payloads, srcs, device, steps, warmup, in_off=1
             "ms_per_gather": round(region_ms / steps, 4)}
 
 
-def latency_sweep(torch, rog, wl, device, steps, warmup):
+def latency_sweep(torch, rog, wl, device, steps=LATENCY_CALLS, warmup=LATENCY_WARMUP):
     """The two-payload case and the size sweep's 1 - 128 KiB payloads: every
-    call event-timed; p10 / p50 / p90 and all samples (µs)."""
+    call event-timed (``steps`` calls after ``warmup``); p10 / p50 / p90, the
+    number of calls and all samples (µs)."""
     rows = []
     cases = wl.config1() + [c for c in wl.config2() if c.S <= 128 * wl.KiB]
     stream = torch.cuda.current_stream(device).cuda_stream
@@ -303,7 +319,7 @@ def latency_sweep(torch, rog, wl, device, steps, warmup):
         rows.append({"case": "c%d#%d" % (case.config, case.index), "W": case.W, "S_KiB": case.S // wl.KiB,
                      "path": plan["path"], "kernel": plan["kernel"],
                      "p10_us": round(s["p10_us"], 2), "p50_us": round(s["p50_us"], 2),
-                     "p90_us": round(s["p90_us"], 2),
+                     "p90_us": round(s["p90_us"], 2), "n": s["n"],
                      "eff_GBps": round(gbps(2 * case.W * case.S, s["p50_us"] * 1e-3), 1),
                      "samples_us": [round(1e3 * x, 2) for x in per_call]})
     return rows
@@ -435,14 +451,14 @@ def bandwidth_sweep(torch, rog, device, calls, out_mib=SWEEP_OUT_MIB, footprint=
     return rows
 
 
-def launch_floor(torch, device, steps, warmup):
+def launch_floor(torch, device, steps=LATENCY_CALLS, warmup=LATENCY_WARMUP):
     """The eager floor of the per-call p50: one tiny torch kernel (a 1-element
     fill) issued from Python between the same two event records as a gather."""
     x = torch.empty(1, dtype=torch.int32, device=device)
     per_call, _ = time_calls(torch, x.zero_, steps, warmup)
     s = summarize_ms(per_call)
     return {"p10_us": round(s["p10_us"], 2), "p50_us": round(s["p50_us"], 2), "p90_us": round(s["p90_us"], 2),
-            "how": "torch zero_ of a 1-element tensor, event-timed like the small gathers"}
+            "n": s["n"], "how": "torch zero_ of a 1-element tensor, event-timed like the small gathers"}
 
 
 CROSSOVER_TOTALS = (256, 1024, 4096, 8192, 16384, 32768, 40960, 49152, 65536, 81920, 98304,
@@ -564,32 +580,45 @@ def reduce_misaligned(torch, rog, srcs, aligned_out, stream, steps, warmup, in_o
             "GBps": round(gbps(moved * steps, region_ms), 1), "mean_launch_us": round(1e3 * region_ms / steps, 2)}
 
 
-def reduce_cpu_baseline(payloads, got, budget_s, sample=1 << 22):
-    """The CPU oracle, single-threaded, on a bounded sample of the large sum
-    (its first ``sample`` elements of all W payloads) repeated for about
-    ``budget_s`` seconds; the sample of the GPU's output must equal it."""
+def reduce_cpu_baseline(payloads, got, budget_s, sample=1 << 22, threads=None):
+    """The CPU oracle on a bounded sample of the large sum (its first
+    ``sample`` elements of all W payloads), repeated for about ``budget_s``
+    seconds on one core and on every core this process may use (the oracle's
+    sum called unchanged on element slices from a pool of threads); the sample
+    of the GPU's output must equal it."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import oracle
+    T = threads or len(os.sched_getaffinity(0))
     srcs = [p[:sample] for p in payloads]
     want = np.empty(sample, np.uint16)
     oracle.reduce_c(srcs, want, "bf16")
     if not np.array_equal(got[:sample], want):
         raise AssertionError("the GPU's rank-ordered sum differs from the oracle's on the sample")
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.reduce_c(srcs, want, "bf16")
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    moved = (len(srcs) + 1) * sample * 2 * reps
-    return {"value": round(moved / el / 1e9, 2), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d x the first %d elements of the W=%d bf16 sum (%.1f s, single-threaded C loop)"
-                      % (reps, sample, len(srcs), el)}
+    reps1, el1 = repeat_for(lambda: oracle.reduce_c(srcs, want, "bf16"), budget_s)
+    pieces = slices(sample, 4 * T)
+    many = np.empty(sample, np.uint16)
+
+    def piece(lohi):
+        lo, hi = lohi
+        oracle.reduce_c([s[lo:hi] for s in srcs], many[lo:hi], "bf16")
+
+    with ThreadPoolExecutor(max_workers=T) as pool:
+        list(pool.map(piece, pieces))
+        repsT, elT = repeat_for(lambda: list(pool.map(piece, pieces)), budget_s)
+    if not np.array_equal(many, want):
+        raise AssertionError("the many-core oracle sum differs from the single-core one")
+    moved = (len(srcs) + 1) * sample * 2
+    return {"value": round(moved * repsT / elT / 1e9, 2), "unit": "GB/s", "cores": T, "kind": "oracle",
+            "sample": "%d x the first %d elements of the W=%d bf16 sum (%.1f s) on %d threads, each calling "
+                      "the C loop on slices of %d elements" % (repsT, sample, len(srcs), elT, T, sample // len(pieces)),
+            "single_core": {"value": round(moved * reps1 / el1 / 1e9, 2), "unit": "GB/s", "cores": 1,
+                            "sample": "%d x the same sample (%.1f s)" % (reps1, el1)}}
 
 
-def reduce_latency(torch, rog, wl, device, steps, warmup):
-    """The pages' per-rank sizes 1 KiB - 4 MiB at W = 2 and 8: per-call p50."""
+def reduce_latency(torch, rog, wl, device, steps=LATENCY_CALLS, warmup=LATENCY_WARMUP):
+    """The pages' per-rank sizes 1 KiB - 4 MiB at W = 2 and 8: per-call p50 over
+    ``steps`` event-timed calls."""
     stream = torch.cuda.current_stream(device).cuda_stream
     rows = []
     for c in wl.reduce_config2():
@@ -599,7 +628,7 @@ def reduce_latency(torch, rog, wl, device, steps, warmup):
         sm = summarize_ms(per_call)
         rows.append({"W": c.W, "KiB_per_rank": c.n * c.esize // 1024, "path": p["path"],
                      "p10_us": round(sm["p10_us"], 2), "p50_us": round(sm["p50_us"], 2),
-                     "p90_us": round(sm["p90_us"], 2)})
+                     "p90_us": round(sm["p90_us"], 2), "n": sm["n"]})
     return rows
 
 
@@ -713,24 +742,61 @@ def host_cpu():
     return {"model": model, "cores_available": len(os.sched_getaffinity(0))}
 
 
-def cpu_baseline(case, payloads, budget_s):
-    """The CPU oracle, single-threaded, on the full headline gather repeated for
-    about ``budget_s`` seconds of CPU work."""
-    import numpy as np
-    from oracle import oracle
-    out = np.empty(case.W * case.S, np.uint8)
-    oracle.gather_c(payloads, out)                  # untimed first touch of `out`
+def slices(n, parts):
+    """[lo, hi) pieces that cut range(n) into ``parts`` near-equal slices."""
+    parts = max(1, min(parts, n))
+    return [(n * k // parts, n * (k + 1) // parts) for k in range(parts)]
+
+
+def repeat_for(fn, budget_s):
+    """Call fn() until about budget_s seconds have passed; (calls, seconds)."""
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.gather_c(payloads, out)
+        fn()
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
-            break
-    moved = 2 * case.W * case.S * reps
-    return {"value": round(moved / el / 1e9, 2), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d x the full W=8 x 64 MiB gather (%.1f s, single-threaded C per-byte loop)"
-                      % (reps, el), "host": host_cpu()}
+            return reps, el
+
+
+def cpu_baseline(case, payloads, budget_s, threads=None):
+    """The CPU oracle on the full headline gather, repeated for about
+    ``budget_s`` seconds: once on one core, once on every core this process
+    may use.  The many-core form calls the oracle's gather unchanged on (payload,
+    slice) pieces -- one payload per call, source and output pointers offset --
+    from a pool of threads (the calls release the interpreter lock), so the
+    bytes written are those of the single call.  The line reports the many-core
+    figure, the single-core one beside it."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import oracle
+    T = threads or len(os.sched_getaffinity(0))
+    S = case.S
+    out = np.empty(case.W * S, np.uint8)
+    oracle.gather_c(payloads, out)                  # untimed first touch of `out`
+    reps1, el1 = repeat_for(lambda: oracle.gather_c(payloads, out), budget_s)
+    per_payload = max(1, -(-4 * T // case.W))       # about 4 pieces per thread
+    pieces = [(r, lo, hi) for r in range(case.W) for lo, hi in slices(S, per_payload)]
+
+    def piece(job):
+        r, lo, hi = job
+        oracle.gather_c([payloads[r][lo:hi]], out[r * S + lo: r * S + hi])
+
+    with ThreadPoolExecutor(max_workers=T) as pool:
+        list(pool.map(piece, pieces))               # untimed warm-up of the pool
+        repsT, elT = repeat_for(lambda: list(pool.map(piece, pieces)), budget_s)
+    want = np.concatenate(payloads)
+    if not np.array_equal(out, want):
+        raise AssertionError("the many-core oracle gather differs from the concatenation")
+    moved = 2 * case.W * S
+    host = host_cpu()
+    return {"value": round(moved * repsT / elT / 1e9, 2), "unit": "GB/s", "cores": T, "kind": "oracle",
+            "sample": "%d x the full W=8 x 64 MiB gather (%.1f s) on %d threads, each calling the C per-byte "
+                      "loop on (payload, slice) pieces of %d-%d bytes" % (repsT, elT, T, S // per_payload,
+                                                                          -(-S // per_payload)),
+            "cpu_model": host["model"], "cores_available": host["cores_available"],
+            "single_core": {"value": round(moved * reps1 / el1 / 1e9, 2), "unit": "GB/s", "cores": 1,
+                            "sample": "%d x the full gather (%.1f s), one call per gather" % (reps1, el1)}}
 
 
 def main(argv=None):
@@ -750,6 +816,8 @@ def main(argv=None):
                     help="time both forced rog_reduce paths over small outputs instead")
     ap.add_argument("--crossover", action="store_true",
                     help="time both forced paths over small outputs instead (one JSON line per case)")
+    ap.add_argument("--sweep-only", action="store_true",
+                    help="time only the warm and cold bandwidth sweeps (2 - 512 MiB outputs), for traces")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: --gpus %d is not supported (use --gpus 1)" % args.gpus,
@@ -772,6 +840,11 @@ def main(argv=None):
         return 0
     if args.crossover:
         crossover(torch, rog, device, args.steps, args.warmup)
+        return 0
+    if args.sweep_only:
+        print(json.dumps({"bandwidth_sweep": bandwidth_sweep(torch, rog, device, 20),
+                          "bandwidth_sweep_mid": bandwidth_sweep(torch, rog, device, 50, out_mib=SWEEP_MID_OUT_MIB)}),
+              flush=True)
         return 0
 
     case, payloads, plan, per_call, region_ms, srcs = headline(torch, rog, wl, device, args.steps, args.warmup)
@@ -796,8 +869,8 @@ def main(argv=None):
     extras["misaligned"] = misaligned(torch, rog, case, payloads, srcs, device,
                                       max(10, args.steps // 5), max(2, args.warmup // 5))
     if not args.headline_only:
-        extras["latency"] = latency_sweep(torch, rog, wl, device, args.steps, args.warmup)
-        extras["latency_floor"] = launch_floor(torch, device, args.steps, args.warmup)
+        extras["latency"] = latency_sweep(torch, rog, wl, device)
+        extras["latency_floor"] = launch_floor(torch, device)
         extras["latency_native"] = {"skipped": "--no-native"} if args.no_native else latency_native()
         extras["latency_in_graph"] = graph_latency(torch, rog, wl, device)
         extras["gather_many"] = batch_bench(torch, rog, wl, device, BATCH_STEPS,
@@ -808,11 +881,11 @@ def main(argv=None):
         extras["bandwidth_sweep_mid"] = bandwidth_sweep(torch, rog, device, 50, out_mib=SWEEP_MID_OUT_MIB)
         big, rpayloads, rgot = reduce_bandwidth(torch, rog, wl, device, args.steps, args.warmup)
         extras["reduce"] = {"bandwidth": big,
-                            "latency": reduce_latency(torch, rog, wl, device, args.steps, args.warmup),
+                            "latency": reduce_latency(torch, rog, wl, device),
                             "batched": reduce_batch(torch, rog, wl, device, BATCH_STEPS,
                                                     max(BATCH_WARMUP, args.warmup))}
-        cpu = cpu_baseline(case, payloads, args.cpu_budget)
-        extras["reduce"]["cpu_baseline"] = reduce_cpu_baseline(rpayloads, rgot, min(5.0, args.cpu_budget))
+        cpu = cpu_baseline(case, payloads, args.cpu_budget / 2)
+        extras["reduce"]["cpu_baseline"] = reduce_cpu_baseline(rpayloads, rgot, min(2.5, args.cpu_budget / 4))
         del rpayloads, rgot
     else:
         extras["reduce"] = {"bandwidth": reduce_bandwidth(torch, rog, wl, device, max(10, args.steps // 2),

@@ -114,6 +114,67 @@ __device__ __forceinline__ uint32_t batch_tensor(const uint32_t (&first)[kMaxBat
     return lo;
 }
 
+// A launch's arguments read through the kernel-argument segment pointer.  The
+// kernels take one argument struct by value, which the AMDGPU ABI places at
+// offset 0 of that segment; reading it through the segment pointer keeps every
+// read a scalar load from the segment, where mixing constant- and
+// variable-index reads of the by-value parameter makes the compiler copy it
+// to scratch first.
+template <typename Args>
+__device__ __forceinline__ const Args &launch_args() {
+    // A C cast: it converts the constant address space of the segment pointer.
+    return *(const Args *)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
+// The payload pointers of a launch as the multi-WG FLAT kernel looks them up:
+// the first eight are read into scalar registers together with the other
+// kernel arguments, so that a wave's payload lookup (r < 8) is a few scalar
+// selects rather than one more scalar load that the chunk's first data load
+// would wait for; later payloads are read from the kernel arguments.
+struct SrcTable {
+    const void *const *all;       // every payload pointer (kernel arguments)
+    const void *p0, *p1, *p2, *p3, *p4, *p5, *p6, *p7;
+    __device__ __forceinline__ explicit SrcTable(const void *const *a)
+        : all(a), p0(a[0]), p1(a[1]), p2(a[2]), p3(a[3]), p4(a[4]), p5(a[5]), p6(a[6]), p7(a[7]) {}
+};
+// Payload r's pointer, r wave-uniform.  Each half of every candidate goes
+// through a cross-lane read (free on a value already in scalar registers), so
+// that the selects stay scalar selects between registers and are not turned
+// back into a load from a selected address.
+__device__ __forceinline__ const void *src_of(const SrcTable &t, uint32_t r) {
+    if (r >= 8) return t.all[r];
+    const void *const c[8] = {t.p0, t.p1, t.p2, t.p3, t.p4, t.p5, t.p6, t.p7};
+    uint32_t los[8], his[8];
+#pragma unroll
+    for (uint32_t i = 0; i < 8; ++i) {
+        const uint64_t v = reinterpret_cast<uint64_t>(c[i]);
+        los[i] = __builtin_amdgcn_readfirstlane(uint32_t(v));
+        his[i] = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+    }
+    uint32_t lo = los[0], hi = his[0];
+#pragma unroll
+    for (uint32_t i = 1; i < 8; ++i) {
+        lo = r == i ? los[i] : lo;
+        hi = r == i ? his[i] : hi;
+    }
+    return reinterpret_cast<const void *>((uint64_t(hi) << 32) | lo);
+}
+__device__ __forceinline__ const void *src_of(const void *const *src, uint32_t r) { return src[r]; }
+// Payload rk's pointer for a per-lane rk (a chunk that crosses payloads).
+__device__ __forceinline__ const void *lane_src(const void *const *src, uint32_t rk) { return src[rk]; }
+__device__ __forceinline__ const void *lane_src(const SrcTable &t, uint32_t rk) { return t.all[rk]; }
+
+// Makes the compiler hold the given values in scalar registers at this point,
+// so that the kernel-argument reads behind them go out as one batch of scalar
+// loads with one wait, before the first branch, rather than in dependent
+// rounds: each round trip lengthens the life of every one-wave workgroup, and
+// at full occupancy that costs copy throughput.  Emits no instruction.
+__device__ __forceinline__ void hold_scalars(const SrcTable &t, uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                             uint32_t e, const Divider &div, const void *out) {
+    asm volatile("" ::"s"(t.p0), "s"(t.p1), "s"(t.p2), "s"(t.p3), "s"(t.p4), "s"(t.p5), "s"(t.p6), "s"(t.p7),
+                 "s"(a), "s"(b), "s"(c), "s"(d), "s"(e), "s"(div.magic), "s"(div.sh1), "s"(div.sh2), "s"(out));
+}
+
 // floor(v / d) by the host-built multiplier (exact for every 32-bit v).
 __device__ __forceinline__ uint32_t divide(uint32_t v, const Divider &d) {
     const uint32_t t = __umulhi(v, d.magic);

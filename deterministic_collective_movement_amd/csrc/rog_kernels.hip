@@ -52,8 +52,8 @@ namespace rog {
 // 64*U vectors, the first chunk shorter by shift so that the others start on
 // the output's 128-byte lines.
 // ---------------------------------------------------------------------------
-template <int U, bool NTL>
-__device__ __forceinline__ void flat_chunk(const void *const *src, vec16 *o, uint32_t n_vec,
+template <int U, bool NTL, typename Src>
+__device__ __forceinline__ void flat_chunk(const Src &src, vec16 *o, uint32_t n_vec,
                                            uint32_t vpr, const Divider &div, uint32_t shift, uint32_t c) {
     constexpr uint32_t kChunk = 64 * U;
     const uint32_t lane = __lane_id();
@@ -69,7 +69,7 @@ __device__ __forceinline__ void flat_chunk(const void *const *src, vec16 *o, uin
     const OutWindow<kStoreAux> w(o + b, n * 16);    // the chunk's output
     if (e <= seg_lo + vpr) {
         // The whole chunk lies in payload r: scalar bases, lane offsets.
-        const vec16 *s = static_cast<const vec16 *>(src[r]) + (b - seg_lo);
+        const vec16 *s = static_cast<const vec16 *>(src_of(src, r)) + (b - seg_lo);
         if (n == kChunk) {
             vec16 v[U];
 #pragma unroll
@@ -93,7 +93,7 @@ __device__ __forceinline__ void flat_chunk(const void *const *src, vec16 *o, uin
             const uint32_t k = b + u * 64 + lane;
             if (k < e) {
                 const uint32_t rk = divide(k, div);
-                const vec16 *s = static_cast<const vec16 *>(src[rk]);
+                const vec16 *s = static_cast<const vec16 *>(lane_src(src, rk));
                 w.st16(16 * (k - b), ld16<NTL>(s + (k - rk * vpr)));
             }
         }
@@ -199,12 +199,17 @@ __device__ __forceinline__ void peer_whole(const uint8_t *s, uint8_t *d, uint64_
 // (xcd_grouped) that keep those lines in one L2: 17-26 % faster there, 1-1.5 %
 // slower on aligned gathers.
 template <bool NTL>
-__global__ __launch_bounds__(kWaveBlock) void rog_flat_kernel(FlatArgs a) {
+__global__ __launch_bounds__(kWaveBlock) void rog_flat_kernel(FlatArgs) {
     constexpr uint32_t kChunk = 64 * kFlatUnroll;
-    const uint32_t n_chunks = flat_chunk_count(a.n_vec, kChunk, a.shift);
-    for (uint32_t vb = blockIdx.x; vb < n_chunks; vb += gridDim.x)
-        flat_chunk<kFlatUnroll, NTL>(a.src, static_cast<vec16 *>(a.out), a.n_vec, a.vpr, a.div, a.shift,
-                                     a.runs ? xcd_grouped(vb, n_chunks) : vb);
+    const FlatArgs &a = launch_args<FlatArgs>();
+    const SrcTable src(a.src);
+    const uint32_t n_vec = a.n_vec, vpr = a.vpr, shift = a.shift, runs = a.runs, grid = a.grid;
+    const Divider div = a.div;
+    vec16 *const out = static_cast<vec16 *>(a.out);
+    hold_scalars(src, n_vec, vpr, shift, runs, grid, div, out);
+    const uint32_t n_chunks = flat_chunk_count(n_vec, kChunk, shift);
+    for (uint32_t vb = blockIdx.x; vb < n_chunks; vb += grid)
+        flat_chunk<kFlatUnroll, NTL>(src, out, n_vec, vpr, div, shift, runs ? xcd_grouped(vb, n_chunks) : vb);
 }
 
 // Single-WG FLAT: one workgroup of as many waves as there are chunks (<= 16),

@@ -159,9 +159,10 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
         return ROG_OK;
     }
     const bool single = path == ROG_PATH_SINGLE_WG;
-    if (total >= kNtLoadMinBytes) info.flags |= ROG_PLAN_NT_LOADS;
+    const bool flat = is_flat(srcs, W, S, out);
+    if (total >= (flat ? kFlatNtLoadMinBytes : kNtLoadMinBytes)) info.flags |= ROG_PLAN_NT_LOADS;
 
-    if (is_flat(srcs, W, S, out)) {
+    if (flat) {
         FlatArgs &a = plan->flat;
         memset(&a, 0, sizeof(a));
         for (int r = 0; r < W; ++r) a.src[r] = srcs[r];
@@ -175,6 +176,7 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
         info.units = a.n_vec;
         info.block = single ? flat_single_block(a.n_vec) : kWaveBlock;
         info.grid = single ? 1 : flat_blocks(a.n_vec, a.shift);
+        a.grid = info.grid;
         info.peer_magic = a.div.magic;
         info.peer_sh1 = a.div.sh1;
         info.peer_sh2 = a.div.sh2;

@@ -112,9 +112,11 @@ typedef struct {
 } rog_plan_info;
 
 /* rog_plan_info.flags: the kernel's 16-byte loads are non-temporal (streamed
- * past the caches); set when the W*S source bytes are too many to stay in the
- * 256 MB Infinity Cache.  16-byte stores are always non-temporal; a gather's
- * are also written through the L2 caches at device scope.  Affects speed only. */
+ * past the caches); set when the W*S source bytes are too many for the 256 MB
+ * Infinity Cache to serve repeated calls well: from 128 MiB for a FLAT gather,
+ * from 384 MiB for a PEER gather, a batch or a sum.  16-byte stores are always
+ * non-temporal; a gather's are also written through the L2 caches at device
+ * scope.  Affects speed only. */
 #define ROG_PLAN_NT_LOADS 1u
 /* rog_plan_info.flags: the multi-workgroup PEER or REDUCE kernel reads at least
  * one source body as aligned 16-byte granules, each lane taking the granule
@@ -200,8 +202,13 @@ ROG_API rog_status rog_gather_many(const rog_gather_desc *descs, int n, int W,
 ROG_API rog_status rog_plan(const void *const *srcs, int W, size_t bytes_per_rank,
                             const void *out, rog_path path, rog_plan_info *info);
 
-/* Output bytes up to which ROG_PATH_AUTO takes the single-workgroup path
- * (inclusive), measured on MI355X. */
+/* Output bytes W*S up to which ROG_PATH_AUTO takes the single-workgroup path
+ * (inclusive), measured on MI355X: 32 KiB.  The pages' counterpart is
+ * kAllGatherSingleBlockMaxBytes (RL-Align/RL-Kernel PR #491, section "What",
+ * the kAllGatherSingleBlockMaxBytes bullet): one block copying the whole
+ * output wins only for small outputs, the bound compares output bytes, and its
+ * B200 value (64 KiB) was found by measuring both paths, as this one was on
+ * gfx950.  Never fails; a constant of the build. */
 ROG_API size_t rog_single_wg_max_bytes(void);
 
 /*
@@ -220,8 +227,10 @@ ROG_API size_t rog_single_wg_max_bytes(void);
  * This is the reduction at the heart of the pages' deterministic all_reduce
  * and reduce_scatter (RL-Align/RL-Kernel PR #491, "Not in this PR": their
  * single-block paths grow with size as the gather's did; 523 us at 256 KiB
- * per rank on 8 GPUs).  The pages print no arithmetic; the order and precision
- * above are this library's reading.  On one GPU the W ranks are W caller-owned
+ * per rank on 8 GPUs).  The pages print no arithmetic: they call their backend
+ * a fixed tree (the author's replies on the benchmark's recorded backend)
+ * without saying which; the left-deep rank-order chain in binary32 above is
+ * this library's reading of it.  On one GPU the W ranks are W caller-owned
  * device buffers: an all-reduce is rog_reduce over the W inputs, rank r's share
  * of a reduce-scatter is rog_reduce over the W inputs' r-th shards.
  *
@@ -261,7 +270,12 @@ ROG_API rog_status rog_reduce_plan(const void *const *srcs, int W, size_t count,
                                    const void *out, rog_path path, rog_plan_info *info);
 
 /* Source bytes (W * count * element size) up to which ROG_PATH_AUTO runs
- * rog_reduce on one workgroup (inclusive), measured on MI355X. */
+ * rog_reduce on one workgroup (inclusive), measured on MI355X: 64 KiB.  The
+ * bound is compared with input bytes because the pages' all-reduce /
+ * reduce-scatter fast-path bound is (RL-Align/RL-Kernel PR #491, the author's
+ * reply on the benchmark's --size-bytes: the 256 KiB threshold is tested on
+ * the per-rank input, world size x the output for reduce_scatter).  Never
+ * fails; a constant of the build. */
 ROG_API size_t rog_reduce_single_wg_max_bytes(void);
 
 /* One tensor of a batched sum: W source pointers, its output, its count. */
@@ -289,7 +303,11 @@ typedef struct {
 ROG_API rog_status rog_reduce_many(const rog_reduce_desc *descs, int n, int W, rog_dtype dtype,
                                    hipStream_t stream);
 
-/* Largest W accepted (kernel-argument capacity). */
+/* Largest W accepted: 64, the capacity of the kernel arguments, which carry
+ * every source pointer.  The pages' collectives run over a same-host group of
+ * at most eight ranks (RL-Align/RL-Kernel PR #491, "Security Architecture
+ * Review", "Security Blast Radius"), so every group size they use fits.
+ * Never fails; a constant of the build. */
 ROG_API int rog_max_peers(void);
 
 /* Largest n accepted by rog_gather_many, and the largest n*W. */

@@ -17,7 +17,10 @@ addition of two binary32 numbers in binary64 followed by one rounding to
 binary32 is the correctly rounded binary32 sum: 53 >= 2*24 + 2), rounds to
 bf16 with its own integer arithmetic and to binary16 through ``struct``'s half
 format.  The reading of the pages it follows is
-stated in ``rog_oracle.c``.
+stated in ``rog_oracle.c``: the pages name their reduction a fixed tree but
+print neither its order nor its precision, so the sum is PARITY UNPINNED
+against the pages' own order; its pins fix the left-deep rank-order chain in
+binary32 that this library defines.
 
 Definition (RL-Align/RL-Kernel PR #491, "perf(cuda): vectorize the deterministic
 all-gather copy and right-size its single-block path", section "What", the

@@ -60,7 +60,12 @@ void rog_oracle_gather_many(const unsigned char *const *srcs, unsigned char *con
  * collectives beside the gather and say only that their results must not
  * depend on timing (RL-Align/RL-Kernel PR #491, section "Not in this PR", on
  * the all_reduce / reduce_scatter single-block paths); they print no
- * arithmetic.  The reading taken here is the plainest deterministic one:
+ * arithmetic; they name the backend a fixed tree (cuda_ipc_fixed_tree, the
+ * author's replies on the benchmark's recorded backend) and leave its
+ * reduction untouched and unprinted.  PARITY UNPINNED against the pages' own
+ * reduction order: the tests pin this definition, not the backend's tree.
+ * The reading taken here is the plainest deterministic one, a left-deep
+ * chain in rank order:
  *
  *     out[i] = round( ((x_0[i] + x_1[i]) + x_2[i]) + ... + x_{W-1}[i] )
  *

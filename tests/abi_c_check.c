@@ -9,7 +9,9 @@
  * a batch of three tensors in one launch, S = 0, and the argument errors that
  * must be reported before anything is enqueued; rank-ordered sums (bf16 and
  * binary32, every path, element offsets, in place) against the oracle's sum,
- * and a batch of binary16 sums in one launch; the plans' cache-policy and
+ * and a batch of binary16 sums in one launch; both batched calls captured
+ * into a HIP graph, which must hold exactly one node, a kernel launch, and
+ * whose replays must match the oracle; the plans' cache-policy and
  * shared-granule flags.
  * Exit status 0 = every check passed; the first failure is printed.
  */
@@ -45,6 +47,50 @@ static unsigned char byte_at(unsigned seed, size_t i) {
     x ^= x >> 13;
     x *= 0x5bd1e995u;
     return (unsigned char)(x >> 24);
+}
+
+/* The nodes of a captured graph: how many in all, how many kernel launches. */
+static int kernel_nodes(hipGraph_t g, size_t *total) {
+    size_t n = 0;
+    CHECK_HIP(hipGraphGetNodes(g, NULL, &n));
+    hipGraphNode_t *nodes = (hipGraphNode_t *)malloc((n ? n : 1) * sizeof *nodes);
+    CHECK_HIP(hipGraphGetNodes(g, nodes, &n));
+    int k = 0;
+    for (size_t i = 0; i < n; ++i) {
+        hipGraphNodeType t;
+        CHECK_HIP(hipGraphNodeGetType(nodes[i], &t));
+        if (t == hipGraphNodeTypeKernel) ++k;
+    }
+    free(nodes);
+    *total = n;
+    return k;
+}
+
+/* A batched call captured from `st`: exactly one node, a kernel launch (the
+ * pages' all_gather_many synchronises the ranks once for the whole list,
+ * RL-Align/RL-Kernel PR #491, review thread on the benchmark's all_gather_many
+ * row; here the whole list is one launch).  Returns the instantiated graph,
+ * or NULL after counting a failure. */
+static hipGraphExec_t capture_one_launch(hipStream_t st, int is_sum, const void *descs, int n, int W,
+                                         rog_dtype dtype, const char *what) {
+    hipGraph_t g;
+    CHECK_HIP(hipStreamBeginCapture(st, hipStreamCaptureModeGlobal));
+    const rog_status s = is_sum ? rog_reduce_many((const rog_reduce_desc *)descs, n, W, dtype, st)
+                                : rog_gather_many((const rog_gather_desc *)descs, n, W, st);
+    CHECK_HIP(hipStreamEndCapture(st, &g));
+    size_t total = 0;
+    const int k = kernel_nodes(g, &total);
+    if (s != ROG_OK || k != 1 || total != 1) {
+        fprintf(stderr, "FAIL %s: captured status %s, %zu nodes, %d kernel nodes (want 1, 1)\n", what,
+                rog_status_string(s), total, k);
+        ++failures;
+        CHECK_HIP(hipGraphDestroy(g));
+        return NULL;
+    }
+    hipGraphExec_t ex;
+    CHECK_HIP(hipGraphInstantiate(&ex, g, NULL, NULL, 0));
+    CHECK_HIP(hipGraphDestroy(g));
+    return ex;
 }
 
 /* One gather of W payloads of S bytes at the given offsets, on `path`. */
@@ -135,6 +181,22 @@ static void batch_case(hipStream_t st) {
                 ++failures;
             }
         }
+        /* The same call captured: one kernel node; three replays, each over
+         * outputs cleared by eager work in between, each compared in full. */
+        hipGraphExec_t ex = capture_one_launch(st, 0, desc, N, W, ROG_DTYPE_F32, "batch graph");
+        for (int rep = 0; ex && rep < 3; ++rep) {
+            for (int t = 0; t < N; ++t) CHECK_HIP(hipMemset(dout[t], FILL, W * sizes[t] + 5));
+            CHECK_HIP(hipGraphLaunch(ex, st));
+            CHECK_HIP(hipStreamSynchronize(st));
+            for (int t = 0; t < N; ++t) {
+                CHECK_HIP(hipMemcpy(got[t], desc[t].out, W * sizes[t], hipMemcpyDeviceToHost));
+                if (memcmp(got[t], want[t], W * sizes[t]) != 0) {
+                    fprintf(stderr, "FAIL batch graph replay %d tensor %d\n", rep, t);
+                    ++failures;
+                }
+            }
+        }
+        if (ex) CHECK_HIP(hipGraphExecDestroy(ex));
     }
     for (int t = 0; t < N; ++t) {
         for (int r = 0; r < W; ++r) {
@@ -290,6 +352,21 @@ static void reduce_batch_case(hipStream_t st) {
                 ++failures;
             }
         }
+        /* Captured: one kernel node; three replays over cleared outputs. */
+        hipGraphExec_t ex = capture_one_launch(st, 1, desc, N, W, ROG_DTYPE_F16, "reduce batch graph");
+        for (int rep = 0; ex && rep < 3; ++rep) {
+            for (int t = 0; t < N; ++t) CHECK_HIP(hipMemset(dout[t], FILL, counts[t] * 2 + 2));
+            CHECK_HIP(hipGraphLaunch(ex, st));
+            CHECK_HIP(hipStreamSynchronize(st));
+            for (int t = 0; t < N; ++t) {
+                CHECK_HIP(hipMemcpy(got[t], dout[t], counts[t] * 2, hipMemcpyDeviceToHost));
+                if (memcmp(got[t], want[t], counts[t] * 2) != 0) {
+                    fprintf(stderr, "FAIL reduce batch graph replay %d tensor %d\n", rep, t);
+                    ++failures;
+                }
+            }
+        }
+        if (ex) CHECK_HIP(hipGraphExecDestroy(ex));
     }
     for (int t = 0; t < N; ++t) {
         for (int r = 0; r < W; ++r) {

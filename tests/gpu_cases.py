@@ -20,6 +20,13 @@ def guarded_host(nbytes: int, off: int) -> np.ndarray:
     return np.full(wl.GUARD + off + nbytes + wl.GUARD, wl.GUARD_BYTE, dtype=np.uint8)
 
 
+def _sync(t: torch.Tensor) -> None:
+    """Wait for the GPU work on t's device; nothing to wait for on the CPU,
+    where the harness's own mutation tests run it."""
+    if t.device.type == "cuda":
+        torch.cuda.synchronize(t.device)
+
+
 class Placed:
     """A gather's payloads and output in guarded buffers, on host and device."""
 
@@ -34,7 +41,7 @@ class Placed:
         for p, o in zip(payloads, in_offs):
             h = guarded_host(self.S, o)
             h[wl.GUARD + o: wl.GUARD + o + self.S] = p
-            d = torch.from_numpy(h).to(device)
+            d = torch.from_numpy(h).to(device, copy=True)   # never an alias of h, also on the CPU
             self.src_host.append(h)
             self.src_dev.append(d)
             self.srcs.append(d[wl.GUARD + o: wl.GUARD + o + self.S])
@@ -56,7 +63,7 @@ class Placed:
         self.out_dev.fill_(wl.GUARD_BYTE)
 
     def check(self, label: str) -> None:
-        torch.cuda.synchronize()
+        _sync(self.out_dev)
         got = self.out_dev.cpu().numpy()
         want = self.expected()
         if not np.array_equal(got, want):
@@ -152,7 +159,7 @@ class PlacedReduce:
             h = guarded_host(nb, o * self.es)
             start = wl.GUARD + o * self.es
             h[start:start + nb] = p.view(np.uint8)
-            d = torch.from_numpy(h).to(device)
+            d = torch.from_numpy(h).to(device, copy=True)   # never an alias of h, also on the CPU
             self.src_host.append(h)
             self.src_dev.append(d)
             self.srcs.append(d[start:start + nb].view(TORCH_DTYPES[dtype]))
@@ -182,13 +189,20 @@ class PlacedReduce:
             self.out_dev.fill_(wl.GUARD_BYTE)
 
     def check(self, label: str) -> None:
-        torch.cuda.synchronize()
+        _sync(self.out_dev)
         buf = self.out_dev.cpu().numpy()
         nb = self.n * self.es
-        if self.in_place < 0:
-            pre, post = buf[:self.out_start], buf[self.out_start + nb:]
-            if not (np.all(pre == wl.GUARD_BYTE) and np.all(post == wl.GUARD_BYTE)):
-                raise AssertionError("%s: a guard byte changed" % label)
+        # Outside [out_start, out_start + nb) the buffer must be as it was: the
+        # guards, and for an in-place sum the source buffer's own guards.
+        before = self.src_host[self.in_place] if self.in_place >= 0 else None
+        pre, post = buf[:self.out_start], buf[self.out_start + nb:]
+        if before is None:
+            intact = np.all(pre == wl.GUARD_BYTE) and np.all(post == wl.GUARD_BYTE)
+        else:
+            intact = (np.array_equal(pre, before[:self.out_start])
+                      and np.array_equal(post, before[self.out_start + nb:]))
+        if not intact:
+            raise AssertionError("%s: a guard byte changed" % label)
         got = buf[self.out_start:self.out_start + nb].copy().view(oracle.REDUCE_DTYPES[self.dtype])
         ok = _same_elements(got, self.expected(), self.dtype)
         if not ok.all():

@@ -187,6 +187,23 @@ def test_streamed_flat_gather_off_the_line_grid(gpu):
     gc.run_all_paths(placed, "streamed flat, out 16 past a line", paths=(rog.ROG_PATH_AUTO,))
 
 
+@pytest.mark.parametrize("W,S,offs", [(2, 64 << 20, (0, 0)), (8, 16 << 20, (16, 48)), (4, (32 << 20) - 1024, (0, 0))],
+                         ids=["2x64MiB", "8x16MiB_off_lines", "4x32MiB-1KiB"])
+def test_flat_gathers_around_the_streaming_bound(gpu, W, S, offs):
+    """FLAT gathers stream their loads from 128 MiB of sources: at the bound
+    (2 x 64 MiB and, off the line grid, 8 x 16 MiB) and just below it (cached
+    loads), every byte against the oracle."""
+    rng = np.random.default_rng(W * 1000 + S % 997)
+    payloads = [np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(W)]
+    in_off, out_off = offs
+    placed = gc.Placed(payloads, [(in_off - wl.GUARD) % 128] * W, (out_off - wl.GUARD) % 128, gpu)
+    assert placed.out.data_ptr() % 128 == out_off and placed.srcs[0].data_ptr() % 128 == in_off
+    plan = rog.rog_plan(placed.srcs, placed.out)
+    assert plan["kernel"] == "flat" and plan["path"] == "multi_wg"
+    assert plan["nt_loads"] is (W * S >= 128 << 20)
+    gc.run_all_paths(placed, "flat %d x %d" % (W, S), paths=(rog.ROG_PATH_AUTO,))
+
+
 @pytest.mark.parametrize("S,W", [(16 * 1000, 4), (4095, 3), (1 << 20, 8)])
 def test_exact_in_place_segments(gpu, S, W):
     """Payloads 1 and 3 already sit in their own output segments."""

@@ -221,6 +221,19 @@ def test_streamed_sums_take_the_granule_form(gpu, dtype, n, offs):
                             paths=(rog.ROG_PATH_AUTO,))
 
 
+@pytest.mark.parametrize("which,offs", [(3, ((1, 0, 3, 2, 5, 4, 7, 6), None)), (0, ((2,) * 8, None))],
+                         ids=["srcs3_mixed", "srcs0_in2"])
+def test_streamed_sum_in_place(gpu, which, offs):
+    """An in-place sum (out is srcs[which]) over 384 MiB of sources, which takes
+    the granule form: every element against the oracle, and the in-place
+    buffer's own guards and every other source unchanged."""
+    in_offs = offs[0]
+    placed = gc.PlacedReduce(_streamed_payloads("bf16", 24 << 20), in_offs, 0, "bf16", gpu, in_place=which)
+    plan = rog.rog_reduce_plan(placed.srcs, placed.out)
+    assert plan["path"] == "multi_wg" and plan["nt_loads"] and plan["shifted_loads"]
+    gc.run_reduce_all_paths(placed, "streamed in place srcs[%d]" % which, paths=(rog.ROG_PATH_AUTO,))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_streamed_batch_with_small_tensors(gpu, dtype):
     """A batch of sums over 384 MiB or more of sources takes the granule form
