@@ -297,6 +297,7 @@ struct ReduceArgs {
     uint64_t count;             // elements
     uint32_t W;
     uint32_t n_chunks;          // multi-WG
+    uint32_t grid;              // multi-WG: workgroups launched (the grid stride)
 };
 
 // ---------------------------------------------------------------------------

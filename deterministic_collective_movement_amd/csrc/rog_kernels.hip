@@ -221,6 +221,9 @@ __global__ __launch_bounds__(kSingleBlock) void rog_flat_single_kernel(FlatArgs 
 
 // Multi-WG PEER: one wave per workgroup and per body chunk, chunks grouped by
 // XCD, grid-strided over the n_chunks = W * chunks_per_peer chunks.
+// (The argument reads are left as the compiler orders them: read in one batch,
+// as the FLAT kernel does, the streamed-load gathers at odd offsets measured
+// 1-2 % slower.)
 template <bool NTL>
 __global__ __launch_bounds__(kWaveBlock) void rog_peer_kernel(PeerArgs a) {
     for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x) {

@@ -289,6 +289,7 @@ rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype d
         a.n_chunks = reduce_chunks(bytes);
         info.block = kWaveBlock;
         info.grid = std::min(a.n_chunks, max_grid(kWaveBlock));
+        a.grid = info.grid;
         // The granule form where loads stream past the caches (kReduceShift).
         if (kReduceShift == 2 || (kReduceShift == 1 && (info.flags & ROG_PLAN_NT_LOADS)))
             info.flags |= ROG_PLAN_SHIFTED_LOADS;

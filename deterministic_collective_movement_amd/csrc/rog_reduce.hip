@@ -243,9 +243,17 @@ __device__ __forceinline__ void sum_chunk(const void *const *src, uint32_t W, vo
 // first; without runs the granule form measured 8 % slower), grid-strided
 // over a capped grid.
 template <int DT, bool NTL, bool SH>
-__global__ __launch_bounds__(kWaveBlock) void rog_reduce_kernel(ReduceArgs a) {
-    for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x)
-        sum_chunk<DT, NTL, SH>(a.src, a.W, a.out, a.count, ROG_REDUCE_XCD ? xcd_grouped(vb, a.n_chunks) : vb);
+__global__ __launch_bounds__(kWaveBlock) void rog_reduce_kernel(ReduceArgs) {
+    // Every argument the first chunk needs, the first eight source pointers
+    // included, in one batch of scalar loads with one wait.
+    const ReduceArgs &a = launch_args<ReduceArgs>();
+    const SrcTable src(a.src);
+    const uint32_t n_chunks = a.n_chunks, W = a.W, grid = a.grid;
+    const uint64_t count = a.count;
+    void *const out = a.out;
+    hold_scalars(src, n_chunks, W, uint32_t(count), uint32_t(count >> 32), grid, out);
+    for (uint32_t vb = blockIdx.x; vb < n_chunks; vb += grid)
+        sum_chunk<DT, NTL, SH>(a.src, W, out, count, ROG_REDUCE_XCD ? xcd_grouped(vb, n_chunks) : vb);
 }
 
 // Batch: the tensors' chunks laid end to end; a wave finds its tensor by a
