@@ -7,7 +7,7 @@
 // out[r*S + i] = src_r[i].  The pages' fix replaced a loop that moved one byte
 // per thread and divided by the payload size for every byte.  Here:
 //
-//  * FLAT kernel (output, S and every payload 16-byte aligned): one flat loop
+//  * FLAT kernel (output, S and every payload 16-byte aligned): a single loop
 //    over all W*S/16 vectors of the output, so every wave stays busy across
 //    payload boundaries.  A 64-lane wave owns a chunk of 64*U consecutive
 //    vectors; each of its U loads and U stores is one dwordx4 instruction over

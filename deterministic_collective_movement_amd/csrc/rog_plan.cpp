@@ -5,14 +5,16 @@
 //
 // Decisions follow RL-Align/RL-Kernel PR #491 ("perf(cuda): vectorize the
 // deterministic all-gather copy and right-size its single-block path"):
-//  * "What", copy_rank_ordered bullet: one flat loop over all peers' 16-byte
-//    vectors when the output, the size and every payload are 16-byte aligned;
-//    otherwise each peer on its own, 16-byte vectors only where both sides
-//    are aligned and single bytes elsewhere.
+//  * "What", copy_rank_ordered bullet: if the output address, the payload
+//    size and every source address are multiples of 16, a single loop walks
+//    the 16-byte vectors of all payloads as one range; if not, payloads are
+//    copied one by one, in vectors only where source and destination allow
+//    it, byte by byte for the rest.
 //  * "What", kAllGatherSingleBlockMaxBytes bullet: the single-block path is
 //    chosen by output size, inclusive; the bound here is measured on MI355X.
-//  * review thread on grid sizing: size the multi-block grid from the vector
-//    count when the aligned path applies, from the per-peer work otherwise.
+//  * review thread on grid sizing: the multi-block grid follows the number of
+//    16-byte vectors on the aligned path and each payload's own work on the
+//    other.
 //  * author's reply on the benchmark sizes: the all-reduce's single-block
 //    bound is tested on input bytes; rog_reduce's bound likewise counts source
 //    bytes (W * count * element size).

@@ -9,7 +9,8 @@ the same bytes.
 The workloads follow the pages' measurements: RL-Align/RL-Kernel PR #491
 ("Results", B200 and H100 tables: BF16 payloads of 1 KiB .. 4 MiB per rank at
 2, 4 and 8 ranks, median of 100 calls) and its size test ("Tests": byte sizes
-across the single-block threshold, odd tails, misaligned input and output).
+on both sides of the one-block bound, sizes that end off a 16-byte boundary,
+and sources and outputs at byte offsets).
 The batched mix borrows the 8627 x 8192 BF16 activation shape of
 vllm-project/vllm PR #57037 ("[Benchmark] Add all-reduce rank-skew
 calibration", the reproduction command and its results table).

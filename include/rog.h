@@ -71,7 +71,7 @@ typedef enum {
 
 typedef enum {
     ROG_KERNEL_NONE = 0,     /* nothing to copy (S == 0): nothing is launched       */
-    ROG_KERNEL_FLAT = 1,     /* one flat loop over all peers' 16-byte vectors        */
+    ROG_KERNEL_FLAT = 1,     /* a single loop over every payload's 16-byte vectors  */
     ROG_KERNEL_PEER = 2,     /* per payload: byte head, 16-byte body (aligned
                                 stores, loads at any alignment), byte tail          */
     ROG_KERNEL_REDUCE = 3    /* rank-ordered sum: element head, 16-byte body of
