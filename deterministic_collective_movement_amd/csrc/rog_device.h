@@ -175,6 +175,10 @@ __device__ __forceinline__ void hold_scalars(const SrcTable &t, uint32_t a, uint
                  "s"(a), "s"(b), "s"(c), "s"(d), "s"(e), "s"(div.magic), "s"(div.sh1), "s"(div.sh2), "s"(out));
 }
 
+__device__ __forceinline__ void hold_scalars(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t e,
+                                             const Divider &div, const void *out) {
+    asm volatile("" ::"s"(a), "s"(b), "s"(c), "s"(d), "s"(e), "s"(div.magic), "s"(div.sh1), "s"(div.sh2), "s"(out));
+}
 __device__ __forceinline__ void hold_scalars(const SrcTable &t, uint32_t a, uint32_t b, uint32_t c, uint32_t d,
                                              uint32_t e, const void *out) {
     asm volatile("" ::"s"(t.p0), "s"(t.p1), "s"(t.p2), "s"(t.p3), "s"(t.p4), "s"(t.p5), "s"(t.p6), "s"(t.p7),

@@ -255,6 +255,7 @@ struct PeerArgs {
     uint32_t chunks_per_peer;
     uint32_t n_chunks;
     Divider cdiv;
+    uint32_t grid;    // multi-WG: workgroups launched (the grid stride)
 };
 
 // One tensor of a batch.  Chunks [first, first + n_chunks) of the launch

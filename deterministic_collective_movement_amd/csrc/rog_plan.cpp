@@ -201,6 +201,7 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
             a.cdiv = make_divider(a.chunks_per_peer);
             info.block = kWaveBlock;
             info.grid = std::min(a.n_chunks, max_grid(kWaveBlock));
+            a.grid = info.grid;
             if (info.flags & ROG_PLAN_NT_LOADS)
                 for (int r = 0; r < W; ++r)
                     if (shifted_body(srcs[r], addr(out) + uint64_t(r) * S, S, kPeerShift))
