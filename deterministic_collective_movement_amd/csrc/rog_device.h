@@ -175,6 +175,9 @@ __device__ __forceinline__ void hold_scalars(const SrcTable &t, uint32_t a, uint
                  "s"(a), "s"(b), "s"(c), "s"(d), "s"(e), "s"(div.magic), "s"(div.sh1), "s"(div.sh2), "s"(out));
 }
 
+__device__ __forceinline__ void hold_scalars(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t e) {
+    asm volatile("" ::"s"(a), "s"(b), "s"(c), "s"(d), "s"(e));
+}
 __device__ __forceinline__ void hold_scalars(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t e,
                                              const Divider &div, const void *out) {
     asm volatile("" ::"s"(a), "s"(b), "s"(c), "s"(d), "s"(e), "s"(div.magic), "s"(div.sh1), "s"(div.sh2), "s"(out));

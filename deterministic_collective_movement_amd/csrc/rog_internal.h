@@ -283,6 +283,7 @@ struct BatchArgs {
     uint32_t W;
     uint32_t n_chunks;                // all tensors' chunks
     uint32_t aligned_chunks;          // chunks of the line-aligned FLAT tensors, which come first
+    uint32_t grid;                    // workgroups launched (the grid stride)
 };
 
 static_assert(sizeof(BatchArgs) <= 4096, "kernel arguments must stay below 4 KiB");
@@ -336,6 +337,7 @@ struct ReduceBatchArgs {
     uint32_t n;
     uint32_t W;
     uint32_t n_chunks;                // all tensors' chunks
+    uint32_t grid;                    // workgroups launched (the grid stride)
 };
 
 static_assert(sizeof(ReduceBatchArgs) <= 4096, "kernel arguments must stay below 4 KiB");

@@ -258,15 +258,19 @@ __global__ __launch_bounds__(kSingleBlock) void rog_peer_single_kernel(PeerArgs 
 // (Runs over the aligned FLAT chunks too measured 5 % slower on an aligned
 // batch; no runs at all, 9 % slower on 8 x 64 MiB PEER payloads.)
 template <bool NTL>
-__global__ __launch_bounds__(kWaveBlock) void rog_batch_kernel(BatchArgs a) {
-    for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x) {
-        const uint32_t c = vb < a.aligned_chunks
-                               ? vb
-                               : a.aligned_chunks + xcd_grouped(vb - a.aligned_chunks, a.n_chunks - a.aligned_chunks);
-        const uint32_t lo = batch_tensor(a.first, a.n, c);
+__global__ __launch_bounds__(kWaveBlock) void rog_batch_kernel(BatchArgs) {
+    const BatchArgs &a = launch_args<BatchArgs>();
+    const uint32_t n_chunks = a.n_chunks, aligned = a.aligned_chunks, n = a.n, W = a.W, grid = a.grid;
+    hold_scalars(n_chunks, aligned, n, W, grid);
+    for (uint32_t vb = blockIdx.x; vb < n_chunks; vb += grid) {
+        const uint32_t c = vb < aligned ? vb : aligned + xcd_grouped(vb - aligned, n_chunks - aligned);
+        const uint32_t lo = batch_tensor(a.first, n, c);
         const BatchTensor &t = a.t[lo];
         const uint32_t lc = c - a.first[lo];
-        const void *const *src = a.src + lo * a.W;
+        // the tensor's fields either form needs, in one batch of scalar loads
+        hold_scalars(lc, t.flat, t.vpr, t.n_vec, t.shift, t.div, reinterpret_cast<const void *>(t.out));
+        hold_scalars(t.chunks_per_peer, uint32_t(t.S), uint32_t(t.S >> 32), 0u, 0u);
+        const void *const *src = a.src + lo * W;
         if (t.flat) {
             flat_chunk<kFlatUnroll, NTL>(src, reinterpret_cast<vec16 *>(t.out), t.n_vec, t.vpr, t.div, t.shift, lc);
         } else {

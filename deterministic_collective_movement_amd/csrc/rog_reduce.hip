@@ -259,12 +259,15 @@ __global__ __launch_bounds__(kWaveBlock) void rog_reduce_kernel(ReduceArgs) {
 // Batch: the tensors' chunks laid end to end; a wave finds its tensor by a
 // scalar binary search over the tensors' first chunks.
 template <int DT, bool NTL, bool SH>
-__global__ __launch_bounds__(kWaveBlock) void rog_reduce_batch_kernel(ReduceBatchArgs a) {
-    for (uint32_t vb = blockIdx.x; vb < a.n_chunks; vb += gridDim.x) {
-        const uint32_t c = ROG_REDUCE_XCD ? xcd_grouped(vb, a.n_chunks) : vb;
-        const uint32_t lo = batch_tensor(a.first, a.n, c);
+__global__ __launch_bounds__(kWaveBlock) void rog_reduce_batch_kernel(ReduceBatchArgs) {
+    const ReduceBatchArgs &a = launch_args<ReduceBatchArgs>();
+    const uint32_t n_chunks = a.n_chunks, n = a.n, W = a.W, grid = a.grid;
+    hold_scalars(n_chunks, n, W, grid, 0u);
+    for (uint32_t vb = blockIdx.x; vb < n_chunks; vb += grid) {
+        const uint32_t c = ROG_REDUCE_XCD ? xcd_grouped(vb, n_chunks) : vb;
+        const uint32_t lo = batch_tensor(a.first, n, c);
         const ReduceTensor &t = a.t[lo];
-        sum_chunk<DT, NTL, SH>(a.src + lo * a.W, a.W, reinterpret_cast<void *>(t.out), t.count, c - a.first[lo]);
+        sum_chunk<DT, NTL, SH>(a.src + lo * W, W, reinterpret_cast<void *>(t.out), t.count, c - a.first[lo]);
     }
 }
 
