@@ -32,13 +32,16 @@ def kernels(tmp_path_factory):
 def _parse(text):
     meta = text[text.index("amdhsa.kernels:"):]
     ks = {}
-    for block in meta.split("  - .")[1:]:
+    for block in re.split(r"\n  - \.", meta)[1:]:
         name = re.search(r"\.name:\s+(\S+)", block)
         if not name:
             continue
         get = lambda k: int(re.search(r"\.%s:\s+(\d+)" % k, block).group(1))  # noqa: E731
+        explicit = [(int(o), int(z)) for o, z, kind in
+                    re.findall(r"\.offset:\s+(\d+)\s+\.size:\s+(\d+)\s+\.value_kind:\s+(\w+)", block)
+                    if not kind.startswith("hidden_")]
         ks[name.group(1)] = {"scratch": get("private_segment_fixed_size"), "vgpr": get("vgpr_count"),
-                             "max_wg": get("max_flat_workgroup_size"),
+                             "max_wg": get("max_flat_workgroup_size"), "explicit_args": explicit,
                              "dyn_stack": re.search(r"uses_dynamic_stack:\s+true", block) is not None}
     return ks
 
@@ -59,3 +62,12 @@ def test_no_scratch_and_vgprs_fit(kernels):
         # waves on each of the 4 SIMDs of a CU.
         budget = 512 // max(1, k["max_wg"] // 256)
         assert k["vgpr"] <= min(budget, 512), (name, k)
+
+
+def test_one_argument_struct_at_offset_zero(kernels):
+    """The multi-WG kernels read their argument struct through the
+    kernel-argument segment pointer, as the struct at offset 0: every kernel
+    takes exactly one explicit argument, by value, at offset 0."""
+    for name, k in kernels.items():
+        assert len(k["explicit_args"]) == 1, (name, k["explicit_args"])
+        assert k["explicit_args"][0][0] == 0, (name, k["explicit_args"])

@@ -134,6 +134,20 @@ def test_payload_boundaries_inside_wave_chunks(gpu, W, vpr):
     gc.run_all_paths(placed, "tagged W=%d vpr=%d" % (W, vpr))
 
 
+@pytest.mark.parametrize("W", [8, 9, 12, 16, 33, 64])
+@pytest.mark.parametrize("S", [1024, 16 * 1000, 65536 + 16])
+def test_flat_payloads_past_the_preloaded_pointers(gpu, W, S):
+    """The multi-WG FLAT kernel holds the first eight payload pointers in
+    scalar registers and reads the others from its arguments: tagged payloads
+    on both sides of that boundary, chunks inside one payload and chunks
+    across payloads, every byte against the oracle."""
+    payloads = [wl.tagged_payload(r, S) for r in range(W)]
+    placed = gc.Placed(payloads, [0] * W, 0, gpu)
+    plan = rog.rog_plan(placed.srcs, placed.out, rog.ROG_PATH_MULTI_WG)
+    assert plan["kernel"] == "flat" and plan["path"] == "multi_wg"
+    gc.run_all_paths(placed, "tagged W=%d S=%d" % (W, S), paths=(rog.ROG_PATH_MULTI_WG,))
+
+
 # Output offsets past the 64-byte guard: the output then sits 16 * k bytes past
 # a 128-byte line for every k in 0..7, so the multi-WG FLAT kernel cuts its
 # first chunk short by each possible shift.
