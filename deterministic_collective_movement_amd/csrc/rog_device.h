@@ -168,7 +168,9 @@ __device__ __forceinline__ const void *lane_src(const SrcTable &t, uint32_t rk) 
 // so that the kernel-argument reads behind them go out as one batch of scalar
 // loads with one wait, before the first branch, rather than in dependent
 // rounds: each round trip lengthens the life of every one-wave workgroup, and
-// at full occupancy that costs copy throughput.  Emits no instruction.
+// at full occupancy that costs copy throughput.  Emits no instruction.  One
+// overload per argument set a kernel holds (FLAT; PEER and the batches; the
+// sum).
 __device__ __forceinline__ void hold_scalars(const SrcTable &t, uint32_t a, uint32_t b, uint32_t c, uint32_t d,
                                              uint32_t e, const Divider &div, const void *out) {
     asm volatile("" ::"s"(t.p0), "s"(t.p1), "s"(t.p2), "s"(t.p3), "s"(t.p4), "s"(t.p5), "s"(t.p6), "s"(t.p7),
