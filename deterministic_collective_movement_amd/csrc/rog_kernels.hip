@@ -197,7 +197,11 @@ __device__ __forceinline__ void peer_whole(const uint8_t *s, uint8_t *d, uint64_
 // 128-byte lines, chunks go to the XCDs round-robin.  Otherwise neighbouring
 // chunks read parts of the same source lines, and they go to the XCDs in runs
 // (xcd_grouped) that keep those lines in one L2: 17-26 % faster there, 1-1.5 %
-// slower on aligned gathers.
+// slower on aligned gathers.  The arguments, the first eight payload pointers
+// included, are read in one batch of scalar loads and a wave picks its
+// payload's pointer with scalar selects, so it waits for one scalar round trip
+// before its first data load (three before: small multi-WG gathers 0.1-0.2 us
+// faster, cold 64 MiB outputs half a point to a point).
 template <bool NTL>
 __global__ __launch_bounds__(kWaveBlock) void rog_flat_kernel(FlatArgs) {
     constexpr uint32_t kChunk = 64 * kFlatUnroll;
