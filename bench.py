@@ -391,17 +391,22 @@ BATCH_WARMUP = 40
 BATCH_STEPS = 20
 
 SWEEP_OUT_MIB = (64, 128, 256, 512)
+SWEEP_CALLS = 40               # timed calls per case of the 64 - 512 MiB sweep (at least two passes over the sets)
 SWEEP_MID_OUT_MIB = (2, 8, 32)
 SWEEP_FOOTPRINT = 2 << 30      # bytes of rotating buffer sets per cold case (8 x the 256 MB cache)
 
 
-def bandwidth_sweep(torch, rog, device, calls, out_mib=SWEEP_OUT_MIB, footprint=SWEEP_FOOTPRINT):
+def bandwidth_sweep(torch, rog, device, calls, out_mib=SWEEP_OUT_MIB, footprint=SWEEP_FOOTPRINT, graph=False):
     """Aligned gathers with outputs of ``out_mib`` (64 - 512 MiB by default,
-    the "outputs >= 64 MiB" of the headline target) at W = 2 and 8, timed two ways over ``calls`` back-to-back
-    launches: warm, the same buffers every call (as the pages time a call), and
-    cold, rotating through K buffer sets that together span ``footprint`` bytes,
-    so that no call finds its sources in the 256 MB Infinity Cache.  Sampled
-    bytes of every set are checked against its sources."""
+    the "outputs >= 64 MiB" of the headline target) at W = 2 and 8, timed two
+    ways over the same number of back-to-back launches (``calls``, or two
+    passes over the sets if that is more): warm, the same buffers every call
+    (as the pages time a call), and cold, rotating through K buffer sets that
+    together span ``footprint`` bytes, so that no call finds its sources in the
+    256 MB Infinity Cache.  With ``graph`` the launches are captured into a HIP
+    graph and the replay is timed, which takes the host's launch path (about
+    3.5 µs a call from Python, more than a small gather's kernel) out of the
+    interval.  Sampled bytes of every set are checked against its sources."""
     lib = rog.lib()
     stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
     g = torch.Generator(device=device)
@@ -425,22 +430,40 @@ def bandwidth_sweep(torch, rog, device, calls, out_mib=SWEEP_OUT_MIB, footprint=
                         raise RuntimeError("rog_gather failed")
                 torch.cuda.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                if not graph:
+                    e0.record()
+                    for _, _, ptrs, o in seq:
+                        lib.rog_gather(ptrs, W, S, o, stream)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    return e0.elapsed_time(e1) / len(seq)
+                gr = torch.cuda.CUDAGraph()
+                side = torch.cuda.Stream(device=device)
+                side.wait_stream(torch.cuda.current_stream(device))
+                with torch.cuda.graph(gr, stream=side):
+                    sp = ctypes.c_void_p(side.cuda_stream)
+                    for _, _, ptrs, o in seq:
+                        if lib.rog_gather(ptrs, W, S, o, sp) != 0:
+                            raise RuntimeError("rog_gather failed under capture")
+                gr.replay()
+                torch.cuda.synchronize()
                 e0.record()
-                for _, _, ptrs, o in seq:
-                    lib.rog_gather(ptrs, W, S, o, stream)
+                gr.replay()
                 e1.record()
                 torch.cuda.synchronize()
                 return e0.elapsed_time(e1) / len(seq)
 
-            warm_ms = run([sets[0]] * calls)
-            cold_ms = run([sets[i % K] for i in range(max(calls, 2 * K))])
+            n_calls = max(calls, 2 * K)
+            warm_ms = run([sets[0]] * n_calls)
+            cold_ms = run([sets[i % K] for i in range(n_calls)])
             for srcs, out, _, _ in sets:
                 for r in range(W):
                     for lo in (0, S // 2, S - 1024):
                         if not torch.equal(out[r * S + lo: r * S + lo + 1024], srcs[r][lo:lo + 1024]):
                             raise AssertionError("sweep gather W=%d S=%d wrong at rank %d" % (W, S, r))
             moved = 2 * W * S
-            rows.append({"W": W, "out_MiB": mib, "sets": K,
+            rows.append({"W": W, "out_MiB": mib, "sets": K, "calls": n_calls,
+                         "timed": "graph replay" if graph else "eager launches",
                          "warm_GBps": round(gbps(moved, warm_ms), 1),
                          "warm_pct_of_peak": round(100 * gbps(moved, warm_ms) / PEAK_HBM_GBPS, 1),
                          "cold_GBps": round(gbps(moved, cold_ms), 1),
@@ -842,7 +865,9 @@ def main(argv=None):
         crossover(torch, rog, device, args.steps, args.warmup)
         return 0
     if args.sweep_only:
-        print(json.dumps({"bandwidth_sweep": bandwidth_sweep(torch, rog, device, 20),
+        # eager launches throughout: under a kernel trace, graph-replayed
+        # kernels carry the tracer's own cost per node
+        print(json.dumps({"bandwidth_sweep": bandwidth_sweep(torch, rog, device, SWEEP_CALLS),
                           "bandwidth_sweep_mid": bandwidth_sweep(torch, rog, device, 50, out_mib=SWEEP_MID_OUT_MIB)}),
               flush=True)
         return 0
@@ -876,9 +901,10 @@ def main(argv=None):
         extras["gather_many"] = batch_bench(torch, rog, wl, device, BATCH_STEPS,
                                             max(BATCH_WARMUP, args.warmup))
         extras["d2d_copy_ceiling"] = d2d_ceiling(torch, device, case.W * case.S, 20, 3)
-        extras["bandwidth_sweep"] = bandwidth_sweep(torch, rog, device, 20)
+        extras["bandwidth_sweep"] = bandwidth_sweep(torch, rog, device, SWEEP_CALLS)
         # the size sweep's 1 and 4 MiB payloads (outputs of 2 - 32 MiB), warm and cold
-        extras["bandwidth_sweep_mid"] = bandwidth_sweep(torch, rog, device, 50, out_mib=SWEEP_MID_OUT_MIB)
+        extras["bandwidth_sweep_mid"] = bandwidth_sweep(torch, rog, device, 50, out_mib=SWEEP_MID_OUT_MIB,
+                                                        graph=True)
         big, rpayloads, rgot = reduce_bandwidth(torch, rog, wl, device, args.steps, args.warmup)
         extras["reduce"] = {"bandwidth": big,
                             "latency": reduce_latency(torch, rog, wl, device),
