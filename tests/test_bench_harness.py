@@ -167,3 +167,45 @@ def test_native_latency_harness_builds():
         pytest.skip("no gcc or librog.so not built")
     path = bench.build_native()
     assert os.access(path, os.X_OK)
+
+
+def test_slices_cover_the_range_once():
+    for n, parts in [(10, 3), (7, 7), (5, 9), (1 << 20, 64), (1, 1)]:
+        pieces = bench.slices(n, parts)
+        assert pieces[0][0] == 0 and pieces[-1][1] == n
+        assert all(a[1] == b[0] for a, b in zip(pieces, pieces[1:]))
+        assert all(hi > lo for lo, hi in pieces)
+        assert len(pieces) == min(parts, n)
+
+
+def test_cpu_baselines_report_cores_and_the_single_core_figure():
+    """Both oracle legs on a small stand-in case: the line carries the
+    many-core figure with its thread count, the single-core one beside it,
+    and the many-core results equal the single-call ones."""
+    import numpy as np
+    from deterministic_collective_movement_amd import workloads as wl
+    from oracle import oracle
+
+    class Case:
+        W, S = 3, 100_003
+    payloads = [wl.random_bytes(5, r, Case.S) for r in range(Case.W)]
+    cpu = bench.cpu_baseline(Case, payloads, 0.05, threads=4)
+    assert cpu["kind"] == "oracle" and cpu["cores"] == 4 and cpu["unit"] == "GB/s" and cpu["value"] > 0
+    assert cpu["single_core"]["cores"] == 1 and cpu["single_core"]["value"] > 0
+    assert "cpu_model" in cpu and cpu["cores_available"] >= 1
+    rp = wl.reduce_payloads(6, 8, 5000, "bf16")
+    want = np.empty(5000, np.uint16)
+    oracle.reduce_c(rp, want, "bf16")
+    red = bench.reduce_cpu_baseline(rp, want, 0.05, sample=5000, threads=3)
+    assert red["cores"] == 3 and red["single_core"]["cores"] == 1
+    with pytest.raises(AssertionError):
+        bad = want.copy()
+        bad[7] ^= 1
+        bench.reduce_cpu_baseline(rp, bad, 0.01, sample=5000, threads=2)
+
+
+def test_latency_legs_time_a_fixed_hundred_calls():
+    import inspect
+    for fn in (bench.latency_sweep, bench.reduce_latency, bench.launch_floor):
+        params = inspect.signature(fn).parameters
+        assert params["steps"].default == bench.LATENCY_CALLS == 100
