@@ -98,22 +98,6 @@ __host__ __device__ inline vec16 cut16(vec16 lo, vec16 hi, uint32_t m) {
     }
 }
 
-// The tensor of a batch launch of n tensors that owns chunk c: the last t
-// with first[t] <= c (first[] strictly increases), by a scalar binary search
-// over the kernel arguments.  Measured 4-5 % faster on the 16-tensor batches
-// than counting all entries in scalar registers, whose ~90 scalar
-// instructions per 1 KiB chunk cost more than the search's few dependent
-// loads.
-__device__ __forceinline__ uint32_t batch_tensor(const uint32_t (&first)[kMaxBatch], uint32_t n, uint32_t c) {
-    uint32_t lo = 0, hi = n;
-    while (hi - lo > 1) {
-        const uint32_t mid = (lo + hi) / 2;
-        if (first[mid] <= c) lo = mid;
-        else hi = mid;
-    }
-    return lo;
-}
-
 // A launch's arguments read through the kernel-argument segment pointer.  The
 // kernels take one argument struct by value, which the AMDGPU ABI places at
 // offset 0 of that segment; reading it through the segment pointer keeps every

@@ -223,6 +223,57 @@ inline uint32_t flat_shift(uint64_t out, uint64_t n_vec) {
     return n_vec < (uint64_t(1) << 31) ? uint32_t((out & 127) >> 4) : 0;
 }
 
+// A batch launch's chunks are its tensors' chunks laid end to end; tensor t
+// owns chunks [first[t], first[t + 1]).  To find the tensor of chunk c
+// without a full binary search of dependent loads, the chunk space is cut into
+// kBatchBuckets buckets of 2^shift chunks, and bucket_lo[b] names the tensor
+// that owns the first chunk of bucket b (bucket_lo[kBatchBuckets] the last
+// tensor).  Chunk c's tensor lies in [bucket_lo[b], bucket_lo[b + 1]] for
+// b = c >> shift, so the search runs only over the tensors that meet the
+// bucket: none at all for a chunk of a tensor larger than a bucket.
+constexpr uint32_t kBatchBuckets = 256;
+struct BatchLookup {
+    uint32_t shift;                          // log2 of the chunks per bucket
+    uint32_t bucket_lo[kBatchBuckets / 4 + 1];   // entry b in byte b % 4 of word b / 4; b <= kBatchBuckets
+};
+static_assert(kMaxBatch <= 256, "bucket entries are bytes");
+
+// Entry b of a bucket table, read as whole 32-bit words (scalar loads; the
+// device has no scalar byte load, and a byte read from memory would become a
+// vector load).
+__host__ __device__ inline uint32_t bucket_entry(const BatchLookup &lk, uint32_t b) {
+    return (lk.bucket_lo[b >> 2] >> (8 * (b & 3))) & 0xFFu;
+}
+
+// The tensor that owns chunk c (c below the launch's chunk count, first[0] == 0
+// and first[] strictly increasing over the tensors).
+__host__ __device__ inline uint32_t batch_tensor(const uint32_t *first, const BatchLookup &lk, uint32_t c) {
+    const uint32_t b = c >> lk.shift;
+    uint32_t lo = bucket_entry(lk, b), hi = bucket_entry(lk, b + 1) + 1;
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) / 2;
+        if (first[mid] <= c) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Fill lk for n tensors (n >= 1) with first chunks first[0 .. n) and
+// n_chunks chunks in all (n_chunks >= 1).
+inline void plan_lookup(const uint32_t *first, uint32_t n, uint32_t n_chunks, BatchLookup *lk) {
+    uint32_t shift = 0;
+    while (((n_chunks - 1) >> shift) >= kBatchBuckets) ++shift;
+    lk->shift = shift;
+    for (uint32_t w = 0; w < kBatchBuckets / 4 + 1; ++w) lk->bucket_lo[w] = 0;
+    uint32_t t = 0;
+    for (uint32_t b = 0; b <= kBatchBuckets; ++b) {
+        const uint64_t c0 = uint64_t(b) << shift;
+        const uint32_t c = c0 < n_chunks ? uint32_t(c0) : n_chunks - 1;
+        while (t + 1 < n && first[t + 1] <= c) ++t;
+        lk->bucket_lo[b >> 2] |= t << (8 * (b & 3));
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Kernel arguments
 // ---------------------------------------------------------------------------
@@ -284,6 +335,7 @@ struct BatchArgs {
     uint32_t n_chunks;                // all tensors' chunks
     uint32_t aligned_chunks;          // chunks of the line-aligned FLAT tensors, which come first
     uint32_t grid;                    // workgroups launched (the grid stride)
+    BatchLookup lookup;               // chunk -> tensor buckets
 };
 
 static_assert(sizeof(BatchArgs) <= 4096, "kernel arguments must stay below 4 KiB");
@@ -338,6 +390,7 @@ struct ReduceBatchArgs {
     uint32_t W;
     uint32_t n_chunks;                // all tensors' chunks
     uint32_t grid;                    // workgroups launched (the grid stride)
+    BatchLookup lookup;               // chunk -> tensor buckets
 };
 
 static_assert(sizeof(ReduceBatchArgs) <= 4096, "kernel arguments must stay below 4 KiB");

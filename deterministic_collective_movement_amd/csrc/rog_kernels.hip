@@ -264,11 +264,11 @@ __global__ __launch_bounds__(kSingleBlock) void rog_peer_single_kernel(PeerArgs 
 template <bool NTL>
 __global__ __launch_bounds__(kWaveBlock) void rog_batch_kernel(BatchArgs) {
     const BatchArgs &a = launch_args<BatchArgs>();
-    const uint32_t n_chunks = a.n_chunks, aligned = a.aligned_chunks, n = a.n, W = a.W, grid = a.grid;
-    hold_scalars(n_chunks, aligned, n, W, grid);
+    const uint32_t n_chunks = a.n_chunks, aligned = a.aligned_chunks, W = a.W, grid = a.grid;
+    hold_scalars(n_chunks, aligned, a.lookup.shift, W, grid);
     for (uint32_t vb = blockIdx.x; vb < n_chunks; vb += grid) {
         const uint32_t c = vb < aligned ? vb : aligned + xcd_grouped(vb - aligned, n_chunks - aligned);
-        const uint32_t lo = batch_tensor(a.first, n, c);
+        const uint32_t lo = batch_tensor(a.first, a.lookup, c);
         const BatchTensor &t = a.t[lo];
         const uint32_t lc = c - a.first[lo];
         // the tensor's fields either form needs, in one batch of scalar loads

@@ -149,3 +149,99 @@ def test_reduce_batch_layout(shim, data, n, W, dtype):
     source_bytes = sum(W * cnt * es for _, _, cnt in tensors)
     nt = source_bytes >= 384 << 20
     assert meta[2] == int(nt) and meta[3] == int(nt)   # the granule form exactly with streamed loads
+
+
+def _lookup(shim, tensors, W, chunks):
+    keep = [(ctypes.c_void_p * W)(*srcs) for srcs, _, _ in tensors]
+    descs = (rog.rog_gather_desc * max(1, len(tensors)))()
+    for i, (srcs, o, S) in enumerate(tensors):
+        descs[i].srcs = ctypes.cast(keep[i], ctypes.POINTER(ctypes.c_void_p))
+        descs[i].out = ctypes.c_void_p(o)
+        descs[i].bytes_per_rank = S
+    q = (ctypes.c_uint32 * len(chunks))(*chunks)
+    got = (ctypes.c_uint32 * len(chunks))()
+    shift = ctypes.c_uint32()
+    assert shim.rog_test_batch_lookup(descs, len(tensors), W, q, len(chunks), got, ctypes.byref(shift)) == 0
+    return list(got), shift.value
+
+
+def _owner(first, c):
+    import bisect
+    return bisect.bisect_right(first, c) - 1
+
+
+@settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(data=st.data(), n=st.integers(1, 32), W=st.sampled_from([1, 2, 4]))
+def test_batch_lookup_finds_every_chunks_tensor(shim, data, n, W):
+    """The kernels' chunk -> tensor lookup (a bucket table, then a search over
+    the tensors that meet the bucket) against a plain search over the first
+    chunks: every chunk of small batches, and the first, last and random
+    chunks of every tensor of large ones (up to 2^28 chunks)."""
+    tensors = []
+    for t in range(n):
+        S = data.draw(st.one_of(st.just(0), st.integers(1, 3000),
+                                st.sampled_from([16, 1024, 65536, 1 << 20, 1 << 24, 1 << 28])))
+        base = BASE + t * (1 << 34)
+        srcs = [base + r * (1 << 30) for r in range(W)]
+        tensors.append((srcs, base + (W + 1) * (1 << 30) + data.draw(st.sampled_from([0, 16, 3])), S))
+    status, planned, meta = plan_batch(shim, tensors, W)
+    assert status == 0
+    if not planned:
+        return
+    first = [p["first"] for p in planned]
+    total = meta[0]
+    if total <= 20000:
+        chunks = list(range(total))
+    else:
+        chunks = []
+        for k, p in enumerate(planned):
+            lo, hi = p["first"], p["first"] + p["n_chunks"]
+            chunks += [lo, hi - 1, (lo + hi) // 2]
+            chunks += [data.draw(st.integers(lo, hi - 1)) for _ in range(3)]
+    got, shift = _lookup(shim, tensors, W, chunks)
+    assert ((total - 1) >> shift) < 256
+    assert got == [_owner(first, c) for c in chunks]
+
+
+def test_batch_lookup_many_small_tensors_in_one_bucket(shim):
+    """Thirty-one one-chunk tensors and one huge one: the small ones share the
+    first bucket, and the search among them still finds each."""
+    W = 1
+    tensors = [([BASE + t * (1 << 32)], BASE + t * (1 << 32) + (1 << 31), 1024) for t in range(31)]
+    tensors.append(([BASE + 40 * (1 << 32)], BASE + 41 * (1 << 32), 1 << 30))
+    status, planned, meta = plan_batch(shim, tensors, W)
+    assert status == 0 and len(planned) == 32
+    first = [p["first"] for p in planned]
+    chunks = list(range(0, 64)) + [meta[0] - 1, meta[0] // 2]
+    got, shift = _lookup(shim, tensors, W, chunks)
+    assert shift > 0
+    assert got == [_owner(first, c) for c in chunks]
+
+
+@settings(max_examples=80, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(data=st.data(), n=st.integers(1, 32), W=st.sampled_from([1, 3]))
+def test_reduce_batch_lookup_finds_every_chunks_tensor(shim, data, n, W):
+    tensors = []
+    for t in range(n):
+        cnt = data.draw(st.one_of(st.just(0), st.integers(1, 20_000), st.sampled_from([1 << 16, 1 << 22, 1 << 27])))
+        base = BASE + t * (1 << 34)
+        tensors.append(([base + r * (1 << 30) for r in range(W)], base + (W + 1) * (1 << 30), cnt))
+    status, planned, meta = plan_reduce_batch(shim, tensors, W, 0)
+    assert status == 0
+    if not planned:
+        return
+    first = [p["first"] for p in planned]
+    chunks = []
+    for p in planned:
+        lo, hi = p["first"], p["first"] + p["n_chunks"]
+        chunks += [lo, hi - 1, (lo + hi) // 2, data.draw(st.integers(lo, hi - 1))]
+    keep = [(ctypes.c_void_p * W)(*srcs) for srcs, _, _ in tensors]
+    descs = (rog.rog_reduce_desc * len(tensors))()
+    for i, (srcs, o, cnt) in enumerate(tensors):
+        descs[i].srcs = ctypes.cast(keep[i], ctypes.POINTER(ctypes.c_void_p))
+        descs[i].out = ctypes.c_void_p(o)
+        descs[i].count = cnt
+    q = (ctypes.c_uint32 * len(chunks))(*chunks)
+    got = (ctypes.c_uint32 * len(chunks))()
+    assert shim.rog_test_reduce_batch_lookup(descs, len(tensors), W, 0, q, len(chunks), got) == 0
+    assert list(got) == [_owner(first, c) for c in chunks]
