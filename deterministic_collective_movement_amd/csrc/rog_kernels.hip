@@ -32,9 +32,10 @@
 //    both sides are aligned); the bytes written are the same.  Multi-WG, the body is cut into 1 KiB chunks,
 //    one wave per chunk, all payloads at once; single-WG, the one workgroup
 //    takes the payloads in turn.
-//  * BATCH kernel (rog_gather_many): one launch; every wave finds its tensor by
-//    a scalar binary search over the tensors' first chunks and does one FLAT
-//    or PEER chunk of that tensor.
+//  * BATCH kernel (rog_gather_many): one launch; every wave finds its tensor
+//    through a bucket table of the chunk index (a scalar load of two bucket
+//    entries, then a search only between the tensors those name) and does one
+//    FLAT or PEER chunk of that tensor.
 //
 // Everything a launch needs is in its kernel arguments; there are no scratch
 // buffers, atomics or inter-workgroup synchronisation, and every output byte

@@ -256,8 +256,8 @@ __global__ __launch_bounds__(kWaveBlock) void rog_reduce_kernel(ReduceArgs) {
         sum_chunk<DT, NTL, SH>(a.src, W, out, count, ROG_REDUCE_XCD ? xcd_grouped(vb, n_chunks) : vb);
 }
 
-// Batch: the tensors' chunks laid end to end; a wave finds its tensor by a
-// scalar binary search over the tensors' first chunks.
+// Batch: the tensors' chunks laid end to end; a wave finds its tensor through
+// the bucket table of the chunk index, as the batched gather does.
 template <int DT, bool NTL, bool SH>
 __global__ __launch_bounds__(kWaveBlock) void rog_reduce_batch_kernel(ReduceBatchArgs) {
     const ReduceBatchArgs &a = launch_args<ReduceBatchArgs>();
