@@ -346,7 +346,6 @@ rog_status plan_reduce_batch(const rog_reduce_desc *descs, int n, int W, rog_dty
     args->n_chunks = uint32_t(next);   // 32 tensors of < 2^26 chunks each
     *grid = uint32_t(std::min<uint64_t>(next, max_grid(kWaveBlock)));
     args->grid = *grid;
-    if (k > 0) plan_lookup(args->first, k, args->n_chunks, &args->lookup);
     *nt_loads = source_bytes >= kNtLoadMinBytes;
     *shifted = kReduceShift == 2 || (kReduceShift == 1 && *nt_loads);
     return ROG_OK;

@@ -256,16 +256,16 @@ __global__ __launch_bounds__(kWaveBlock) void rog_reduce_kernel(ReduceArgs) {
         sum_chunk<DT, NTL, SH>(a.src, W, out, count, ROG_REDUCE_XCD ? xcd_grouped(vb, n_chunks) : vb);
 }
 
-// Batch: the tensors' chunks laid end to end; a wave finds its tensor through
-// the bucket table of the chunk index, as the batched gather does.
+// Batch: the tensors' chunks laid end to end; a wave finds its tensor by a
+// scalar binary search over the tensors' first chunks.
 template <int DT, bool NTL, bool SH>
 __global__ __launch_bounds__(kWaveBlock) void rog_reduce_batch_kernel(ReduceBatchArgs) {
     const ReduceBatchArgs &a = launch_args<ReduceBatchArgs>();
     const uint32_t n_chunks = a.n_chunks, W = a.W, grid = a.grid;
-    hold_scalars(n_chunks, a.lookup.shift, W, grid, 0u);
+    hold_scalars(n_chunks, a.n, W, grid, 0u);
     for (uint32_t vb = blockIdx.x; vb < n_chunks; vb += grid) {
         const uint32_t c = ROG_REDUCE_XCD ? xcd_grouped(vb, n_chunks) : vb;
-        const uint32_t lo = batch_tensor(a.first, a.lookup, c);
+        const uint32_t lo = search_tensor(a.first, a.n, c);
         const ReduceTensor &t = a.t[lo];
         sum_chunk<DT, NTL, SH>(a.src + lo * W, W, reinterpret_cast<void *>(t.out), t.count, c - a.first[lo]);
     }

@@ -58,7 +58,7 @@ extern "C" int rog_test_plan_reduce_batch(const rog_reduce_desc *descs, int n, i
     return 0;
 }
 
-// The batch kernels' chunk -> tensor lookup (batch_tensor over the planner's
+// The batched gather's chunk -> tensor lookup (batch_tensor over the planner's
 // bucket table) for chunks[0 .. n_query) of a gather batch: the tensor index
 // of each, written to tensor[].  Returns the planner's status.
 extern "C" int rog_test_batch_lookup(const rog_gather_desc *descs, int n, int W, const uint32_t *chunks,
@@ -73,7 +73,8 @@ extern "C" int rog_test_batch_lookup(const rog_gather_desc *descs, int n, int W,
     return 0;
 }
 
-// The same for a batch of sums.
+// The batched sums' lookup (search_tensor over the planner's first chunks),
+// likewise.
 extern "C" int rog_test_reduce_batch_lookup(const rog_reduce_desc *descs, int n, int W, int dtype,
                                             const uint32_t *chunks, uint32_t n_query, uint32_t *tensor) {
     static rog::ReduceBatchArgs a;
@@ -81,6 +82,6 @@ extern "C" int rog_test_reduce_batch_lookup(const rog_reduce_desc *descs, int n,
     bool nt = false, sh = false;
     const rog_status st = rog::plan_reduce_batch(descs, n, W, rog_dtype(dtype), &a, &grid, &nt, &sh);
     if (st != ROG_OK) return int(st);
-    for (uint32_t i = 0; i < n_query; ++i) tensor[i] = rog::batch_tensor(a.first, a.lookup, chunks[i]);
+    for (uint32_t i = 0; i < n_query; ++i) tensor[i] = rog::search_tensor(a.first, a.n, chunks[i]);
     return 0;
 }
