@@ -42,8 +42,8 @@ constexpr int kMaxBatchPtrs = 192;
 #ifndef ROG_NT_LOAD_MIN_BYTES
 #define ROG_NT_LOAD_MIN_BYTES (384ull << 20)
 #endif
-#ifndef ROG_FLAT_NT_LOAD_MIN_BYTES
-#define ROG_FLAT_NT_LOAD_MIN_BYTES (128ull << 20)
+#ifndef ROG_GATHER_NT_LOAD_MIN_BYTES
+#define ROG_GATHER_NT_LOAD_MIN_BYTES (128ull << 20)
 #endif
 #ifndef ROG_BODY_ALIGN
 #define ROG_BODY_ALIGN 256
@@ -97,15 +97,16 @@ constexpr int kSumStoreAux = ROG_SUM_STORE_AUX;
 // lookup), kSingleUnroll beyond.
 inline int single_flat_unroll(uint64_t n_vec) { return n_vec <= uint64_t(kSingleBlock) ? 1 : kSingleUnroll; }
 // Source bytes from which 16-byte loads are non-temporal: below it the payloads
-// may still sit in the 256 MB Infinity Cache, and cached loads then win.  PEER
-// gathers, batches and sums switch at 384 MiB.  Aligned (FLAT) gathers switch
+// may still sit in the 256 MB Infinity Cache, and cached loads then win.
+// Batches and sums switch at 384 MiB.  A single gather, FLAT or PEER, switches
 // at 128 MiB: there, over buffers that miss the Infinity Cache, streamed loads
-// measured 81-82 % of peak against 78 % cached (128 MiB of output) and 83-84 %
-// against 80 % (256 MiB), while over buffers it still holds they measured
-// 81-83 % against 89-91 % cached; at 64 MiB of output cached loads keep 85 %
-// warm (77 % streamed) and lose 2 points cold (75 % against 77 %).
+// measured 81-82 % of peak against 78 % cached for FLAT (128 MiB of output)
+// and 83-84 % against 80 % (256 MiB), 79-83 % against 77-80 % for PEER (128
+// and 256 MiB), while over buffers it still holds they measured 80-83 %
+// against 89-91 % cached; at 64 MiB of output cached loads keep 85 % warm (77
+// % streamed) and lose 2 points cold (75 % against 77 %).
 constexpr uint64_t kNtLoadMinBytes = ROG_NT_LOAD_MIN_BYTES;
-constexpr uint64_t kFlatNtLoadMinBytes = ROG_FLAT_NT_LOAD_MIN_BYTES;
+constexpr uint64_t kGatherNtLoadMinBytes = ROG_GATHER_NT_LOAD_MIN_BYTES;
 constexpr uint32_t kGridCap = ROG_GRID_CAP;       // workgroups of one launch, at most
 // Destination alignment at which a PEER payload's 16-byte body starts (a power
 // of two >= 16): each wave's 1 KiB of stores then covers whole cache lines.

@@ -162,7 +162,7 @@ rog_status plan_gather(const void *const *srcs, int W, size_t S, const void *out
     }
     const bool single = path == ROG_PATH_SINGLE_WG;
     const bool flat = is_flat(srcs, W, S, out);
-    if (total >= (flat ? kFlatNtLoadMinBytes : kNtLoadMinBytes)) info.flags |= ROG_PLAN_NT_LOADS;
+    if (total >= kGatherNtLoadMinBytes) info.flags |= ROG_PLAN_NT_LOADS;
 
     if (flat) {
         FlatArgs &a = plan->flat;

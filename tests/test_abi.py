@@ -22,8 +22,7 @@ FLAT_BLOCK, FLAT_UNROLL = 64, 1      # multi-WG FLAT: threads per WG, vectors pe
 SINGLE_UNROLL = 4                    # single-WG FLAT: vectors per lane per chunk
 SINGLE_PEER_UNROLL = 4               # single-WG PEER: 16-byte vectors per thread
 PEER_BLOCK = 64                      # multi-WG PEER: one wave per workgroup, 64 body vectors each
-NT_LOAD_MIN_BYTES = 384 << 20        # source bytes from which PEER loads are non-temporal
-FLAT_NT_LOAD_MIN_BYTES = 128 << 20   # the same for FLAT gathers
+GATHER_NT_LOAD_MIN_BYTES = 128 << 20   # source bytes from which a single gather's loads are non-temporal
 OK, INVALID, OVERLAP, TOO_LARGE = (rog.ROG_OK, rog.ROG_ERR_INVALID_ARGUMENT,
                                    rog.ROG_ERR_OVERLAP, rog.ROG_ERR_TOO_LARGE)
 
@@ -277,14 +276,15 @@ def test_nt_load_policy_follows_source_bytes():
     out = 1 << 40
     # FLAT (everything 16-byte aligned)
     for W, S, want in [(8, 64 << 20, True), (8, 16 << 20, True), (8, 8 << 20, False),
-                       (1, FLAT_NT_LOAD_MIN_BYTES, True), (1, FLAT_NT_LOAD_MIN_BYTES - 16, False),
+                       (1, GATHER_NT_LOAD_MIN_BYTES, True), (1, GATHER_NT_LOAD_MIN_BYTES - 16, False),
                        (2, 1024, False)]:
         srcs = [A + (S + 4096) * r for r in range(W)]
         p = rog.rog_plan_ptrs(srcs, S, out)
         assert p["kernel"] == "flat" and p["nt_loads"] is want, (W, S)
     # PEER (sources one byte off)
-    for W, S, want in [(8, 64 << 20, True), (8, 32 << 20, False), (1, NT_LOAD_MIN_BYTES, True),
-                       (1, NT_LOAD_MIN_BYTES - 16, False), (8, 16 << 20, False)]:
+    for W, S, want in [(8, 64 << 20, True), (8, 16 << 20, True), (8, (16 << 20) - 1, False),
+                       (1, GATHER_NT_LOAD_MIN_BYTES, True), (1, GATHER_NT_LOAD_MIN_BYTES - 16, False),
+                       (8, 8 << 20, False)]:
         srcs = [A + 1 + (S + 4096) * r for r in range(W)]
         p = rog.rog_plan_ptrs(srcs, S, out)
         assert p["kernel"] == "peer" and p["nt_loads"] is want, (W, S)

@@ -218,6 +218,24 @@ def test_flat_gathers_around_the_streaming_bound(gpu, W, S, offs):
     gc.run_all_paths(placed, "flat %d x %d" % (W, S), paths=(rog.ROG_PATH_AUTO,))
 
 
+@pytest.mark.parametrize("W,S,io,oo", [(8, (16 << 20) + 5, 1, 3), (8, (16 << 20) - 3, 1, 3),
+                                        (2, (64 << 20) + 1, 0, 1), (4, 32 << 20, 2, 0)],
+                         ids=["8x16MiB+5_at_1_3", "8x16MiB-3_at_1_3", "2x64MiB+1_at_0_1", "4x32MiB_at_2_0"])
+def test_peer_gathers_around_the_streaming_bound(gpu, W, S, io, oo):
+    """PEER gathers stream their loads from 128 MiB of sources, as FLAT ones
+    do, and then read shifted sources as shared granules: just above the bound
+    and just below it (cached, unaligned loads), every byte against the
+    oracle."""
+    rng = np.random.default_rng(W * 7919 + S % 1009 + io)
+    payloads = [np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(W)]
+    placed = gc.Placed(payloads, [io] * W, oo, gpu)
+    plan = rog.rog_plan(placed.srcs, placed.out)
+    assert plan["kernel"] == "peer" and plan["path"] == "multi_wg"
+    assert plan["nt_loads"] is (W * S >= 128 << 20)
+    assert plan["shifted_loads"] == (plan["nt_loads"] and _shares_granules(placed))
+    gc.run_all_paths(placed, "peer %d x %d at (%d, %d)" % (W, S, io, oo), paths=(rog.ROG_PATH_AUTO,))
+
+
 @pytest.mark.parametrize("S,W", [(16 * 1000, 4), (4095, 3), (1 << 20, 8)])
 def test_exact_in_place_segments(gpu, S, W):
     """Payloads 1 and 3 already sit in their own output segments."""

@@ -128,8 +128,8 @@ def test_gather_plan_matches_the_rules(W, S, path, data):
     if not flat:
         mask = sum(1 << r for r, s in enumerate(srcs) if ((s | (out + r * S)) & 15) == 0)
         assert info.vec_ok_mask == mask
-    assert bool(info.flags & rog.ROG_PLAN_NT_LOADS) == (total >= (128 << 20 if flat else 384 << 20))
-    shifted = (not flat and info.path == 2 and total >= 384 << 20
+    assert bool(info.flags & rog.ROG_PLAN_NT_LOADS) == (total >= 128 << 20)
+    shifted = (not flat and info.path == 2 and total >= 128 << 20
                and any(shared_granules(s, out + r * S, S, PEER_MODE) for r, s in enumerate(srcs)))
     assert bool(info.flags & rog.ROG_PLAN_SHIFTED_LOADS) == shifted
 
