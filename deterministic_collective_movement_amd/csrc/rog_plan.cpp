@@ -276,7 +276,7 @@ rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype d
     info.path = path;
     info.kernel = ROG_KERNEL_REDUCE;
     info.units = count;
-    if (uint64_t(W) * bytes >= kNtLoadMinBytes) info.flags |= ROG_PLAN_NT_LOADS;
+    if (sum_nt_loads(uint32_t(W), uint64_t(W) * bytes)) info.flags |= ROG_PLAN_NT_LOADS;
 
     ReduceArgs &a = plan->reduce;
     memset(&a, 0, sizeof(a));
@@ -346,7 +346,7 @@ rog_status plan_reduce_batch(const rog_reduce_desc *descs, int n, int W, rog_dty
     args->n_chunks = uint32_t(next);   // 32 tensors of < 2^26 chunks each
     *grid = uint32_t(std::min<uint64_t>(next, max_grid(kWaveBlock)));
     args->grid = *grid;
-    *nt_loads = source_bytes >= kNtLoadMinBytes;
+    *nt_loads = sum_nt_loads(uint32_t(W), source_bytes);
     *shifted = kReduceShift == 2 || (kReduceShift == 1 && *nt_loads);
     return ROG_OK;
 }
@@ -430,7 +430,7 @@ rog_status plan_batch(const rog_gather_desc *descs, int n, int W, BatchArgs *arg
     if (k > 0) plan_lookup(args->first, k, args->n_chunks, &args->lookup);
     uint64_t source_bytes = 0;
     for (int t = 0; t < n; ++t) source_bytes += totals[t];
-    *nt_loads = source_bytes >= kNtLoadMinBytes;
+    *nt_loads = source_bytes >= kGatherNtLoadMinBytes;
     return ROG_OK;
 }
 

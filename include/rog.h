@@ -113,8 +113,9 @@ typedef struct {
 
 /* rog_plan_info.flags: the kernel's 16-byte loads are non-temporal (streamed
  * past the caches); set when the W*S source bytes are too many for the 256 MB
- * Infinity Cache to serve repeated calls well: from 128 MiB for a single
- * gather (FLAT or PEER), from 384 MiB for a batch or a sum.  16-byte stores are always
+ * Infinity Cache to serve repeated calls well: from 128 MiB for a gather,
+ * single or batched; for a sum (single or batched) of 4 or more sources from
+ * 128 MiB, of 3 sources from 384 MiB, of 1 or 2 never.  16-byte stores are always
  * non-temporal; a gather's are also written through the L2 caches at device
  * scope.  Affects speed only. */
 #define ROG_PLAN_NT_LOADS 1u

@@ -22,6 +22,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 MAXB = 32
 
 
+def sum_streams(W, source_bytes):
+    """The header's rule for a sum's streamed loads: from 4 sources on at
+    128 MiB of sources, with 3 at 384 MiB, with 1 or 2 never."""
+    if W >= 4:
+        return source_bytes >= 128 << 20
+    return W == 3 and source_bytes >= 384 << 20
+
+
 @pytest.fixture(scope="module")
 def shim(tmp_path_factory):
     hipcc = shutil.which("hipcc") or os.path.join(b.ROCM, "bin", "hipcc")
@@ -83,7 +91,8 @@ BASE = 1 << 40
 def test_gather_batch_layout(shim, data, n, W):
     tensors = []
     for t in range(n):
-        S = data.draw(st.one_of(st.just(0), st.integers(1, 5000), st.sampled_from([16, 1024, 4096, 65536, 1 << 20])))
+        S = data.draw(st.one_of(st.just(0), st.integers(1, 5000),
+                                st.sampled_from([16, 1024, 4096, 65536, 1 << 20, 24 << 20])))
         off = data.draw(st.sampled_from([0, 0, 16, 1, 3, 8, 48, 128]))
         base = BASE + t * (1 << 32)
         srcs = [base + r * (1 << 28) + off for r in range(W)]
@@ -103,6 +112,7 @@ def test_gather_batch_layout(shim, data, n, W):
     assert meta[0] == nxt
     assert meta[1] == sum(x[4] for x in want if x[5])
     assert meta[2] == nxt            # one wave per chunk while the grid is not capped
+    assert meta[3] == int(W * sum(S for _, _, S in tensors) >= 128 << 20)   # streamed loads from 128 MiB
 
 
 def test_gather_batch_all_empty(shim):
@@ -147,7 +157,7 @@ def test_reduce_batch_layout(shim, data, n, W, dtype):
         nxt += p["n_chunks"]
     assert meta[0] == nxt and meta[1] == nxt
     source_bytes = sum(W * cnt * es for _, _, cnt in tensors)
-    nt = source_bytes >= 384 << 20
+    nt = sum_streams(W, source_bytes)
     assert meta[2] == int(nt) and meta[3] == int(nt)   # the granule form exactly with streamed loads
 
 

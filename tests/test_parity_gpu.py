@@ -435,3 +435,16 @@ def test_streamed_batch_with_small_misaligned_tensors(gpu):
     out_offs = [3, 0, 0, 1, 0, 3, 7, 2, 9, 0]
     payloads = [[np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(W)] for S in sizes]
     gc.PlacedBatch(W, payloads, in_offs, out_offs, gpu).run("streamed batch, small misaligned tensors")
+
+
+def test_streamed_batch_from_128_MiB(gpu):
+    """A batch streams its loads from 128 MiB of sources, as a single gather
+    does: 8 tensors of 6 MiB + 5 per payload (W = 4, 192 MiB of sources), at
+    odd offsets (shuffled PEER bodies) beside aligned ones, every byte against
+    the oracle."""
+    rng = np.random.default_rng(91)
+    W = 4
+    sizes = [(6 << 20) + 5] * 4 + [6 << 20] * 4
+    payloads = [[np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(W)] for S in sizes]
+    gc.PlacedBatch(W, payloads, [1, 3, 0, 2, 0, 0, 0, 0], [3, 1, 1, 0, 0, 0, 0, 0], gpu).run(
+        "streamed batch of 192 MiB")

@@ -268,3 +268,30 @@ def test_streamed_sums_over_several_source_groups(gpu, W, n, dtype):
     plan = rog.rog_reduce_plan(placed.srcs, placed.out)
     assert plan["nt_loads"] and plan["shifted_loads"]
     gc.run_reduce_all_paths(placed, "streamed W=%d %s" % (W, dtype), paths=(rog.ROG_PATH_AUTO,))
+
+
+@pytest.mark.parametrize("W,n,offs,nt", [
+    (4, 16 << 20, (1, 0), True), (4, (16 << 20) - 8, (1, 0), False),
+    (3, 64 << 20, (0, 1), True), (3, (64 << 20) - 8, (0, 1), False),
+    (2, 96 << 20, (1, 0), False)],
+    ids=["4x32MiB", "4x32MiB-16B", "3x128MiB", "3x128MiB-16B", "2x192MiB"])
+def test_sums_around_the_streaming_bounds(gpu, W, n, offs, nt):
+    """A sum streams its loads (and reads shared granules) from 128 MiB of
+    sources with 4 or more sources, from 384 MiB with 3, never with 2: on both
+    sides of each bound, at element offsets, every element against the
+    oracle."""
+    payloads = wl.reduce_payloads(640 + W, W, n, "bf16")
+    in_off, out_off = offs
+    placed = gc.PlacedReduce(payloads, [in_off] * W, out_off, "bf16", gpu)
+    plan = rog.rog_reduce_plan(placed.srcs, placed.out)
+    assert plan["path"] == "multi_wg" and plan["nt_loads"] is nt and plan["shifted_loads"] is nt
+    gc.run_reduce_all_paths(placed, "sum W=%d n=%d" % (W, n), paths=(rog.ROG_PATH_AUTO,))
+
+
+def test_streamed_batch_of_sums_from_128_MiB(gpu):
+    """A batch of sums with 4 sources streams from 128 MiB of sources: 16
+    tensors of 1.5 Mi bf16 elements (192 MiB of sources) at element offsets,
+    every element against the oracle."""
+    counts = [3 << 19] * 16
+    offs = [[(t + r) % 3 for r in range(4)] for t in range(16)]
+    _batch(47, 4, counts, "bf16", offs).run("batch of sums, 192 MiB of sources")
