@@ -45,8 +45,8 @@ constexpr int kMaxBatchPtrs = 192;
 #ifndef ROG_SUM_NT_LOAD_MIN_BYTES
 #define ROG_SUM_NT_LOAD_MIN_BYTES (128ull << 20)
 #endif
-#ifndef ROG_SUM3_NT_LOAD_MIN_BYTES
-#define ROG_SUM3_NT_LOAD_MIN_BYTES (384ull << 20)
+#ifndef ROG_SUM_GRANULE_MIN_W
+#define ROG_SUM_GRANULE_MIN_W 3
 #endif
 #ifndef ROG_BODY_ALIGN
 #define ROG_BODY_ALIGN 256
@@ -107,21 +107,17 @@ inline int single_flat_unroll(uint64_t n_vec) { return n_vec <= uint64_t(kSingle
 // 80 % (256 MiB), 79-83 % against 77-80 % for PEER and batches (128-312 MiB),
 // while over buffers it still holds they measured 80-83 % against 89-91 %
 // cached; at 64 MiB of output cached loads keep 85 % warm (77 % streamed) and
-// lose 2 points cold (75 % against 77 %).  A sum's switch also picks its
-// form (streamed loads read shared granules), and depends on W: from 4
-// sources on at 128 MiB of sources, where the granule form lifts the slower of
-// warm and cold by 2-22 %; with 3 sources at 384 MiB (at 192 MiB it tied cold
-// and lost 9 % warm, at 384 MiB it won both ways by 4-16 %); with 1 or 2
-// sources never (cached loads won both ways by 8-11 % even at 384 and 512 MiB).
+// lose 2 points cold (75 % against 77 %).  Sums (single or batched) switch at
+// 128 MiB of sources too, and then read shared granules only from 3 sources
+// on: against cached loads, over W = 2 to 8 and 128 to 512 MiB of sources,
+// streamed loads lifted the slower of warm and cold or tied it (1-8 % with
+// the plain form at W = 2, up to 22 % with the granule form from W = 3 on).
+// Against the plain form the granule form lost 6-15 % at W = 2; from W = 3 on
+// it won every case with sources off the output's alignment and lost at most
+// 7 % on aligned ones.
 constexpr uint64_t kGatherNtLoadMinBytes = ROG_GATHER_NT_LOAD_MIN_BYTES;
 constexpr uint64_t kSumNtLoadMinBytes = ROG_SUM_NT_LOAD_MIN_BYTES;
-constexpr uint64_t kSum3NtLoadMinBytes = ROG_SUM3_NT_LOAD_MIN_BYTES;
-// Whether a sum of W sources holding source_bytes in all streams its loads.
-inline bool sum_nt_loads(uint32_t W, uint64_t source_bytes) {
-    if (W >= 4) return source_bytes >= kSumNtLoadMinBytes;
-    if (W == 3) return source_bytes >= kSum3NtLoadMinBytes;
-    return false;
-}
+constexpr uint32_t kSumGranuleMinW = ROG_SUM_GRANULE_MIN_W;
 constexpr uint32_t kGridCap = ROG_GRID_CAP;       // workgroups of one launch, at most
 // Destination alignment at which a PEER payload's 16-byte body starts (a power
 // of two >= 16): each wave's 1 KiB of stores then covers whole cache lines.

@@ -276,7 +276,7 @@ rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype d
     info.path = path;
     info.kernel = ROG_KERNEL_REDUCE;
     info.units = count;
-    if (sum_nt_loads(uint32_t(W), uint64_t(W) * bytes)) info.flags |= ROG_PLAN_NT_LOADS;
+    if (uint64_t(W) * bytes >= kSumNtLoadMinBytes) info.flags |= ROG_PLAN_NT_LOADS;
 
     ReduceArgs &a = plan->reduce;
     memset(&a, 0, sizeof(a));
@@ -293,8 +293,10 @@ rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype d
         info.block = kWaveBlock;
         info.grid = std::min(a.n_chunks, max_grid(kWaveBlock));
         a.grid = info.grid;
-        // The granule form where loads stream past the caches (kReduceShift).
-        if (kReduceShift == 2 || (kReduceShift == 1 && (info.flags & ROG_PLAN_NT_LOADS)))
+        // The granule form where loads stream past the caches, from
+        // kSumGranuleMinW sources on (kReduceShift).
+        if (kReduceShift == 2 ||
+            (kReduceShift == 1 && (info.flags & ROG_PLAN_NT_LOADS) && uint32_t(W) >= kSumGranuleMinW))
             info.flags |= ROG_PLAN_SHIFTED_LOADS;
     }
     return ROG_OK;
@@ -346,8 +348,8 @@ rog_status plan_reduce_batch(const rog_reduce_desc *descs, int n, int W, rog_dty
     args->n_chunks = uint32_t(next);   // 32 tensors of < 2^26 chunks each
     *grid = uint32_t(std::min<uint64_t>(next, max_grid(kWaveBlock)));
     args->grid = *grid;
-    *nt_loads = sum_nt_loads(uint32_t(W), source_bytes);
-    *shifted = kReduceShift == 2 || (kReduceShift == 1 && *nt_loads);
+    *nt_loads = source_bytes >= kSumNtLoadMinBytes;
+    *shifted = kReduceShift == 2 || (kReduceShift == 1 && *nt_loads && uint32_t(W) >= kSumGranuleMinW);
     return ROG_OK;
 }
 

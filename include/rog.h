@@ -113,9 +113,8 @@ typedef struct {
 
 /* rog_plan_info.flags: the kernel's 16-byte loads are non-temporal (streamed
  * past the caches); set when the W*S source bytes are too many for the 256 MB
- * Infinity Cache to serve repeated calls well: from 128 MiB for a gather,
- * single or batched; for a sum (single or batched) of 4 or more sources from
- * 128 MiB, of 3 sources from 384 MiB, of 1 or 2 never.  16-byte stores are always
+ * Infinity Cache to serve repeated calls well: from 128 MiB, for gathers and
+ * sums, single or batched.  16-byte stores are always
  * non-temporal; a gather's are also written through the L2 caches at device
  * scope.  Affects speed only. */
 #define ROG_PLAN_NT_LOADS 1u
@@ -124,8 +123,8 @@ typedef struct {
  * after its own from the next lane.  Only with ROG_PLAN_NT_LOADS.  PEER: set
  * when a payload's body (from the first 256-byte boundary of its output) is
  * not empty and its source sits an odd or 2-mod-4 number of bytes past a
- * 16-byte granule there.  REDUCE: set with ROG_PLAN_NT_LOADS, for every
- * source.  Affects speed only; the bytes are the same. */
+ * 16-byte granule there.  REDUCE: set with ROG_PLAN_NT_LOADS when W >= 3,
+ * for every source.  Affects speed only; the bytes are the same. */
 #define ROG_PLAN_SHIFTED_LOADS 2u
 
 /*

@@ -110,22 +110,16 @@ def test_grid_sizes(count, dtype):
     assert s["grid"] == 1 and s["block"] == min(1024, max(64, -(-(-(-count * es // 16)) // 64) * 64))
 
 
-def test_nt_loads_follow_sources_and_source_bytes():
-    # from 4 sources on, loads stream past the caches from 128 MiB of sources
-    for W in (4, 8, 64):
-        n = (128 << 20) // (2 * W)
+def test_nt_loads_and_granule_form_follow_source_bytes_and_W():
+    # loads stream past the caches from 128 MiB of sources, whatever W; the
+    # granule form comes with them from 3 sources on
+    for W in (1, 2, 3, 4, 8, 64):
+        n = -(-(128 << 20) // (2 * W))
         srcs = [A + i * (1 << 30) for i in range(W)]
-        assert rog.rog_reduce_plan_ptrs(srcs, n, BF16, 1 << 45)["nt_loads"], W
-        assert not rog.rog_reduce_plan_ptrs(srcs, n - 8, BF16, 1 << 45)["nt_loads"], W
-    # with 3 sources from 384 MiB
-    n = (128 << 20) // 2
-    srcs = [A + i * (1 << 30) for i in range(3)]
-    assert rog.rog_reduce_plan_ptrs(srcs, n, BF16, 1 << 45)["nt_loads"]
-    assert not rog.rog_reduce_plan_ptrs(srcs, n - 8, BF16, 1 << 45)["nt_loads"]
-    # with 1 or 2 never
-    for W in (1, 2):
-        srcs = [A + i * (1 << 33) for i in range(W)]
-        assert not rog.rog_reduce_plan_ptrs(srcs, (4 << 30) // 2, BF16, 1 << 45)["nt_loads"], W
+        p = rog.rog_reduce_plan_ptrs(srcs, n, BF16, 1 << 45)
+        assert p["nt_loads"] and p["shifted_loads"] is (W >= 3), W
+        p = rog.rog_reduce_plan_ptrs(srcs, n - 64, BF16, 1 << 45)
+        assert not p["nt_loads"] and not p["shifted_loads"], W
 
 
 def test_binding_errors_map_to_exceptions():

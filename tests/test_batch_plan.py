@@ -22,12 +22,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 MAXB = 32
 
 
-def sum_streams(W, source_bytes):
-    """The header's rule for a sum's streamed loads: from 4 sources on at
-    128 MiB of sources, with 3 at 384 MiB, with 1 or 2 never."""
-    if W >= 4:
-        return source_bytes >= 128 << 20
-    return W == 3 and source_bytes >= 384 << 20
+def sum_forms(W, source_bytes):
+    """The header's rule for a sum: streamed loads from 128 MiB of sources,
+    and then shared granules from 3 sources on.  (nt, granule form)"""
+    nt = source_bytes >= 128 << 20
+    return nt, nt and W >= 3
 
 
 @pytest.fixture(scope="module")
@@ -157,8 +156,8 @@ def test_reduce_batch_layout(shim, data, n, W, dtype):
         nxt += p["n_chunks"]
     assert meta[0] == nxt and meta[1] == nxt
     source_bytes = sum(W * cnt * es for _, _, cnt in tensors)
-    nt = sum_streams(W, source_bytes)
-    assert meta[2] == int(nt) and meta[3] == int(nt)   # the granule form exactly with streamed loads
+    nt, granule = sum_forms(W, source_bytes)
+    assert meta[2] == int(nt) and meta[3] == int(granule)
 
 
 def _lookup(shim, tensors, W, chunks):

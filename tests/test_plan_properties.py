@@ -18,12 +18,11 @@ SINGLE_MAX = rog.rog_single_wg_max_bytes()
 RSINGLE_MAX = rog.rog_reduce_single_wg_max_bytes()
 
 
-def sum_streams(W, source_bytes):
-    """The header's rule for a sum's streamed loads: from 4 sources on at
-    128 MiB of sources, with 3 at 384 MiB, with 1 or 2 never."""
-    if W >= 4:
-        return source_bytes >= 128 << 20
-    return W == 3 and source_bytes >= 384 << 20
+def sum_forms(W, source_bytes):
+    """The header's rule for a sum: streamed loads from 128 MiB of sources,
+    and then shared granules from 3 sources on.  (nt, granule form)"""
+    nt = source_bytes >= 128 << 20
+    return nt, nt and W >= 3
 
 
 def overlap(a, na, b, nb):
@@ -187,9 +186,9 @@ def test_reduce_plan_matches_the_rules(W, n, dt, path, data):
         assert info.block == 64 and info.grid == min(max(1, -(-(nb // 16) // 64)), 0xFFFFFFFF // 64)
     else:
         assert info.grid == 1 and info.block == min(1024, max(64, -(-(-(-nb // 16)) // 64) * 64))
-    nt = sum_streams(W, W * nb)
+    nt, granule = sum_forms(W, W * nb)
     assert bool(info.flags & rog.ROG_PLAN_NT_LOADS) == nt
-    assert bool(info.flags & rog.ROG_PLAN_SHIFTED_LOADS) == (resolved == 2 and nt)
+    assert bool(info.flags & rog.ROG_PLAN_SHIFTED_LOADS) == (resolved == 2 and granule)
 
 
 def test_shared_granule_examples():

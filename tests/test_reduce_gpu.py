@@ -270,26 +270,26 @@ def test_streamed_sums_over_several_source_groups(gpu, W, n, dtype):
     gc.run_reduce_all_paths(placed, "streamed W=%d %s" % (W, dtype), paths=(rog.ROG_PATH_AUTO,))
 
 
-@pytest.mark.parametrize("W,n,offs,nt", [
-    (4, 16 << 20, (1, 0), True), (4, (16 << 20) - 8, (1, 0), False),
-    (3, 64 << 20, (0, 1), True), (3, (64 << 20) - 8, (0, 1), False),
-    (2, 96 << 20, (1, 0), False)],
-    ids=["4x32MiB", "4x32MiB-16B", "3x128MiB", "3x128MiB-16B", "2x192MiB"])
-def test_sums_around_the_streaming_bounds(gpu, W, n, offs, nt):
-    """A sum streams its loads (and reads shared granules) from 128 MiB of
-    sources with 4 or more sources, from 384 MiB with 3, never with 2: on both
-    sides of each bound, at element offsets, every element against the
+@pytest.mark.parametrize("W,n,offs,nt,granule", [
+    (4, 16 << 20, (1, 0), True, True), (4, (16 << 20) - 8, (1, 0), False, False),
+    (3, 22_369_622, (0, 1), True, True), (2, 32 << 20, (1, 0), True, False),
+    (2, (32 << 20) - 8, (1, 0), False, False), (2, 96 << 20, (0, 1), True, False)],
+    ids=["4x32MiB", "4x32MiB-16B", "3x128MiB+4B", "2x64MiB", "2x64MiB-16B", "2x192MiB"])
+def test_sums_around_the_streaming_bound(gpu, W, n, offs, nt, granule):
+    """A sum streams its loads from 128 MiB of sources, and then reads shared
+    granules from 3 sources on (with 2, the plain form with streamed loads):
+    on both sides of the bound, at element offsets, every element against the
     oracle."""
     payloads = wl.reduce_payloads(640 + W, W, n, "bf16")
     in_off, out_off = offs
     placed = gc.PlacedReduce(payloads, [in_off] * W, out_off, "bf16", gpu)
     plan = rog.rog_reduce_plan(placed.srcs, placed.out)
-    assert plan["path"] == "multi_wg" and plan["nt_loads"] is nt and plan["shifted_loads"] is nt
+    assert plan["path"] == "multi_wg" and plan["nt_loads"] is nt and plan["shifted_loads"] is granule
     gc.run_reduce_all_paths(placed, "sum W=%d n=%d" % (W, n), paths=(rog.ROG_PATH_AUTO,))
 
 
 def test_streamed_batch_of_sums_from_128_MiB(gpu):
-    """A batch of sums with 4 sources streams from 128 MiB of sources: 16
+    """A batch of sums streams from 128 MiB of sources, as a single sum does: 16
     tensors of 1.5 Mi bf16 elements (192 MiB of sources) at element offsets,
     every element against the oracle."""
     counts = [3 << 19] * 16
