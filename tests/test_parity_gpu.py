@@ -424,7 +424,7 @@ def test_streamed_payloads_each_misaligned_differently(gpu, streamed_payloads):
 
 
 def test_streamed_batch_with_small_misaligned_tensors(gpu):
-    """A batch whose sources total 384 MiB or more streams its loads, so its
+    """A batch whose sources total 128 MiB or more streams its loads, so its
     misaligned tensors take the shuffled PEER body, down to tensors of a few
     bytes and bodies shorter than one wave: one 100 MiB tensor (W = 4) beside
     small and empty tensors at odd offsets."""

@@ -236,10 +236,10 @@ def test_streamed_sum_in_place(gpu, which, offs):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_streamed_batch_with_small_tensors(gpu, dtype):
-    """A batch of sums over 384 MiB or more of sources takes the granule form
-    for every tensor, down to single elements, bodies shorter than one wave and
-    empty tensors: one 100 MiB-per-source tensor (W = 4) beside small ones at
-    element offsets."""
+    """A batch of sums over 128 MiB or more of sources (W >= 3) takes the
+    granule form for every tensor, down to single elements, bodies shorter
+    than one wave and empty tensors: one 100 MiB-per-source tensor (W = 4)
+    beside small ones at element offsets."""
     big = (100 << 20) // wl.REDUCE_ESIZE[dtype]
     counts = [big, 0, 1, 7, 127, 129, 520, 2049, 33_333, 0, 262_147]
     offs = [[(t + r) % 5 for r in range(4)] for t in range(len(counts))]
