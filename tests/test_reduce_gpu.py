@@ -295,3 +295,12 @@ def test_streamed_batch_of_sums_from_128_MiB(gpu):
     counts = [3 << 19] * 16
     offs = [[(t + r) % 3 for r in range(4)] for t in range(16)]
     _batch(47, 4, counts, "bf16", offs).run("batch of sums, 192 MiB of sources")
+
+
+def test_streamed_batch_of_sums_with_two_sources(gpu):
+    """With 2 sources a streamed batch of sums keeps the plain form: 16 tensors
+    of 4 Mi bf16 elements (256 MiB of sources) at element offsets, every
+    element against the oracle."""
+    counts = [4 << 20] * 16
+    offs = [[(t + r) % 3 for r in range(2)] for t in range(16)]
+    _batch(48, 2, counts, "bf16", offs).run("batch of sums, W = 2, 256 MiB of sources")
