@@ -45,9 +45,6 @@ constexpr int kMaxBatchPtrs = 192;
 #ifndef ROG_SUM_NT_LOAD_MIN_BYTES
 #define ROG_SUM_NT_LOAD_MIN_BYTES (128ull << 20)
 #endif
-#ifndef ROG_SUM_GRANULE_MIN_W
-#define ROG_SUM_GRANULE_MIN_W 3
-#endif
 #ifndef ROG_BODY_ALIGN
 #define ROG_BODY_ALIGN 256
 #endif
@@ -108,16 +105,20 @@ inline int single_flat_unroll(uint64_t n_vec) { return n_vec <= uint64_t(kSingle
 // while over buffers it still holds they measured 80-83 % against 89-91 %
 // cached; at 64 MiB of output cached loads keep 85 % warm (77 % streamed) and
 // lose 2 points cold (75 % against 77 %).  Sums (single or batched) switch at
-// 128 MiB of sources too, and then read shared granules only from 3 sources
-// on: against cached loads, over W = 2 to 8 and 128 to 512 MiB of sources,
-// streamed loads lifted the slower of warm and cold or tied it (1-8 % with
-// the plain form at W = 2, up to 22 % with the granule form from W = 3 on).
-// Against the plain form the granule form lost 6-15 % at W = 2; from W = 3 on
-// it won every case with sources off the output's alignment and lost at most
-// 7 % on aligned ones.
+// 128 MiB of sources too, where they then read shared granules
+// (sum_granule_group): over W = 2 to 16 and 128 to 512 MiB of sources,
+// streamed loads lifted the slower of warm and cold against cached loads or
+// tied it.
 constexpr uint64_t kGatherNtLoadMinBytes = ROG_GATHER_NT_LOAD_MIN_BYTES;
 constexpr uint64_t kSumNtLoadMinBytes = ROG_SUM_NT_LOAD_MIN_BYTES;
-constexpr uint32_t kSumGranuleMinW = ROG_SUM_GRANULE_MIN_W;
+
+// Sources whose granules a lane of the sum's granule form holds in flight at
+// once, by W.  The registers scale with it: 8 sources take 87 VGPRs (5 waves
+// per SIMD), 4 take 54 and 2 take 37 (8 waves each).  Measured over W = 2 to
+// 16 and 256 to 512 MiB of sources: 2 for W <= 2 (24-30 % faster than 8),
+// 4 for W = 3 (9-13 % faster than 8), 8 from W = 4 on (the best group, or
+// within 2.5 % of it).
+inline uint32_t sum_granule_group(uint32_t W) { return W <= 2 ? 2 : W == 3 ? 4 : 8; }
 constexpr uint32_t kGridCap = ROG_GRID_CAP;       // workgroups of one launch, at most
 // Destination alignment at which a PEER payload's 16-byte body starts (a power
 // of two >= 16): each wave's 1 KiB of stores then covers whole cache lines.

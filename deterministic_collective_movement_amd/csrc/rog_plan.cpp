@@ -293,10 +293,8 @@ rog_status plan_reduce(const void *const *srcs, int W, size_t count, rog_dtype d
         info.block = kWaveBlock;
         info.grid = std::min(a.n_chunks, max_grid(kWaveBlock));
         a.grid = info.grid;
-        // The granule form where loads stream past the caches, from
-        // kSumGranuleMinW sources on (kReduceShift).
-        if (kReduceShift == 2 ||
-            (kReduceShift == 1 && (info.flags & ROG_PLAN_NT_LOADS) && uint32_t(W) >= kSumGranuleMinW))
+        // The granule form where loads stream past the caches (kReduceShift).
+        if (kReduceShift == 2 || (kReduceShift == 1 && (info.flags & ROG_PLAN_NT_LOADS)))
             info.flags |= ROG_PLAN_SHIFTED_LOADS;
     }
     return ROG_OK;
@@ -349,7 +347,7 @@ rog_status plan_reduce_batch(const rog_reduce_desc *descs, int n, int W, rog_dty
     *grid = uint32_t(std::min<uint64_t>(next, max_grid(kWaveBlock)));
     args->grid = *grid;
     *nt_loads = source_bytes >= kSumNtLoadMinBytes;
-    *shifted = kReduceShift == 2 || (kReduceShift == 1 && *nt_loads && uint32_t(W) >= kSumGranuleMinW);
+    *shifted = kReduceShift == 2 || (kReduceShift == 1 && *nt_loads);
     return ROG_OK;
 }
 

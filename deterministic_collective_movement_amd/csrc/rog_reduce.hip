@@ -133,25 +133,26 @@ __device__ __forceinline__ vec16 sum_vec(const void *const *src, uint32_t W, uin
 
 // sum_vec for a whole wave of a multi-WG chunk, reading every source as
 // aligned 16-byte granules shared between neighbouring lanes (the PEER
-// gather's scheme): every lane calls it, since the shuffle needs all 64.
+// gather's scheme): every lane calls it, since the shuffle needs all 64.  G
+// sources' granules are in flight at once (sum_granule_group).
 // `live` lanes own a body vector at byte offset off; `own_hi` lanes (lane 63
 // and the body's last lane) load the granule after their own themselves, as
 // a cached load.  body is the body's first byte offset: source r's bytes sit
 // m_r = (src_r + body) % 16 bytes past a granule in every lane.
-template <int DT, bool NTL>
+template <int DT, bool NTL, uint32_t G>
 __device__ __forceinline__ vec16 sum_vec_wave(const void *const *src, uint32_t W, uint64_t off, uint64_t body,
                                               bool live, bool own_hi, bool next_in_body) {
     constexpr int E = Elem<DT>::kPerVec;
     float acc[E];
-    for (uint32_t r0 = 0; r0 < W; r0 += kGroup) {
-        const uint32_t g = min(W - r0, kGroup);
-        vec16 v[kGroup], h[kGroup];
-        uint32_t m[kGroup];
+    for (uint32_t r0 = 0; r0 < W; r0 += G) {
+        const uint32_t g = min(W - r0, G);
+        vec16 v[G], h[G];
+        uint32_t m[G];
         // The few cached loads of the granules after the wave's last go out
         // before the group's streamed loads: issued after them, they waited
         // behind them and the sum ran 3-6% slower.
 #pragma unroll
-        for (uint32_t q = 0; q < kGroup; ++q) {
+        for (uint32_t q = 0; q < G; ++q) {
             v[q] = h[q] = vec16{0, 0, 0, 0};
             m[q] = 0;
             if (q < g) {
@@ -163,14 +164,14 @@ __device__ __forceinline__ vec16 sum_vec_wave(const void *const *src, uint32_t W
             }
         }
 #pragma unroll
-        for (uint32_t q = 0; q < kGroup; ++q) {
+        for (uint32_t q = 0; q < G; ++q) {
             if (q < g && live) {
                 const uint8_t *s = static_cast<const uint8_t *>(src[r0 + q]);
                 v[q] = ld16<NTL>(reinterpret_cast<const vec16 *>(s + off - m[q]));
             }
         }
 #pragma unroll
-        for (uint32_t q = 0; q < kGroup; ++q) {
+        for (uint32_t q = 0; q < G; ++q) {
             if (q < g) {
                 const vec16 next = from_next_lane(v[q]);
                 float x[E];
@@ -214,7 +215,7 @@ __device__ __forceinline__ void sum_elem(const void *const *src, uint32_t W, uin
 // source 0 is read in whole 128-byte lines (split_anchored); else one
 // unaligned load per lane and source, the body cut at out's first 256-byte
 // boundary (split_payload).
-template <int DT, bool NTL, bool SH>
+template <int DT, bool NTL, bool SH, uint32_t G>
 __device__ __forceinline__ void sum_chunk(const void *const *src, uint32_t W, void *out, uint64_t count,
                                           uint32_t j) {
     const uint32_t lane = __lane_id();
@@ -231,7 +232,7 @@ __device__ __forceinline__ void sum_chunk(const void *const *src, uint32_t W, vo
     const bool live = off < cut.hi;
     if constexpr (SH) {
         const bool own_hi = live && (lane == 63 || off + 16 >= cut.hi);
-        const vec16 v = sum_vec_wave<DT, NTL>(src, W, off, cut.lo, live, own_hi, off + 16 < cut.hi);
+        const vec16 v = sum_vec_wave<DT, NTL, G>(src, W, off, cut.lo, live, own_hi, off + 16 < cut.hi);
         if (live) w.st16(16 * lane, v);
     } else if (live) {
         w.st16(16 * lane, sum_vec<DT, NTL>(src, W, off));
@@ -242,7 +243,7 @@ __device__ __forceinline__ void sum_chunk(const void *const *src, uint32_t W, vo
 // handed to the XCDs in runs (a chunk's last granule is its neighbour's
 // first; without runs the granule form measured 8 % slower), grid-strided
 // over a capped grid.
-template <int DT, bool NTL, bool SH>
+template <int DT, bool NTL, bool SH, uint32_t G>
 __global__ __launch_bounds__(kWaveBlock) void rog_reduce_kernel(ReduceArgs) {
     // Every argument the first chunk needs, the first eight source pointers
     // included, in one batch of scalar loads with one wait.
@@ -253,12 +254,12 @@ __global__ __launch_bounds__(kWaveBlock) void rog_reduce_kernel(ReduceArgs) {
     void *const out = a.out;
     hold_scalars(src, n_chunks, W, uint32_t(count), uint32_t(count >> 32), grid, out);
     for (uint32_t vb = blockIdx.x; vb < n_chunks; vb += grid)
-        sum_chunk<DT, NTL, SH>(a.src, W, out, count, ROG_REDUCE_XCD ? xcd_grouped(vb, n_chunks) : vb);
+        sum_chunk<DT, NTL, SH, G>(a.src, W, out, count, ROG_REDUCE_XCD ? xcd_grouped(vb, n_chunks) : vb);
 }
 
 // Batch: the tensors' chunks laid end to end; a wave finds its tensor by a
 // scalar binary search over the tensors' first chunks.
-template <int DT, bool NTL, bool SH>
+template <int DT, bool NTL, bool SH, uint32_t G>
 __global__ __launch_bounds__(kWaveBlock) void rog_reduce_batch_kernel(ReduceBatchArgs) {
     const ReduceBatchArgs &a = launch_args<ReduceBatchArgs>();
     const uint32_t n_chunks = a.n_chunks, W = a.W, grid = a.grid;
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(kWaveBlock) void rog_reduce_batch_kernel(ReduceBatc
         const uint32_t c = ROG_REDUCE_XCD ? xcd_grouped(vb, n_chunks) : vb;
         const uint32_t lo = search_tensor(a.first, a.n, c);
         const ReduceTensor &t = a.t[lo];
-        sum_chunk<DT, NTL, SH>(a.src + lo * W, W, reinterpret_cast<void *>(t.out), t.count, c - a.first[lo]);
+        sum_chunk<DT, NTL, SH, G>(a.src + lo * W, W, reinterpret_cast<void *>(t.out), t.count, c - a.first[lo]);
     }
 }
 
@@ -292,10 +293,13 @@ template <typename K>
 const void *kfn(K *k) { return reinterpret_cast<const void *>(k); }
 
 template <int DT>
-const void *reduce_kernel(bool single, bool ntl, bool sh) {
+const void *reduce_kernel(bool single, bool ntl, bool sh, uint32_t g) {
     if (single) return ntl ? kfn(&rog_reduce_single_kernel<DT, true>) : kfn(&rog_reduce_single_kernel<DT, false>);
-    if (sh) return ntl ? kfn(&rog_reduce_kernel<DT, true, true>) : kfn(&rog_reduce_kernel<DT, false, true>);
-    return ntl ? kfn(&rog_reduce_kernel<DT, true, false>) : kfn(&rog_reduce_kernel<DT, false, false>);
+    if (sh && ntl)
+        return g == 2 ? kfn(&rog_reduce_kernel<DT, true, true, 2>)
+             : g == 4 ? kfn(&rog_reduce_kernel<DT, true, true, 4>) : kfn(&rog_reduce_kernel<DT, true, true, 8>);
+    if (sh) return kfn(&rog_reduce_kernel<DT, false, true, kGroup>);
+    return ntl ? kfn(&rog_reduce_kernel<DT, true, false, kGroup>) : kfn(&rog_reduce_kernel<DT, false, false, kGroup>);
 }
 
 rog_status launch_reduce(Plan &p, hipStream_t stream) {
@@ -304,9 +308,10 @@ rog_status launch_reduce(Plan &p, hipStream_t stream) {
     const bool single = i.path == ROG_PATH_SINGLE_WG;
     const bool ntl = (i.flags & ROG_PLAN_NT_LOADS) != 0;
     const bool sh = (i.flags & ROG_PLAN_SHIFTED_LOADS) != 0;
-    const void *k = p.dtype == ROG_DTYPE_BF16  ? reduce_kernel<ROG_DTYPE_BF16>(single, ntl, sh)
-                    : p.dtype == ROG_DTYPE_F16 ? reduce_kernel<ROG_DTYPE_F16>(single, ntl, sh)
-                                               : reduce_kernel<ROG_DTYPE_F32>(single, ntl, sh);
+    const uint32_t g = sum_granule_group(p.reduce.W);
+    const void *k = p.dtype == ROG_DTYPE_BF16  ? reduce_kernel<ROG_DTYPE_BF16>(single, ntl, sh, g)
+                    : p.dtype == ROG_DTYPE_F16 ? reduce_kernel<ROG_DTYPE_F16>(single, ntl, sh, g)
+                                               : reduce_kernel<ROG_DTYPE_F32>(single, ntl, sh, g);
     void *params[] = {&p.reduce};
     const hipError_t e = hipLaunchKernel(k, dim3(i.grid), dim3(i.block), params, 0, stream);
     if (e != hipSuccess) {
@@ -317,9 +322,12 @@ rog_status launch_reduce(Plan &p, hipStream_t stream) {
 }
 
 template <int DT>
-const void *reduce_batch_kernel(bool ntl, bool sh) {
-    if (sh) return ntl ? kfn(&rog_reduce_batch_kernel<DT, true, true>) : kfn(&rog_reduce_batch_kernel<DT, false, true>);
-    return ntl ? kfn(&rog_reduce_batch_kernel<DT, true, false>) : kfn(&rog_reduce_batch_kernel<DT, false, false>);
+const void *reduce_batch_kernel(bool ntl, bool sh, uint32_t g) {
+    if (sh && ntl)
+        return g == 2 ? kfn(&rog_reduce_batch_kernel<DT, true, true, 2>)
+             : g == 4 ? kfn(&rog_reduce_batch_kernel<DT, true, true, 4>) : kfn(&rog_reduce_batch_kernel<DT, true, true, 8>);
+    if (sh) return kfn(&rog_reduce_batch_kernel<DT, false, true, kGroup>);
+    return ntl ? kfn(&rog_reduce_batch_kernel<DT, true, false, kGroup>) : kfn(&rog_reduce_batch_kernel<DT, false, false, kGroup>);
 }
 
 }  // namespace
@@ -361,9 +369,10 @@ ROG_API rog_status rog_reduce_many(const rog_reduce_desc *descs, int n, int W, r
     bool ntl = false, sh = false;
     const rog_status st = rog::plan_reduce_batch(descs, n, W, dtype, &args, &grid, &ntl, &sh);
     if (st != ROG_OK || grid == 0) return st;
-    const void *k = dtype == ROG_DTYPE_BF16  ? rog::reduce_batch_kernel<ROG_DTYPE_BF16>(ntl, sh)
-                    : dtype == ROG_DTYPE_F16 ? rog::reduce_batch_kernel<ROG_DTYPE_F16>(ntl, sh)
-                                             : rog::reduce_batch_kernel<ROG_DTYPE_F32>(ntl, sh);
+    const uint32_t g = rog::sum_granule_group(uint32_t(W));
+    const void *k = dtype == ROG_DTYPE_BF16  ? rog::reduce_batch_kernel<ROG_DTYPE_BF16>(ntl, sh, g)
+                    : dtype == ROG_DTYPE_F16 ? rog::reduce_batch_kernel<ROG_DTYPE_F16>(ntl, sh, g)
+                                             : rog::reduce_batch_kernel<ROG_DTYPE_F32>(ntl, sh, g);
     void *params[] = {&args};
     const hipError_t e = hipLaunchKernel(k, dim3(grid), dim3(rog::kWaveBlock), params, 0, stream);
     if (e != hipSuccess) {

@@ -123,8 +123,8 @@ typedef struct {
  * after its own from the next lane.  Only with ROG_PLAN_NT_LOADS.  PEER: set
  * when a payload's body (from the first 256-byte boundary of its output) is
  * not empty and its source sits an odd or 2-mod-4 number of bytes past a
- * 16-byte granule there.  REDUCE: set with ROG_PLAN_NT_LOADS when W >= 3,
- * for every source.  Affects speed only; the bytes are the same. */
+ * 16-byte granule there.  REDUCE: set with ROG_PLAN_NT_LOADS, for every
+ * source.  Affects speed only; the bytes are the same. */
 #define ROG_PLAN_SHIFTED_LOADS 2u
 
 /*

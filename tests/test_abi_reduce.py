@@ -110,14 +110,14 @@ def test_grid_sizes(count, dtype):
     assert s["grid"] == 1 and s["block"] == min(1024, max(64, -(-(-(-count * es // 16)) // 64) * 64))
 
 
-def test_nt_loads_and_granule_form_follow_source_bytes_and_W():
-    # loads stream past the caches from 128 MiB of sources, whatever W; the
-    # granule form comes with them from 3 sources on
+def test_nt_loads_and_granule_form_follow_source_bytes():
+    # loads stream past the caches from 128 MiB of sources, whatever W, and
+    # the granule form comes with them
     for W in (1, 2, 3, 4, 8, 64):
         n = -(-(128 << 20) // (2 * W))
         srcs = [A + i * (1 << 30) for i in range(W)]
         p = rog.rog_reduce_plan_ptrs(srcs, n, BF16, 1 << 45)
-        assert p["nt_loads"] and p["shifted_loads"] is (W >= 3), W
+        assert p["nt_loads"] and p["shifted_loads"], W
         p = rog.rog_reduce_plan_ptrs(srcs, n - 64, BF16, 1 << 45)
         assert not p["nt_loads"] and not p["shifted_loads"], W
 

@@ -24,9 +24,9 @@ MAXB = 32
 
 def sum_forms(W, source_bytes):
     """The header's rule for a sum: streamed loads from 128 MiB of sources,
-    and then shared granules from 3 sources on.  (nt, granule form)"""
+    and then shared granules.  (nt, granule form)"""
     nt = source_bytes >= 128 << 20
-    return nt, nt and W >= 3
+    return nt, nt
 
 
 @pytest.fixture(scope="module")

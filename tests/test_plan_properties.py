@@ -20,9 +20,9 @@ RSINGLE_MAX = rog.rog_reduce_single_wg_max_bytes()
 
 def sum_forms(W, source_bytes):
     """The header's rule for a sum: streamed loads from 128 MiB of sources,
-    and then shared granules from 3 sources on.  (nt, granule form)"""
+    and then shared granules.  (nt, granule form)"""
     nt = source_bytes >= 128 << 20
-    return nt, nt and W >= 3
+    return nt, nt
 
 
 def overlap(a, na, b, nb):

@@ -236,7 +236,7 @@ def test_streamed_sum_in_place(gpu, which, offs):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_streamed_batch_with_small_tensors(gpu, dtype):
-    """A batch of sums over 128 MiB or more of sources (W >= 3) takes the
+    """A batch of sums over 128 MiB or more of sources takes the
     granule form for every tensor, down to single elements, bodies shorter
     than one wave and empty tensors: one 100 MiB-per-source tensor (W = 4)
     beside small ones at element offsets."""
@@ -272,14 +272,13 @@ def test_streamed_sums_over_several_source_groups(gpu, W, n, dtype):
 
 @pytest.mark.parametrize("W,n,offs,nt,granule", [
     (4, 16 << 20, (1, 0), True, True), (4, (16 << 20) - 8, (1, 0), False, False),
-    (3, 22_369_622, (0, 1), True, True), (2, 32 << 20, (1, 0), True, False),
-    (2, (32 << 20) - 8, (1, 0), False, False), (2, 96 << 20, (0, 1), True, False)],
+    (3, 22_369_622, (0, 1), True, True), (2, 32 << 20, (1, 0), True, True),
+    (2, (32 << 20) - 8, (1, 0), False, False), (2, 96 << 20, (0, 1), True, True)],
     ids=["4x32MiB", "4x32MiB-16B", "3x128MiB+4B", "2x64MiB", "2x64MiB-16B", "2x192MiB"])
 def test_sums_around_the_streaming_bound(gpu, W, n, offs, nt, granule):
-    """A sum streams its loads from 128 MiB of sources, and then reads shared
-    granules from 3 sources on (with 2, the plain form with streamed loads):
-    on both sides of the bound, at element offsets, every element against the
-    oracle."""
+    """A sum streams its loads from 128 MiB of sources and then reads shared
+    granules, two, four or eight sources at a time by W: on both sides of the
+    bound, at element offsets, every element against the oracle."""
     payloads = wl.reduce_payloads(640 + W, W, n, "bf16")
     in_off, out_off = offs
     placed = gc.PlacedReduce(payloads, [in_off] * W, out_off, "bf16", gpu)
@@ -298,9 +297,9 @@ def test_streamed_batch_of_sums_from_128_MiB(gpu):
 
 
 def test_streamed_batch_of_sums_with_two_sources(gpu):
-    """With 2 sources a streamed batch of sums keeps the plain form: 16 tensors
-    of 4 Mi bf16 elements (256 MiB of sources) at element offsets, every
-    element against the oracle."""
+    """A streamed batch of sums with 2 sources (granules two sources at a
+    time): 16 tensors of 4 Mi bf16 elements (256 MiB of sources) at element
+    offsets, every element against the oracle."""
     counts = [4 << 20] * 16
     offs = [[(t + r) % 3 for r in range(2)] for t in range(16)]
     _batch(48, 2, counts, "bf16", offs).run("batch of sums, W = 2, 256 MiB of sources")
