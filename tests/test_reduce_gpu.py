@@ -303,3 +303,18 @@ def test_streamed_batch_of_sums_with_two_sources(gpu):
     counts = [4 << 20] * 16
     offs = [[(t + r) % 3 for r in range(2)] for t in range(16)]
     _batch(48, 2, counts, "bf16", offs).run("batch of sums, W = 2, 256 MiB of sources")
+
+
+@pytest.mark.parametrize("W", [2, 3])
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_streamed_small_W_sums_in_every_element_type(gpu, dtype, W):
+    """The granule form with two and four sources' granules in flight (W = 2
+    and 3) in binary16 and binary32, just past 128 MiB of sources, sources at
+    their own element offsets: every element against the oracle."""
+    es = wl.REDUCE_ESIZE[dtype]
+    n = (128 << 20) // (W * es) + 17
+    payloads = wl.reduce_payloads(660 + W, W, n, dtype, "bits" if dtype == "f16" else "uniform")
+    placed = gc.PlacedReduce(payloads, [(r * 3 + 1) % 5 for r in range(W)], 2, dtype, gpu)
+    plan = rog.rog_reduce_plan(placed.srcs, placed.out)
+    assert plan["path"] == "multi_wg" and plan["nt_loads"] and plan["shifted_loads"]
+    gc.run_reduce_all_paths(placed, "streamed W=%d %s" % (W, dtype), paths=(rog.ROG_PATH_AUTO,))
