@@ -581,6 +581,70 @@ def reduce_bandwidth(torch, rog, wl, device, steps, warmup):
     return big, payloads, got
 
 
+REDUCE_SWEEP_CASES = ((2, 0), (2, 1), (3, 0), (3, 1), (8, 0), (8, 1))   # (W, source element offset)
+REDUCE_SWEEP_SOURCE_MIB = 512
+
+
+def reduce_sweep(torch, rog, device, calls, footprint=SWEEP_FOOTPRINT):
+    """Rank-ordered bf16 sums over 512 MiB of sources at W = 2, 3 and 8, the
+    sources aligned with the output or one element off it, timed warm (the
+    same buffers every call) and cold (rotating sets spanning ``footprint``
+    bytes) over the same number of back-to-back launches, as the gather
+    sweep is.  Each row records the launch's form (streamed loads, shared
+    granules).  Sampled outputs are compared with a float32 sum in rank
+    order, rounded once to bf16 (torch on the device), in every set."""
+    lib = rog.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    g = torch.Generator(device=device)
+    g.manual_seed(20261)
+    rows = []
+    for W, off in REDUCE_SWEEP_CASES:
+        n = ((REDUCE_SWEEP_SOURCE_MIB << 20) // (2 * W)) // 64 * 64
+        K = max(1, footprint // ((W + 1) * n * 2))
+        sets = []
+        for _ in range(K):
+            bufs = [torch.randn(n + off, device=device, generator=g).to(torch.bfloat16) for _ in range(W)]
+            srcs = [b[off:] for b in bufs]
+            out = torch.empty(n, dtype=torch.bfloat16, device=device)
+            sets.append((srcs, out, (ctypes.c_void_p * W)(*[x.data_ptr() for x in srcs]),
+                         ctypes.c_void_p(out.data_ptr()), bufs))
+        plan = rog.rog_reduce_plan(sets[0][0], sets[0][1])
+
+        def run(seq):
+            for _, _, ptrs, o, _ in (seq * 2)[:max(K + 1, 10)]:
+                if lib.rog_reduce(ptrs, W, n, rog.ROG_DTYPE_BF16, o, stream) != 0:
+                    raise RuntimeError("rog_reduce failed")
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _, _, ptrs, o, _ in seq:
+                lib.rog_reduce(ptrs, W, n, rog.ROG_DTYPE_BF16, o, stream)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / len(seq)
+
+        n_calls = max(calls, 2 * K)
+        warm_ms = run([sets[0]] * n_calls)
+        cold_ms = run([sets[i % K] for i in range(n_calls)])
+        for srcs, out, _, _, _ in sets:
+            for lo in (0, n // 2, n - 4096):
+                acc = srcs[0][lo:lo + 4096].float()
+                for r in range(1, W):
+                    acc = acc + srcs[r][lo:lo + 4096].float()
+                if not torch.equal(out[lo:lo + 4096].view(torch.int16), acc.to(torch.bfloat16).view(torch.int16)):
+                    raise AssertionError("sweep sum W=%d offset %d wrong at element %d" % (W, off, lo))
+        moved = (W + 1) * n * 2
+        rows.append({"W": W, "source_MiB": W * n * 2 >> 20, "src_elem_offset": off, "sets": K, "calls": n_calls,
+                     "nt_loads": plan["nt_loads"], "granules": plan["shifted_loads"],
+                     "warm_GBps": round(gbps(moved, warm_ms), 1),
+                     "warm_pct_of_peak": round(100 * gbps(moved, warm_ms) / PEAK_HBM_GBPS, 1),
+                     "cold_GBps": round(gbps(moved, cold_ms), 1),
+                     "cold_pct_of_peak": round(100 * gbps(moved, cold_ms) / PEAK_HBM_GBPS, 1)})
+        del sets
+        torch.cuda.empty_cache()
+    return rows
+
+
 def reduce_misaligned(torch, rog, srcs, aligned_out, stream, steps, warmup, in_off=1, out_off=0):
     """The same sum with every source at element offset ``in_off`` of its own
     buffer and the output at element offset ``out_off``: 2-byte source shifts,
@@ -907,6 +971,7 @@ def main(argv=None):
                                                         graph=True)
         big, rpayloads, rgot = reduce_bandwidth(torch, rog, wl, device, args.steps, args.warmup)
         extras["reduce"] = {"bandwidth": big,
+                            "sweep": reduce_sweep(torch, rog, device, SWEEP_CALLS),
                             "latency": reduce_latency(torch, rog, wl, device),
                             "batched": reduce_batch(torch, rog, wl, device, BATCH_STEPS,
                                                     max(BATCH_WARMUP, args.warmup))}
