@@ -396,31 +396,35 @@ SWEEP_MID_OUT_MIB = (2, 8, 32)
 SWEEP_FOOTPRINT = 2 << 30      # bytes of rotating buffer sets per cold case (8 x the 256 MB cache)
 
 
-def bandwidth_sweep(torch, rog, device, calls, out_mib=SWEEP_OUT_MIB, footprint=SWEEP_FOOTPRINT, graph=False):
-    """Aligned gathers with outputs of ``out_mib`` (64 - 512 MiB by default,
-    the "outputs >= 64 MiB" of the headline target) at W = 2 and 8, timed two
-    ways over the same number of back-to-back launches (``calls``, or two
-    passes over the sets if that is more): warm, the same buffers every call
-    (as the pages time a call), and cold, rotating through K buffer sets that
-    together span ``footprint`` bytes, so that no call finds its sources in the
-    256 MB Infinity Cache.  With ``graph`` the launches are captured into a HIP
-    graph and the replay is timed, which takes the host's launch path (about
-    3.5 µs a call from Python, more than a small gather's kernel) out of the
-    interval.  Sampled bytes of every set are checked against its sources."""
+def bandwidth_sweep(torch, rog, device, calls, out_mib=SWEEP_OUT_MIB, footprint=SWEEP_FOOTPRINT, graph=False,
+                    ws=(2, 8), offsets=(0, 0)):
+    """Gathers with outputs of ``out_mib`` (64 - 512 MiB by default, the
+    "outputs >= 64 MiB" of the headline target) at each W of ``ws``, aligned
+    or with every source and the output at the byte ``offsets`` (source,
+    output) of their buffers, timed two ways over the same number of
+    back-to-back launches (``calls``, or two passes over the sets if that is
+    more): warm, the same buffers every call (as the pages time a call), and
+    cold, rotating through K buffer sets that together span ``footprint``
+    bytes, so that no call finds its sources in the 256 MB Infinity Cache.
+    With ``graph`` the launches are captured into a HIP graph and the replay is
+    timed, which takes the host's launch path (about 3.5 µs a call from Python,
+    more than a small gather's kernel) out of the interval.  Sampled bytes of
+    every set are checked against its sources."""
+    src_off, out_off = offsets
     lib = rog.lib()
     stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
     g = torch.Generator(device=device)
     g.manual_seed(20260)
     rows = []
-    for W in (2, 8):
+    for W in ws:
         for mib in out_mib:
             S = (mib << 20) // W
             K = max(1, footprint // (2 * W * S))
             sets = []
             for _ in range(K):
-                srcs = [torch.randint(0, 256, (S,), dtype=torch.uint8, device=device, generator=g)
-                        for _ in range(W)]
-                out = torch.empty(W * S, dtype=torch.uint8, device=device)
+                srcs = [torch.randint(0, 256, (S + src_off,), dtype=torch.uint8, device=device,
+                                      generator=g)[src_off:] for _ in range(W)]
+                out = torch.empty(W * S + out_off, dtype=torch.uint8, device=device)[out_off:]
                 sets.append((srcs, out, (ctypes.c_void_p * W)(*[x.data_ptr() for x in srcs]),
                              ctypes.c_void_p(out.data_ptr())))
 
@@ -462,7 +466,8 @@ def bandwidth_sweep(torch, rog, device, calls, out_mib=SWEEP_OUT_MIB, footprint=
                         if not torch.equal(out[r * S + lo: r * S + lo + 1024], srcs[r][lo:lo + 1024]):
                             raise AssertionError("sweep gather W=%d S=%d wrong at rank %d" % (W, S, r))
             moved = 2 * W * S
-            rows.append({"W": W, "out_MiB": mib, "sets": K, "calls": n_calls,
+            kernel = rog.rog_plan(sets[0][0], sets[0][1])["kernel"]
+            rows.append({"W": W, "out_MiB": mib, "offsets": list(offsets), "kernel": kernel, "sets": K, "calls": n_calls,
                          "timed": "graph replay" if graph else "eager launches",
                          "warm_GBps": round(gbps(moved, warm_ms), 1),
                          "warm_pct_of_peak": round(100 * gbps(moved, warm_ms) / PEAK_HBM_GBPS, 1),
@@ -966,6 +971,9 @@ def main(argv=None):
                                             max(BATCH_WARMUP, args.warmup))
         extras["d2d_copy_ceiling"] = d2d_ceiling(torch, device, case.W * case.S, 20, 3)
         extras["bandwidth_sweep"] = bandwidth_sweep(torch, rog, device, SWEEP_CALLS)
+        # the same at byte offsets 1 (sources) and 3 (output): the PEER kernel
+        extras["bandwidth_sweep_misaligned"] = bandwidth_sweep(torch, rog, device, SWEEP_CALLS, ws=(8,),
+                                                               offsets=(1, 3))
         # the size sweep's 1 and 4 MiB payloads (outputs of 2 - 32 MiB), warm and cold
         extras["bandwidth_sweep_mid"] = bandwidth_sweep(torch, rog, device, 50, out_mib=SWEEP_MID_OUT_MIB,
                                                         graph=True)
