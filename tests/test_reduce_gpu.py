@@ -318,3 +318,16 @@ def test_streamed_small_W_sums_in_every_element_type(gpu, dtype, W):
     plan = rog.rog_reduce_plan(placed.srcs, placed.out)
     assert plan["path"] == "multi_wg" and plan["nt_loads"] and plan["shifted_loads"]
     gc.run_reduce_all_paths(placed, "streamed W=%d %s" % (W, dtype), paths=(rog.ROG_PATH_AUTO,))
+
+
+@pytest.mark.parametrize("W", [1, 5, 6, 7])
+def test_streamed_sums_with_partly_filled_groups(gpu, W):
+    """Streamed bf16 sums whose sources fill their group of granules only in
+    part (W = 1 of 2; W = 5, 6 and 7 of 8), just past 128 MiB of sources, at
+    element offsets: every element against the oracle."""
+    n = (128 << 20) // (W * 2) + 33
+    payloads = wl.reduce_payloads(680 + W, W, n, "bf16")
+    placed = gc.PlacedReduce(payloads, [(r * 2 + 1) % 7 for r in range(W)], 1, "bf16", gpu)
+    plan = rog.rog_reduce_plan(placed.srcs, placed.out)
+    assert plan["path"] == "multi_wg" and plan["nt_loads"] and plan["shifted_loads"]
+    gc.run_reduce_all_paths(placed, "streamed W=%d bf16" % W, paths=(rog.ROG_PATH_AUTO,))
