@@ -14,14 +14,15 @@
 // vectors, an element tail.  The body starts at out's first 256-byte boundary
 // (split_payload), or, in the granule form, where source 0 is read in whole
 // 128-byte lines (split_anchored).  A body lane loads the 16 bytes at the same
-// offset of every source, with up to 8 loads in flight, accumulates them in
-// rank order and stores one aligned 16-byte vector.  Where the loads stay cached, each source takes one
-// global_load_dwordx4 per lane at its own alignment; where they stream past
-// the caches (ROG_PLAN_NT_LOADS, then ROG_PLAN_SHIFTED_LOADS), the launch
-// takes the granule form, which reads every source as aligned granules, each
-// lane rebuilding its bytes from its own granule and the next lane's, as the
-// PEER gather does (measured faster there at every alignment, and slower with
-// cached loads).  Multi-WG: one wave per 1 KiB chunk of the body,
+// offset of every source, accumulates them in rank order and stores one
+// aligned 16-byte vector.  Where the loads stay cached, each source takes one
+// global_load_dwordx4 per lane at its own alignment, up to 8 sources' loads in
+// flight; where they stream past the caches (ROG_PLAN_NT_LOADS, then
+// ROG_PLAN_SHIFTED_LOADS), the launch takes the granule form, which reads every
+// source as aligned granules, each lane rebuilding its bytes from its own
+// granule and the next lane's, as the PEER gather does (measured faster there
+// at every alignment, and mostly slower with cached loads), with 2, 4 or 8
+// sources' granules in flight by W (sum_granule_group).  Multi-WG: one wave per 1 KiB chunk of the body,
 // chunks handed to the XCDs in runs (xcd_grouped); single-WG: one workgroup
 // strides over the whole output; batch (rog_reduce_many): every tensor's
 // chunks in one launch.  Bandwidth bound: (W + 1) * count * esize bytes per
