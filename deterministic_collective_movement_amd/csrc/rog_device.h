@@ -17,6 +17,17 @@ __device__ __forceinline__ vec16 ld16(const vec16 *p) {
     else return *p;
 }
 
+// A 16-byte vector in the global address space: loads through such a pointer
+// are global_load (a scalar base plus lane offsets where the base is
+// wave-uniform), where a generic pointer rebuilt from scalar registers would
+// give flat_load with a 64-bit address per lane.
+typedef const __attribute__((address_space(1))) vec16 gvec16;
+template <bool NT>
+__device__ __forceinline__ vec16 ld16(gvec16 *p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
 // The 16 bytes at p, any byte alignment.
 template <bool NT>
 __device__ __forceinline__ vec16 ldu16(const uint8_t *p) {

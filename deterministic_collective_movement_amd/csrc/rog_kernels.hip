@@ -70,7 +70,7 @@ __device__ __forceinline__ void flat_chunk(const Src &src, vec16 *o, uint32_t n_
     const OutWindow<kStoreAux> w(o + b, n * 16);    // the chunk's output
     if (e <= seg_lo + vpr) {
         // The whole chunk lies in payload r: scalar bases, lane offsets.
-        const vec16 *s = static_cast<const vec16 *>(src_of(src, r)) + (b - seg_lo);
+        gvec16 *s = (gvec16 *)src_of(src, r) + (b - seg_lo);
         if (n == kChunk) {
             vec16 v[U];
 #pragma unroll
@@ -94,7 +94,7 @@ __device__ __forceinline__ void flat_chunk(const Src &src, vec16 *o, uint32_t n_
             const uint32_t k = b + u * 64 + lane;
             if (k < e) {
                 const uint32_t rk = divide(k, div);
-                const vec16 *s = static_cast<const vec16 *>(lane_src(src, rk));
+                gvec16 *s = (gvec16 *)lane_src(src, rk);
                 w.st16(16 * (k - b), ld16<NTL>(s + (k - rk * vpr)));
             }
         }
@@ -280,7 +280,10 @@ __global__ __launch_bounds__(kWaveBlock) void rog_batch_kernel(BatchArgs) {
             flat_chunk<kFlatUnroll, NTL>(src, reinterpret_cast<vec16 *>(t.out), t.n_vec, t.vpr, t.div, t.shift, lc);
         } else {
             const uint32_t r = divide(lc, t.div);
-            peer_chunk<NTL>(static_cast<const uint8_t *>(src[r]), reinterpret_cast<uint8_t *>(t.out) + uint64_t(r) * t.S,
+            // the output address through a global pointer, so that the head
+            // and tail byte stores are global stores rather than flat ones
+            uint8_t *const d = (uint8_t *)(__attribute__((address_space(1))) uint8_t *)t.out;
+            peer_chunk<NTL>(static_cast<const uint8_t *>(src[r]), d + uint64_t(r) * t.S,
                             t.S, lc - r * t.chunks_per_peer);
         }
     }

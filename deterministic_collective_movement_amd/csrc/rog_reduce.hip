@@ -269,7 +269,9 @@ __global__ __launch_bounds__(kWaveBlock) void rog_reduce_batch_kernel(ReduceBatc
         const uint32_t c = ROG_REDUCE_XCD ? xcd_grouped(vb, n_chunks) : vb;
         const uint32_t lo = search_tensor(a.first, a.n, c);
         const ReduceTensor &t = a.t[lo];
-        sum_chunk<DT, NTL, SH, G>(a.src + lo * W, W, reinterpret_cast<void *>(t.out), t.count, c - a.first[lo]);
+        // the output address through a global pointer: global head and tail stores
+        void *const out = (void *)(__attribute__((address_space(1))) uint8_t *)t.out;
+        sum_chunk<DT, NTL, SH, G>(a.src + lo * W, W, out, t.count, c - a.first[lo]);
     }
 }
 
