@@ -203,7 +203,7 @@ def test_batch_lookup_finds_every_chunks_tensor(shim, data, n, W):
         chunks = list(range(total))
     else:
         chunks = []
-        for k, p in enumerate(planned):
+        for p in planned:
             lo, hi = p["first"], p["first"] + p["n_chunks"]
             chunks += [lo, hi - 1, (lo + hi) // 2]
             chunks += [data.draw(st.integers(lo, hi - 1)) for _ in range(3)]
@@ -235,7 +235,7 @@ def test_reduce_batch_lookup_finds_every_chunks_tensor(shim, data, n, W):
         cnt = data.draw(st.one_of(st.just(0), st.integers(1, 20_000), st.sampled_from([1 << 16, 1 << 22, 1 << 27])))
         base = BASE + t * (1 << 34)
         tensors.append(([base + r * (1 << 30) for r in range(W)], base + (W + 1) * (1 << 30), cnt))
-    status, planned, meta = plan_reduce_batch(shim, tensors, W, 0)
+    status, planned, _ = plan_reduce_batch(shim, tensors, W, 0)
     assert status == 0
     if not planned:
         return
