@@ -343,6 +343,47 @@ def test_largest_vector_index(gpu):
     torch.cuda.empty_cache()
 
 
+def test_largest_misaligned_gather(gpu):
+    """PEER at the top of the size range: W = 8 payloads of 8 GiB - 21 bytes
+    (W*S = 2^36 - 168) with the sources at byte offset 1 and the output at 3,
+    so streamed loads and the lane shuffle.  Checked through properties that
+    hold at any size: sampled windows at both ends and in the middle of every
+    segment equal their source bytes, and the filled stretches between them
+    carry the per-rank value."""
+    W = 8
+    S = (1 << 33) - 21
+    total = W * S
+    free, _ = torch.cuda.mem_get_info(gpu)
+    if free < 2 * total + (8 << 30):
+        pytest.skip("needs %d GiB of free device memory" % ((2 * total >> 30) + 8))
+    bufs, srcs = [], []
+    for r in range(W):
+        t = torch.empty(S + 1, dtype=torch.uint8, device=gpu)
+        t.fill_(r * 31 + 5)
+        bufs.append(t)
+        srcs.append(t[1:])
+    rng = np.random.default_rng(98)
+    win = 4096
+    windows = [0, S - win, S // 2 + 7]
+    for r in range(W):
+        for lo in windows:
+            srcs[r][lo:lo + win].copy_(torch.from_numpy(np.frombuffer(rng.bytes(win), np.uint8).copy()))
+    obuf = torch.empty(total + 3, dtype=torch.uint8, device=gpu)
+    out = obuf[3:]
+    plan = rog.rog_plan(srcs, out)
+    assert plan["kernel"] == "peer" and plan["path"] == "multi_wg" and plan["nt_loads"] and plan["shifted_loads"]
+    print("largest misaligned gather W=8 S=%d" % S, flush=True)
+    rog.rog_gather(srcs, out)
+    torch.cuda.synchronize()
+    for r in range(W):
+        for lo in windows:
+            assert torch.equal(out[r * S + lo: r * S + lo + win].cpu(), srcs[r][lo:lo + win].cpu()), (r, lo)
+        mid = out[r * S + win: r * S + win + (1 << 20)].cpu()
+        assert torch.all(mid == r * 31 + 5), r
+    del out, obuf, srcs, bufs
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("W", [1, 3])
 def test_every_source_and_destination_misalignment(gpu, W):
     """The per-peer path's head / aligned body / tail cut for every pair of

@@ -331,3 +331,45 @@ def test_streamed_sums_with_partly_filled_groups(gpu, W):
     plan = rog.rog_reduce_plan(placed.srcs, placed.out)
     assert plan["path"] == "multi_wg" and plan["nt_loads"] and plan["shifted_loads"]
     gc.run_reduce_all_paths(placed, "streamed W=%d bf16" % W, paths=(rog.ROG_PATH_AUTO,))
+
+
+def test_largest_sum(gpu):
+    """A sum at the top of the size range: W = 2 bf16 sources of 2^35 - 64
+    elements (an output of 2^36 - 128 bytes), the sources one element off the
+    output, so streamed loads and the granule form.  Checked through
+    properties that hold at any size: sampled windows at both ends and in the
+    middle equal a float32 sum in rank order rounded once to bf16, and the
+    filled stretches between them hold the exact sum of the fill values."""
+    W = 2
+    n = (1 << 35) - 64
+    free, _ = torch.cuda.mem_get_info(gpu)
+    need = (W + 1) * 2 * n
+    if free < need + (8 << 30):
+        pytest.skip("needs %d GiB of free device memory" % ((need >> 30) + 8))
+    fills = (1.5, 0.25)                      # 1.75: exact in bf16
+    bufs, srcs = [], []
+    for r in range(W):
+        t = torch.empty(n + 1, dtype=torch.bfloat16, device=gpu)
+        t.fill_(fills[r])
+        bufs.append(t)
+        srcs.append(t[1:])
+    g = torch.Generator(device=gpu)
+    g.manual_seed(97)
+    win = 8192
+    windows = [0, n - win, n // 2 + 5]
+    for r in range(W):
+        for lo in windows:
+            srcs[r][lo:lo + win].copy_(torch.randn(win, device=gpu, generator=g).to(torch.bfloat16))
+    out = torch.empty(n, dtype=torch.bfloat16, device=gpu)
+    plan = rog.rog_reduce_plan(srcs, out)
+    assert plan["path"] == "multi_wg" and plan["nt_loads"] and plan["shifted_loads"]
+    print("largest sum W=2 n=%d" % n, flush=True)
+    rog.rog_reduce(srcs, out)
+    torch.cuda.synchronize()
+    for lo in windows:
+        want = (srcs[0][lo:lo + win].float() + srcs[1][lo:lo + win].float()).to(torch.bfloat16)
+        assert torch.equal(out[lo:lo + win].view(torch.int16).cpu(), want.view(torch.int16).cpu()), lo
+    mid = out[win: win + (1 << 20)].float().cpu()
+    assert torch.all(mid == 1.75)
+    del out, srcs, bufs
+    torch.cuda.empty_cache()
