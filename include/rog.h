@@ -114,9 +114,9 @@ typedef struct {
 /* rog_plan_info.flags: the kernel's 16-byte loads are non-temporal (streamed
  * past the caches); set when the W*S source bytes are too many for the 256 MB
  * Infinity Cache to serve repeated calls well: from 128 MiB, for gathers and
- * sums, single or batched.  16-byte stores are always
- * non-temporal; a gather's are also written through the L2 caches at device
- * scope.  Affects speed only. */
+ * sums, single or batched.  16-byte stores are always non-temporal; a
+ * gather's are also written through the L2 caches at device scope.  Affects
+ * speed only. */
 #define ROG_PLAN_NT_LOADS 1u
 /* rog_plan_info.flags: the multi-workgroup PEER or REDUCE kernel reads at least
  * one source body as aligned 16-byte granules, each lane taking the granule
