@@ -18,9 +18,9 @@ __device__ __forceinline__ vec16 ld16(const vec16 *p) {
 }
 
 // A 16-byte vector in the global address space: loads through such a pointer
-// are global_load (a scalar base plus lane offsets where the base is
-// wave-uniform), where a generic pointer rebuilt from scalar registers would
-// give flat_load with a 64-bit address per lane.
+// are global_load instructions, where a generic pointer rebuilt from scalar
+// registers would give flat_load (which also waits on the LDS counter and
+// checks the address's aperture).
 typedef const __attribute__((address_space(1))) vec16 gvec16;
 template <bool NT>
 __device__ __forceinline__ vec16 ld16(gvec16 *p) {
