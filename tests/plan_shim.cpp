@@ -85,3 +85,6 @@ extern "C" int rog_test_reduce_batch_lookup(const rog_reduce_desc *descs, int n,
     for (uint32_t i = 0; i < n_query; ++i) tensor[i] = rog::search_tensor(a.first, a.n, chunks[i]);
     return 0;
 }
+
+// The sum's granule group by W (sources whose granules a lane keeps in flight).
+extern "C" uint32_t rog_test_sum_granule_group(uint32_t W) { return rog::sum_granule_group(W); }

@@ -254,3 +254,12 @@ def test_reduce_batch_lookup_finds_every_chunks_tensor(shim, data, n, W):
     got = (ctypes.c_uint32 * len(chunks))()
     assert shim.rog_test_reduce_batch_lookup(descs, len(tensors), W, 0, q, len(chunks), got) == 0
     assert list(got) == [_owner(first, c) for c in chunks]
+
+
+def test_sum_granule_group_by_W(shim):
+    """The granule form keeps 2 sources' granules in flight for W <= 2, 4 for
+    W = 3 and 8 from W = 4 on (the measured rule)."""
+    shim.rog_test_sum_granule_group.restype = ctypes.c_uint32
+    shim.rog_test_sum_granule_group.argtypes = [ctypes.c_uint32]
+    got = [shim.rog_test_sum_granule_group(W) for W in range(1, 65)]
+    assert got == [2, 2, 4] + [8] * 61
