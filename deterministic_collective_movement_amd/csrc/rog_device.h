@@ -28,10 +28,6 @@ __device__ __forceinline__ vec16 ld16(gvec16 *p) {
     else return *p;
 }
 
-// Keeps a load whose value nothing else uses (a touch that warms a cache
-// line): the compiler may not drop it, and waits for it here.
-__device__ __forceinline__ void keep_loaded(vec16 v) { asm volatile("" ::"v"(v.x)); }
-
 // The 16 bytes at p, any byte alignment.
 template <bool NT>
 __device__ __forceinline__ vec16 ldu16(const uint8_t *p) {

@@ -60,9 +60,6 @@ constexpr int kMaxBatchPtrs = 192;
 #ifndef ROG_GRID_CAP
 #define ROG_GRID_CAP (1u << 30)
 #endif
-#ifndef ROG_TOUCH_AHEAD
-#define ROG_TOUCH_AHEAD 65536
-#endif
 
 // Output bytes up to which ROG_PATH_AUTO uses the single-workgroup path
 // (inclusive), measured by sweeping both forced paths.
@@ -134,26 +131,6 @@ static_assert(kBodyAlign >= 16 && (kBodyAlign & (kBodyAlign - 1)) == 0, "body al
 // its neighbour, which then sits in the same L2).
 constexpr uint32_t kXcds = 8;
 constexpr uint32_t kXcdRun = ROG_XCD_RUN;
-// Touches ahead of streamed loads.  Where a multi-WG gather's loads stream, two
-// lanes of each wave also read one 16-byte granule each, cached, from two lines
-// (the first and the middle one) of the chunk kTouchAhead vectors further on in
-// the same payload; that chunk's own streamed loads then find those lines in
-// L2.  HBM reads stay the same (512.1 MiB against 512.0 per 8 x 64 MiB
-// gather), yet aligned gathers run 4-6 % faster warm and 2-6 % faster cold
-// (8 x 16 to 64 MiB and 2 x 256 MiB), on XCD runs 5 % and batched 4 %;
-// misaligned (PEER) ones 4-5 % warm and cold, in either load form.  One
-// line per chunk gains 2-3 %; four gain warm but lose cold; eight lose both.
-// Touching the very next chunk loses 3-4 %, and touching on every eighth
-// chunk only gains nothing.  Distances of 16384 to 524288 vectors measured
-// alike wherever the touched chunk goes to the toucher's XCD (32768 and 65536
-// within 2 %, the farther one ahead warm and behind cold); 32768 on XCD runs
-// touches another XCD's chunk and loses 6.5 %.  65536 vectors is 1024 chunks:
-// whole round-robin cycles (8) and whole XCD-run spans (8 * kXcdRun), so the
-// touched chunk shares the toucher's L2 under both mappings.  Sums take no
-// touches: one per source (4 bytes, to spare registers) gained 5-7 % warm at
-// W = 8 but lost 1-6 % cold, and lost at W = 4; 16-byte ones lost a third.
-constexpr uint32_t kTouchAhead = ROG_TOUCH_AHEAD;
-static_assert(kTouchAhead % (64 * kXcds * kXcdRun) == 0, "touched chunks share the toucher's XCD");
 // Multi-WG PEER body loads, where the loads stream past the caches, at a
 // source misaligned by m = 1..15 bytes from its 16-byte granule: 0 = one
 // unaligned 16-byte load per lane; 1 = for m not a multiple of 4, one aligned

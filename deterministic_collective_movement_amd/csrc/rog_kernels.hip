@@ -55,8 +55,7 @@ namespace rog {
 // ---------------------------------------------------------------------------
 template <int U, bool NTL, typename Src>
 __device__ __forceinline__ void flat_chunk(const Src &src, vec16 *o, uint32_t n_vec,
-                                           uint32_t vpr, const Divider &div, uint32_t shift, uint32_t c,
-                                           uint32_t ahead) {
+                                           uint32_t vpr, const Divider &div, uint32_t shift, uint32_t c) {
     constexpr uint32_t kChunk = 64 * U;
     const uint32_t lane = __lane_id();
     // b < e = b + n <= n_vec < 2^32, and b + kChunk - 1 <= 2^32 - 1 (shift is
@@ -76,16 +75,8 @@ __device__ __forceinline__ void flat_chunk(const Src &src, vec16 *o, uint32_t n_
             vec16 v[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) v[u] = ld16<NTL>(s + u * 64 + lane);
-            // Streamed loads: lanes 62 and 63 touch the first and the middle
-            // granule of the chunk `ahead` vectors on, if payload r holds it.
-            vec16 t = vec16{0, 0, 0, 0};
-            if constexpr (NTL) {
-                const uint32_t tk = ahead + (lane & 1) * (kChunk / 2);
-                if (ahead != 0 && lane >= 62 && uint64_t(b) + tk < uint64_t(seg_lo) + vpr) t = ld16<false>(s + tk);
-            }
 #pragma unroll
             for (int u = 0; u < U; ++u) w.st16(16 * (u * 64 + lane), v[u]);
-            if constexpr (NTL) keep_loaded(t);
         } else {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -117,7 +108,7 @@ __device__ __forceinline__ void flat_copy(const FlatArgs &a, uint32_t waves) {
     const uint32_t wave = uniform(threadIdx.x / 64);
     const uint32_t n_chunks = flat_chunk_count(a.n_vec, kChunk, a.shift);
     for (uint32_t c = wave; c < n_chunks; c += waves)
-        flat_chunk<U, NTL>(a.src, static_cast<vec16 *>(a.out), a.n_vec, a.vpr, a.div, a.shift, c, 0);
+        flat_chunk<U, NTL>(a.src, static_cast<vec16 *>(a.out), a.n_vec, a.vpr, a.div, a.shift, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -153,20 +144,8 @@ __device__ __forceinline__ void peer_chunk(const uint8_t *s, uint8_t *d, uint64_
     const uint64_t off = w0 + 16 * lane;
     const bool live = off < cut.hi;
     const uint32_t m = uniform(uint32_t(reinterpret_cast<uintptr_t>(s + cut.lo)) & 15);
-    // Streamed loads: lanes 62 and 63 touch the granules holding the first and
-    // the middle byte of body chunk j + kTouchAhead / 64, where the body
-    // reaches them (then the touching lane is live too).
-    const uint64_t to = w0 + uint64_t(kTouchAhead) * 16 + (lane & 1) * 512;
-    const bool touch = NTL && lane >= 62 && to < cut.hi;
-    const vec16 *const tp = reinterpret_cast<const vec16 *>(reinterpret_cast<uintptr_t>(s + to) & ~uintptr_t(15));
-    vec16 t = vec16{0, 0, 0, 0};
     if (!NTL || !shift_granules(m, kPeerShift)) {
-        if (live) {
-            const vec16 x = ldu16<NTL>(s + off);
-            if (touch) t = ld16<false>(tp);
-            w.st16(16 * lane, x);
-        }
-        if constexpr (NTL) keep_loaded(t);
+        if (live) w.st16(16 * lane, ldu16<NTL>(s + off));
         return;
     }
     const vec16 *g = reinterpret_cast<const vec16 *>(s + off - m);
@@ -176,11 +155,9 @@ __device__ __forceinline__ void peer_chunk(const uint8_t *s, uint8_t *d, uint64_
     vec16 lo = vec16{0, 0, 0, 0}, hi = lo;
     if (live) lo = ld16<NTL>(g);
     if (own_hi) hi = ld16<false>(g + 1);  // cached; in flight beside lo
-    if (touch) t = ld16<false>(tp);
     // Lane l + 1's granule; all 64 lanes take part in the shuffle.
     const vec16 next = from_next_lane(lo);
     if (live) w.st16(16 * lane, cut16(lo, own_hi ? hi : next, m));
-    keep_loaded(t);
 }
 
 // One workgroup of nt threads, the whole payload: head and tail bytes, then the
@@ -237,8 +214,7 @@ __global__ __launch_bounds__(kWaveBlock) void rog_flat_kernel(FlatArgs) {
     hold_scalars(src, n_vec, vpr, shift, runs, grid, div, out);
     const uint32_t n_chunks = flat_chunk_count(n_vec, kChunk, shift);
     for (uint32_t vb = blockIdx.x; vb < n_chunks; vb += grid)
-        flat_chunk<kFlatUnroll, NTL>(src, out, n_vec, vpr, div, shift, runs ? xcd_grouped(vb, n_chunks) : vb,
-                                     kTouchAhead);
+        flat_chunk<kFlatUnroll, NTL>(src, out, n_vec, vpr, div, shift, runs ? xcd_grouped(vb, n_chunks) : vb);
 }
 
 // Single-WG FLAT: one workgroup of as many waves as there are chunks (<= 16),
@@ -301,8 +277,7 @@ __global__ __launch_bounds__(kWaveBlock) void rog_batch_kernel(BatchArgs) {
         hold_scalars(t.chunks_per_peer, uint32_t(t.S), uint32_t(t.S >> 32), 0u, 0u);
         const void *const *src = a.src + lo * W;
         if (t.flat) {
-            flat_chunk<kFlatUnroll, NTL>(src, reinterpret_cast<vec16 *>(t.out), t.n_vec, t.vpr, t.div, t.shift, lc,
-                                         kTouchAhead);
+            flat_chunk<kFlatUnroll, NTL>(src, reinterpret_cast<vec16 *>(t.out), t.n_vec, t.vpr, t.div, t.shift, lc);
         } else {
             const uint32_t r = divide(lc, t.div);
             // the output address through a global pointer, so that the head

@@ -478,38 +478,6 @@ def test_streamed_batch_with_small_misaligned_tensors(gpu):
     gc.PlacedBatch(W, payloads, in_offs, out_offs, gpu).run("streamed batch, small misaligned tensors")
 
 
-# Streamed multi-WG gathers (FLAT, PEER and batched) also touch the chunk 65536
-# vectors (1 MiB) ahead in the same payload.  64 payloads of 2 MiB + 33
-# vectors (131105; 131105 mod 64 = 33, so the chunks start at every residue
-# across the payloads) put those touches on each payload's last vectors, the
-# very last one included; 131080 vectors (2 MiB + 128 B) keep the payloads on
-# the line grid, where chunks go to the XCDs round-robin.
-@pytest.mark.parametrize("vpr,io,oo", [(131105, 0, 0), (131080, 0, 0), (131105, 1, 3), (131105, 4, 0)],
-                         ids=["flat_xcd_runs", "flat_round_robin", "peer_shared_granules", "peer_unaligned_loads"])
-def test_touches_ahead_reach_the_payload_ends(gpu, vpr, io, oo):
-    W = 64
-    S = vpr * 16 + (5 if io else 0)
-    rng = np.random.default_rng(vpr + io)
-    payloads = [np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(W)]
-    placed = gc.Placed(payloads, [io] * W, oo, gpu)
-    plan = rog.rog_plan(placed.srcs, placed.out)
-    assert plan["nt_loads"] and plan["path"] == "multi_wg"
-    assert plan["kernel"] == ("peer" if io else "flat")
-    gc.run_all_paths(placed, "touches at the payload ends, %d x %d at (%d, %d)" % (W, S, io, oo),
-                     paths=(rog.ROG_PATH_AUTO,))
-
-
-def test_batch_touches_ahead_reach_the_payload_ends(gpu):
-    """The batched form of the case above: two tensors of 32 payloads of
-    4 MiB + 33 vectors, one aligned (FLAT chunks on XCD runs), one at offsets
-    (1, 3) (PEER chunks), 256 MiB of sources."""
-    rng = np.random.default_rng(262177)
-    W = 32
-    sizes = [262177 * 16, 262177 * 16 + 5]
-    payloads = [[np.frombuffer(rng.bytes(S), np.uint8).copy() for _ in range(W)] for S in sizes]
-    gc.PlacedBatch(W, payloads, [0, 1], [0, 3], gpu).run("streamed batch, touches at the payload ends")
-
-
 def test_streamed_batch_from_128_MiB(gpu):
     """A batch streams its loads from 128 MiB of sources, as a single gather
     does: 8 tensors of 6 MiB + 5 per payload (W = 4, 192 MiB of sources), at
