@@ -23,7 +23,9 @@ ceiling and the HBM figure the HIP runtime reports; aligned gathers with
 2 - 512 MiB outputs, warm and with rotating buffer sets (cold); the
 rank-ordered sum (rog_reduce: W = 8 bf16 payloads of 64 MiB, aligned and one
 element off, the pages' per-rank sizes of 1 KiB - 4 MiB at W = 2 and 8, and a
-16-tensor rog_reduce_many); and the CPU oracle on bounded samples of the
+16-tensor rog_reduce_many); the headline gather and the W = 8 sum in four
+cache states (back to back on one set, over four rotating sets, and after a
+1 GiB read-only or read-write pass over other memory); and the CPU oracle on bounded samples of the
 headline gather and of the large sum (the CPU-baseline legs, the only ones
 that call the oracle).
 
@@ -650,6 +652,112 @@ def reduce_sweep(torch, rog, device, calls, footprint=SWEEP_FOOTPRINT):
     return rows
 
 
+CACHE_STATE_SETS = 4
+CACHE_STATE_CALLS = 20
+CACHE_STATE_PASS_BYTES = 1 << 30   # 4 x the 256 MB Infinity Cache
+
+
+def cache_states(torch, rog, device, calls=CACHE_STATE_CALLS):
+    """The headline gather (W = 8 x 64 MiB) and the rank-ordered sum of eight
+    aligned bf16 payloads of 64 MiB, each in four cache states: back to back
+    over one buffer set (as the headline is timed); back to back over four
+    rotating sets (4.5 GiB for the gather, 2.3 GiB for the sum: no set's
+    lines can still sit in the 256 MB Infinity Cache when it comes round
+    again); and each call after a 1 GiB pass over other memory, read-only
+    (the caches then hold clean lines of other data) or read-write (dirty
+    lines, which the call's own cache allocations must write back first).
+    The last two time each call alone, with events around it.  Every set's
+    output is checked (gather: whole; sum: sampled against a float32 sum in
+    rank order)."""
+    lib = rog.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    g = torch.Generator(device=device)
+    g.manual_seed(4044)
+    scratch = torch.zeros(CACHE_STATE_PASS_BYTES // 8, dtype=torch.int64, device=device)
+    sink = torch.empty(1, dtype=torch.int64, device=device)
+    passes = {"after_read_pass": lambda: torch.sum(scratch, dim=0, keepdim=True, out=sink),
+              "after_write_pass": lambda: scratch.add_(1)}
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def back_to_back(call, seq):
+        for x in (seq * 2)[:len(seq) + CACHE_STATE_SETS]:
+            call(x)
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for x in seq:
+            call(x)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / len(seq)
+
+    def after_pass(call, x, pass_fn):
+        call(x)
+        total = 0.0
+        for _ in range(calls):
+            pass_fn()
+            a, b = ev(), ev()
+            a.record()
+            call(x)
+            b.record()
+            torch.cuda.synchronize()
+            total += a.elapsed_time(b)
+        return total / calls
+
+    def states(op, call, sets, moved):
+        ms = {"back_to_back": back_to_back(call, [sets[0]] * calls),
+              "rotating_%d_sets" % len(sets): back_to_back(call, [sets[i % len(sets)] for i in range(calls)])}
+        for name, fn in passes.items():
+            ms[name] = after_pass(call, sets[0], fn)
+        base = gbps(moved, ms["back_to_back"])
+        return [{"op": op, "state": k, "GBps": round(gbps(moved, v), 1),
+                 "pct_of_peak": round(100 * gbps(moved, v) / PEAK_HBM_GBPS, 1),
+                 "vs_back_to_back": round(gbps(moved, v) / base, 3)} for k, v in ms.items()]
+
+    W, S = 8, 64 << 20
+    sets = []
+    for _ in range(CACHE_STATE_SETS):
+        srcs = [torch.randint(0, 256, (S,), dtype=torch.uint8, device=device, generator=g) for _ in range(W)]
+        out = torch.empty(W * S, dtype=torch.uint8, device=device)
+        sets.append((srcs, out, (ctypes.c_void_p * W)(*[x.data_ptr() for x in srcs]), ctypes.c_void_p(out.data_ptr())))
+
+    def gather(x):
+        if lib.rog_gather(x[2], W, ctypes.c_size_t(S), x[3], stream) != 0:
+            raise RuntimeError("rog_gather failed")
+
+    rows = states("gather", gather, sets, 2 * W * S)
+    for srcs, out, _, _ in sets:
+        if not torch.equal(out, torch.cat(srcs)):
+            raise AssertionError("cache-state gather wrong")
+    del sets
+    torch.cuda.empty_cache()
+
+    n = S // 2
+    sets = []
+    for _ in range(CACHE_STATE_SETS):
+        srcs = [torch.randn(n, device=device, generator=g).to(torch.bfloat16) for _ in range(W)]
+        out = torch.empty(n, dtype=torch.bfloat16, device=device)
+        sets.append((srcs, out, (ctypes.c_void_p * W)(*[x.data_ptr() for x in srcs]), ctypes.c_void_p(out.data_ptr())))
+
+    def reduce(x):
+        if lib.rog_reduce(x[2], W, ctypes.c_size_t(n), rog.ROG_DTYPE_BF16, x[3], stream) != 0:
+            raise RuntimeError("rog_reduce failed")
+
+    rows += states("sum", reduce, sets, (W + 1) * n * 2)
+    for srcs, out, _, _ in sets:
+        for lo in (0, n // 2, n - 4096):
+            acc = srcs[0][lo:lo + 4096].float()
+            for r in range(1, W):
+                acc = acc + srcs[r][lo:lo + 4096].float()
+            if not torch.equal(out[lo:lo + 4096].view(torch.int16), acc.to(torch.bfloat16).view(torch.int16)):
+                raise AssertionError("cache-state sum wrong at element %d" % lo)
+    del sets, scratch
+    torch.cuda.empty_cache()
+    return rows
+
+
 def reduce_misaligned(torch, rog, srcs, aligned_out, stream, steps, warmup, in_off=1, out_off=0):
     """The same sum with every source at element offset ``in_off`` of its own
     buffer and the output at element offset ``out_off``: 2-byte source shifts,
@@ -988,6 +1096,7 @@ def main(argv=None):
                             "latency": reduce_latency(torch, rog, wl, device),
                             "batched": reduce_batch(torch, rog, wl, device, BATCH_STEPS,
                                                     max(BATCH_WARMUP, args.warmup))}
+        extras["cache_states"] = cache_states(torch, rog, device)
         cpu = cpu_baseline(case, payloads, args.cpu_budget / 2)
         extras["reduce"]["cpu_baseline"] = reduce_cpu_baseline(rpayloads, rgot, min(2.5, args.cpu_budget / 4))
         del rpayloads, rgot
