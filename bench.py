@@ -1020,6 +1020,8 @@ def main(argv=None):
                     help="time only the warm and cold bandwidth sweeps (2 - 512 MiB outputs), for traces")
     ap.add_argument("--reduce-sweep-only", action="store_true",
                     help="time only the rank-ordered sums' warm and cold sweep (W = 2, 3, 8), for counter runs")
+    ap.add_argument("--cache-states-only", action="store_true",
+                    help="time only the headline gather and W = 8 sum in the four cache states, for traces")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: --gpus %d is not supported (use --gpus 1)" % args.gpus,
@@ -1042,6 +1044,9 @@ def main(argv=None):
         return 0
     if args.crossover:
         crossover(torch, rog, device, args.steps, args.warmup)
+        return 0
+    if args.cache_states_only:
+        print(json.dumps({"cache_states": cache_states(torch, rog, device)}), flush=True)
         return 0
     if args.reduce_sweep_only:
         print(json.dumps({"reduce_sweep": reduce_sweep(torch, rog, device, SWEEP_CALLS)}), flush=True)
