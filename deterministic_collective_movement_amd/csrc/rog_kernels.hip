@@ -29,9 +29,9 @@
 //    their bytes from their own granule and the next lane's (a lane shuffle
 //    and v_alignbyte), which streams faster than split unaligned loads.  The
 //    pages' fallback copies such payloads byte by byte (vectors only where
-//    both sides are aligned); the bytes written are the same.  Multi-WG, the body is cut into 1 KiB chunks,
-//    one wave per chunk, all payloads at once; single-WG, the one workgroup
-//    takes the payloads in turn.
+//    both sides are aligned); the bytes written are the same.  Multi-WG, the
+//    body is cut into 1 KiB chunks, one wave per chunk, all payloads at once;
+//    single-WG, the one workgroup takes the payloads in turn.
 //  * BATCH kernel (rog_gather_many): one launch; every wave finds its tensor
 //    through a bucket table of the chunk index (a scalar load of two bucket
 //    entries, then a search only between the tensors those name) and does one
