@@ -95,6 +95,23 @@ __device__ __forceinline__ vec16 narrow(const float (&a)[Elem<DT>::kPerVec]) {
     return v;
 }
 
+// Lane 63's cached load of an aligned source in the granule form (see
+// sum_vec_wave) goes to the next chunk's line whose 128-byte place alternates
+// by rank from this many sources on (0: never), else to the next chunk's
+// first granule.  Measured over W = 2 to 16: from W = 5 it gained up to 8 %
+// over buffers no cache holds; at W = 4 it gained 4 % there and lost 2-3 %
+// back to back, at W = 2 it lost 1-2 %.
+#ifndef ROG_SUM_TOUCH_SPREAD_MIN_W
+#define ROG_SUM_TOUCH_SPREAD_MIN_W 5
+#endif
+constexpr uint32_t kSumTouchSpreadMinW = ROG_SUM_TOUCH_SPREAD_MIN_W;
+// Waves per SIMD the multi-WG sum kernels are compiled for at least: the
+// 8-source granule form then keeps 5 (95 VGPRs; 98 and 4 waves otherwise,
+// which measured up to 10 % slower at W = 4 and 6).
+#ifndef ROG_SUM_WAVES_PER_EU
+#define ROG_SUM_WAVES_PER_EU 5
+#endif
+
 #ifndef ROG_REDUCE_GROUP
 #define ROG_REDUCE_GROUP 8
 #endif
@@ -137,36 +154,56 @@ __device__ __forceinline__ vec16 sum_vec(const void *const *src, uint32_t W, uin
 // gather's scheme): every lane calls it, since the shuffle needs all 64.  G
 // sources' granules are in flight at once (sum_granule_group).
 // `live` lanes own a body vector at byte offset off; `own_hi` lanes (lane 63
-// and the body's last lane) load the granule after their own themselves, as
-// a cached load.  body is the body's first byte offset: source r's bytes sit
-// m_r = (src_r + body) % 16 bytes past a granule in every lane.
+// and the body's last lane) make one cached load per source themselves: the
+// granule after their own where the source is misaligned, a granule of the
+// next chunk where it is aligned.  body and hi are the body's first and end
+// byte offsets: source r's bytes sit m_r = (src_r + body) % 16 bytes past a
+// granule in every lane.
 template <int DT, bool NTL, uint32_t G>
 __device__ __forceinline__ vec16 sum_vec_wave(const void *const *src, uint32_t W, uint64_t off, uint64_t body,
-                                              bool live, bool own_hi, bool next_in_body) {
+                                              uint64_t hi, bool live, bool own_hi) {
     constexpr int E = Elem<DT>::kPerVec;
     float acc[E];
     for (uint32_t r0 = 0; r0 < W; r0 += G) {
         const uint32_t g = min(W - r0, G);
         vec16 v[G], h[G];
         uint32_t m[G];
-        // The few cached loads of the granules after the wave's last go out
+        // The few cached loads of lane 63 (and the body's last lane) go out
         // before the group's streamed loads: issued after them, they waited
         // behind them and the sum ran 3-6% slower.  They are the sum's only
-        // loads that allocate in the Infinity Cache.  Against none at all on
-        // aligned sources (W = 2 to 8): back to back over the same buffers,
-        // where their lines are still there for the next call, 5-14 % faster;
-        // after other work has left dirty lines there, where each allocation
-        // first writes one back, 4-13 % slower; otherwise 2-5 % faster.
+        // loads that allocate in the Infinity Cache.  On aligned sources they
+        // read no byte of the sum, yet against none at all (W = 2 to 8) they
+        // measured 5-14 % faster back to back over the same buffers, where
+        // their lines are still there for the next call, 2-5 % faster over
+        // buffers no cache holds, and 4-13 % slower after other work has left
+        // dirty lines there (each allocation first writes one back).  Over
+        // buffers no cache holds, the gain needs the loaded lines on several
+        // 128-byte places of a 1 KiB block: when all W landed on one place,
+        // as the first granule of the next chunk does for sources on 2 MiB
+        // boundaries, the W = 8 sum ran 6.3 TB/s against 6.8-6.9 with the
+        // places alternating by rank.  So from W = kSumTouchSpreadMinW on, an
+        // aligned source's load goes to the next chunk's line that alternates
+        // the place by rank, whatever the sources' own places.
 #pragma unroll
         for (uint32_t q = 0; q < G; ++q) {
             v[q] = h[q] = vec16{0, 0, 0, 0};
             m[q] = 0;
             if (q < g) {
                 const uint8_t *s = static_cast<const uint8_t *>(src[r0 + q]);
-                m[q] = uniform(uint32_t(reinterpret_cast<uintptr_t>(s) + body) & 15);
+                const uint32_t a = uniform(uint32_t(reinterpret_cast<uintptr_t>(s) + body));
+                m[q] = a & 15;
                 const vec16 *gp = reinterpret_cast<const vec16 *>(s + off - m[q]);
-                // past the body's end only where that granule holds payload bytes
-                if (own_hi && (m[q] != 0 || next_in_body)) h[q] = ld16<false>(gp + 1);
+                // Misaligned: the granule after the lane's own holds payload
+                // bytes (line 0, read even past the body's end).  Aligned:
+                // line `line` of the next chunk, whose place in a 1 KiB block,
+                // (a >> 7) + line, is 4 * (r & 1); read inside the body only.
+                // One conditional load with a uniform offset: split into two
+                // branches, the loads waited for one another.
+                uint32_t line = 0;
+                if constexpr (G >= 8 && kSumTouchSpreadMinW != 0)   // smaller groups serve W < 5 only
+                    if (W >= kSumTouchSpreadMinW && m[q] == 0) line = (4u * ((r0 + q) & 1u) - (a >> 7)) & 7u;
+                if (own_hi && (m[q] != 0 || off + 32 + 128 * uint64_t(line) <= hi))
+                    h[q] = ld16<false>(gp + 1 + 8 * line);
             }
         }
 #pragma unroll
@@ -238,7 +275,7 @@ __device__ __forceinline__ void sum_chunk(const void *const *src, uint32_t W, vo
     const bool live = off < cut.hi;
     if constexpr (SH) {
         const bool own_hi = live && (lane == 63 || off + 16 >= cut.hi);
-        const vec16 v = sum_vec_wave<DT, NTL, G>(src, W, off, cut.lo, live, own_hi, off + 16 < cut.hi);
+        const vec16 v = sum_vec_wave<DT, NTL, G>(src, W, off, cut.lo, cut.hi, live, own_hi);
         if (live) w.st16(16 * lane, v);
     } else if (live) {
         w.st16(16 * lane, sum_vec<DT, NTL>(src, W, off));
@@ -250,7 +287,8 @@ __device__ __forceinline__ void sum_chunk(const void *const *src, uint32_t W, vo
 // first; without runs the granule form measured 8 % slower), grid-strided
 // over a capped grid.
 template <int DT, bool NTL, bool SH, uint32_t G>
-__global__ __launch_bounds__(kWaveBlock) void rog_reduce_kernel(ReduceArgs) {
+__global__ __launch_bounds__(kWaveBlock) __attribute__((amdgpu_waves_per_eu(ROG_SUM_WAVES_PER_EU)))
+void rog_reduce_kernel(ReduceArgs) {
     // Every argument the first chunk needs, the first eight source pointers
     // included, in one batch of scalar loads with one wait.
     const ReduceArgs &a = launch_args<ReduceArgs>();
@@ -266,7 +304,8 @@ __global__ __launch_bounds__(kWaveBlock) void rog_reduce_kernel(ReduceArgs) {
 // Batch: the tensors' chunks laid end to end; a wave finds its tensor by a
 // scalar binary search over the tensors' first chunks.
 template <int DT, bool NTL, bool SH, uint32_t G>
-__global__ __launch_bounds__(kWaveBlock) void rog_reduce_batch_kernel(ReduceBatchArgs) {
+__global__ __launch_bounds__(kWaveBlock) __attribute__((amdgpu_waves_per_eu(ROG_SUM_WAVES_PER_EU)))
+void rog_reduce_batch_kernel(ReduceBatchArgs) {
     const ReduceBatchArgs &a = launch_args<ReduceBatchArgs>();
     const uint32_t n_chunks = a.n_chunks, W = a.W, grid = a.grid;
     hold_scalars(n_chunks, a.n, W, grid, 0u);
