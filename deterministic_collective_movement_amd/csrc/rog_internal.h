@@ -113,7 +113,7 @@ constexpr uint64_t kGatherNtLoadMinBytes = ROG_GATHER_NT_LOAD_MIN_BYTES;
 constexpr uint64_t kSumNtLoadMinBytes = ROG_SUM_NT_LOAD_MIN_BYTES;
 
 // Sources whose granules a lane of the sum's granule form holds in flight at
-// once, by W.  The registers scale with it: 8 sources take 87 VGPRs (5 waves
+// once, by W.  The registers scale with it: 8 sources take 95 VGPRs (5 waves
 // per SIMD), 4 take 54 and 2 take 37 (8 waves each).  Measured over W = 2 to
 // 16 and 256 to 512 MiB of sources: 2 for W <= 2 (24-30 % faster than 8),
 // 4 for W = 3 (9-13 % faster than 8), 8 from W = 4 on (the best group, or
