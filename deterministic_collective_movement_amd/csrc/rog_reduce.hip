@@ -98,11 +98,13 @@ __device__ __forceinline__ vec16 narrow(const float (&a)[Elem<DT>::kPerVec]) {
 // Lane 63's cached load of an aligned source in the granule form (see
 // sum_vec_wave) goes to the next chunk's line whose 128-byte place alternates
 // by rank from this many sources on (0: never), else to the next chunk's
-// first granule.  Measured over W = 2 to 16: from W = 5 it gained up to 8 %
-// over buffers no cache holds; at W = 4 it gained 4 % there and lost 2-3 %
-// back to back, at W = 2 it lost 1-2 %.
+// first granule.  Measured over W = 2 to 16, sources on one line place and
+// buffers no cache holds: W = 5 to 16 gained 4-9 %, W = 4 3-4 % (0 to -3 %
+// back to back over two boxes); W = 2 lost 1-2 %.  Placements already spread
+// stayed within about 1 %.  W = 2 and 3 take the smaller granule groups,
+// which leave it out.
 #ifndef ROG_SUM_TOUCH_SPREAD_MIN_W
-#define ROG_SUM_TOUCH_SPREAD_MIN_W 5
+#define ROG_SUM_TOUCH_SPREAD_MIN_W 4
 #endif
 constexpr uint32_t kSumTouchSpreadMinW = ROG_SUM_TOUCH_SPREAD_MIN_W;
 // Waves per SIMD the multi-WG sum kernels are compiled for at least: the
@@ -200,7 +202,7 @@ __device__ __forceinline__ vec16 sum_vec_wave(const void *const *src, uint32_t W
                 // One conditional load with a uniform offset: split into two
                 // branches, the loads waited for one another.
                 uint32_t line = 0;
-                if constexpr (G >= 8 && kSumTouchSpreadMinW != 0)   // smaller groups serve W < 5 only
+                if constexpr (G >= 8 && kSumTouchSpreadMinW != 0)   // smaller groups serve W < 4 only
                     if (W >= kSumTouchSpreadMinW && m[q] == 0) line = (4u * ((r0 + q) & 1u) - (a >> 7)) & 7u;
                 if (own_hi && (m[q] != 0 || off + 32 + 128 * uint64_t(line) <= hi))
                     h[q] = ld16<false>(gp + 1 + 8 * line);
