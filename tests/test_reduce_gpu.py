@@ -333,6 +333,29 @@ def test_streamed_sums_with_partly_filled_groups(gpu, W):
     gc.run_reduce_all_paths(placed, "streamed W=%d bf16" % W, paths=(rog.ROG_PATH_AUTO,))
 
 
+@pytest.mark.parametrize("W,in_offs,tail", [
+    (4, (0, 64, 8, 200), 48),
+    (6, (0, 0, 64, 0, 128, 448), 400),
+    (8, (0, 64, 128, 8, 0, 72, 200, 16), 48),
+    (8, (0, 1, 64, 3, 0, 8, 5, 192), 400)],
+    ids=["W4_aligned", "W6_aligned", "W8_aligned", "W8_mixed"])
+def test_streamed_aligned_sums_with_a_short_last_chunk(gpu, W, in_offs, tail):
+    """Streamed sums (just past 128 MiB of sources) whose aligned sources sit
+    on assorted 128-byte line places, the body ending `tail` bytes into its
+    last 1 KiB chunk: from W = 4 the last lane of each wave reads an aligned
+    source's granule of the next chunk at a line chosen by rank, inside the
+    body only; the mixed case has misaligned sources beside aligned ones.
+    Source 0 sits 64 bytes past a line (the guard), so the body starts 64
+    bytes in.  Every element against the oracle."""
+    n = ((128 << 20) // (2 * W) // 512 + 1) * 512 + (64 + tail) // 2
+    assert (2 * n - 64) % 1024 == tail and wl.GUARD == 64
+    payloads = wl.reduce_payloads(700 + W + sum(in_offs), W, n, "bf16")
+    placed = gc.PlacedReduce(payloads, in_offs, 0, "bf16", gpu)
+    plan = rog.rog_reduce_plan(placed.srcs, placed.out)
+    assert plan["path"] == "multi_wg" and plan["nt_loads"] and plan["shifted_loads"]
+    gc.run_reduce_all_paths(placed, "streamed aligned W=%d offs=%s" % (W, in_offs), paths=(rog.ROG_PATH_AUTO,))
+
+
 def test_largest_sum(gpu):
     """A sum at the top of the size range: W = 2 bf16 sources of 2^35 - 64
     elements (an output of 2^36 - 128 bytes), the sources one element off the
