@@ -928,6 +928,33 @@ def hbm_from_runtime(device_index):
     return vals
 
 
+def device_env(torch, device):
+    """What the figures were measured on: the GPU's architecture name and
+    compute-unit count, the HIP runtime's version, torch's own versions, and
+    the digest of the gather kernels' sources the traffic figure is tied to."""
+    env = {}
+    try:
+        props = torch.cuda.get_device_properties(device)
+        env["gcn_arch"] = getattr(props, "gcnArchName", None)
+        env["compute_units"] = props.multi_processor_count
+        env["hbm_bytes"] = props.total_memory
+    except Exception as e:   # the line is still printed without them
+        env["device_error"] = str(e)
+    try:
+        from deterministic_collective_movement_amd import rog
+        paths = sorted(rog._hip_runtimes_mapped())
+        if len(paths) == 1:
+            v = ctypes.c_int(0)
+            if ctypes.CDLL(paths[0]).hipRuntimeGetVersion(ctypes.byref(v)) == 0:
+                env["hip_runtime_version"] = v.value
+    except Exception as e:
+        env["hip_error"] = str(e)
+    env["torch"] = torch.__version__
+    env["torch_hip"] = getattr(torch.version, "hip", None)
+    env["gather_kernel_sources_sha256"] = kernel_source_digest()
+    return env
+
+
 def host_cpu():
     """Model name and the number of cores this process may run on."""
     model = None
@@ -1110,6 +1137,7 @@ def main(argv=None):
                                                           max(2, args.warmup // 2))[0]}
         cpu = None
     extras["device"] = torch.cuda.get_device_name(device)
+    extras["env"] = device_env(torch, device)
     extras["hbm_from_runtime"] = hbm_from_runtime(device.index or 0)
     config = {"workload": "rank-ordered gather of W=8 aligned bf16 payloads of 64 MiB into a 512 MiB "
                           "output (1 GiB moved per step)",
