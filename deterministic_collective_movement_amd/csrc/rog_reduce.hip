@@ -22,8 +22,11 @@
 // source as aligned granules, each lane rebuilding its bytes from its own
 // granule and the next lane's, as the PEER gather does (measured faster there
 // at every alignment, and mostly slower with cached loads), with 2, 4 or 8
-// sources' granules in flight by W (sum_granule_group).  Multi-WG: one wave
-// per 1 KiB chunk of the body, chunks handed to the XCDs in runs
+// sources' granules in flight by W (sum_granule_group); the last lane of each
+// wave reads one granule per source with a cached load, which for an aligned
+// source of a sum of four or more (it needs none) is aimed so that those
+// lines alternate between two 128-byte places of a 1 KiB block by rank.
+// Multi-WG: one wave per 1 KiB chunk of the body, chunks handed to the XCDs in runs
 // (xcd_grouped); single-WG: one workgroup strides over the whole output;
 // batch (rog_reduce_many): every tensor's chunks in one launch.  Bandwidth
 // bound: (W + 1) * count * esize bytes per sum.
