@@ -103,9 +103,55 @@ def latency_native(timeout_s=120):
     return json.loads(r.stdout)
 
 
+def launch_floor_native(timeout_s=60):
+    """Run the launch-floor harness (``bench_floor``, built beside
+    ``bench_native``) in a child process: per kernel (null, load, store) and
+    grid, the µs per launch eagerly and replayed back to back from a graph."""
+    import subprocess
+    if not os.path.exists(FLOOR_BIN):
+        return {"error": "bench_floor not built"}
+    try:
+        r = subprocess.run([FLOOR_BIN], capture_output=True, text=True, timeout=timeout_s)
+    except subprocess.TimeoutExpired:
+        return {"error": "timed out"}
+    if r.returncode != 0:
+        return {"error": "exit %d: %s" % (r.returncode, r.stderr.strip()[-200:])}
+    return [json.loads(line) for line in r.stdout.splitlines() if line.strip()]
+
+
 # ---------------------------------------------------------------------------
 # Pure helpers (CPU-testable)
 # ---------------------------------------------------------------------------
+
+def one_launch_bound(rows, floor_us, lo_mib=128, hi_mib=512):
+    """The best a cold gather of each ``bandwidth_sweep`` row could do with one
+    launch per gather: its bytes at the cold streaming rate the same sweep
+    measures between ``lo_mib`` and ``hi_mib`` of output (difference of the
+    times per gather, per W), plus ``floor_us``, the cost of an empty launch
+    back to back.  Per W: the rate, and per row the bound in µs and in % of
+    the peak beside the measured cold figure."""
+    by_w = {}
+    for r in rows:
+        by_w.setdefault(r["W"], {})[r["out_MiB"]] = r
+    out = {"floor_us_per_launch": round(floor_us, 3), "cold_stream_GBps": {}, "rows": []}
+    for W, rs in sorted(by_w.items()):
+        if lo_mib not in rs or hi_mib not in rs:
+            continue
+        lo, hi = rs[lo_mib], rs[hi_mib]
+        dt_us = hi["cold_us_per_gather"] - lo["cold_us_per_gather"]
+        if dt_us <= 0:
+            continue
+        rate = 2 * (hi_mib - lo_mib) * (1 << 20) / (dt_us * 1e3)          # GB/s
+        out["cold_stream_GBps"][str(W)] = round(rate, 1)
+        for mib in sorted(rs):
+            moved = 2 * mib * (1 << 20)
+            bound_us = moved / (rate * 1e3) + floor_us
+            out["rows"].append({"W": W, "out_MiB": mib, "bound_us": round(bound_us, 2),
+                                "bound_pct_of_peak": round(100 * moved / (bound_us * 1e3) / PEAK_HBM_GBPS, 1),
+                                "cold_us_per_gather": rs[mib]["cold_us_per_gather"],
+                                "cold_pct_of_peak": rs[mib]["cold_pct_of_peak"]})
+    return out
+
 
 def percentile(xs, q):
     """Linear-interpolated percentile (q in [0, 100]) of a non-empty sequence."""
@@ -1116,6 +1162,15 @@ def main(argv=None):
                                             max(BATCH_WARMUP, args.warmup))
         extras["d2d_copy_ceiling"] = d2d_ceiling(torch, device, case.W * case.S, 20, 3)
         extras["bandwidth_sweep"] = bandwidth_sweep(torch, rog, device, SWEEP_CALLS)
+        if not args.no_native:
+            # the empty launch's cost back to back (graph replay, grids of up to
+            # 1024 workgroups) bounds what any one launch per gather can reach
+            floor = launch_floor_native()
+            null = [x["graph_us_per_launch"] for x in floor if x["kernel"] == "null" and x["grid"] <= 1024] \
+                if isinstance(floor, list) else []
+            extras["bandwidth_sweep_bound"] = (one_launch_bound(extras["bandwidth_sweep"], statistics.median(null))
+                                               if null else {"error": floor.get("error", "no null rows")
+                                                             if isinstance(floor, dict) else "no null rows"})
         # the same at byte offsets 1 (sources) and 3 (output): the PEER kernel
         extras["bandwidth_sweep_misaligned"] = bandwidth_sweep(torch, rog, device, SWEEP_CALLS, ws=(8,),
                                                                offsets=(1, 3))

@@ -209,3 +209,32 @@ def test_latency_legs_time_a_fixed_hundred_calls():
     for fn in (bench.latency_sweep, bench.reduce_latency, bench.launch_floor):
         params = inspect.signature(fn).parameters
         assert params["steps"].default == bench.LATENCY_CALLS == 100
+
+
+def test_one_launch_bound_recovers_the_stream_rate_and_the_floor():
+    """Gathers whose cold time is exactly floor + bytes / rate: the bound finds
+    that rate from the 128 and 512 MiB rows and puts every row at its own time;
+    a row slower than the bound stays above it."""
+    import bench
+    rate, floor = 6800.0, 1.65          # GB/s, µs
+    rows = []
+    for W in (2, 8):
+        for mib in (64, 128, 256, 512):
+            moved = 2 * mib * (1 << 20)
+            t = floor + moved / (rate * 1e3) + (0.9 if mib == 64 else 0.0)   # 64 MiB: 0.9 µs of ramp
+            rows.append({"W": W, "out_MiB": mib, "cold_us_per_gather": t,
+                         "cold_pct_of_peak": 100 * moved / (t * 1e3) / bench.PEAK_HBM_GBPS})
+    b = bench.one_launch_bound(rows, floor)
+    assert b["floor_us_per_launch"] == 1.65
+    assert set(b["cold_stream_GBps"]) == {"2", "8"}
+    assert all(abs(v - rate) < 0.2 for v in b["cold_stream_GBps"].values())
+    assert len(b["rows"]) == 8
+    for r in b["rows"]:
+        moved = 2 * r["out_MiB"] * (1 << 20)
+        assert abs(r["bound_us"] - (floor + moved / (rate * 1e3))) < 0.01
+        if r["out_MiB"] == 64:
+            assert r["bound_pct_of_peak"] > r["cold_pct_of_peak"]
+        else:
+            assert abs(r["bound_pct_of_peak"] - r["cold_pct_of_peak"]) < 0.1
+    # rows without both reference sizes give no rate
+    assert bench.one_launch_bound([x for x in rows if x["out_MiB"] != 512], floor)["rows"] == []
