@@ -24,7 +24,7 @@
 // at every alignment, and mostly slower with cached loads), with 2, 4 or 8
 // sources' granules in flight by W (sum_granule_group); the last lane of each
 // wave reads one granule per source with a cached load, which for an aligned
-// source of a sum of four or more (it needs none) is aimed so that those
+// source of a sum of three or more (it needs none) is aimed so that those
 // lines alternate between two 128-byte places of a 1 KiB block by rank.
 // Multi-WG: one wave per 1 KiB chunk of the body, chunks handed to the XCDs in runs
 // (xcd_grouped); single-WG: one workgroup strides over the whole output;
@@ -103,11 +103,12 @@ __device__ __forceinline__ vec16 narrow(const float (&a)[Elem<DT>::kPerVec]) {
 // by rank from this many sources on (0: never), else to the next chunk's
 // first granule.  Measured over W = 2 to 16, sources on one line place and
 // buffers no cache holds: W = 5 to 16 gained 4-9 %, W = 4 3-4 % (0 to -3 %
-// back to back over two boxes); W = 2 lost 1-2 %.  Placements already spread
-// stayed within about 1 %.  W = 2 and 3 take the smaller granule groups,
-// which leave it out.
+// back to back over two boxes), W = 3 4 % (1-2 % lost where the three
+// sources already sat on distinct places); W = 2 lost 1-2 %.  Other
+// placements stayed within about 1 % from W = 4 on.  W = 2 takes the
+// two-source granule group, which leaves it out.
 #ifndef ROG_SUM_TOUCH_SPREAD_MIN_W
-#define ROG_SUM_TOUCH_SPREAD_MIN_W 4
+#define ROG_SUM_TOUCH_SPREAD_MIN_W 3
 #endif
 constexpr uint32_t kSumTouchSpreadMinW = ROG_SUM_TOUCH_SPREAD_MIN_W;
 // Waves per SIMD the multi-WG sum kernels are compiled for at least: the
@@ -205,7 +206,7 @@ __device__ __forceinline__ vec16 sum_vec_wave(const void *const *src, uint32_t W
                 // One conditional load with a uniform offset: split into two
                 // branches, the loads waited for one another.
                 uint32_t line = 0;
-                if constexpr (G >= 8 && kSumTouchSpreadMinW != 0)   // smaller groups serve W < 4 only
+                if constexpr (G >= 4 && kSumTouchSpreadMinW != 0)   // the group of 2 serves W <= 2 only
                     if (W >= kSumTouchSpreadMinW && m[q] == 0) line = (4u * ((r0 + q) & 1u) - (a >> 7)) & 7u;
                 if (own_hi && (m[q] != 0 || off + 32 + 128 * uint64_t(line) <= hi))
                     h[q] = ld16<false>(gp + 1 + 8 * line);
