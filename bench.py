@@ -20,10 +20,12 @@ from a HIP graph of 100 calls, and timed from C by bench_native.c (a child
 process), next to the eager floor of one tiny torch kernel timed the same way;
 the batched gather (16 tensors, W = 4, one launch, after 40 untimed calls); the device-to-device copy
 ceiling and the HBM figure the HIP runtime reports; aligned gathers with
-2 - 512 MiB outputs, warm and with rotating buffer sets (cold); the
+2 - 512 MiB outputs, warm and with rotating buffer sets (cold), beside the
+bound one launch per gather allows (from bench_floor, a child process); the
 rank-ordered sum (rog_reduce: W = 8 bf16 payloads of 64 MiB, aligned and one
-element off, the pages' per-rank sizes of 1 KiB - 4 MiB at W = 2 and 8, and a
-16-tensor rog_reduce_many); the headline gather and the W = 8 sum in four
+element off, the pages' per-rank sizes of 1 KiB - 4 MiB at W = 2 and 8, a
+16-tensor rog_reduce_many, and W = 8 and 3 with the sources placed three ways
+in memory); the headline gather and the W = 8 sum in four
 cache states (back to back on one set, over four rotating sets, and after a
 1 GiB read-only or read-write pass over other memory); and the CPU oracle on bounded samples of the
 headline gather and of the large sum (the CPU-baseline legs, the only ones
@@ -698,6 +700,80 @@ def reduce_sweep(torch, rog, device, calls, footprint=SWEEP_FOOTPRINT):
     return rows
 
 
+SUM_PLACEMENT_CASES = (8, 3)                          # W
+SUM_PLACEMENT_STRIDES = (None, 512, 128)              # None: one allocation per source
+SUM_PLACEMENT_SOURCE_MIB = 64                         # per source
+
+
+def sum_placements(torch, rog, device, calls=SWEEP_CALLS, footprint=SWEEP_FOOTPRINT):
+    """The rank-ordered sum of W aligned bf16 sources of 64 MiB (W = 8 and 3)
+    with the sources placed three ways: each in its own allocation (large
+    allocations start on 2 MiB boundaries, so every source sits on the same
+    128-byte place of a 1 KiB block), or carved from one allocation at strides
+    of 64 MiB + 512 bytes (places alternating between two) or + 128 bytes
+    (every source on its own place).  Timed warm (one set) and cold (rotating
+    sets spanning ``footprint`` bytes) over the same number of back-to-back
+    launches, as the other sweeps; sampled outputs of every set checked
+    against a float32 sum in rank order rounded once to bf16."""
+    lib = rog.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    g = torch.Generator(device=device)
+    g.manual_seed(31337)
+    n = (SUM_PLACEMENT_SOURCE_MIB << 20) // 2
+    rows = []
+    for W in SUM_PLACEMENT_CASES:
+        K = max(2, footprint // ((W + 1) * n * 2))
+        for stride in SUM_PLACEMENT_STRIDES:
+            sets = []
+            for _ in range(K):
+                if stride is None:
+                    keep = [torch.empty(n, dtype=torch.bfloat16, device=device) for _ in range(W)]
+                    srcs = keep
+                else:
+                    step = 2 * n + stride
+                    big = torch.empty(W * step, dtype=torch.uint8, device=device)
+                    keep = [big]
+                    srcs = [big[r * step: r * step + 2 * n].view(torch.bfloat16) for r in range(W)]
+                for x in srcs:
+                    x.copy_(torch.randn(n, device=device, generator=g))
+                out = torch.empty(n, dtype=torch.bfloat16, device=device)
+                sets.append((srcs, out, (ctypes.c_void_p * W)(*[x.data_ptr() for x in srcs]),
+                             ctypes.c_void_p(out.data_ptr()), keep))
+            places = [(x.data_ptr() >> 7) & 7 for x in sets[0][0]]
+
+            def run(seq):
+                for _, _, ptrs, o, _ in (seq * 2)[:max(K + 1, 10)]:
+                    if lib.rog_reduce(ptrs, W, n, rog.ROG_DTYPE_BF16, o, stream) != 0:
+                        raise RuntimeError("rog_reduce failed")
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _, _, ptrs, o, _ in seq:
+                    lib.rog_reduce(ptrs, W, n, rog.ROG_DTYPE_BF16, o, stream)
+                e1.record()
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) / len(seq)
+
+            n_calls = max(calls, 2 * K)
+            warm_ms = run([sets[0]] * n_calls)
+            cold_ms = run([sets[i % K] for i in range(n_calls)])
+            for srcs, out, _, _, _ in sets:
+                for lo in (0, n // 2, n - 4096):
+                    acc = srcs[0][lo:lo + 4096].float()
+                    for r in range(1, W):
+                        acc = acc + srcs[r][lo:lo + 4096].float()
+                    if not torch.equal(out[lo:lo + 4096].view(torch.int16), acc.to(torch.bfloat16).view(torch.int16)):
+                        raise AssertionError("placement sum W=%d stride %s wrong at element %d" % (W, stride, lo))
+            moved = (W + 1) * n * 2
+            rows.append({"W": W, "placement": "own allocations" if stride is None else "stride 64 MiB + %d B" % stride,
+                         "line_places": places, "sets": K, "calls": n_calls,
+                         "warm_GBps": round(gbps(moved, warm_ms), 1), "cold_GBps": round(gbps(moved, cold_ms), 1),
+                         "cold_pct_of_peak": round(100 * gbps(moved, cold_ms) / PEAK_HBM_GBPS, 1)})
+            del sets
+            torch.cuda.empty_cache()
+    return rows
+
+
 CACHE_STATE_SETS = 4
 CACHE_STATE_CALLS = 20
 CACHE_STATE_PASS_BYTES = 1 << 30   # 4 x the 256 MB Infinity Cache
@@ -1095,6 +1171,8 @@ def main(argv=None):
                     help="time only the rank-ordered sums' warm and cold sweep (W = 2, 3, 8), for counter runs")
     ap.add_argument("--cache-states-only", action="store_true",
                     help="time only the headline gather and W = 8 sum in the four cache states, for traces")
+    ap.add_argument("--sum-placements-only", action="store_true",
+                    help="time only the W = 8 and 3 sums with their sources placed three ways, for traces")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: --gpus %d is not supported (use --gpus 1)" % args.gpus,
@@ -1120,6 +1198,9 @@ def main(argv=None):
         return 0
     if args.cache_states_only:
         print(json.dumps({"cache_states": cache_states(torch, rog, device)}), flush=True)
+        return 0
+    if args.sum_placements_only:
+        print(json.dumps({"sum_placements": sum_placements(torch, rog, device)}), flush=True)
         return 0
     if args.reduce_sweep_only:
         print(json.dumps({"reduce_sweep": reduce_sweep(torch, rog, device, SWEEP_CALLS)}), flush=True)
@@ -1183,6 +1264,7 @@ def main(argv=None):
                             "latency": reduce_latency(torch, rog, wl, device),
                             "batched": reduce_batch(torch, rog, wl, device, BATCH_STEPS,
                                                     max(BATCH_WARMUP, args.warmup))}
+        extras["reduce"]["placements"] = sum_placements(torch, rog, device)
         extras["cache_states"] = cache_states(torch, rog, device)
         cpu = cpu_baseline(case, payloads, args.cpu_budget / 2)
         extras["reduce"]["cpu_baseline"] = reduce_cpu_baseline(rpayloads, rgot, min(2.5, args.cpu_budget / 4))
